@@ -1,0 +1,209 @@
+"""Seeded synthetic inputs: waveforms, clip lengths and random-init weights.
+
+This module only draws inputs.  It holds none of the encoder's arithmetic
+(no framing, transform, mel, norm or attention) and imports neither the HIP
+library nor the oracle, so both sides of a parity test can take their inputs
+from it.
+
+Workloads (all 16 kHz mono float32, weights N(0, 0.02^2), biases 0, gains 1):
+  * ``tiny``    1 x 1.0 s sinusoid mixture, 2 layers, float32 weights;
+  * ``clip30``  1 x 30 s sinusoid mixture, 32 layers, weights stored in bf16;
+  * ``batch64`` 64 clips of U{5 s .. 30 s} (80,000..480,000 samples), padded
+                to the longest; 32 layers, bf16 weights;
+  * ``long10m`` 1 x 600 s segment mixture, 32 layers, bf16 weights;
+  * ``hour``    1 x 3,600 s segment mixture, 32 layers, bf16 weights.
+
+Sinusoid mixture: three tones with frequencies U(100, 4000) Hz, amplitudes
+U(0.1, 0.3) and phases U(0, 2 pi), plus Gaussian noise of sigma 0.01.
+Segment mixture: segments of U(2, 8) s (whole samples) cycling tone mixture
+-> amplitude-modulated noise 0.1 (0.5 + 0.5 sin(2 pi f_m t + phi)) eps with
+f_m ~ U(2, 8) Hz -> silence 1e-4 eps -> tone mixture ...; the last segment is
+cut to the exact length.
+
+Weights are drawn tensor by tensor from ``numpy.random.default_rng`` seeded
+with (1234, layer + 1, tensor id), so a prefix of layers is the same draw whatever
+the total depth.  "Stored in bf16" means each drawn value is rounded to the
+nearest bfloat16 (ties to even) and kept as a float32 holding that value.
+"""
+
+import numpy as np
+
+SAMPLE_RATE = 16000
+D_MODEL = 1280
+N_HEADS = 10
+HEAD_DIM = 128
+FFN_DIM = 4 * D_MODEL
+IN_DIM = 1024
+WEIGHT_SEED = 1234
+WEIGHT_STD = 0.02
+
+WORKLOADS = {
+    # name: (audio seed, kind, n_layers, bf16 weights)
+    "tiny": (1, "tone", 2, False),
+    "clip30": (2, "tone", 32, True),
+    "batch64": (3, "tone_batch", 32, True),
+    "long10m": (4, "segments", 32, True),
+    "hour": (5, "segments", 32, True),
+}
+WORKLOAD_ORDER = ["tiny", "clip30", "batch64", "long10m", "hour"]
+
+_DURATION_S = {"tiny": 1.0, "clip30": 30.0, "long10m": 600.0, "hour": 3600.0}
+
+# (name, shape kind, layer-local id); order is fixed and never reused.
+_LAYER_TENSORS = [
+    ("ln1_g", "gain", 0), ("ln1_b", "bias_d", 1),
+    ("w_qkv", "w_qkv", 2), ("b_qkv", "bias_qkv", 3),
+    ("q_g", "gain_h", 4), ("q_b", "bias_h", 5),
+    ("k_g", "gain_h", 6), ("k_b", "bias_h", 7),
+    ("w_o", "w_o", 8), ("b_o", "bias_d", 9),
+    ("ln2_g", "gain", 10), ("ln2_b", "bias_d", 11),
+    ("w_up", "w_up", 12), ("b_up", "bias_f", 13),
+    ("w_down", "w_down", 14), ("b_down", "bias_d", 15),
+]
+
+
+def tone_mixture(rng, n):
+    """Three random tones plus N(0, 0.01^2) noise, n samples, float32."""
+    t = np.arange(n, dtype=np.float64) / SAMPLE_RATE
+    freqs = rng.uniform(100.0, 4000.0, size=3)
+    amps = rng.uniform(0.1, 0.3, size=3)
+    phases = rng.uniform(0.0, 2.0 * np.pi, size=3)
+    x = np.zeros(n, dtype=np.float64)
+    for f, a, p in zip(freqs, amps, phases):
+        x += a * np.sin(2.0 * np.pi * f * t + p)
+    x += 0.01 * rng.standard_normal(n)
+    return x.astype(np.float32)
+
+
+def _am_noise(rng, n):
+    t = np.arange(n, dtype=np.float64) / SAMPLE_RATE
+    fm = rng.uniform(2.0, 8.0)
+    ph = rng.uniform(0.0, 2.0 * np.pi)
+    env = 0.5 + 0.5 * np.sin(2.0 * np.pi * fm * t + ph)
+    return (0.1 * env * rng.standard_normal(n)).astype(np.float32)
+
+
+def _silence(rng, n):
+    return (1e-4 * rng.standard_normal(n)).astype(np.float32)
+
+
+def segment_mixture(rng, n):
+    """Cycling 2-8 s segments: tones, AM noise, near-silence; n samples."""
+    out = np.empty(n, dtype=np.float32)
+    makers = (tone_mixture, _am_noise, _silence)
+    pos, kind = 0, 0
+    while pos < n:
+        seg = int(rng.integers(2 * SAMPLE_RATE, 8 * SAMPLE_RATE + 1))
+        seg = min(seg, n - pos)
+        out[pos:pos + seg] = makers[kind](rng, seg)
+        pos += seg
+        kind = (kind + 1) % 3
+    return out
+
+
+def batch_lengths(seed=3, batch=64):
+    """Clip lengths for the 64-clip batch: uniform integers in [80,000, 480,000]."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(80_000, 480_000 + 1, size=batch).astype(np.int64)
+
+
+def workload_audio(name):
+    """(audio [B, N_max] float32 zero-padded, lengths int64 [B]) for a workload."""
+    seed, kind, _, _ = WORKLOADS[name]
+    if kind == "tone_batch":
+        lengths = batch_lengths(seed)
+        audio = np.zeros((len(lengths), int(lengths.max())), dtype=np.float32)
+        for b, n in enumerate(lengths):
+            audio[b, :n] = tone_mixture(np.random.default_rng((seed, b)), int(n))
+        return audio, lengths
+    n = int(round(_DURATION_S[name] * SAMPLE_RATE))
+    rng = np.random.default_rng(seed)
+    x = tone_mixture(rng, n) if kind == "tone" else segment_mixture(rng, n)
+    return x[None, :], np.array([n], dtype=np.int64)
+
+
+def custom_audio(lengths, seed, kind="tone"):
+    """Padded batch of tone (or segment) mixtures with the given lengths."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    nmax = int(lengths.max()) if len(lengths) else 0
+    audio = np.zeros((len(lengths), nmax), dtype=np.float32)
+    maker = tone_mixture if kind == "tone" else segment_mixture
+    for b, n in enumerate(lengths):
+        if n > 0:
+            audio[b, :n] = maker(np.random.default_rng((seed, b)), int(n))
+    return audio, lengths
+
+
+def round_bf16(a, inplace=False):
+    """Nearest bfloat16 value (ties to even) of float32 a, kept as float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if not inplace:
+        a = a.copy()
+    if not np.all(np.isfinite(a)):
+        raise ValueError("round_bf16 expects finite values")
+    u = a.view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += lsb
+    u += np.uint32(0x7FFF)
+    u &= np.uint32(0xFFFF0000)
+    return a
+
+
+def _shape(kind, d, dh, f, in_dim):
+    return {
+        "gain": (d,), "bias_d": (d,), "gain_h": (dh,), "bias_h": (dh,),
+        "w_qkv": (3 * d, d), "bias_qkv": (3 * d,), "w_o": (d, d),
+        "w_up": (f, d), "bias_f": (f,), "w_down": (d, f), "w_in": (d, in_dim),
+    }[kind]
+
+
+def _draw(kind, shape, rng, perturb):
+    if kind.startswith("w_"):
+        out = np.empty(shape, dtype=np.float32)
+        rng.standard_normal(out=out, dtype=np.float32)
+        out *= np.float32(WEIGHT_STD)
+        return out
+    if kind.startswith("gain"):
+        if perturb:
+            return (1.0 + 0.1 * rng.standard_normal(shape)).astype(np.float32)
+        return np.ones(shape, dtype=np.float32)
+    if perturb:
+        return (0.1 * rng.standard_normal(shape)).astype(np.float32)
+    return np.zeros(shape, dtype=np.float32)
+
+
+def make_weights(n_layers, bf16=True, perturb=False, d=D_MODEL, dh=HEAD_DIM,
+                 ffn=FFN_DIM, in_dim=IN_DIM, seed=WEIGHT_SEED):
+    """Random-init weights as a dict (see the oracle's encoder for the keys).
+
+    ``perturb`` replaces the zero biases and unit gains by N(0, 0.1^2) and
+    1 + N(0, 0.1^2) draws, so that every bias and affine term is exercised.
+    """
+    def tensor(layer, tid, kind):
+        # layer -1 holds the tensors outside the stack; SeedSequence needs >= 0
+        key = (seed, layer + 1, tid)
+        if perturb and not kind.startswith("w_"):
+            key = key + (1,)
+        rng = np.random.default_rng(key)
+        a = _draw(kind, _shape(kind, d, dh, ffn, in_dim), rng, perturb)
+        return round_bf16(a, inplace=True) if bf16 else a
+
+    w = {
+        "w_in": tensor(-1, 0, "w_in"),
+        "b_in": tensor(-1, 1, "bias_d"),
+        "lnf_g": tensor(-1, 2, "gain"),
+        "lnf_b": tensor(-1, 3, "bias_d"),
+        "layers": [],
+    }
+    for layer in range(n_layers):
+        w["layers"].append({name: tensor(layer, tid, kind)
+                            for name, kind, tid in _LAYER_TENSORS})
+    return w
+
+
+def workload_weights(name, n_layers=None, perturb=False):
+    """Weights for a workload (optionally only its first n_layers layers)."""
+    _, _, depth, bf16 = WORKLOADS[name]
+    return make_weights(depth if n_layers is None else n_layers, bf16=bf16,
+                        perturb=perturb)

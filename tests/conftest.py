@@ -1,0 +1,32 @@
+"""Shared pytest set-up: the ``gpu`` marker and the repository on sys.path."""
+
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line(
+        "markers", "gpu: needs an MI355X (runs the HIP library through its C ABI)")
+
+
+def read_golden(name):
+    """key -> float from a ``tests/golden`` text fixture (comments after '#')."""
+    out = {}
+    with open(os.path.join(ROOT, "tests", "golden", name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                key, val = line.split()
+                out[key] = float(val)
+    return out
+
+
+@pytest.fixture(scope="session")
+def page_figures():
+    return read_golden("page_figures.txt")
