@@ -1,0 +1,203 @@
+/*
+ * speech_encoder.h -- C ABI of the MI355X (gfx950) speech-encoder library
+ * (libspeech_encoder.so).
+ *
+ * What it computes.  The page "Nemotron 3.5 Transcribe: From Recorded Speech to
+ * Dataset Audits" (flozi.net), section "How audio and speakers reach the
+ * language model", describes the ASR encoder branch: a 16 kHz mono waveform is
+ * turned into 128 log-mel features (25 ms Hann window, 512-point FFT, 10 ms
+ * hop); eight successive frames are stacked (about 100 frames/s down to 12.5
+ * positions/s, 80 ms per position) and projected to width 1,280; 32
+ * Transformer layers with ten heads, QK normalisation, rotary position
+ * embeddings and feed-forward expansion four produce one continuous
+ * 1,280-wide vector per position.  The section "How one hour fits into 65,536
+ * positions" gives 12.5 positions per second; the gmlx page's Limits table
+ * and the first page bound a recording at one hour.
+ *
+ * Where the page is silent this library reads it as follows (the CPU oracle
+ * used by the tests makes the same choices): frame t = samples
+ * [160 t, 160 t + 400), F = 1 + floor((N - 400) / 160) frames (0 if N < 400);
+ * periodic Hann window; power spectrum |X_k|^2, k = 0..256; Slaney mel bank
+ * with peak-1 triangles; natural log of (energy + 2^-24); P = ceil(F / 8)
+ * positions with frame-major stacking and zero tail frames; linear maps with
+ * bias in the [out, in] layout; pre-norm blocks with a final LayerNorm;
+ * LayerNorm with biased variance and eps 1e-5; QK-norm = LayerNorm over each
+ * head's 128 dims (gain/bias shared by heads), before rotation; rotation of
+ * pairs (i, i + 64) by p * 10000^(-i/64); bidirectional attention over the
+ * whole clip; FFN 1280 -> 5120 -> 1280 with exact-erf GELU.
+ *
+ * Precision.  GEMM and attention operands are bf16 with fp32 accumulation;
+ * the residual stream, norm statistics, softmax and rotation run in fp32; the
+ * frontend runs in fp32 with float64-built tables.
+ *
+ * Conventions for every call below.
+ *   - Device pointers are HIP device memory on the current device; host
+ *     pointers are ordinary host memory.  "stream" is a hipStream_t on which
+ *     all device work of the call is enqueued; calls return without waiting
+ *     for that work (except enc_create, which is synchronous).
+ *   - Every argument and size check happens before anything is enqueued: a
+ *     call that returns an error has not written any output.
+ *   - A return value other than ENC_OK leaves a message for
+ *     enc_last_error() (per thread).  No C++ exception crosses the ABI.
+ *   - One context serves one stream / host thread at a time.
+ */
+#ifndef SPEECH_ENCODER_H
+#define SPEECH_ENCODER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENC_ABI_VERSION 1
+
+/* Status codes. */
+#define ENC_OK 0
+#define ENC_ERR_ARG 1       /* NULL pointer, bad version, batch < 1, length < 0 ... */
+#define ENC_ERR_TOO_LONG 2  /* a clip longer than one hour (57,600,000 samples)      */
+#define ENC_ERR_NOMEM 3     /* device memory (or the workspace cap) does not fit     */
+#define ENC_ERR_HIP 4       /* a HIP runtime call or kernel launch failed            */
+
+/* Element type of the weight tensors handed to enc_create. */
+#define ENC_F32 0
+#define ENC_BF16 1
+
+/* Model constants. */
+#define ENC_D_MODEL 1280
+#define ENC_N_HEADS 10
+#define ENC_HEAD_DIM 128
+#define ENC_FFN_DIM 5120
+#define ENC_N_MELS 128
+#define ENC_STACK 8
+#define ENC_MAX_SAMPLES 57600000LL
+
+/* One Transformer layer: DEVICE pointers, element type enc_weights.dtype,
+ * linear weights row-major [out, in]. */
+typedef struct enc_layer_weights {
+  const void* ln1_g;   /* [1280]        pre-attention LayerNorm gain          */
+  const void* ln1_b;   /* [1280]        and bias                              */
+  const void* w_qkv;   /* [3840, 1280]  rows 0..1279 Q, 1280..2559 K, rest V  */
+  const void* b_qkv;   /* [3840]                                              */
+  const void* q_g;     /* [128]         QK-norm gain/bias for q (all heads)   */
+  const void* q_b;     /* [128]                                               */
+  const void* k_g;     /* [128]         QK-norm gain/bias for k (all heads)   */
+  const void* k_b;     /* [128]                                               */
+  const void* w_o;     /* [1280, 1280]  attention output projection           */
+  const void* b_o;     /* [1280]                                              */
+  const void* ln2_g;   /* [1280]        pre-FFN LayerNorm                     */
+  const void* ln2_b;   /* [1280]                                              */
+  const void* w_up;    /* [5120, 1280]  FFN expansion                         */
+  const void* b_up;    /* [5120]                                              */
+  const void* w_down;  /* [1280, 5120]  FFN contraction                       */
+  const void* b_down;  /* [1280]                                              */
+} enc_layer_weights;
+
+typedef struct enc_weights {
+  int32_t abi_version;              /* must be ENC_ABI_VERSION                 */
+  int32_t n_layers;                 /* >= 1 (32 for the full encoder)          */
+  int32_t dtype;                    /* ENC_F32 or ENC_BF16, for every tensor   */
+  int32_t reserved;                 /* 0                                       */
+  const void* w_in;                 /* [1280, 1024] stacked-frame projection   */
+  const void* b_in;                 /* [1280]                                  */
+  const enc_layer_weights* layers;  /* HOST array of n_layers entries          */
+  const void* lnf_g;                /* [1280] final LayerNorm                  */
+  const void* lnf_b;                /* [1280]                                  */
+} enc_weights;
+
+typedef struct enc_ctx enc_ctx;
+
+/*
+ * enc_create: copy the weights into a new context.
+ *   w    host struct describing device tensors (see enc_weights).  Matrices
+ *        are converted to bf16 (round to nearest even) and biases/gains to
+ *        fp32 in context-owned device memory; the caller may free its tensors
+ *        once the call returns.  The context also builds its constant tables
+ *        (window, FFT twiddles, mel bank, rotation cos/sin) on the host in
+ *        float64 and uploads them as fp32.
+ *   out  receives the handle (host pointer).
+ * Synchronous.  Errors: ENC_ERR_ARG (NULL, wrong abi_version, n_layers < 1,
+ * unknown dtype, NULL tensor), ENC_ERR_NOMEM, ENC_ERR_HIP.
+ */
+int enc_create(const enc_weights* w, enc_ctx** out);
+
+/*
+ * enc_logmel: log-mel features of a batch of clips (frontend only).
+ *   audio    DEVICE fp32 [batch, N_max], row-major, N_max = max(lengths);
+ *            clip b is audio[b, 0 : lengths[b]], the rest is ignored.
+ *   lengths  HOST int64 [batch], samples per clip, 0 <= lengths[b] <= 57,600,000.
+ *   out      DEVICE fp32 [batch, F_max, 128], F_max = F(N_max); frames
+ *            t >= F(lengths[b]) are written as 0.0.
+ * Errors: ENC_ERR_ARG (NULL, batch < 1, negative length), ENC_ERR_TOO_LONG,
+ * ENC_ERR_HIP.  audio may be NULL only if N_max == 0.
+ */
+int enc_logmel(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+               float* out, hipStream_t stream);
+
+/*
+ * enc_forward: the whole encoder, waveform to embeddings.
+ *   audio, lengths as for enc_logmel.
+ *   out_embeddings  DEVICE bf16 [batch, P_max, 1280], P_max = ceil(F_max / 8);
+ *            row p of clip b is its position-p embedding for p < P_b =
+ *            ceil(F(lengths[b]) / 8) and 0 otherwise.  Each clip is encoded
+ *            as its own sequence: its rows do not depend on the other clips
+ *            or on the padding.
+ * The context keeps a workspace sized by the batch's total positions; a call
+ * that needs a larger one first waits for the stream, then reallocates.  The
+ * environment variable ENC_WORKSPACE_CAP_BYTES, read at each call, caps the
+ * workspace: a call that would need more returns ENC_ERR_NOMEM, as does one
+ * whose allocation fails.  Errors: as enc_logmel, plus ENC_ERR_NOMEM.
+ */
+int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                void* out_embeddings, hipStream_t stream);
+
+/* enc_destroy: wait for the context's device work and free it.  NULL is a
+ * no-op. */
+void enc_destroy(enc_ctx* ctx);
+
+/*
+ * enc_shapes: host-only.  F_max and P_max (HOST int64 out-pointers) of a
+ * batch.  Errors: ENC_ERR_ARG, ENC_ERR_TOO_LONG.
+ */
+int enc_shapes(const int64_t* lengths, int32_t batch, int64_t* f_max, int64_t* p_max);
+
+/*
+ * enc_workspace_bytes: host-only.  Device bytes enc_forward's workspace needs
+ * for this batch (independent of n_layers >= 1).  Errors: ENC_ERR_ARG,
+ * ENC_ERR_TOO_LONG.
+ */
+int enc_workspace_bytes(int32_t n_layers, const int64_t* lengths, int32_t batch, size_t* bytes);
+
+/* enc_last_error: message of this thread's last failed call ("" if none). */
+const char* enc_last_error(void);
+
+/*
+ * Kernel timing for measurement.  enc_profile_kernel(ctx, id) brackets every
+ * launch of kernel class id (ENC_K_*) made by later enc_forward calls with a
+ * pair of HIP events on the call's stream; id = -1 turns this off.
+ * enc_profile_read(ctx, &launches, &total_ms) waits for those events and
+ * returns the number of bracketed launches and their summed duration, then
+ * clears the record.  Errors: ENC_ERR_ARG, ENC_ERR_HIP.
+ */
+#define ENC_K_FRONTEND 0
+#define ENC_K_GEMM_IN 1
+#define ENC_K_LAYERNORM 2
+#define ENC_K_GEMM_QKV 3
+#define ENC_K_QKNORM_ROPE 4
+#define ENC_K_ATTENTION 5
+#define ENC_K_GEMM_O 6
+#define ENC_K_GEMM_UP 7
+#define ENC_K_GEMM_DOWN 8
+#define ENC_K_FINAL_NORM 9
+#define ENC_K_COUNT 10
+int enc_profile_kernel(enc_ctx* ctx, int32_t kernel_id);
+int enc_profile_read(enc_ctx* ctx, int64_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEECH_ENCODER_H */

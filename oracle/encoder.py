@@ -100,46 +100,61 @@ def attention(q, k, v, block=1024):
     return out
 
 
-def encoder_layer(x, lw):
-    """One pre-norm Transformer layer on x [T, d] (float32)."""
+def encoder_layer(x, lw, rows=None):
+    """One pre-norm Transformer layer on x [T, d] (float32).
+
+    ``rows`` (optional index array) returns only those output rows; keys and
+    values still come from every position, so each returned row equals the
+    corresponding row of the full computation.
+    """
     x = _f32(x)
     t, d = x.shape
     dh = len(lw["q_g"])
     n_heads = d // dh
+    qrows = np.arange(t) if rows is None else np.asarray(rows)
     a = layer_norm(x, lw["ln1_g"], lw["ln1_b"])
-    qkv = linear(a, lw["w_qkv"], lw["b_qkv"])
+    w_qkv, b_qkv = _f32(lw["w_qkv"]), _f32(lw["b_qkv"])
+    kv = linear(a, w_qkv[d:], b_qkv[d:])
+    qx = linear(a[qrows], w_qkv[:d], b_qkv[:d])
     cos, sin = rope_tables(t, dh)
     heads = []
     for h in range(n_heads):
-        q = qkv[:, h * dh:(h + 1) * dh]
-        k = qkv[:, d + h * dh:d + (h + 1) * dh]
-        v = qkv[:, 2 * d + h * dh:2 * d + (h + 1) * dh]
-        q = apply_rope(layer_norm(q, lw["q_g"], lw["q_b"]), cos, sin)
+        q = qx[:, h * dh:(h + 1) * dh]
+        k = kv[:, h * dh:(h + 1) * dh]
+        v = kv[:, d + h * dh:d + (h + 1) * dh]
+        q = apply_rope(layer_norm(q, lw["q_g"], lw["q_b"]), cos[qrows], sin[qrows])
         k = apply_rope(layer_norm(k, lw["k_g"], lw["k_b"]), cos, sin)
         heads.append(attention(q, k, v))
     o = np.concatenate(heads, axis=-1)
-    x = x + linear(o, lw["w_o"], lw["b_o"])
-    a = layer_norm(x, lw["ln2_g"], lw["ln2_b"])
+    xr = x[qrows] + linear(o, lw["w_o"], lw["b_o"])
+    a = layer_norm(xr, lw["ln2_g"], lw["ln2_b"])
     u = gelu(linear(a, lw["w_up"], lw["b_up"]))
-    return x + linear(u, lw["w_down"], lw["b_down"])
+    return xr + linear(u, lw["w_down"], lw["b_down"])
 
 
-def encode_from_logmel(feats, weights, n_layers=None):
-    """Stack, project and run the encoder on one clip's log-mel [F, 128]."""
+def encode_from_logmel(feats, weights, n_layers=None, rows=None):
+    """Stack, project and run the encoder on one clip's log-mel [F, 128].
+
+    ``rows`` limits the output (and the last layer's queries) to those
+    positions; earlier layers always run on every position.
+    """
     layers = weights["layers"] if n_layers is None else weights["layers"][:n_layers]
     s = stack_frames(feats)
     d = weights["w_in"].shape[0]
     if s.shape[0] == 0:
         return np.zeros((0, d), dtype=np.float32)
     x = linear(s, weights["w_in"], weights["b_in"])
-    for lw in layers:
-        x = encoder_layer(x, lw)
+    if rows is not None and not layers:
+        x = x[np.asarray(rows)]
+    for i, lw in enumerate(layers):
+        last = i == len(layers) - 1
+        x = encoder_layer(x, lw, rows if last else None)
     return layer_norm(x, weights["lnf_g"], weights["lnf_b"])
 
 
-def encode(x, weights, n_layers=None):
-    """Embeddings [ceil(F/8), d] of one clip's waveform x."""
-    return encode_from_logmel(logmel(x), weights, n_layers)
+def encode(x, weights, n_layers=None, rows=None):
+    """Embeddings [ceil(F/8), d] of one clip's waveform x (or only ``rows``)."""
+    return encode_from_logmel(logmel(x), weights, n_layers, rows)
 
 
 def encode_batch(audio, lengths, weights, n_layers=None):

@@ -1,0 +1,234 @@
+"""ctypes binding of libspeech_encoder.so (the C ABI in include/speech_encoder.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's kernels.  The
+library is required: if it is missing this module raises instead of falling
+back to anything else.
+
+Function names follow the C calls: ``enc_create``, ``enc_logmel``,
+``enc_forward``, ``enc_destroy``, ``enc_shapes``, ``enc_workspace_bytes``,
+``enc_last_error``, ``enc_profile_kernel``, ``enc_profile_read``.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libspeech_encoder.so")
+
+ENC_OK, ENC_ERR_ARG, ENC_ERR_TOO_LONG, ENC_ERR_NOMEM, ENC_ERR_HIP = 0, 1, 2, 3, 4
+ENC_F32, ENC_BF16 = 0, 1
+ENC_ABI_VERSION = 1
+D_MODEL, N_MELS = 1280, 128
+
+KERNELS = ["frontend", "gemm_in", "layernorm", "gemm_qkv", "qknorm_rope", "attention",
+           "gemm_o", "gemm_up", "gemm_down", "final_norm"]
+
+EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_destroy", "enc_shapes",
+           "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
+
+_LAYER_FIELDS = ["ln1_g", "ln1_b", "w_qkv", "b_qkv", "q_g", "q_b", "k_g", "k_b",
+                 "w_o", "b_o", "ln2_g", "ln2_b", "w_up", "b_up", "w_down", "b_down"]
+
+
+class EncLayerWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in _LAYER_FIELDS]
+
+
+class EncWeights(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("w_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(EncLayerWeights)),
+                ("lnf_g", ctypes.c_void_p), ("lnf_b", ctypes.c_void_p)]
+
+
+class EncoderError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Open the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m speech_audio_encoder_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.enc_create.argtypes = [ctypes.POINTER(EncWeights), ctypes.POINTER(ctypes.c_void_p)]
+    lib.enc_logmel.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
+                               ctypes.c_void_p, ctypes.c_void_p]
+    lib.enc_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
+                                ctypes.c_void_p, ctypes.c_void_p]
+    lib.enc_destroy.argtypes = [ctypes.c_void_p]
+    lib.enc_destroy.restype = None
+    lib.enc_shapes.argtypes = [i64p, ctypes.c_int32, i64p, i64p]
+    lib.enc_workspace_bytes.argtypes = [ctypes.c_int32, i64p, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.enc_last_error.restype = ctypes.c_char_p
+    lib.enc_last_error.argtypes = []
+    lib.enc_profile_kernel.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    lib.enc_profile_read.argtypes = [ctypes.c_void_p, i64p, ctypes.POINTER(ctypes.c_double)]
+    for name in EXPORTS:
+        if name not in ("enc_destroy", "enc_last_error"):
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def enc_last_error():
+    return load_library().enc_last_error().decode()
+
+
+def _check(code):
+    if code != ENC_OK:
+        raise EncoderError(code, enc_last_error())
+
+
+def _lengths_array(lengths):
+    arr = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64).reshape(-1))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def enc_shapes(lengths):
+    """(F_max, P_max) of a batch, computed by the library on the host."""
+    arr, ptr = _lengths_array(lengths)
+    f, p = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().enc_shapes(ptr, len(arr), ctypes.byref(f), ctypes.byref(p)))
+    return f.value, p.value
+
+
+def enc_workspace_bytes(n_layers, lengths):
+    arr, ptr = _lengths_array(lengths)
+    out = ctypes.c_size_t()
+    _check(load_library().enc_workspace_bytes(n_layers, ptr, len(arr), ctypes.byref(out)))
+    return out.value
+
+
+def _stream_handle(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def enc_create(weights, dtype="bf16", device="cuda"):
+    """Create a context from a weights dict (numpy or torch tensors).
+
+    The tensors are put on the device in the requested element type for the
+    duration of the call only: the library copies them into its own memory.
+    Returns the context handle (an int).
+    """
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    keep = []
+
+    def dev(a):
+        t = torch.as_tensor(np.asarray(a, dtype=np.float32)) if not torch.is_tensor(a) else a
+        t = t.to(device=device, dtype=tdt).contiguous()
+        keep.append(t)
+        return ctypes.c_void_p(t.data_ptr())
+
+    layers = (EncLayerWeights * len(weights["layers"]))()
+    for i, lw in enumerate(weights["layers"]):
+        for name in _LAYER_FIELDS:
+            setattr(layers[i], name, dev(lw[name]))
+    w = EncWeights(abi_version=ENC_ABI_VERSION, n_layers=len(weights["layers"]),
+                   dtype=ENC_BF16 if dtype == "bf16" else ENC_F32, reserved=0,
+                   w_in=dev(weights["w_in"]), b_in=dev(weights["b_in"]),
+                   layers=layers, lnf_g=dev(weights["lnf_g"]), lnf_b=dev(weights["lnf_b"]))
+    torch.cuda.synchronize()
+    handle = ctypes.c_void_p()
+    _check(load_library().enc_create(ctypes.byref(w), ctypes.byref(handle)))
+    del keep
+    return handle.value
+
+
+def enc_create_raw(weights_struct):
+    """enc_create on a caller-built EncWeights (for argument-check tests)."""
+    handle = ctypes.c_void_p()
+    code = load_library().enc_create(ctypes.byref(weights_struct), ctypes.byref(handle))
+    return code, handle.value
+
+
+def enc_destroy(ctx):
+    load_library().enc_destroy(ctypes.c_void_p(ctx))
+
+
+def enc_logmel(ctx, audio, lengths, out=None, stream=None):
+    """Log-mel features: audio cuda fp32 [B, N_max] -> fp32 [B, F_max, 128]."""
+    import torch
+    arr, ptr = _lengths_array(lengths)
+    f_max, _ = enc_shapes(arr)
+    if out is None:
+        out = torch.empty((len(arr), f_max, N_MELS), dtype=torch.float32, device=audio.device)
+    _check(load_library().enc_logmel(ctypes.c_void_p(ctx), ctypes.c_void_p(audio.data_ptr()),
+                                     ptr, len(arr), ctypes.c_void_p(out.data_ptr()),
+                                     _stream_handle(stream)))
+    return out
+
+
+def enc_forward(ctx, audio, lengths, out=None, stream=None):
+    """Embeddings: audio cuda fp32 [B, N_max] -> bf16 [B, P_max, 1280]."""
+    import torch
+    arr, ptr = _lengths_array(lengths)
+    _, p_max = enc_shapes(arr)
+    if out is None:
+        out = torch.empty((len(arr), p_max, D_MODEL), dtype=torch.bfloat16, device=audio.device)
+    _check(load_library().enc_forward(ctypes.c_void_p(ctx), ctypes.c_void_p(audio.data_ptr()),
+                                      ptr, len(arr), ctypes.c_void_p(out.data_ptr()),
+                                      _stream_handle(stream)))
+    return out
+
+
+def enc_forward_raw(ctx, audio_ptr, lengths, out_ptr, stream_ptr=0):
+    """enc_forward with raw pointers; returns the status code (tests)."""
+    arr, ptr = _lengths_array(lengths)
+    return load_library().enc_forward(ctypes.c_void_p(ctx), ctypes.c_void_p(audio_ptr), ptr,
+                                      len(arr), ctypes.c_void_p(out_ptr),
+                                      ctypes.c_void_p(stream_ptr))
+
+
+def enc_profile_kernel(ctx, name_or_id):
+    kid = KERNELS.index(name_or_id) if isinstance(name_or_id, str) else int(name_or_id)
+    _check(load_library().enc_profile_kernel(ctypes.c_void_p(ctx), kid))
+
+
+def enc_profile_read(ctx):
+    """(launches, total_ms) of the bracketed kernel since the last read."""
+    n, ms = ctypes.c_int64(), ctypes.c_double()
+    _check(load_library().enc_profile_read(ctypes.c_void_p(ctx), ctypes.byref(n),
+                                           ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+class Encoder:
+    """Owns one context; ``logmel`` and ``forward`` enqueue on torch's current stream."""
+
+    def __init__(self, weights, dtype="bf16", device="cuda"):
+        self.ctx = enc_create(weights, dtype=dtype, device=device)
+
+    def logmel(self, audio, lengths, out=None):
+        return enc_logmel(self.ctx, audio, lengths, out)
+
+    def forward(self, audio, lengths, out=None):
+        return enc_forward(self.ctx, audio, lengths, out)
+
+    def close(self):
+        if self.ctx:
+            enc_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,95 @@
+// Internal interface between the host runtime and the gfx950 kernels.
+// Every launcher is asynchronous on the given stream and returns the launch
+// status; shapes are validated by the caller before anything is enqueued.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace enc {
+
+struct Cpx {
+  float re, im;
+};
+
+constexpr int MEL_NNZ_MAX = 1024;
+
+// Constant tables of the frontend, built on the host in float64.
+struct FrontendTables {
+  float hann[WIN];              // periodic Hann window
+  Cpx tw256[256];               // exp(-2 pi i m / 256)
+  Cpx tw512[NBIN];              // exp(-2 pi i k / 512), k = 0..256
+  int32_t mel_start[NMEL];      // first bin with nonzero weight
+  int32_t mel_count[NMEL];      // number of bins from mel_start
+  int32_t mel_offset[NMEL];     // offset of the band's weights in mel_w
+  float mel_w[MEL_NNZ_MAX];
+};
+
+// ---------------------------------------------------------------- frontend
+// Log-mel of every (clip, frame) pair into out[batch, f_max, 128] (float32),
+// zero for frames t >= n_frames[b].
+hipError_t launch_logmel_padded(const float* audio, int64_t audio_stride, const int32_t* n_frames,
+                                int batch, int64_t f_max, const FrontendTables* tab, float* out,
+                                hipStream_t stream);
+
+// Log-mel in the stacked layout the input projection reads: clip b owns
+// packed frames [frame_base[b], frame_base[b] + 8 P_b); frames past F_b are 0.
+// out is bf16 [total_frames, 128] == [sum P_b, 1024].
+hipError_t launch_logmel_stacked(const float* audio, int64_t audio_stride, const int32_t* n_frames,
+                                 const int32_t* frame_base, int batch, int64_t total_frames,
+                                 const FrontendTables* tab, bf16_t* out, hipStream_t stream);
+
+// -------------------------------------------------------------------- GEMM
+// C[M, N] (op)= A[M, K] * W[N, K]^T + bias[N]; A, W bf16 row-major
+// (K contiguous), fp32 accumulation.  N % 128 == 0, K % 64 == 0.
+enum class Epilogue {
+  kBiasBf16,          // C (bf16)  = acc + bias
+  kBiasGeluBf16,      // C (bf16)  = gelu(acc + bias)
+  kBiasResidualF32,   // C (fp32) += acc + bias
+  kBiasF32,           // C (fp32)  = acc + bias
+};
+
+hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
+                       const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
+                       hipStream_t stream);
+
+// ------------------------------------------------------------------- norms
+// y[r, :] = LN(x[r, :]) * g + b over d = 1280, fp32 statistics, bf16 output.
+hipError_t launch_layernorm(const float* x, const float* g, const float* b, bf16_t* y,
+                            int64_t rows, hipStream_t stream);
+
+// In place on qkv [rows, 3840] bf16, per attention tile (clip tile_seq[i],
+// positions tile_p0[i] .. +127) and head: q <- RoPE(LN_q(q)), k <- RoPE(LN_k(k)),
+// and v copied transposed to vt[h][d][vt_base[b] + p] (ld_vt per d), with
+// zeros for p in [P_b, roundup(P_b, 64)).  cu_seq[b] is clip b's first row.
+hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* vt_base,
+                              const int32_t* tile_seq, const int32_t* tile_p0, int n_tiles,
+                              const float* qg, const float* qb, const float* kg, const float* kb,
+                              const float* rope_cos, const float* rope_sin, bf16_t* vt,
+                              int64_t ld_vt, hipStream_t stream);
+
+// out[b, p, :] = LN_f(x[cu_seq[b] + p, :]) for p < P_b, else 0; bf16 output
+// of shape [batch, p_max, 1280].
+hipError_t launch_final_norm(const float* x, const float* g, const float* b, const int32_t* cu_seq,
+                             int batch, int64_t p_max, bf16_t* out, hipStream_t stream);
+
+// Element conversions used when weights are copied into the context.
+hipError_t launch_to_bf16(const void* src, bool src_is_bf16, bf16_t* dst, int64_t n,
+                          hipStream_t stream);
+hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t n,
+                         hipStream_t stream);
+
+// --------------------------------------------------------------- attention
+// Bidirectional softmax attention per clip and head.  q, k are the first two
+// 1280-column groups of qkv [rows, 3840]; v comes transposed from vt (clip b
+// at columns vt_base[b]..., zero past P_b up to a multiple of 64).  Work tile
+// i covers queries [tile_q0[i], min(tile_q0[i] + 128, P_b)) of clip
+// tile_seq[i].  out is bf16 [rows, 1280] with head h in columns h*128...
+hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
+                            const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
+                            const int32_t* tile_q0, int n_tiles, bf16_t* out,
+                            hipStream_t stream);
+
+}  // namespace enc

@@ -1,0 +1,618 @@
+// Host runtime behind the C ABI in include/speech_encoder.h: argument checks,
+// the per-call length plan, weight copy-in, constant tables, the workspace and
+// the launch sequence of one forward pass.
+//
+// Method: "Nemotron 3.5 Transcribe: From Recorded Speech to Dataset Audits",
+// section "How audio and speakers reach the language model" (frontend, 8-frame
+// stacking, width-1,280 projection, 32 Transformer layers); section "How one
+// hour fits into 65,536 positions" (12.5 positions per second, 45,000 per
+// hour).  The host never waits for the device inside enc_forward except when
+// the workspace has to grow.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/speech_encoder.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace enc;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(ENC_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t frames_of(int64_t n) { return n < WIN ? 0 : 1 + (n - WIN) / HOP; }
+int64_t positions_of(int64_t f) { return (f + STACK - 1) / STACK; }
+
+// ------------------------------------------------------------ constant tables
+// Slaney mel scale: linear at 200/3 Hz per mel below 1 kHz, logarithmic above
+// with a step of ln(6.4)/27 per mel.
+double hz_to_mel(double f) {
+  const double f_sp = 200.0 / 3.0, logstep = std::log(6.4) / 27.0;
+  if (f < 1000.0) return f / f_sp;
+  return 1000.0 / f_sp + std::log(f / 1000.0) / logstep;
+}
+double mel_to_hz(double m) {
+  const double f_sp = 200.0 / 3.0, logstep = std::log(6.4) / 27.0;
+  const double m_break = 1000.0 / f_sp;
+  if (m < m_break) return m * f_sp;
+  return 1000.0 * std::exp(logstep * (m - m_break));
+}
+
+bool build_frontend_tables(FrontendTables* t) {
+  const double pi = 3.14159265358979323846;
+  for (int n = 0; n < WIN; ++n) t->hann[n] = (float)(0.5 - 0.5 * std::cos(2.0 * pi * n / WIN));
+  for (int m = 0; m < 256; ++m) {
+    const double a = -2.0 * pi * m / 256.0;
+    t->tw256[m] = {(float)std::cos(a), (float)std::sin(a)};
+  }
+  for (int k = 0; k < NBIN; ++k) {
+    const double a = -2.0 * pi * k / 512.0;
+    t->tw512[k] = {(float)std::cos(a), (float)std::sin(a)};
+  }
+  // 130 band edges equally spaced in mel from 0 Hz to 8 kHz; triangle m rises
+  // from edge m to edge m+1 and falls to edge m+2 (linear in Hz), peak 1.
+  double edge[NMEL + 2];
+  const double top = hz_to_mel(8000.0);
+  for (int i = 0; i < NMEL + 2; ++i) edge[i] = mel_to_hz(top * i / (NMEL + 1));
+  int off = 0;
+  for (int m = 0; m < NMEL; ++m) {
+    int first = -1, count = 0;
+    for (int k = 0; k < NBIN; ++k) {
+      const double f = k * 16000.0 / NFFT;
+      const double up = (f - edge[m]) / (edge[m + 1] - edge[m]);
+      const double down = (edge[m + 2] - f) / (edge[m + 2] - edge[m + 1]);
+      const double w = std::max(0.0, std::min(up, down));
+      if (w > 0.0) {
+        if (first < 0) first = k;
+        // bands are contiguous runs of bins
+        if (k != first + count) return false;
+        if (off + count >= MEL_NNZ_MAX) return false;
+        t->mel_w[off + count] = (float)w;
+        ++count;
+      }
+    }
+    if (first < 0) return false;
+    t->mel_start[m] = first;
+    t->mel_count[m] = count;
+    t->mel_offset[m] = off;
+    off += count;
+  }
+  return true;
+}
+
+// -------------------------------------------------------------- launch plan
+struct Plan {
+  int batch = 0;
+  int64_t f_max = 0, p_max = 0;
+  int64_t rows = 0;                 // sum of P_b
+  std::vector<int32_t> n_frames;    // [batch]
+  std::vector<int32_t> frame_base;  // [batch]  8 * cu_seq[b]
+  std::vector<int32_t> cu_seq;      // [batch + 1]
+  std::vector<int32_t> vt_base;     // [batch]  first V^T column of each clip
+  int64_t vt_cols = 0;              // sum of roundup(P_b, 64)
+  std::vector<int32_t> tile_seq, tile_q0;
+};
+
+constexpr int ATT_QB = 128;
+
+int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles) {
+  if (!lengths) return fail(ENC_ERR_ARG, "lengths is NULL");
+  if (batch < 1) return fail(ENC_ERR_ARG, "batch must be >= 1");
+  p->batch = batch;
+  p->n_frames.resize(batch);
+  p->frame_base.resize(batch);
+  p->cu_seq.resize(batch + 1);
+  p->vt_base.resize(batch);
+  int64_t nmax = 0, rows = 0, vcols = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = lengths[b];
+    if (n < 0) return fail(ENC_ERR_ARG, "lengths[" + std::to_string(b) + "] is negative");
+    if (n > MAX_SAMPLES)
+      return fail(ENC_ERR_TOO_LONG, "lengths[" + std::to_string(b) + "] = " + std::to_string(n) +
+                                        " exceeds one hour (57600000 samples)");
+    nmax = std::max(nmax, n);
+    const int64_t f = frames_of(n);
+    p->n_frames[b] = (int32_t)f;
+    p->cu_seq[b] = (int32_t)rows;
+    p->frame_base[b] = (int32_t)(rows * STACK);
+    p->vt_base[b] = (int32_t)vcols;
+    rows += positions_of(f);
+    vcols += (positions_of(f) + 63) / 64 * 64;
+  }
+  p->vt_cols = vcols;
+  p->cu_seq[batch] = (int32_t)rows;
+  if (rows * STACK > INT32_MAX) return fail(ENC_ERR_TOO_LONG, "batch has too many frames");
+  p->rows = rows;
+  p->f_max = frames_of(nmax);
+  p->p_max = positions_of(p->f_max);
+  p->tile_seq.clear();
+  p->tile_q0.clear();
+  if (with_tiles) {
+    for (int b = 0; b < batch; ++b) {
+      const int len = p->cu_seq[b + 1] - p->cu_seq[b];
+      for (int q0 = 0; q0 < len; q0 += ATT_QB) {
+        p->tile_seq.push_back(b);
+        p->tile_q0.push_back(q0);
+      }
+    }
+  }
+  return ENC_OK;
+}
+
+// Workspace layout for `rows` packed positions (offsets in bytes).
+struct Layout {
+  size_t x, a, qkv, o, u, vt, total;
+  int64_t ld_vt;
+};
+
+Layout layout_for(int64_t rows, int64_t vt_cols) {
+  Layout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const size_t r = (size_t)std::max<int64_t>(rows, 1);
+  l.x = take(r * D * 4);
+  l.a = take(r * D * 2);
+  l.qkv = take(r * 3 * D * 2);
+  l.o = take(r * D * 2);
+  l.u = take(r * std::max(FF, DIN) * 2);   // also holds the stacked log-mel
+  l.ld_vt = std::max<int64_t>(vt_cols, 64);
+  l.vt = take((size_t)H * DH * l.ld_vt * 2);
+  l.total = off;
+  return l;
+}
+
+struct LayerW {
+  bf16_t *w_qkv, *w_o, *w_up, *w_down;
+  float *ln1_g, *ln1_b, *b_qkv, *q_g, *q_b, *k_g, *k_b, *b_o, *ln2_g, *ln2_b, *b_up, *b_down;
+};
+
+}  // namespace
+
+struct enc_ctx {
+  int device = 0;
+  int n_layers = 0;
+  void* wmat = nullptr;   // bf16 matrices
+  void* wvec = nullptr;   // fp32 vectors
+  bf16_t* w_in = nullptr;
+  float *b_in = nullptr, *lnf_g = nullptr, *lnf_b = nullptr;
+  std::vector<LayerW> layers;
+  FrontendTables* tables = nullptr;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  int32_t* plan_dev = nullptr;
+  size_t plan_cap = 0;      // int32 entries
+  int32_t* plan_host = nullptr;
+  size_t plan_host_cap = 0;
+  hipEvent_t plan_copied = nullptr;
+  bool plan_pending = false;
+  hipStream_t last_stream = nullptr;
+  bool has_last_stream = false;
+  int prof_kernel = -1;
+  std::vector<hipEvent_t> prof_events;   // pairs
+  size_t prof_used = 0;
+};
+
+namespace {
+
+void release(enc_ctx* c) {
+  if (!c) return;
+  (void)hipDeviceSynchronize();
+  (void)hipFree(c->wmat);
+  (void)hipFree(c->wvec);
+  (void)hipFree(c->tables);
+  (void)hipFree(c->rope_cos);
+  (void)hipFree(c->rope_sin);
+  (void)hipFree(c->ws);
+  (void)hipFree(c->plan_dev);
+  if (c->plan_host) (void)hipHostFree(c->plan_host);
+  if (c->plan_copied) (void)hipEventDestroy(c->plan_copied);
+  for (hipEvent_t e : c->prof_events) (void)hipEventDestroy(e);
+  delete c;
+}
+
+// Upload the plan's int32 arrays (concatenated) to ctx->plan_dev on `stream`.
+int upload_plan(enc_ctx* c, const std::vector<const std::vector<int32_t>*>& parts,
+                std::vector<int32_t*>* dev_ptrs, hipStream_t stream) {
+  size_t total = 0;
+  for (auto* v : parts) total += align_up(v->size(), 64);
+  total = std::max<size_t>(total, 64);
+  hipError_t e;
+  if (c->plan_pending) {
+    e = hipEventSynchronize(c->plan_copied);
+    if (e != hipSuccess) return hip_fail(e, "waiting for the previous plan upload");
+    c->plan_pending = false;
+  }
+  if (total > c->plan_host_cap) {
+    if (c->plan_host) (void)hipHostFree(c->plan_host);
+    c->plan_host = nullptr;
+    c->plan_host_cap = 0;
+    e = hipHostMalloc((void**)&c->plan_host, total * 4, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(ENC_ERR_NOMEM, "pinned plan buffer allocation failed");
+    c->plan_host_cap = total;
+  }
+  if (total > c->plan_cap) {
+    if (c->plan_dev) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+      (void)hipFree(c->plan_dev);
+      c->plan_dev = nullptr;
+      c->plan_cap = 0;
+    }
+    e = hipMalloc((void**)&c->plan_dev, total * 4);
+    if (e != hipSuccess) return fail(ENC_ERR_NOMEM, "plan buffer allocation failed");
+    c->plan_cap = total;
+  }
+  size_t off = 0;
+  dev_ptrs->clear();
+  for (auto* v : parts) {
+    if (!v->empty()) std::memcpy(c->plan_host + off, v->data(), v->size() * 4);
+    dev_ptrs->push_back(c->plan_dev + off);
+    off += align_up(v->size(), 64);
+  }
+  e = hipMemcpyAsync(c->plan_dev, c->plan_host, off * 4, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "plan upload");
+  e = hipEventRecord(c->plan_copied, stream);
+  if (e != hipSuccess) return hip_fail(e, "plan event");
+  c->plan_pending = true;
+  return ENC_OK;
+}
+
+int switch_stream(enc_ctx* c, hipStream_t stream) {
+  if (c->has_last_stream && c->last_stream != stream) {
+    hipError_t e = hipStreamSynchronize(c->last_stream);
+    if (e != hipSuccess) return hip_fail(e, "synchronizing the previous stream");
+  }
+  c->last_stream = stream;
+  c->has_last_stream = true;
+  return ENC_OK;
+}
+
+int check_device(enc_ctx* c) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != c->device)
+    return fail(ENC_ERR_ARG, "context was created on device " + std::to_string(c->device) +
+                                 " but device " + std::to_string(dev) + " is current");
+  return ENC_OK;
+}
+
+// Profiling bracket around one launch of kernel class `id`.
+struct ProfScope {
+  enc_ctx* c;
+  hipStream_t s;
+  bool on;
+  size_t idx;
+  ProfScope(enc_ctx* ctx, int id, hipStream_t stream) : c(ctx), s(stream), on(ctx->prof_kernel == id) {
+    if (!on) return;
+    idx = c->prof_used;
+    while (c->prof_events.size() < idx + 2) {
+      hipEvent_t ev;
+      if (hipEventCreate(&ev) != hipSuccess) { on = false; return; }
+      c->prof_events.push_back(ev);
+    }
+    (void)hipEventRecord(c->prof_events[idx], s);
+  }
+  ~ProfScope() {
+    if (!on) return;
+    (void)hipEventRecord(c->prof_events[idx + 1], s);
+    c->prof_used = idx + 2;
+  }
+};
+
+#define ENC_LAUNCH(id, call)                                  \
+  do {                                                        \
+    ProfScope _ps(ctx, id, stream);                           \
+    hipError_t _e = (call);                                   \
+    if (_e != hipSuccess) return hip_fail(_e, #call);         \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* enc_last_error(void) { return g_last_error.c_str(); }
+
+int enc_shapes(const int64_t* lengths, int32_t batch, int64_t* f_max, int64_t* p_max) {
+  if (!f_max || !p_max) return fail(ENC_ERR_ARG, "NULL output pointer");
+  Plan p;
+  int rc = make_plan(lengths, batch, &p, false);
+  if (rc != ENC_OK) return rc;
+  *f_max = p.f_max;
+  *p_max = p.p_max;
+  return ENC_OK;
+}
+
+int enc_workspace_bytes(int32_t n_layers, const int64_t* lengths, int32_t batch, size_t* bytes) {
+  if (!bytes) return fail(ENC_ERR_ARG, "NULL output pointer");
+  if (n_layers < 1) return fail(ENC_ERR_ARG, "n_layers must be >= 1");
+  Plan p;
+  int rc = make_plan(lengths, batch, &p, false);
+  if (rc != ENC_OK) return rc;
+  *bytes = layout_for(p.rows, p.vt_cols).total;
+  return ENC_OK;
+}
+
+int enc_create(const enc_weights* w, enc_ctx** out) {
+  if (!w || !out) return fail(ENC_ERR_ARG, "NULL argument");
+  *out = nullptr;
+  if (w->abi_version != ENC_ABI_VERSION)
+    return fail(ENC_ERR_ARG, "abi_version " + std::to_string(w->abi_version) + " != " +
+                                 std::to_string(ENC_ABI_VERSION));
+  if (w->n_layers < 1) return fail(ENC_ERR_ARG, "n_layers must be >= 1");
+  if (w->dtype != ENC_F32 && w->dtype != ENC_BF16) return fail(ENC_ERR_ARG, "unknown dtype");
+  if (!w->w_in || !w->b_in || !w->lnf_g || !w->lnf_b || !w->layers)
+    return fail(ENC_ERR_ARG, "NULL weight tensor");
+  for (int i = 0; i < w->n_layers; ++i) {
+    const enc_layer_weights& L = w->layers[i];
+    const void* ptrs[] = {L.ln1_g, L.ln1_b, L.w_qkv, L.b_qkv, L.q_g, L.q_b, L.k_g, L.k_b,
+                          L.w_o, L.b_o, L.ln2_g, L.ln2_b, L.w_up, L.b_up, L.w_down, L.b_down};
+    for (const void* p : ptrs)
+      if (!p) return fail(ENC_ERR_ARG, "NULL tensor in layer " + std::to_string(i));
+  }
+
+  enc_ctx* c = new (std::nothrow) enc_ctx();
+  if (!c) return fail(ENC_ERR_NOMEM, "host allocation failed");
+  hipError_t e = hipGetDevice(&c->device);
+  if (e != hipSuccess) { release(c); return hip_fail(e, "hipGetDevice"); }
+  c->n_layers = w->n_layers;
+  const int L = w->n_layers;
+  const bool src_bf16 = w->dtype == ENC_BF16;
+
+  // bf16 matrices and fp32 vectors, one allocation each.
+  const size_t per_layer_mat = (size_t)3 * D * D + (size_t)D * D + 2 * (size_t)FF * D;
+  const size_t n_mat = (size_t)D * DIN + (size_t)L * per_layer_mat;
+  const size_t per_layer_vec = 2 * D + 3 * D + 4 * DH + D + 2 * D + FF + D;
+  const size_t n_vec = 3 * (size_t)D + (size_t)L * per_layer_vec;
+  if (hipMalloc(&c->wmat, n_mat * 2) != hipSuccess || hipMalloc(&c->wvec, n_vec * 4) != hipSuccess) {
+    release(c);
+    return fail(ENC_ERR_NOMEM, "weight allocation failed");
+  }
+  bf16_t* pm = (bf16_t*)c->wmat;
+  float* pv = (float*)c->wvec;
+  int rc = ENC_OK;
+  auto mat = [&](const void* src, size_t n) {
+    bf16_t* dst = pm;
+    pm += n;
+    if (rc == ENC_OK) {
+      hipError_t err = launch_to_bf16(src, src_bf16, dst, (int64_t)n, nullptr);
+      if (err != hipSuccess) rc = hip_fail(err, "weight conversion");
+    }
+    return dst;
+  };
+  auto vec = [&](const void* src, size_t n) {
+    float* dst = pv;
+    pv += n;
+    if (rc == ENC_OK) {
+      hipError_t err = launch_to_f32(src, src_bf16, dst, (int64_t)n, nullptr);
+      if (err != hipSuccess) rc = hip_fail(err, "weight conversion");
+    }
+    return dst;
+  };
+  c->w_in = mat(w->w_in, (size_t)D * DIN);
+  c->b_in = vec(w->b_in, D);
+  c->lnf_g = vec(w->lnf_g, D);
+  c->lnf_b = vec(w->lnf_b, D);
+  c->layers.resize(L);
+  for (int i = 0; i < L; ++i) {
+    const enc_layer_weights& s = w->layers[i];
+    LayerW& d = c->layers[i];
+    d.w_qkv = mat(s.w_qkv, (size_t)3 * D * D);
+    d.w_o = mat(s.w_o, (size_t)D * D);
+    d.w_up = mat(s.w_up, (size_t)FF * D);
+    d.w_down = mat(s.w_down, (size_t)D * FF);
+    d.ln1_g = vec(s.ln1_g, D);
+    d.ln1_b = vec(s.ln1_b, D);
+    d.b_qkv = vec(s.b_qkv, 3 * D);
+    d.q_g = vec(s.q_g, DH);
+    d.q_b = vec(s.q_b, DH);
+    d.k_g = vec(s.k_g, DH);
+    d.k_b = vec(s.k_b, DH);
+    d.b_o = vec(s.b_o, D);
+    d.ln2_g = vec(s.ln2_g, D);
+    d.ln2_b = vec(s.ln2_b, D);
+    d.b_up = vec(s.b_up, FF);
+    d.b_down = vec(s.b_down, D);
+  }
+  if (rc != ENC_OK) { release(c); return rc; }
+
+  // Constant tables.
+  FrontendTables* host_tab = new (std::nothrow) FrontendTables();
+  if (!host_tab) { release(c); return fail(ENC_ERR_NOMEM, "host allocation failed"); }
+  if (!build_frontend_tables(host_tab)) {
+    delete host_tab;
+    release(c);
+    return fail(ENC_ERR_HIP, "mel filterbank construction failed");
+  }
+  std::vector<float> rc_cos((size_t)MAX_POS * (DH / 2)), rc_sin((size_t)MAX_POS * (DH / 2));
+  for (int p = 0; p < MAX_POS; ++p)
+    for (int i = 0; i < DH / 2; ++i) {
+      const double ang = (double)p * std::pow(10000.0, -(double)i / (DH / 2));
+      rc_cos[(size_t)p * (DH / 2) + i] = (float)std::cos(ang);
+      rc_sin[(size_t)p * (DH / 2) + i] = (float)std::sin(ang);
+    }
+  const size_t rope_bytes = rc_cos.size() * 4;
+  if (hipMalloc((void**)&c->tables, sizeof(FrontendTables)) != hipSuccess ||
+      hipMalloc((void**)&c->rope_cos, rope_bytes) != hipSuccess ||
+      hipMalloc((void**)&c->rope_sin, rope_bytes) != hipSuccess) {
+    delete host_tab;
+    release(c);
+    return fail(ENC_ERR_NOMEM, "table allocation failed");
+  }
+  e = hipMemcpy(c->tables, host_tab, sizeof(FrontendTables), hipMemcpyHostToDevice);
+  delete host_tab;
+  if (e == hipSuccess) e = hipMemcpy(c->rope_cos, rc_cos.data(), rope_bytes, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(c->rope_sin, rc_sin.data(), rope_bytes, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&c->plan_copied, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    release(c);
+    return hip_fail(e, "enc_create upload");
+  }
+  *out = c;
+  return ENC_OK;
+}
+
+void enc_destroy(enc_ctx* ctx) { release(ctx); }
+
+int enc_logmel(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch, float* out,
+               hipStream_t stream) {
+  if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  Plan p;
+  int rc = make_plan(lengths, batch, &p, false);
+  if (rc != ENC_OK) return rc;
+  int64_t nmax = 0;
+  for (int b = 0; b < batch; ++b) nmax = std::max(nmax, lengths[b]);
+  if (nmax > 0 && !audio) return fail(ENC_ERR_ARG, "audio is NULL");
+  if (p.f_max > 0 && !out) return fail(ENC_ERR_ARG, "out is NULL");
+  if ((rc = check_device(ctx)) != ENC_OK) return rc;
+  if (p.f_max == 0) return ENC_OK;
+  if ((rc = switch_stream(ctx, stream)) != ENC_OK) return rc;
+  std::vector<int32_t*> dev;
+  if ((rc = upload_plan(ctx, {&p.n_frames}, &dev, stream)) != ENC_OK) return rc;
+  ENC_LAUNCH(ENC_K_FRONTEND, launch_logmel_padded(audio, nmax, dev[0], batch, p.f_max,
+                                                  ctx->tables, out, stream));
+  return ENC_OK;
+}
+
+int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                void* out_embeddings, hipStream_t stream) {
+  if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  Plan p;
+  int rc = make_plan(lengths, batch, &p, true);
+  if (rc != ENC_OK) return rc;
+  int64_t nmax = 0;
+  for (int b = 0; b < batch; ++b) nmax = std::max(nmax, lengths[b]);
+  if (nmax > 0 && !audio) return fail(ENC_ERR_ARG, "audio is NULL");
+  if (p.p_max > 0 && !out_embeddings) return fail(ENC_ERR_ARG, "out_embeddings is NULL");
+  if ((rc = check_device(ctx)) != ENC_OK) return rc;
+  if (p.p_max == 0) return ENC_OK;
+
+  // Memory admission before any launch.
+  const Layout lay = layout_for(p.rows, p.vt_cols);
+  if (const char* cap = std::getenv("ENC_WORKSPACE_CAP_BYTES")) {
+    const unsigned long long lim = std::strtoull(cap, nullptr, 10);
+    if ((unsigned long long)lay.total > lim)
+      return fail(ENC_ERR_NOMEM, "workspace of " + std::to_string(lay.total) +
+                                     " bytes exceeds ENC_WORKSPACE_CAP_BYTES=" + cap);
+  }
+  if ((rc = switch_stream(ctx, stream)) != ENC_OK) return rc;
+  if (lay.total > ctx->ws_bytes) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    (void)hipFree(ctx->ws);
+    ctx->ws = nullptr;
+    ctx->ws_bytes = 0;
+    e = hipMalloc(&ctx->ws, lay.total);
+    if (e != hipSuccess) {
+      ctx->ws = nullptr;
+      (void)hipGetLastError();
+      return fail(ENC_ERR_NOMEM, "workspace allocation of " + std::to_string(lay.total) +
+                                     " bytes failed");
+    }
+    ctx->ws_bytes = lay.total;
+  }
+  // The workspace row layout depends on `rows`; the pointers below follow it.
+  char* ws = (char*)ctx->ws;
+  float* x = (float*)(ws + lay.x);
+  bf16_t* a = (bf16_t*)(ws + lay.a);
+  bf16_t* qkv = (bf16_t*)(ws + lay.qkv);
+  bf16_t* o = (bf16_t*)(ws + lay.o);
+  bf16_t* u = (bf16_t*)(ws + lay.u);
+  bf16_t* vt = (bf16_t*)(ws + lay.vt);
+  bf16_t* stk = u;
+
+  std::vector<int32_t*> dev;
+  if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.cu_seq, &p.vt_base, &p.tile_seq,
+                              &p.tile_q0},
+                        &dev, stream)) != ENC_OK)
+    return rc;
+  const int32_t* d_nf = dev[0];
+  const int32_t* d_fb = dev[1];
+  const int32_t* d_cu = dev[2];
+  const int32_t* d_vb = dev[3];
+  const int32_t* d_ts = dev[4];
+  const int32_t* d_tq = dev[5];
+  const int64_t R = p.rows;
+  const int n_tiles = (int)p.tile_seq.size();
+
+  ENC_LAUNCH(ENC_K_FRONTEND, launch_logmel_stacked(audio, nmax, d_nf, d_fb, batch, R * STACK,
+                                                   ctx->tables, stk, stream));
+  ENC_LAUNCH(ENC_K_GEMM_IN, launch_gemm(Epilogue::kBiasF32, stk, DIN, ctx->w_in, DIN, ctx->b_in, x,
+                                        D, R, D, DIN, stream));
+  for (int li = 0; li < ctx->n_layers; ++li) {
+    const LayerW& Lw = ctx->layers[li];
+    ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln1_g, Lw.ln1_b, a, R, stream));
+    ENC_LAUNCH(ENC_K_GEMM_QKV, launch_gemm(Epilogue::kBiasBf16, a, D, Lw.w_qkv, D, Lw.b_qkv, qkv,
+                                           3 * D, R, 3 * D, D, stream));
+    ENC_LAUNCH(ENC_K_QKNORM_ROPE,
+               launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, Lw.q_g, Lw.q_b, Lw.k_g,
+                                  Lw.k_b, ctx->rope_cos, ctx->rope_sin, vt, lay.ld_vt, stream));
+    ENC_LAUNCH(ENC_K_ATTENTION,
+               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, o, stream));
+    ENC_LAUNCH(ENC_K_GEMM_O, launch_gemm(Epilogue::kBiasResidualF32, o, D, Lw.w_o, D, Lw.b_o, x,
+                                         D, R, D, D, stream));
+    ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln2_g, Lw.ln2_b, a, R, stream));
+    ENC_LAUNCH(ENC_K_GEMM_UP, launch_gemm(Epilogue::kBiasGeluBf16, a, D, Lw.w_up, D, Lw.b_up, u,
+                                          FF, R, FF, D, stream));
+    ENC_LAUNCH(ENC_K_GEMM_DOWN, launch_gemm(Epilogue::kBiasResidualF32, u, FF, Lw.w_down, FF,
+                                            Lw.b_down, x, D, R, D, FF, stream));
+  }
+  ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_cu, batch, p.p_max,
+                                                 (bf16_t*)out_embeddings, stream));
+  return ENC_OK;
+}
+
+int enc_profile_kernel(enc_ctx* ctx, int32_t kernel_id) {
+  if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  if (kernel_id < -1 || kernel_id >= ENC_K_COUNT) return fail(ENC_ERR_ARG, "unknown kernel id");
+  ctx->prof_kernel = kernel_id;
+  ctx->prof_used = 0;
+  return ENC_OK;
+}
+
+int enc_profile_read(enc_ctx* ctx, int64_t* launches, double* total_ms) {
+  if (!ctx || !launches || !total_ms) return fail(ENC_ERR_ARG, "NULL argument");
+  double sum = 0.0;
+  for (size_t i = 0; i + 1 < ctx->prof_used; i += 2) {
+    hipError_t e = hipEventSynchronize(ctx->prof_events[i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "profile event");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, ctx->prof_events[i], ctx->prof_events[i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "profile elapsed time");
+    sum += ms;
+  }
+  *launches = (int64_t)(ctx->prof_used / 2);
+  *total_ms = sum;
+  ctx->prof_used = 0;
+  return ENC_OK;
+}
+
+}  // extern "C"

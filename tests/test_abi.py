@@ -1,0 +1,91 @@
+"""The C-ABI library: it loads, exports every declared symbol, and its
+host-only calls and argument checks behave as the header states (CPU only;
+nothing here launches device work)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from speech_audio_encoder_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "speech_encoder.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|void|const char\*)\s+(enc_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("enc_create", "enc_logmel", "enc_forward", "enc_destroy"):
+        assert required in names
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("n,f,p", [(0, 0, 0), (399, 0, 0), (400, 1, 1), (560, 2, 1),
+                                   (16_000, 98, 13), (480_000, 2_998, 375),
+                                   (57_600_000, 359_998, 45_000)])
+def test_enc_shapes_closed_form(n, f, p):
+    assert binding.enc_shapes([n]) == (f, p)
+
+
+def test_enc_shapes_batch_uses_longest():
+    assert binding.enc_shapes([400, 480_000, 16_000]) == (2_998, 375)
+
+
+def test_argument_errors(lib):
+    with pytest.raises(binding.EncoderError) as e:
+        binding.enc_shapes([100, -1])
+    assert e.value.code == binding.ENC_ERR_ARG
+    with pytest.raises(binding.EncoderError) as e:
+        binding.enc_shapes([57_600_001])
+    assert e.value.code == binding.ENC_ERR_TOO_LONG
+    assert "one hour" in binding.enc_last_error()
+    f, p = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.enc_shapes(None, 1, ctypes.byref(f), ctypes.byref(p)) == binding.ENC_ERR_ARG
+    arr = (ctypes.c_int64 * 1)(400)
+    assert lib.enc_shapes(arr, 0, ctypes.byref(f), ctypes.byref(p)) == binding.ENC_ERR_ARG
+
+
+def test_workspace_bytes_grows_with_positions():
+    a = binding.enc_workspace_bytes(32, [480_000])
+    b = binding.enc_workspace_bytes(32, [480_000, 480_000])
+    assert 0 < a < b
+    # at least the fp32 residual, bf16 activations, qkv and FFN buffers
+    assert a >= 375 * (1280 * 4 + 1280 * 2 * 2 + 3840 * 2 + 5120 * 2)
+    with pytest.raises(binding.EncoderError):
+        binding.enc_workspace_bytes(0, [480_000])
+
+
+def test_enc_create_rejects_bad_structs(lib):
+    w = binding.EncWeights(abi_version=99, n_layers=1, dtype=binding.ENC_BF16)
+    code, _ = binding.enc_create_raw(w)
+    assert code == binding.ENC_ERR_ARG and "abi_version" in binding.enc_last_error()
+    w = binding.EncWeights(abi_version=binding.ENC_ABI_VERSION, n_layers=0, dtype=binding.ENC_BF16)
+    assert binding.enc_create_raw(w)[0] == binding.ENC_ERR_ARG
+    w = binding.EncWeights(abi_version=binding.ENC_ABI_VERSION, n_layers=1, dtype=7)
+    assert binding.enc_create_raw(w)[0] == binding.ENC_ERR_ARG
+    w = binding.EncWeights(abi_version=binding.ENC_ABI_VERSION, n_layers=1, dtype=binding.ENC_F32)
+    assert binding.enc_create_raw(w)[0] == binding.ENC_ERR_ARG   # NULL tensors
+    assert lib.enc_create(None, None) == binding.ENC_ERR_ARG
+
+
+def test_null_context_is_rejected(lib):
+    arr = (ctypes.c_int64 * 1)(16000)
+    assert lib.enc_forward(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
+    assert lib.enc_logmel(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
+    lib.enc_destroy(None)   # no-op

@@ -1,0 +1,301 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on MI355X.
+
+Tolerances, as the method specification fixes them:
+  * log-mel: max |gpu - oracle| <= 1e-3 over valid frames (fp32);
+  * embeddings: max |gpu - oracle| <= 2e-2 * max |oracle| over valid rows;
+  * padded frames / rows: exactly 0; frame and position counts exact.
+Workloads are the five seeded synthetic ones (1 s tiny, 30 s clip, 64-clip
+batch, 10 min, 1 h) plus ragged and degenerate batches.  Where the oracle
+cannot finish the full 32-layer stack at a size in seconds, the test runs the
+full length with fewer layers (the same weight draw) and compares every row,
+or a spread of sampled rows; the full-depth run is checked through properties
+that hold at any size.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from speech_audio_encoder_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+LOGMEL_TOL = 1e-3
+EMB_REL_TOL = 2e-2
+
+
+def say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="session")
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch
+
+
+@pytest.fixture(scope="session")
+def binding_mod(torch_mod):
+    from speech_audio_encoder_amd import binding
+    binding.load_library()
+    return binding
+
+
+_WEIGHTS = {}
+
+
+def get_weights(kind):
+    if kind not in _WEIGHTS:
+        if kind == "bf16":
+            _WEIGHTS[kind] = workloads.make_weights(32, bf16=True)
+        elif kind == "tiny":
+            _WEIGHTS[kind] = workloads.workload_weights("tiny")
+        elif kind == "perturbed":
+            _WEIGHTS[kind] = workloads.make_weights(2, bf16=False, perturb=True)
+    return _WEIGHTS[kind]
+
+
+def prefix(w, n):
+    return dict(w, layers=w["layers"][:n])
+
+
+_CTX = {}
+
+
+@pytest.fixture(scope="session")
+def ctx_for(binding_mod):
+    def get(kind, n_layers, dtype):
+        key = (kind, n_layers, dtype)
+        if key not in _CTX:
+            say(f"enc_create {key}")
+            _CTX[key] = binding_mod.Encoder(prefix(get_weights(kind), n_layers), dtype=dtype)
+        return _CTX[key]
+    yield get
+    for enc in _CTX.values():
+        enc.close()
+    _CTX.clear()
+
+
+def to_dev(torch, audio):
+    return torch.from_numpy(np.ascontiguousarray(audio)).cuda()
+
+
+def check_logmel(got, audio, lengths):
+    ref = oracle.logmel_batch(audio, lengths)
+    assert got.shape == ref.shape
+    worst = 0.0
+    for b, n in enumerate(lengths):
+        f = oracle.frame_count(n)
+        if f:
+            worst = max(worst, float(np.abs(got[b, :f] - ref[b, :f]).max()))
+        assert np.all(got[b, f:] == 0.0), f"clip {b}: padded frames not zero"
+    assert worst <= LOGMEL_TOL, f"log-mel max abs error {worst:.3e}"
+    return worst
+
+
+def check_embeddings(got, ref, label):
+    got = np.asarray(got, dtype=np.float32)
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    scale = float(np.abs(ref).max()) if ref.size else 1.0
+    say(f"{label}: max abs err {err:.4e}, max |ref| {scale:.3f}, ratio {err / scale:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= EMB_REL_TOL * scale, f"{label}: {err:.3e} > {EMB_REL_TOL} * {scale:.3f}"
+
+
+# ------------------------------------------------------------------ log-mel
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
+def test_logmel_parity(name, torch_mod, ctx_for):
+    torch = torch_mod
+    say(f"logmel {name}")
+    audio, lengths = workloads.workload_audio(name)
+    enc = ctx_for("tiny", 2, "f32")
+    f_max, _ = enc_shapes_host(lengths)
+    out = torch.full((len(lengths), f_max, 128), float("nan"), device="cuda")
+    enc.logmel(to_dev(torch, audio), lengths, out=out)
+    torch.cuda.synchronize()
+    worst = check_logmel(out.cpu().numpy(), audio, lengths)
+    say(f"logmel {name}: max abs err {worst:.3e}")
+
+
+def enc_shapes_host(lengths):
+    f = oracle.frame_count(max(lengths))
+    return f, oracle.position_count(f)
+
+
+def test_logmel_edge_lengths(torch_mod, ctx_for):
+    torch = torch_mod
+    lengths = [0, 399, 400, 401, 559, 560, 1000, 16037]
+    audio, lengths = workloads.custom_audio(lengths, seed=31)
+    enc = ctx_for("tiny", 2, "f32")
+    f_max, _ = enc_shapes_host(lengths)
+    out = torch.full((len(lengths), f_max, 128), float("nan"), device="cuda")
+    enc.logmel(to_dev(torch, audio), lengths, out=out)
+    torch.cuda.synchronize()
+    check_logmel(out.cpu().numpy(), audio, lengths)
+
+
+def test_logmel_loud_and_silent_frames(torch_mod, ctx_for):
+    # full-scale square wave next to digital silence: widest dynamic range
+    torch = torch_mod
+    n = 48_000
+    x = np.zeros((1, n), np.float32)
+    x[0, :16_000] = np.sign(np.sin(2 * np.pi * 440 * np.arange(16_000) / 16_000)).astype(np.float32)
+    x[0, 32_000:] = 1e-4 * np.random.default_rng(5).standard_normal(16_000).astype(np.float32)
+    enc = ctx_for("tiny", 2, "f32")
+    out = enc.logmel(to_dev(torch, x), [n])
+    torch.cuda.synchronize()
+    check_logmel(out.cpu().numpy(), x, [n])
+
+
+# ------------------------------------------------------------------ forward
+def run_forward(torch, enc, audio, lengths, canary=True):
+    _, p_max = enc_shapes_host(lengths)
+    out = torch.empty((len(lengths), p_max, 1280), dtype=torch.bfloat16, device="cuda")
+    if canary:
+        out.fill_(float("nan"))
+    enc.forward(to_dev(torch, audio), lengths, out=out)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def test_forward_tiny_fp32_weights(torch_mod, ctx_for):
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("tiny")
+    w = get_weights("tiny")
+    got = run_forward(torch, ctx_for("tiny", 2, "f32"), audio, lengths)
+    ref = oracle.encode_batch(audio, lengths, w)
+    assert got.shape == (1, 13, 1280)
+    check_embeddings(got[0], ref[0], "tiny")
+
+
+def test_forward_clip30_full_depth(torch_mod, ctx_for):
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("clip30")
+    got = run_forward(torch, ctx_for("bf16", 32, "bf16"), audio, lengths)
+    say("oracle clip30 (32 layers)")
+    ref = oracle.encode_batch(audio, lengths, get_weights("bf16"))
+    assert got.shape == (1, 375, 1280)
+    check_embeddings(got[0], ref[0], "clip30")
+
+
+def test_forward_batch64_sampled_clips(torch_mod, ctx_for):
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("batch64")
+    got = run_forward(torch, ctx_for("bf16", 32, "bf16"), audio, lengths)
+    pos = [oracle.position_count(oracle.frame_count(n)) for n in lengths]
+    assert got.shape == (64, max(pos), 1280)
+    for b in range(64):
+        assert np.all(got[b, pos[b]:] == 0.0)
+    picks = sorted({int(np.argmin(lengths)), int(np.argmax(lengths)), 17, 42})
+    for b in picks:
+        say(f"oracle batch64 clip {b} ({lengths[b]} samples)")
+        ref = oracle.encode(audio[b, :lengths[b]], get_weights("bf16"))
+        check_embeddings(got[b, :pos[b]], ref, f"batch64 clip {b}")
+
+
+def test_forward_long10m_two_layers(torch_mod, ctx_for):
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("long10m")
+    got = run_forward(torch, ctx_for("bf16", 2, "bf16"), audio, lengths)
+    say("oracle long10m (2 layers, all 7500 rows)")
+    ref = oracle.encode(audio[0], prefix(get_weights("bf16"), 2))
+    check_embeddings(got[0], ref, "long10m/2 layers")
+
+
+def test_forward_hour_one_layer_sampled_rows(torch_mod, ctx_for):
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("hour")
+    got = run_forward(torch, ctx_for("bf16", 1, "bf16"), audio, lengths)
+    assert got.shape == (1, 45_000, 1280)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 44_871, 44_999],
+                                     np.random.default_rng(0).integers(0, 45_000, 58)]))
+    say(f"oracle hour (1 layer, {len(rows)} rows)")
+    ref = oracle.encode(audio[0], prefix(get_weights("bf16"), 1), rows=rows)
+    check_embeddings(got[0, rows], ref, "hour/1 layer")
+
+
+@pytest.mark.parametrize("name", ["long10m", "hour"])
+def test_forward_full_depth_properties(name, torch_mod, ctx_for):
+    # 32 layers at full length: finite, final-LN moments (gain 1, bias 0),
+    # deterministic across calls.
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio(name)
+    enc = ctx_for("bf16", 32, "bf16")
+    a = run_forward(torch, enc, audio, lengths)
+    b = run_forward(torch, enc, audio, lengths, canary=False)
+    assert np.all(np.isfinite(a))
+    np.testing.assert_array_equal(a, b)
+    mean = a[0].mean(axis=1)
+    var = a[0].var(axis=1)
+    say(f"{name}: |row mean| max {np.abs(mean).max():.2e}, row var in [{var.min():.4f}, {var.max():.4f}]")
+    assert np.abs(mean).max() < 1e-2
+    assert np.abs(var - 1.0).max() < 2e-2
+
+
+def test_forward_ragged_perturbed_weights(torch_mod, ctx_for):
+    # nonzero biases and gains; clips spanning several query/key tiles, exact
+    # tile multiples, a clip of one position and clips with no position.
+    torch = torch_mod
+    lengths = [200_000, 400, 0, 399, 16_000, 400 + 1023 * 160, 81_840]
+    audio, lengths = workloads.custom_audio(lengths, seed=41)
+    w = get_weights("perturbed")
+    got = run_forward(torch, ctx_for("perturbed", 2, "f32"), audio, lengths)
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        assert np.all(got[b, p:] == 0.0), f"clip {b}: padded rows not zero"
+        if p:
+            ref = oracle.encode(audio[b, :n], w)
+            check_embeddings(got[b, :p], ref, f"ragged clip {b} (P={p})")
+
+
+def test_forward_batch_invariance(torch_mod, ctx_for):
+    torch = torch_mod
+    audio, lengths = workloads.custom_audio([123_456, 480_000, 50_000], seed=51)
+    enc = ctx_for("bf16", 2, "bf16")
+    together = run_forward(torch, enc, audio, lengths)
+    for b, n in enumerate(lengths):
+        alone = run_forward(torch, enc, audio[b:b + 1, :n], [n])
+        p = alone.shape[1]
+        np.testing.assert_array_equal(together[b, :p], alone[0])
+
+
+def test_forward_workspace_cap_and_errors_leave_output(torch_mod, ctx_for, binding_mod):
+    torch = torch_mod
+    binding = binding_mod
+    enc = ctx_for("tiny", 2, "f32")
+    audio, lengths = workloads.workload_audio("tiny")
+    dev = to_dev(torch, audio)
+    out = torch.full((1, 13, 1280), float("nan"), dtype=torch.bfloat16, device="cuda")
+    os.environ["ENC_WORKSPACE_CAP_BYTES"] = "1000"
+    try:
+        code = binding.enc_forward_raw(enc.ctx, dev.data_ptr(), lengths, out.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream)
+    finally:
+        del os.environ["ENC_WORKSPACE_CAP_BYTES"]
+    assert code == binding.ENC_ERR_NOMEM
+    code = binding.enc_forward_raw(enc.ctx, dev.data_ptr(), [-5], out.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    assert code == binding.ENC_ERR_ARG
+    code = binding.enc_forward_raw(enc.ctx, dev.data_ptr(), [57_600_001], out.data_ptr(),
+                                   torch.cuda.current_stream().cuda_stream)
+    assert code == binding.ENC_ERR_TOO_LONG
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
+    # and the context still works afterwards
+    got = run_forward(torch, enc, audio, lengths)
+    assert np.all(np.isfinite(got))
+
+
+def test_forward_all_clips_too_short(torch_mod, ctx_for):
+    torch = torch_mod
+    enc = ctx_for("tiny", 2, "f32")
+    audio, lengths = workloads.custom_audio([10, 399], seed=61)
+    out = enc.forward(to_dev(torch, audio), lengths)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (2, 0, 1280)

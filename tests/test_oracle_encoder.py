@@ -293,3 +293,13 @@ def test_encoder_output_is_normalised():
     e = oracle.encode(audio[0], w)
     np.testing.assert_allclose(e.mean(axis=1), 0.0, atol=1e-5)
     np.testing.assert_allclose(e.var(axis=1), 1.0, atol=1e-3)
+
+
+def test_row_subset_matches_full_layer():
+    w = small_weights(n_layers=2)
+    rng = np.random.default_rng(16)
+    feats = rng.standard_normal((80, 128)).astype(np.float32)
+    full = oracle.encode_from_logmel(feats, w)
+    rows = np.array([0, 3, 9])
+    np.testing.assert_allclose(oracle.encode_from_logmel(feats, w, rows=rows), full[rows],
+                               rtol=1e-5, atol=1e-5)
