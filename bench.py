@@ -1,0 +1,222 @@
+"""Throughput of the speech-encoder forward pass on one MI355X.
+
+One step = one ``enc_forward`` call over one batch of synthetic audio already
+resident in HBM: log-mel frontend, 8-frame stack, input projection, 32
+Transformer layers, final norm (bf16 operands, fp32 accumulation).  Prints one
+JSON line with audio-seconds encoded per second, the achieved fraction of the
+bf16 MFMA peak, the roofline of the dominant kernel (timed with HIP events on
+the library's stream during the timed steps) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from speech_audio_encoder_amd import workloads  # noqa: E402
+
+SAMPLE_RATE = 16000
+D, FF, DIN, H, DH = 1280, 5120, 1024, 10, 128
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+DESCRIPTIONS = {
+    "tiny": "1 clip x 1.0 s tones, 2-layer encoder",
+    "clip30": "1 clip x 30 s tones, 32-layer encoder",
+    "batch64": "64 clips x U(5-30 s) tones (variable length, masked), 32-layer encoder",
+    "long10m": "1 clip x 600 s segment mix, 32-layer encoder, full attention",
+    "hour": "1 clip x 3600 s segment mix, 32-layer encoder, full attention",
+}
+
+
+def positions(n):
+    f = 0 if n < 400 else 1 + (n - 400) // 160
+    return (f + 7) // 8
+
+
+def gemm_flops_per_layer(rows):
+    return 2 * rows * (3 * D * D + D * D + 2 * D * FF)
+
+
+def attention_flops_per_layer(pos):
+    return sum(4 * p * p * DH * H for p in pos)
+
+
+def kernel_flops(name, rows, pos):
+    """Algorithmic MFMA flops of one launch of a kernel class."""
+    return {
+        "gemm_in": 2 * rows * D * DIN,
+        "gemm_qkv": 2 * rows * 3 * D * D,
+        "gemm_o": 2 * rows * D * D,
+        "gemm_up": 2 * rows * D * FF,
+        "gemm_down": 2 * rows * FF * D,
+        "attention": attention_flops_per_layer(pos),
+    }.get(name)
+
+
+def kernel_bytes(name, rows, lengths):
+    """Algorithmic HBM bytes of one launch of the memory-bound kernel classes."""
+    return {
+        "frontend": 4 * int(sum(lengths)) + 2 * 128 * 8 * rows,   # audio in, bf16 stack out
+        "layernorm": rows * D * (4 + 2),
+        "qknorm_rope": rows * (2 * D * 2 * 2 + D * 2 * 2),         # q,k read+write, v read+write
+        "final_norm": rows * D * (4 + 2),
+    }.get(name)
+
+
+def cpu_baseline(audio, lengths, weights, budget_s=12.0):
+    """Time the oracle (as it stands) on whole clips until ~budget_s of CPU."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    order = np.argsort(lengths)          # shortest first keeps the sample bounded
+    done_samples, spent, clips = 0, 0.0, 0
+    for b in order:
+        n = int(lengths[b])
+        t0 = time.perf_counter()
+        oracle.encode(audio[b, :n], weights)
+        spent += time.perf_counter() - t0
+        done_samples += n
+        clips += 1
+        if spent >= budget_s:
+            break
+    secs = done_samples / SAMPLE_RATE
+    return {"value": secs / spent, "unit": "audio-s/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{clips} whole clip(s) of the workload, shortest first, "
+                      f"{secs:.1f} audio-s, 32 layers, {spent:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batch64", choices=list(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true",
+                    help="also time every kernel class (extra untimed steps)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the encoder batch would be split by clips across ranks, which this "
+              "build does not implement).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from speech_audio_encoder_amd import binding
+
+    torch.cuda.set_device(0)
+    audio, lengths = workloads.workload_audio(args.workload)
+    weights = workloads.workload_weights(args.workload)
+    n_layers = len(weights["layers"])
+    dtype = "bf16" if workloads.WORKLOADS[args.workload][3] else "f32"
+    enc = binding.Encoder(weights, dtype=dtype)
+    x = torch.from_numpy(audio).cuda()
+    lengths = [int(n) for n in lengths]
+    pos = [positions(n) for n in lengths]
+    rows = sum(pos)
+    _, p_max = binding.enc_shapes(lengths)
+    out = torch.empty((len(lengths), p_max, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        enc.forward(x, lengths, out=out)
+    torch.cuda.synchronize()
+
+    breakdown = {}
+    if args.breakdown:
+        for kname in binding.KERNELS:
+            binding.enc_profile_kernel(enc.ctx, kname)
+            enc.forward(x, lengths, out=out)
+            n, ms = binding.enc_profile_read(enc.ctx)
+            breakdown[kname] = {"launches": n, "ms": round(ms, 4)}
+        binding.enc_profile_kernel(enc.ctx, -1)
+        torch.cuda.synchronize()
+
+    # Dominant kernel: the FFN expansion GEMM (a third of all MFMA flops here);
+    # it is bracketed with HIP events on the library's stream during the timed steps.
+    dom = "gemm_up"
+    if breakdown:
+        dom = max(breakdown, key=lambda k: breakdown[k]["ms"])
+    binding.enc_profile_kernel(enc.ctx, dom)
+
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        enc.forward(x, lengths, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    n_dom, dom_ms = binding.enc_profile_read(enc.ctx)
+    binding.enc_profile_kernel(enc.ctx, -1)
+
+    ms_per_step = gpu_ms / args.steps
+    audio_s = sum(lengths) / SAMPLE_RATE
+    value = audio_s / (ms_per_step / 1000.0)
+    total_flops = (n_layers * (gemm_flops_per_layer(rows) + attention_flops_per_layer(pos))
+                   + 2 * rows * D * DIN)
+    mfma_pct = 100.0 * total_flops / (ms_per_step / 1000.0) / (PEAK_BF16_TFLOPS * 1e12)
+
+    avg_ms = dom_ms / max(n_dom, 1)
+    fl = kernel_flops(dom, rows, pos)
+    if fl is not None:
+        achieved = fl / (avg_ms / 1000.0) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(avg_ms, 5), "launches": n_dom,
+                "flops_per_launch": fl}
+    else:
+        by = kernel_bytes(dom, rows, lengths)
+        achieved = by / (avg_ms / 1000.0) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None, "avg_launch_ms": round(avg_ms, 5), "launches": n_dom,
+                "bytes_per_launch": by}
+
+    result = {
+        "metric": "audio-seconds encoded/sec (bf16 encoder fwd) + % MFMA peak, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "audio-s/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "wall_ms_per_step": round(1000.0 * wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "mfma_pct_of_peak": round(mfma_pct, 2),
+        "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
+                   "clips": len(lengths), "audio_seconds": round(audio_s, 3),
+                   "positions": rows, "layers": n_layers,
+                   "algorithmic_tflop_per_step": round(total_flops / 1e12, 4)},
+        "roofline": roof,
+    }
+    if breakdown:
+        result["kernel_ms_per_step"] = breakdown
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(audio, lengths, weights)
+    enc.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,10 +13,17 @@
 // Stockham FFT of length 256 (four stages, one radix-4 butterfly per lane per
 // stage, ping-pong through LDS) gives Z, and the split
 //   X[k] = (Z[k] + conj Z[-k]) / 2 - i W512^k (Z[k] - conj Z[-k]) / 2
-// recovers the 257 non-negative bins.  Twiddles, window and mel weights come
-// from tables the host builds in float64 and rounds once to float32.
+// recovers the 257 non-negative bins.
+//
+// Precision: the window, transform, power and mel sums run in float64 (tables
+// built on the host in float64), only the log is rounded to float32.  Below
+// 1 kHz the mel bands are narrower than one bin, so a band's energy can be a
+// single bin's power; when that power is small, a float32 transform's absolute
+// error (about 1e-6 of the frame's spectral norm) turns into a log error of
+// order 1e-3.  In float64 that error is ~1e-11.  The cost is ~14 kflop of
+// fp64 per frame, small next to the frame's 2.3 KB of memory traffic.
 // Memory traffic is the audio read (frames overlap by 240 samples; the overlap
-// is served from cache) plus the feature write: HBM-bound by design.
+// is served from cache) plus the feature write.
 
 #include "common.h"
 #include "kernels.h"
@@ -54,7 +61,7 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
     bf16_t* __restrict__ out_bf16)            // [sum 8 P_b, 128]       (STACKED)
 {
   __shared__ c32 buf[WAVES][2][256];
-  __shared__ float pw[WAVES][NBIN + 3];
+  __shared__ double pw[WAVES][NBIN + 3];
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -83,11 +90,10 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
       const int n = lane + 64 * r;
       if (valid && n < WIN / 2) {
         // the row stride (longest clip) may be odd: two 4-byte loads
-        const float s0 = x[2 * n], s1 = x[2 * n + 1];
-        const float2 w = *reinterpret_cast<const float2*>(tab->hann + 2 * n);
-        v[r] = {s0 * w.x, s1 * w.y};
+        const double s0 = x[2 * n], s1 = x[2 * n + 1];
+        v[r] = {s0 * tab->hann[2 * n], s1 * tab->hann[2 * n + 1]};
       } else {
-        v[r] = {0.f, 0.f};
+        v[r] = {0.0, 0.0};
       }
     }
   }
@@ -127,12 +133,12 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
       const c32 a = Z[k & 255];
       const c32 zc = Z[(256 - k) & 255];
       const c32 bconj = {zc.re, -zc.im};
-      const c32 e = {0.5f * (a.re + bconj.re), 0.5f * (a.im + bconj.im)};
-      const c32 d = {0.5f * (a.re - bconj.re), 0.5f * (a.im - bconj.im)};
+      const c32 e = {0.5 * (a.re + bconj.re), 0.5 * (a.im + bconj.im)};
+      const c32 d = {0.5 * (a.re - bconj.re), 0.5 * (a.im - bconj.im)};
       // o = -i d, then X = e + W512^k o
       const c32 o = {d.im, -d.re};
       const c32 wo = cmul(tab->tw512[k], o);
-      const float xr = e.re + wo.re, xi = e.im + wo.im;
+      const double xr = e.re + wo.re, xi = e.im + wo.im;
       pw[wave][k] = xr * xr + xi * xi;
     }
   }
@@ -146,10 +152,10 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
     if (valid) {
       const int k0 = tab->mel_start[m];
       const int cnt = tab->mel_count[m];
-      const float* wm = tab->mel_w + tab->mel_offset[m];
-      float acc = 0.f;
+      const double* wm = tab->mel_w + tab->mel_offset[m];
+      double acc = 0.0;
       for (int i = 0; i < cnt; ++i) acc += wm[i] * pw[wave][k0 + i];
-      val = logf(acc + 5.9604644775390625e-08f);   // 2^-24 guard
+      val = (float)log(acc + 5.9604644775390625e-08);   // 2^-24 guard
     }
     if (STACKED) out_bf16[g * NMEL + m] = f32_to_bf16(val);
     else out_f32[g * NMEL + m] = val;

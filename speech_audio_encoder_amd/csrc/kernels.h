@@ -11,20 +11,20 @@
 namespace enc {
 
 struct Cpx {
-  float re, im;
+  double re, im;
 };
 
 constexpr int MEL_NNZ_MAX = 1024;
 
 // Constant tables of the frontend, built on the host in float64.
 struct FrontendTables {
-  float hann[WIN];              // periodic Hann window
+  double hann[WIN];             // periodic Hann window
   Cpx tw256[256];               // exp(-2 pi i m / 256)
-  Cpx tw512[NBIN];              // exp(-2 pi i k / 512), k = 0..256
+  Cpx tw512[NBIN + 1];          // exp(-2 pi i k / 512), k = 0..256 (+1 pad)
   int32_t mel_start[NMEL];      // first bin with nonzero weight
   int32_t mel_count[NMEL];      // number of bins from mel_start
   int32_t mel_offset[NMEL];     // offset of the band's weights in mel_w
-  float mel_w[MEL_NNZ_MAX];
+  double mel_w[MEL_NNZ_MAX];
 };
 
 // ---------------------------------------------------------------- frontend

@@ -61,14 +61,14 @@ double mel_to_hz(double m) {
 
 bool build_frontend_tables(FrontendTables* t) {
   const double pi = 3.14159265358979323846;
-  for (int n = 0; n < WIN; ++n) t->hann[n] = (float)(0.5 - 0.5 * std::cos(2.0 * pi * n / WIN));
+  for (int n = 0; n < WIN; ++n) t->hann[n] = 0.5 - 0.5 * std::cos(2.0 * pi * n / WIN);
   for (int m = 0; m < 256; ++m) {
     const double a = -2.0 * pi * m / 256.0;
-    t->tw256[m] = {(float)std::cos(a), (float)std::sin(a)};
+    t->tw256[m] = {std::cos(a), std::sin(a)};
   }
-  for (int k = 0; k < NBIN; ++k) {
+  for (int k = 0; k <= NBIN; ++k) {
     const double a = -2.0 * pi * k / 512.0;
-    t->tw512[k] = {(float)std::cos(a), (float)std::sin(a)};
+    t->tw512[k] = {std::cos(a), std::sin(a)};
   }
   // 130 band edges equally spaced in mel from 0 Hz to 8 kHz; triangle m rises
   // from edge m to edge m+1 and falls to edge m+2 (linear in Hz), peak 1.
@@ -88,7 +88,7 @@ bool build_frontend_tables(FrontendTables* t) {
         // bands are contiguous runs of bins
         if (k != first + count) return false;
         if (off + count >= MEL_NNZ_MAX) return false;
-        t->mel_w[off + count] = (float)w;
+        t->mel_w[off + count] = w;
         ++count;
       }
     }
