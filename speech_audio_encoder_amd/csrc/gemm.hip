@@ -9,15 +9,27 @@
 // "How audio and speakers reach the language model" (width 1,280, feed-forward
 // expansion four; exact-erf GELU is this build's reading of the activation).
 //
-// Design: a workgroup owns a BM x BN output tile and walks K in steps of 64.
-// Each step stages A and W tiles in LDS (16-byte chunks, XOR-swizzled by row
-// so the MFMA operand reads spread over the banks) while the next step's tiles
-// are already in flight into registers.  The MFMA is v_mfma_f32_32x32x16_bf16
-// with W as its first operand, so each lane ends up owning one output row and
-// runs of four consecutive output columns: the epilogue stores 8- or 16-byte
-// vectors and adds bias / residual / GELU in registers.  Workgroups are
-// renumbered so that the ones the dispatcher sends to one XCD walk adjacent
-// tiles and share that XCD's L2.
+// Two kernels share the output tiling (256 x 256 tiles, numbered in groups of
+// four tile rows so that neighbouring tiles share A rows and W columns):
+//
+//  * gemm_big_kernel -- persistent, one workgroup per CU, four wavefronts of
+//    128 x 128 outputs each (16 MFMA 32x32x16 accumulators, held in AGPRs).
+//    It covers every full round of tiles.  Operands go straight from global
+//    memory into LDS with global_load_lds_dwordx4 (no register staging; the
+//    XOR swizzle that keeps the MFMA operand reads conflict-free is applied on
+//    the global side by choosing which 16-byte chunk each lane fetches).  A
+//    four-stage ring of 32-wide K steps (4 x 32 KB) keeps three steps of loads
+//    in flight; one barrier per step.  The stream of steps runs on across the
+//    workgroup's tiles, so the next tile's loads overlap this tile's epilogue.
+//  * gemm_small_kernel -- the tiles left after the last full round, each cut
+//    into four 128 x 128 pieces so that the final partial round finishes in a
+//    quarter of the time (a 256 x 256 tile per CU would leave most CUs idle).
+//
+// Each lane ends up owning one output row and runs of four consecutive
+// columns: the epilogue adds bias / residual / GELU in registers and stores
+// 8- or 16-byte vectors.
+
+#include <cstdlib>
 
 #include "common.h"
 #include "kernels.h"
@@ -26,175 +38,406 @@ namespace enc {
 
 namespace {
 
-constexpr int BK = 64;
+constexpr int BIG = 256;    // big tile edge
+constexpr int BKS = 32;     // big kernel K step
+constexpr int NSTAGE = 4;   // LDS ring depth of the big kernel
+constexpr int GROUP_M = 4;  // tile rows per ordering group
 
+// Exact-erf GELU, x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), with erf taken from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+// t = 1 / (1 + p z), z >= 0, absolute error below 1.5e-7 -- far below the
+// bf16 rounding of the output -- at one reciprocal, one exponential and five
+// fused multiply-adds instead of a general-purpose erf.
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = 1.0f - poly * __expf(-z * z);      // erf(|x| / sqrt 2)
+  const float phi2 = x >= 0.0f ? 1.0f + e : 1.0f - e;  // 2 Phi(x)
+  return 0.5f * x * phi2;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, Epilogue EPI>
-__global__ __launch_bounds__(64 * WAVES_M * WAVES_N) void gemm_kernel(
-    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
-    const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int N, int K,
-    int tiles_m, int tiles_n) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int WTM = BM / WAVES_M;
-  constexpr int WTN = BN / WAVES_N;
-  constexpr int FM = WTM / 32;
-  constexpr int FN = WTN / 32;
-  constexpr int A_CHUNKS = BM * BK / 8;       // 16-byte chunks per A tile
-  constexpr int W_CHUNKS = BN * BK / 8;
-  constexpr int A_PER_T = A_CHUNKS / NT;
-  constexpr int W_PER_T = W_CHUNKS / NT;
-  static_assert(A_CHUNKS % NT == 0 && W_CHUNKS % NT == 0, "tile/thread mismatch");
+// Big-tile coordinates of tile t: groups of GROUP_M tile rows, column-major
+// inside a group, so that consecutive tiles (which run together on one XCD)
+// touch few distinct A row blocks and W column blocks.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = GROUP_M * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int r = t - group * per_group;
+  tm = first_m + r % gsize;
+  tn = r / gsize;
+}
 
-  __shared__ uint4 sA[A_CHUNKS];
-  __shared__ uint4 sW[W_CHUNKS];
-
-  // XCD-aware renumbering: hardware block b runs on XCD b % 8; give each XCD a
-  // contiguous range of logical tiles (n fastest, so an XCD reuses A rows).
-  const int nblocks = tiles_m * tiles_n;
-  const int b = blockIdx.x;
-  int logical;
-  {
-    const int per = nblocks / 8, rem = nblocks % 8;
-    const int xcd = b % 8, idx = b / 8;
-    logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + idx;
+// Apply the epilogue to four consecutive columns n..n+3 of row m; bv holds
+// their biases.
+template <Epilogue EPI>
+__device__ __forceinline__ void store4(void* __restrict__ Cv, int64_t ldc, int64_t m, int n,
+                                       float4 bv, float a0, float a1, float a2, float a3) {
+  float o0 = a0 + bv.x, o1 = a1 + bv.y, o2 = a2 + bv.z, o3 = a3 + bv.w;
+  if constexpr (EPI == Epilogue::kBiasGeluBf16) {
+    o0 = gelu_erf(o0); o1 = gelu_erf(o1); o2 = gelu_erf(o2); o3 = gelu_erf(o3);
   }
-  const int tm = logical / tiles_n;
-  const int tn = logical % tiles_n;
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
+  if constexpr (EPI == Epilogue::kBiasBf16 || EPI == Epilogue::kBiasGeluBf16) {
+    bf16_t* C = reinterpret_cast<bf16_t*>(Cv);
+    *reinterpret_cast<uint2*>(C + m * ldc + n) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+  } else {
+    float* C = reinterpret_cast<float*>(Cv);
+    float4* dst = reinterpret_cast<float4*>(C + m * ldc + n);
+    if constexpr (EPI == Epilogue::kBiasResidualF32) {
+      const float4 r = *dst;
+      o0 += r.x; o1 += r.y; o2 += r.z; o3 += r.w;
+    }
+    *dst = make_float4(o0, o1, o2, o3);
+  }
+}
+
+// Biases of columns nb + 8q + 4 lhi .. +3 for q = 0..3.  nb is uniform across
+// the wavefront, so the 32 values come through scalar loads (which do not
+// queue behind the vector-memory DMAs still in flight); each lane then keeps
+// the half that matches its lhi.
+__device__ __forceinline__ void load_bias32(const float* __restrict__ bias, int nb, int lhi,
+                                            float4 (&bv)[4]) {
+  nb = __builtin_amdgcn_readfirstlane(nb);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 lo = *reinterpret_cast<const float4*>(bias + nb + 8 * q);
+    const float4 hi = *reinterpret_cast<const float4*>(bias + nb + 8 * q + 4);
+    bv[q] = lhi ? hi : lo;
+  }
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane DMA from global memory into LDS (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds + 16 l.
+__device__ __forceinline__ void dma16(const void* gptr, lds_void* lds) {
+  __builtin_amdgcn_global_load_lds(gptr, lds, 16, 0, 0);
+}
+
+// ----------------------------------------------------------- big (persistent)
+template <Epilogue EPI>
+__global__ __launch_bounds__(256, 1) void gemm_big_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
+    const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int K,
+    int tiles_m, int tiles_n, int n_big) {
+  // Stage layout (uint4 units): A rows 0..255 x 4 chunks, then W rows x 4.
+  constexpr int STG = 2 * BIG * BKS / 8;
+  // Distinct arrays, referenced statically, so the compiler can tell a DMA
+  // into one stage from reads of another and does not wait on it.
+  __shared__ uint4 st0[STG];
+  __shared__ uint4 st1[STG];
+  __shared__ uint4 st2[STG];
+  __shared__ uint4 st3[STG];
+
+  const int G = gridDim.x;
+  const int wg = blockIdx.x;
+  // Hardware block wg runs on XCD wg % 8: give each XCD a contiguous slot range.
+  const int slot = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
+  const int my_tiles = slot < n_big ? (n_big - 1 - slot) / G + 1 : 0;
+  const int KT = K / BKS;
+  const int S = my_tiles * KT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave % WAVES_M;
-  const int wn = wave / WAVES_M;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
 
-  // Global -> register staging.
-  uint4 ra[A_PER_T], rw[W_PER_T];
-  auto load_tiles = [&](int k0) {
+  // DMA lane mapping: wavefront load i of wave w covers tile rows
+  // (w*4 + i)*16 + lane/4 (16 rows of 64 B); lane%4 is the physical chunk,
+  // holding logical chunk (lane%4) ^ ((row/2) % 4).
+  const int drow = wave * 64 + (lane >> 2);
+  const int dcol = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
+  // Issue state: tile ir of this workgroup, k step ikt, and the per-lane
+  // source rows of that tile (rows past M re-read row M-1; dropped later).
+  int ir = 0, ikt = 0;
+  const bf16_t* ia[4];
+  const bf16_t* iw[4];
+  auto set_issue_tile = [&]() {
+    if (ir >= my_tiles) return;
+    int tm, tn;
+    tile_coords(ir * G + slot, tiles_m, tiles_n, tm, tn);
+    const int64_t am = (int64_t)tm * BIG;
+    const int64_t wn0 = (int64_t)tn * BIG;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int row = c >> 3, kc = c & 7;
-      const int64_t gm = m0 + row;
-      if (gm < M)
-        ra[i] = *reinterpret_cast<const uint4*>(A + gm * lda + k0 + kc * 8);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      ia[i] = A + min<int64_t>(am + drow + 16 * i, M - 1) * lda + dcol;
+      iw[i] = W + (wn0 + drow + 16 * i) * ldw + dcol;
+    }
+  };
+  auto issue = [&](uint4* stage) {
+    if (ir >= my_tiles) return;
+    const int k0 = ikt * BKS;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dma16(ia[i] + k0, (lds_void*)(stage + (wave * 4 + i) * 64));
+      dma16(iw[i] + k0, (lds_void*)(stage + BIG * 4 + (wave * 4 + i) * 64));
+    }
+    if (++ikt == KT) {
+      ikt = 0;
+      ++ir;
+      set_issue_tile();
+    }
+  };
+  set_issue_tile();
+
+  // Operand reads: row r of a stage, logical chunk c -> uint4 r*4 + (c ^ ((r/2)%4)).
+  const int rsw = (l32 >> 1) & 3;
+  const int wofs = BIG * 4 + (wn * 128 + l32) * 4;
+  const int aofs = (wm * 128 + l32) * 4;
+
+  f32x16 acc[4][4];
+  bf16x8 fw0[4], fa0[4], fw1[4], fa1[4];
+  auto load = [&](const uint4* sp, int sl, bf16x8 (&fw)[4], bf16x8 (&fa)[4]) {
+    const int pc = (2 * sl + lhi) ^ rsw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 u = sp[wofs + i * 128 + pc];
+      fw[i] = *reinterpret_cast<const bf16x8*>(&u);
     }
 #pragma unroll
-    for (int i = 0; i < W_PER_T; ++i) {
-      const int c = tid + i * NT;
+    for (int j = 0; j < 4; ++j) {
+      const uint4 u = sp[aofs + j * 128 + pc];
+      fa[j] = *reinterpret_cast<const bf16x8*>(&u);
+    }
+  };
+  auto mma = [&](const bf16x8 (&fw)[4], const bf16x8 (&fa)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
+  };
+  // Spread 8 LDS reads between 16 MFMAs.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
+
+  issue(st0);
+  issue(st1);
+  issue(st2);
+  int g = 0;
+  int since_epi = 0;   // steps since the last epilogue (its stores count in vmcnt)
+  bool pend = false;   // fw1/fa1 hold the second half of the previous step
+
+  // One K step on stage `cur`; the loads of step g + 3 go to `nxt`.  Before the
+  // barrier each wave waits for its own loads of step g (the two younger steps
+  // may stay in flight) and for its LDS reads of step g - 1 (whose stage the
+  // loads of step g + 3 overwrite).  The barrier is the bare s_barrier: the
+  // waits above are all the ordering it needs, and a fenced barrier would also
+  // wait for the younger loads.
+#define ENC_BIG_STEP(cur, nxt)                                                   \
+  do {                                                                           \
+    if (g + 2 >= S) __builtin_amdgcn_s_waitcnt(0);                               \
+    else if (since_epi > 0 && since_epi < 4) asm volatile("s_waitcnt vmcnt(63)"); \
+    else asm volatile("s_waitcnt vmcnt(16)");                                    \
+    asm volatile("s_waitcnt lgkmcnt(0)");                                        \
+    __builtin_amdgcn_s_barrier();                                                \
+    load(cur, 0, fw0, fa0);                                                      \
+    issue(nxt);                                                                  \
+    if (pend) { mma(fw1, fa1); interleave(); }                                   \
+    load(cur, 1, fw1, fa1);                                                      \
+    mma(fw0, fa0);                                                               \
+    interleave();                                                                \
+    pend = true;                                                                 \
+    ++g;                                                                         \
+    if (since_epi > 0) ++since_epi;                                              \
+  } while (0)
+
+  for (int r = 0; r < my_tiles; ++r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+    for (int kt = 0; kt < KT; kt += NSTAGE) {
+      ENC_BIG_STEP(st0, st3);
+      ENC_BIG_STEP(st1, st0);
+      ENC_BIG_STEP(st2, st1);
+      ENC_BIG_STEP(st3, st2);
+    }
+    mma(fw1, fa1);
+    pend = false;
+
+    int tm, tn;
+    tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
+    const int64_t mb = (int64_t)tm * BIG + wm * 128 + l32;
+    const int nw = tn * BIG + wn * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 bv[4];
+      load_bias32(bias, nw + i * 32, lhi, bv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t m = mb + j * 32;
+        if (m < M) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            store4<EPI>(Cv, ldc, m, nw + i * 32 + 8 * q + 4 * lhi, bv[q], acc[i][j][4 * q],
+                        acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        }
+      }
+    }
+    since_epi = 1;
+  }
+#undef ENC_BIG_STEP
+}
+
+// ------------------------------------------------------------- small (tail)
+// Tiles [t_begin, t_end) of the big tiling, each as four 128 x 128 pieces;
+// 128 x 128 per workgroup, four wavefronts of 64 x 64, K in steps of 64
+// through registers and one LDS buffer.
+constexpr int SBK = 64;
+
+template <Epilogue EPI>
+__global__ __launch_bounds__(256) void gemm_small_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
+    const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int K,
+    int tiles_m, int tiles_n, int t_begin) {
+  constexpr int BM = 128, BN = 128;
+  constexpr int CH = BM * SBK / 8;          // 16-byte chunks per operand tile
+  __shared__ uint4 sA[CH];
+  __shared__ uint4 sW[CH];
+
+  const int piece = blockIdx.x & 3;
+  int tm, tn;
+  tile_coords(t_begin + (int)(blockIdx.x >> 2), tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BIG + (piece & 1) * BM;
+  const int64_t n0 = (int64_t)tn * BIG + (piece >> 1) * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+
+  uint4 ra[4], rw[4];
+  auto load_tiles = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * 256;
       const int row = c >> 3, kc = c & 7;
-      rw[i] = *reinterpret_cast<const uint4*>(W + (int64_t)(n0 + row) * ldw + k0 + kc * 8);
+      const int64_t gm = min<int64_t>(m0 + row, M - 1);
+      ra[i] = *reinterpret_cast<const uint4*>(A + gm * lda + k0 + kc * 8);
+      rw[i] = *reinterpret_cast<const uint4*>(W + (n0 + row) * ldw + k0 + kc * 8);
     }
   };
   auto store_tiles = [&]() {
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int c = tid + i * NT;
+    for (int i = 0; i < 4; ++i) {
+      const int c = tid + i * 256;
       const int row = c >> 3, kc = c & 7;
       sA[row * 8 + (kc ^ (row & 7))] = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < W_PER_T; ++i) {
-      const int c = tid + i * NT;
-      const int row = c >> 3, kc = c & 7;
       sW[row * 8 + (kc ^ (row & 7))] = rw[i];
     }
   };
 
-  f32x16 acc[FN][FM];
+  f32x16 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < FN; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int l32 = lane & 31;
-  const int lhi = lane >> 5;
-
   load_tiles(0);
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  for (int k0 = 0; k0 < K; k0 += SBK) {
     __syncthreads();
     store_tiles();
     __syncthreads();
-    if (k0 + BK < K) load_tiles(k0 + BK);
+    if (k0 + SBK < K) load_tiles(k0 + SBK);
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
+    for (int s = 0; s < SBK / 16; ++s) {
       const int chunk = 2 * s + lhi;
-      bf16x8 fw[FN], fa[FM];
+      bf16x8 fw[2], fa[2];
 #pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        const int row = wn * WTN + i * 32 + l32;
+      for (int i = 0; i < 2; ++i) {
+        const int row = wn * 64 + i * 32 + l32;
         const uint4 u = sW[row * 8 + (chunk ^ (row & 7))];
         fw[i] = *reinterpret_cast<const bf16x8*>(&u);
       }
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int row = wm * WTM + j * 32 + l32;
+      for (int j = 0; j < 2; ++j) {
+        const int row = wm * 64 + j * 32 + l32;
         const uint4 u = sA[row * 8 + (chunk ^ (row & 7))];
         fa[j] = *reinterpret_cast<const bf16x8*>(&u);
       }
 #pragma unroll
-      for (int i = 0; i < FN; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < FM; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
     }
   }
 
-  // Epilogue.  Block (i, j) holds C^T: lane -> row m = ... + l32, register v
-  // -> column n = ... + 8 (v / 4) + 4 lhi + v % 4.
 #pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int64_t m = m0 + wm * WTM + j * 32 + l32;
-    if (m >= M) continue;
+  for (int i = 0; i < 2; ++i) {
+    const int nw = (int)(n0 + wn * 64 + i * 32);
+    float4 bv[4];
+    load_bias32(bias, nw, lhi, bv);
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+    for (int j = 0; j < 2; ++j) {
+      const int64_t m = m0 + wm * 64 + j * 32 + l32;
+      if (m >= M) continue;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * WTN + i * 32 + 8 * g + 4 * lhi;
-        const float4 bv = *reinterpret_cast<const float4*>(bias + n);
-        float o0 = acc[i][j][4 * g + 0] + bv.x;
-        float o1 = acc[i][j][4 * g + 1] + bv.y;
-        float o2 = acc[i][j][4 * g + 2] + bv.z;
-        float o3 = acc[i][j][4 * g + 3] + bv.w;
-        if constexpr (EPI == Epilogue::kBiasGeluBf16) {
-          o0 = gelu_erf(o0); o1 = gelu_erf(o1); o2 = gelu_erf(o2); o3 = gelu_erf(o3);
-        }
-        if constexpr (EPI == Epilogue::kBiasBf16 || EPI == Epilogue::kBiasGeluBf16) {
-          bf16_t* C = reinterpret_cast<bf16_t*>(Cv);
-          uint2 pk = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
-          *reinterpret_cast<uint2*>(C + m * ldc + n) = pk;
-        } else {
-          float* C = reinterpret_cast<float*>(Cv);
-          float4* dst = reinterpret_cast<float4*>(C + m * ldc + n);
-          if constexpr (EPI == Epilogue::kBiasResidualF32) {
-            const float4 r = *dst;
-            o0 += r.x; o1 += r.y; o2 += r.z; o3 += r.w;
-          }
-          *dst = make_float4(o0, o1, o2, o3);
-        }
-      }
+      for (int q = 0; q < 4; ++q)
+        store4<EPI>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], acc[i][j][4 * q],
+                    acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
     }
   }
+}
+
+int g_num_cus = 0;
+
+int num_cus() {
+  if (g_num_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      g_num_cus = n;
+    else
+      g_num_cus = 256;
+  }
+  return g_num_cus;
 }
 
 template <Epilogue EPI>
 hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, const float* bias,
                     void* C, int64_t ldc, int64_t M, int N, int K, hipStream_t stream) {
-  constexpr int BM = 128, BN = 128;
-  const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = N / BN;
-  const int blocks = tiles_m * tiles_n;
-  gemm_kernel<BM, BN, 2, 2, EPI><<<dim3(blocks), dim3(256), 0, stream>>>(
-      A, lda, W, ldw, bias, C, ldc, M, N, K, tiles_m, tiles_n);
-  return hipGetLastError();
+  const int tiles_m = (int)((M + BIG - 1) / BIG);
+  const int tiles_n = N / BIG;
+  const int tiles = tiles_m * tiles_n;
+  const int cus = num_cus();
+  // Full rounds go to the persistent kernel, the remainder to the small one.
+  const int n_big = (tiles / cus) * cus;
+  if (n_big > 0) {
+    gemm_big_kernel<EPI><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M, K,
+                                                              tiles_m, tiles_n, n_big);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (tiles > n_big) {
+    gemm_small_kernel<EPI><<<dim3(4 * (tiles - n_big)), dim3(256), 0, stream>>>(
+        A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -203,7 +446,7 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t*
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                        hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (N % 128 != 0 || K % BK != 0) return hipErrorInvalidValue;
+  if (N % BIG != 0 || K % (BKS * NSTAGE) != 0 || K % SBK != 0) return hipErrorInvalidValue;
   switch (epi) {
     case Epilogue::kBiasBf16:
       return launch_t<Epilogue::kBiasBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, stream);
