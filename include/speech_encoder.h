@@ -28,7 +28,8 @@
  *
  * Precision.  GEMM and attention operands are bf16 with fp32 accumulation;
  * the residual stream, norm statistics, softmax and rotation run in fp32; the
- * frontend runs in fp32 with float64-built tables.
+ * frontend's window, transform, power and mel sums run in float64 and its log
+ * is rounded to fp32.
  *
  * Conventions for every call below.
  *   - Device pointers are HIP device memory on the current device; host
@@ -116,8 +117,9 @@ typedef struct enc_ctx enc_ctx;
  *        are converted to bf16 (round to nearest even) and biases/gains to
  *        fp32 in context-owned device memory; the caller may free its tensors
  *        once the call returns.  The context also builds its constant tables
- *        (window, FFT twiddles, mel bank, rotation cos/sin) on the host in
- *        float64 and uploads them as fp32.
+ *        on the host in float64 (window, FFT twiddles and mel bank, kept in
+ *        float64; rotation cos/sin, rounded once to fp32) and allocates its
+ *        fixed scratch (split-K partial sums, 64 MiB).
  *   out  receives the handle (host pointer).
  * Synchronous.  Errors: ENC_ERR_ARG (NULL, wrong abi_version, n_layers < 1,
  * unknown dtype, NULL tensor), ENC_ERR_NOMEM, ENC_ERR_HIP.
@@ -143,8 +145,12 @@ int enc_logmel(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t
  *   out_embeddings  DEVICE bf16 [batch, P_max, 1280], P_max = ceil(F_max / 8);
  *            row p of clip b is its position-p embedding for p < P_b =
  *            ceil(F(lengths[b]) / 8) and 0 otherwise.  Each clip is encoded
- *            as its own sequence: its rows do not depend on the other clips
- *            or on the padding.
+ *            as its own sequence: attention and norms never mix clips, and
+ *            padding never reaches a clip.  The batch's total length does
+ *            choose how the matrix products split their last round of tiles,
+ *            so a clip's rows may differ from a run of that clip alone by
+ *            fp32 summation order (rounding); repeating a call with the same
+ *            batch gives bit-identical output.
  * The context keeps a workspace sized by the batch's total positions; a call
  * that needs a larger one first waits for the stream, then reallocates.  The
  * environment variable ENC_WORKSPACE_CAP_BYTES, read at each call, caps the

@@ -21,9 +21,10 @@
 //    four-stage ring of 32-wide K steps (4 x 32 KB) keeps three steps of loads
 //    in flight; one barrier per step.  The stream of steps runs on across the
 //    workgroup's tiles, so the next tile's loads overlap this tile's epilogue.
-//  * gemm_small_kernel -- the tiles left after the last full round, each cut
-//    into four 128 x 128 pieces so that the final partial round finishes in a
-//    quarter of the time (a 256 x 256 tile per CU would leave most CUs idle).
+//  * gemm_splitk_kernel + splitk_reduce_kernel -- the tiles left after the
+//    last full round, cut into 128 x 128 pieces and split along K so that the
+//    final partial round spreads over every CU (a 256 x 256 tile per CU would
+//    leave most CUs idle for a whole tile time).
 //
 // Each lane ends up owning one output row and runs of four consecutive
 // columns: the epilogue adds bias / residual / GELU in registers and stores
@@ -40,7 +41,6 @@ namespace {
 
 constexpr int BIG = 256;    // big tile edge
 constexpr int BKS = 32;     // big kernel K step
-constexpr int NSTAGE = 4;   // LDS ring depth of the big kernel
 constexpr int GROUP_M = 4;  // tile rows per ordering group
 
 // Exact-erf GELU, x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), with erf taken from
@@ -122,19 +122,31 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_void* lds) {
 }
 
 // ----------------------------------------------------------- big (persistent)
-template <Epilogue EPI>
+template <Epilogue EPI, int NS>
 __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int K,
     int tiles_m, int tiles_n, int n_big) {
   // Stage layout (uint4 units): A rows 0..255 x 4 chunks, then W rows x 4.
   constexpr int STG = 2 * BIG * BKS / 8;
-  // Distinct arrays, referenced statically, so the compiler can tell a DMA
-  // into one stage from reads of another and does not wait on it.
+  // NS stages of 32 KB.  Distinct arrays, referenced statically, so the
+  // compiler can tell a DMA into one stage from reads of another and does not
+  // wait on it (unused ones are not allocated).
+  static_assert(NS == 4 || NS == 5, "ring depth");
   __shared__ uint4 st0[STG];
   __shared__ uint4 st1[STG];
   __shared__ uint4 st2[STG];
   __shared__ uint4 st3[STG];
+  __shared__ uint4 st4[STG];
+  auto stage = [&](int i) -> uint4* {
+    switch (i) {
+      case 0: return st0;
+      case 1: return st1;
+      case 2: return st2;
+      case 3: return st3;
+      default: return st4;
+    }
+  };
 
   const int G = gridDim.x;
   const int wg = blockIdx.x;
@@ -159,13 +171,14 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
   const int dcol = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
   // Issue state: tile ir of this workgroup, k step ikt, and the per-lane
   // source rows of that tile (rows past M re-read row M-1; dropped later).
+  // Past the workgroup's last tile the loads simply repeat that tile's K
+  // range (harmless, and it keeps the step body free of branches).
   int ir = 0, ikt = 0;
   const bf16_t* ia[4];
   const bf16_t* iw[4];
   auto set_issue_tile = [&]() {
-    if (ir >= my_tiles) return;
     int tm, tn;
-    tile_coords(ir * G + slot, tiles_m, tiles_n, tm, tn);
+    tile_coords(min(ir, my_tiles - 1) * G + slot, tiles_m, tiles_n, tm, tn);
     const int64_t am = (int64_t)tm * BIG;
     const int64_t wn0 = (int64_t)tn * BIG;
 #pragma unroll
@@ -175,20 +188,20 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
     }
   };
   auto issue = [&](uint4* stage) {
-    if (ir >= my_tiles) return;
     const int k0 = ikt * BKS;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       dma16(ia[i] + k0, (lds_void*)(stage + (wave * 4 + i) * 64));
       dma16(iw[i] + k0, (lds_void*)(stage + BIG * 4 + (wave * 4 + i) * 64));
     }
+  };
+  auto advance = [&]() {
     if (++ikt == KT) {
       ikt = 0;
       ++ir;
-      set_issue_tile();
+      if (ir < my_tiles) set_issue_tile();
     }
   };
-  set_issue_tile();
 
   // Operand reads: row r of a stage, logical chunk c -> uint4 r*4 + (c ^ ((r/2)%4)).
   const int rsw = (l32 >> 1) & 3;
@@ -196,66 +209,88 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
   const int aofs = (wm * 128 + l32) * 4;
 
   f32x16 acc[4][4];
-  bf16x8 fw0[4], fa0[4], fw1[4], fa1[4];
-  auto load = [&](const uint4* sp, int sl, bf16x8 (&fw)[4], bf16x8 (&fa)[4]) {
-    const int pc = (2 * sl + lhi) ^ rsw;
+  // Operand fragments of a whole 32-wide step (two 16-wide slices: 4 of W and
+  // 4 of A each), double-buffered across steps.
+  bf16x8 fb0[16], fb1[16];
+  auto load = [&](const uint4* sp, bf16x8 (&f)[16]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 u = sp[wofs + i * 128 + pc];
-      fw[i] = *reinterpret_cast<const bf16x8*>(&u);
-    }
+    for (int sl = 0; sl < 2; ++sl) {
+      const int pc = (2 * sl + lhi) ^ rsw;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint4 u = sp[aofs + j * 128 + pc];
-      fa[j] = *reinterpret_cast<const bf16x8*>(&u);
+      for (int i = 0; i < 4; ++i) {
+        const uint4 u = sp[wofs + i * 128 + pc];
+        f[sl * 8 + i] = *reinterpret_cast<const bf16x8*>(&u);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint4 u = sp[aofs + j * 128 + pc];
+        f[sl * 8 + 4 + j] = *reinterpret_cast<const bf16x8*>(&u);
+      }
     }
   };
-  auto mma = [&](const bf16x8 (&fw)[4], const bf16x8 (&fa)[4]) {
+  auto mma = [&](const bf16x8 (&f)[16]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[sl * 8 + i], f[sl * 8 + 4 + j],
+                                                              acc[i][j], 0, 0, 0);
   };
-  // Spread 8 LDS reads between 16 MFMAs.
+  // Within one basic block, spread the 16 LDS reads of step g between the 32
+  // MFMAs of step g - 1 (a wave that issues an MFMA can issue an LDS read
+  // while the matrix core works; a burst of reads would leave it idle).  The
+  // 8 DMAs of step g + NS - 1 go out as one burst before the MFMAs: spread
+  // between them they measured slower.
   auto interleave = [&]() {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    for (int t = 0; t < 16; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
     }
   };
 
-  issue(st0);
-  issue(st1);
-  issue(st2);
-  int g = 0;
+  set_issue_tile();
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) {
+    issue(stage(i));
+    advance();
+  }
   int since_epi = 0;   // steps since the last epilogue (its stores count in vmcnt)
-  bool pend = false;   // fw1/fa1 hold the second half of the previous step
 
-  // One K step on stage `cur`; the loads of step g + 3 go to `nxt`.  Before the
-  // barrier each wave waits for its own loads of step g (the two younger steps
-  // may stay in flight) and for its LDS reads of step g - 1 (whose stage the
-  // loads of step g + 3 overwrite).  The barrier is the bare s_barrier: the
-  // waits above are all the ordering it needs, and a fenced barrier would also
-  // wait for the younger loads.
-#define ENC_BIG_STEP(cur, nxt)                                                   \
-  do {                                                                           \
-    if (g + 2 >= S) __builtin_amdgcn_s_waitcnt(0);                               \
-    else if (since_epi > 0 && since_epi < 4) asm volatile("s_waitcnt vmcnt(63)"); \
-    else asm volatile("s_waitcnt vmcnt(16)");                                    \
-    asm volatile("s_waitcnt lgkmcnt(0)");                                        \
-    __builtin_amdgcn_s_barrier();                                                \
-    load(cur, 0, fw0, fa0);                                                      \
-    issue(nxt);                                                                  \
-    if (pend) { mma(fw1, fa1); interleave(); }                                   \
-    load(cur, 1, fw1, fa1);                                                      \
-    mma(fw0, fa0);                                                               \
-    interleave();                                                                \
-    pend = true;                                                                 \
-    ++g;                                                                         \
-    if (since_epi > 0) ++since_epi;                                              \
-  } while (0)
+  // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+  // 6:4, lgkmcnt 11:8); fields not named are left at their maximum.
+  // WAIT_STEP allows the loads of the NS - 2 younger steps (8 DMAs each).
+  constexpr int WAIT_LGKM0 = 0xC07F;                       // lgkmcnt(0)
+  constexpr int VM = 8 * (NS - 2);
+  constexpr int WAIT_STEP = (VM & 15) | ((VM >> 4) << 14) | 0x0070;  // vmcnt(VM) lgkmcnt(0)
+  constexpr int WAIT_EPI = 0xC07F & ~0x0F00;               // vmcnt(63) lgkmcnt(0)
+
+  // One K step (tile-local index u) on stage u % NS: its fragments go to
+  // fb[u % 2] while the MFMAs of the previous step run from the other buffer
+  // (none on a tile's first step), and the loads of the step NS - 1 ahead go
+  // to the stage just freed.  Before the barrier each wave waits for its own
+  // loads of this step (the younger steps stay in flight; just after an
+  // epilogue its stores count too, hence the looser bound) and for its LDS
+  // reads of the previous step, whose stage the new loads overwrite.  The
+  // barrier is the bare s_barrier: a fenced one would also wait for the
+  // younger loads.
+  auto step = [&](int u, bool first) {
+    if (since_epi > 0 && since_epi < NS)
+      __builtin_amdgcn_s_waitcnt(WAIT_EPI);
+    else
+      __builtin_amdgcn_s_waitcnt(WAIT_STEP);
+    __builtin_amdgcn_s_barrier();
+    issue(stage((u + NS - 1) % NS));
+    if (u & 1) load(stage(u % NS), fb1); else load(stage(u % NS), fb0);
+    if (!first) {
+      if (u & 1) mma(fb0); else mma(fb1);
+      interleave();
+    }
+    advance();
+    if (since_epi > 0) ++since_epi;
+  };
 
   for (int r = 0; r < my_tiles; ++r) {
 #pragma unroll
@@ -264,14 +299,16 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    for (int kt = 0; kt < KT; kt += NSTAGE) {
-      ENC_BIG_STEP(st0, st3);
-      ENC_BIG_STEP(st1, st0);
-      ENC_BIG_STEP(st2, st1);
-      ENC_BIG_STEP(st3, st2);
+    // K / 32 is a multiple of 2 * NS: the stage and fragment buffer of every
+    // step are compile-time constants in the unrolled body.
+#pragma unroll
+    for (int u = 0; u < 2 * NS; ++u) step(u, u == 0);
+    for (int kt = 2 * NS; kt < KT; kt += 2 * NS) {
+#pragma unroll
+      for (int u = 0; u < 2 * NS; ++u) step(u, false);
     }
-    mma(fw1, fa1);
-    pend = false;
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    mma(fb1);
 
     int tm, tn;
     tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
@@ -294,30 +331,39 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
     }
     since_epi = 1;
   }
-#undef ENC_BIG_STEP
+  // Loads past the last step may still be landing in LDS: drain them before
+  // the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
-// ------------------------------------------------------------- small (tail)
-// Tiles [t_begin, t_end) of the big tiling, each as four 128 x 128 pieces;
-// 128 x 128 per workgroup, four wavefronts of 64 x 64, K in steps of 64
-// through registers and one LDS buffer.
+// ------------------------------------------------------------- tail (split K)
+// The tiles left after the last full round: each 256 x 256 tile is cut into
+// four 128 x 128 pieces and K into `splits` equal ranges, so that the tail
+// occupies every CU for a short time instead of a few CUs for a whole tile.
+// Each workgroup writes its fp32 partial sums; splitk_reduce_kernel adds the
+// partials of a piece in a fixed order (deterministic) and applies the
+// epilogue.  128 x 128 per workgroup, four wavefronts of 64 x 64, K in steps
+// of 64 through registers (two steps in flight) and one LDS buffer.
 constexpr int SBK = 64;
+constexpr int PIECE = 128;
 
-template <Epilogue EPI>
-__global__ __launch_bounds__(256) void gemm_small_kernel(
+__global__ __launch_bounds__(256) void gemm_splitk_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
-    const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int K,
-    int tiles_m, int tiles_n, int t_begin) {
-  constexpr int BM = 128, BN = 128;
-  constexpr int CH = BM * SBK / 8;          // 16-byte chunks per operand tile
+    float* __restrict__ part, int64_t M, int K, int tiles_m, int tiles_n, int t_begin,
+    int splits) {
+  constexpr int CH = PIECE * SBK / 8;        // 16-byte chunks per operand tile
   __shared__ uint4 sA[CH];
   __shared__ uint4 sW[CH];
 
-  const int piece = blockIdx.x & 3;
+  const int split = blockIdx.x % splits;
+  const int pid = blockIdx.x / splits;       // piece index
+  const int piece = pid & 3;
   int tm, tn;
-  tile_coords(t_begin + (int)(blockIdx.x >> 2), tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BIG + (piece & 1) * BM;
-  const int64_t n0 = (int64_t)tn * BIG + (piece >> 1) * BN;
+  tile_coords(t_begin + (pid >> 2), tiles_m, tiles_n, tm, tn);
+  const int64_t m0 = (int64_t)tm * BIG + (piece & 1) * PIECE;
+  const int64_t n0 = (int64_t)tn * BIG + (piece >> 1) * PIECE;
+  const int kc = K / splits;
+  const int kb = split * kc;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -327,24 +373,30 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  uint4 ra[4], rw[4];
-  auto load_tiles = [&](int k0) {
+  const bf16_t* ap[4];
+  const bf16_t* wp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = tid + i * 256;
+    const int row = c >> 3, col = (c & 7) * 8;
+    ap[i] = A + min<int64_t>(m0 + row, M - 1) * lda + kb + col;
+    wp[i] = W + (n0 + row) * ldw + kb + col;
+  }
+  uint4 ra[2][4], rw[2][4];
+  auto load_regs = [&](int k0, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int row = c >> 3, kc = c & 7;
-      const int64_t gm = min<int64_t>(m0 + row, M - 1);
-      ra[i] = *reinterpret_cast<const uint4*>(A + gm * lda + k0 + kc * 8);
-      rw[i] = *reinterpret_cast<const uint4*>(W + (n0 + row) * ldw + k0 + kc * 8);
+      ra[buf][i] = *reinterpret_cast<const uint4*>(ap[i] + k0);
+      rw[buf][i] = *reinterpret_cast<const uint4*>(wp[i] + k0);
     }
   };
-  auto store_tiles = [&]() {
+  auto store_tiles = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + i * 256;
-      const int row = c >> 3, kc = c & 7;
-      sA[row * 8 + (kc ^ (row & 7))] = ra[i];
-      sW[row * 8 + (kc ^ (row & 7))] = rw[i];
+      const int row = c >> 3, ch = c & 7;
+      sA[row * 8 + (ch ^ (row & 7))] = ra[buf][i];
+      sW[row * 8 + (ch ^ (row & 7))] = rw[buf][i];
     }
   };
 
@@ -356,12 +408,16 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  load_tiles(0);
-  for (int k0 = 0; k0 < K; k0 += SBK) {
+  const int steps = kc / SBK;
+  load_regs(0, 0);
+  if (steps > 1) load_regs(SBK, 1);
+  for (int st = 0; st < steps; ++st) {
     __syncthreads();
-    store_tiles();
+    if (st & 1) store_tiles(1); else store_tiles(0);
     __syncthreads();
-    if (k0 + SBK < K) load_tiles(k0 + SBK);
+    if (st + 2 < steps) {
+      if (st & 1) load_regs((st + 2) * SBK, 1); else load_regs((st + 2) * SBK, 0);
+    }
 #pragma unroll
     for (int s = 0; s < SBK / 16; ++s) {
       const int chunk = 2 * s + lhi;
@@ -386,21 +442,45 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(
     }
   }
 
+  // Partial layout: [pid][split][128 rows][128 cols] fp32.
+  float* dst = part + ((int64_t)pid * splits + split) * (PIECE * PIECE);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int nw = (int)(n0 + wn * 64 + i * 32);
-    float4 bv[4];
-    load_bias32(bias, nw, lhi, bv);
+  for (int j = 0; j < 2; ++j) {
+    const int r = wm * 64 + j * 32 + l32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t m = m0 + wm * 64 + j * 32 + l32;
-      if (m >= M) continue;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store4<EPI>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], acc[i][j][4 * q],
-                    acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-    }
+      for (int q = 0; q < 4; ++q) {
+        const int c = wn * 64 + i * 32 + 8 * q + 4 * lhi;
+        *reinterpret_cast<float4*>(dst + r * PIECE + c) =
+            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                        acc[i][j][4 * q + 3]);
+      }
   }
+}
+
+// Sum the split partials of each piece (split order 0, 1, ...) and apply the
+// epilogue.  One thread per 4 consecutive columns.
+template <Epilogue EPI>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, void* __restrict__ Cv,
+    int64_t ldc, int64_t M, int tiles_m, int tiles_n, int t_begin, int splits) {
+  const int pid = blockIdx.y;
+  const int piece = pid & 3;
+  int tm, tn;
+  tile_coords(t_begin + (pid >> 2), tiles_m, tiles_n, tm, tn);
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // element in the piece
+  const int r = e / PIECE, c = e % PIECE;
+  const int64_t m = (int64_t)tm * BIG + (piece & 1) * PIECE + r;
+  const int n = tn * BIG + (piece >> 1) * PIECE + c;
+  if (m >= M) return;
+  const float* src = part + (int64_t)pid * splits * (PIECE * PIECE) + e;
+  float4 s = *reinterpret_cast<const float4*>(src);
+  for (int k = 1; k < splits; ++k) {
+    const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)k * (PIECE * PIECE));
+    s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+  }
+  store4<EPI>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), s.x, s.y, s.z, s.w);
 }
 
 int g_num_cus = 0;
@@ -419,22 +499,44 @@ int num_cus() {
 
 template <Epilogue EPI>
 hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, const float* bias,
-                    void* C, int64_t ldc, int64_t M, int N, int K, hipStream_t stream) {
+                    void* C, int64_t ldc, int64_t M, int N, int K, float* part,
+                    size_t part_bytes, hipStream_t stream) {
   const int tiles_m = (int)((M + BIG - 1) / BIG);
   const int tiles_n = N / BIG;
   const int tiles = tiles_m * tiles_n;
   const int cus = num_cus();
-  // Full rounds go to the persistent kernel, the remainder to the small one.
+  // Full rounds go to the persistent kernel, the remainder to the split-K tail.
   const int n_big = (tiles / cus) * cus;
   if (n_big > 0) {
-    gemm_big_kernel<EPI><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M, K,
-                                                              tiles_m, tiles_n, n_big);
+    if ((K / BKS) % 10 == 0)
+      gemm_big_kernel<EPI, 5><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
+                                                                   K, tiles_m, tiles_n, n_big);
+    else
+      gemm_big_kernel<EPI, 4><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
+                                                                   K, tiles_m, tiles_n, n_big);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (tiles > n_big) {
-    gemm_small_kernel<EPI><<<dim3(4 * (tiles - n_big)), dim3(256), 0, stream>>>(
-        A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big);
+    // Split K so that pieces x splits fills about two workgroups per CU, each
+    // with at least two 64-wide steps, within the partial buffer.
+    const int pieces = 4 * (tiles - n_big);
+    const int kblocks = K / SBK;
+    int splits = 1;
+    for (int sp = 2; sp <= kblocks / 2; ++sp) {
+      if (kblocks % sp) continue;
+      if ((int64_t)pieces * sp > 2 * cus) break;
+      if ((size_t)pieces * sp * PIECE * PIECE * sizeof(float) > part_bytes) break;
+      splits = sp;
+    }
+    if ((size_t)pieces * splits * PIECE * PIECE * sizeof(float) > part_bytes)
+      return hipErrorInvalidValue;
+    gemm_splitk_kernel<<<dim3(pieces * splits), dim3(256), 0, stream>>>(
+        A, lda, W, ldw, part, M, K, tiles_m, tiles_n, n_big, splits);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    splitk_reduce_kernel<EPI><<<dim3(PIECE * PIECE / 1024, pieces), dim3(256), 0, stream>>>(
+        part, bias, C, ldc, M, tiles_m, tiles_n, n_big, splits);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -444,18 +546,22 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
 
 hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
-                       hipStream_t stream) {
+                       float* part, size_t part_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (N % BIG != 0 || K % (BKS * NSTAGE) != 0 || K % SBK != 0) return hipErrorInvalidValue;
+  if (N % BIG != 0 || K % (BKS * 8) != 0 || K % SBK != 0) return hipErrorInvalidValue;
   switch (epi) {
     case Epilogue::kBiasBf16:
-      return launch_t<Epilogue::kBiasBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, stream);
+      return launch_t<Epilogue::kBiasBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes,
+                                           stream);
     case Epilogue::kBiasGeluBf16:
-      return launch_t<Epilogue::kBiasGeluBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, stream);
+      return launch_t<Epilogue::kBiasGeluBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
+                                               part_bytes, stream);
     case Epilogue::kBiasResidualF32:
-      return launch_t<Epilogue::kBiasResidualF32>(A, lda, W, ldw, bias, C, ldc, M, N, K, stream);
+      return launch_t<Epilogue::kBiasResidualF32>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
+                                                  part_bytes, stream);
     case Epilogue::kBiasF32:
-      return launch_t<Epilogue::kBiasF32>(A, lda, W, ldw, bias, C, ldc, M, N, K, stream);
+      return launch_t<Epilogue::kBiasF32>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes,
+                                          stream);
   }
   return hipErrorInvalidValue;
 }

@@ -43,7 +43,9 @@ hipError_t launch_logmel_stacked(const float* audio, int64_t audio_stride, const
 
 // -------------------------------------------------------------------- GEMM
 // C[M, N] (op)= A[M, K] * W[N, K]^T + bias[N]; A, W bf16 row-major
-// (K contiguous), fp32 accumulation.  N % 128 == 0, K % 64 == 0.
+// (K contiguous), fp32 accumulation.  N % 256 == 0, K % 256 == 0.
+// `part` is scratch for split-K partial sums (GEMM_PARTIAL_BYTES suffices);
+// calls on one stream may share it.
 enum class Epilogue {
   kBiasBf16,          // C (bf16)  = acc + bias
   kBiasGeluBf16,      // C (bf16)  = gelu(acc + bias)
@@ -51,9 +53,11 @@ enum class Epilogue {
   kBiasF32,           // C (fp32)  = acc + bias
 };
 
+constexpr size_t GEMM_PARTIAL_BYTES = (size_t)2 * 512 * 128 * 128 * sizeof(float);
+
 hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
-                       hipStream_t stream);
+                       float* part, size_t part_bytes, hipStream_t stream);
 
 // ------------------------------------------------------------------- norms
 // y[r, :] = LN(x[r, :]) * g + b over d = 1280, fp32 statistics, bf16 output.

@@ -204,6 +204,7 @@ struct enc_ctx {
   FrontendTables* tables = nullptr;
   float* rope_cos = nullptr;
   float* rope_sin = nullptr;
+  float* gemm_part = nullptr;   // split-K partial sums of the GEMM tails
   void* ws = nullptr;
   size_t ws_bytes = 0;
   int32_t* plan_dev = nullptr;
@@ -229,6 +230,7 @@ void release(enc_ctx* c) {
   (void)hipFree(c->tables);
   (void)hipFree(c->rope_cos);
   (void)hipFree(c->rope_sin);
+  (void)hipFree(c->gemm_part);
   (void)hipFree(c->ws);
   (void)hipFree(c->plan_dev);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
@@ -461,7 +463,8 @@ int enc_create(const enc_weights* w, enc_ctx** out) {
   const size_t rope_bytes = rc_cos.size() * 4;
   if (hipMalloc((void**)&c->tables, sizeof(FrontendTables)) != hipSuccess ||
       hipMalloc((void**)&c->rope_cos, rope_bytes) != hipSuccess ||
-      hipMalloc((void**)&c->rope_sin, rope_bytes) != hipSuccess) {
+      hipMalloc((void**)&c->rope_sin, rope_bytes) != hipSuccess ||
+      hipMalloc((void**)&c->gemm_part, GEMM_PARTIAL_BYTES) != hipSuccess) {
     delete host_tab;
     release(c);
     return fail(ENC_ERR_NOMEM, "table allocation failed");
@@ -566,24 +569,24 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   ENC_LAUNCH(ENC_K_FRONTEND, launch_logmel_stacked(audio, nmax, d_nf, d_fb, batch, R * STACK,
                                                    ctx->tables, stk, stream));
   ENC_LAUNCH(ENC_K_GEMM_IN, launch_gemm(Epilogue::kBiasF32, stk, DIN, ctx->w_in, DIN, ctx->b_in, x,
-                                        D, R, D, DIN, stream));
+                                        D, R, D, DIN, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
   for (int li = 0; li < ctx->n_layers; ++li) {
     const LayerW& Lw = ctx->layers[li];
     ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln1_g, Lw.ln1_b, a, R, stream));
     ENC_LAUNCH(ENC_K_GEMM_QKV, launch_gemm(Epilogue::kBiasBf16, a, D, Lw.w_qkv, D, Lw.b_qkv, qkv,
-                                           3 * D, R, 3 * D, D, stream));
+                                           3 * D, R, 3 * D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_QKNORM_ROPE,
                launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, Lw.q_g, Lw.q_b, Lw.k_g,
                                   Lw.k_b, ctx->rope_cos, ctx->rope_sin, vt, lay.ld_vt, stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
                launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, o, stream));
     ENC_LAUNCH(ENC_K_GEMM_O, launch_gemm(Epilogue::kBiasResidualF32, o, D, Lw.w_o, D, Lw.b_o, x,
-                                         D, R, D, D, stream));
+                                         D, R, D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln2_g, Lw.ln2_b, a, R, stream));
     ENC_LAUNCH(ENC_K_GEMM_UP, launch_gemm(Epilogue::kBiasGeluBf16, a, D, Lw.w_up, D, Lw.b_up, u,
-                                          FF, R, FF, D, stream));
+                                          FF, R, FF, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_GEMM_DOWN, launch_gemm(Epilogue::kBiasResidualF32, u, FF, Lw.w_down, FF,
-                                            Lw.b_down, x, D, R, D, FF, stream));
+                                            Lw.b_down, x, D, R, D, FF, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
   }
   ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_cu, batch, p.p_max,
                                                  (bf16_t*)out_embeddings, stream));

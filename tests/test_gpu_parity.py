@@ -255,14 +255,23 @@ def test_forward_ragged_perturbed_weights(torch_mod, ctx_for):
 
 
 def test_forward_batch_invariance(torch_mod, ctx_for):
+    # A clip's rows alone and inside a batch agree to rounding: attention and
+    # norms never mix clips, but which GEMM tiles take the split-K tail path
+    # depends on the batch's total positions, so the fp32 summation order of
+    # a row can differ.  The same batch twice is bit-identical.
     torch = torch_mod
     audio, lengths = workloads.custom_audio([123_456, 480_000, 50_000], seed=51)
     enc = ctx_for("bf16", 2, "bf16")
     together = run_forward(torch, enc, audio, lengths)
+    again = run_forward(torch, enc, audio, lengths)
+    np.testing.assert_array_equal(together, again)
     for b, n in enumerate(lengths):
         alone = run_forward(torch, enc, audio[b:b + 1, :n], [n])
         p = alone.shape[1]
-        np.testing.assert_array_equal(together[b, :p], alone[0])
+        diff = float(np.abs(together[b, :p] - alone[0]).max())
+        scale = float(np.abs(alone[0]).max())
+        say(f"clip {b}: alone vs batched max abs diff {diff:.3e} (max |x| {scale:.3f})")
+        assert diff <= EMB_REL_TOL * scale
 
 
 def test_forward_workspace_cap_and_errors_leave_output(torch_mod, ctx_for, binding_mod):
