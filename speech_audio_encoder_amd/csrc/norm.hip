@@ -97,9 +97,9 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict
 }
 
 // Workgroup: one attention tile (up to 128 positions of one clip) x one head.
-// Each wavefront normalises and rotates q and k of 32 of the rows (lane holds
-// dims i and i + 64, exactly a rotation pair); the workgroup then writes v
-// transposed through LDS so that every store is 8 consecutive keys of one dim.
+// The wavefronts normalise and rotate q and k of the tile's rows, then each
+// thread transposes an 8 x 8 block of v in registers so that every store is 8
+// consecutive keys of one dim.
 // The clip's keys occupy columns [vt_base[b], vt_base[b] + roundup(P_b, 64))
 // of vt; columns past P_b are written as zeros.
 constexpr int QK_ROWS = 128;
@@ -110,7 +110,6 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const float* __restrict__ qg, const float* __restrict__ qb, const float* __restrict__ kg,
     const float* __restrict__ kb, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, bf16_t* __restrict__ vt, int64_t ld_vt) {
-  __shared__ bf16_t sv[QK_ROWS][DH + 8];
   const int h = blockIdx.y;
   const int seq = tile_seq[blockIdx.x];
   const int p0 = tile_p0[blockIdx.x];
@@ -120,48 +119,101 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  const float gq0 = qg[lane], gq1 = qg[lane + 64], bq0 = qb[lane], bq1 = qb[lane + 64];
-  const float gk0 = kg[lane], gk1 = kg[lane + 64], bk0 = kb[lane], bk1 = kb[lane + 64];
+  // q and k: 16 lanes per (row, head); lane j of a group holds dims 4j..4j+3
+  // and 64+4j..64+4j+3, i.e. four whole rotation pairs, so the rotation is
+  // local and every access is an 8-byte vector.  A wavefront does 4 rows at a
+  // time; the statistics reduce over the 16 lanes of the group.
+  const int sub = lane & 15;
+  const int grp = lane >> 4;
+  const int d0 = sub * 4;
+  const float4 gq0 = *reinterpret_cast<const float4*>(qg + d0);
+  const float4 gq1 = *reinterpret_cast<const float4*>(qg + 64 + d0);
+  const float4 bq0 = *reinterpret_cast<const float4*>(qb + d0);
+  const float4 bq1 = *reinterpret_cast<const float4*>(qb + 64 + d0);
+  const float4 gk0 = *reinterpret_cast<const float4*>(kg + d0);
+  const float4 gk1 = *reinterpret_cast<const float4*>(kg + 64 + d0);
+  const float4 bk0 = *reinterpret_cast<const float4*>(kb + d0);
+  const float4 bk1 = *reinterpret_cast<const float4*>(kb + 64 + d0);
 
-  for (int rr = wave; rr < QK_ROWS; rr += 4) {
+  for (int rr = wave * 4 + grp; rr < QK_ROWS; rr += 16) {
     const int p = p0 + rr;
-    if (p >= len) break;
+    if (p >= len) continue;
     const int64_t r = s0 + p;
-    const float c = rope_cos[(int64_t)p * (DH / 2) + lane];
-    const float s = rope_sin[(int64_t)p * (DH / 2) + lane];
+    const float4 c = *reinterpret_cast<const float4*>(rope_cos + (int64_t)p * (DH / 2) + d0);
+    const float4 sn = *reinterpret_cast<const float4*>(rope_sin + (int64_t)p * (DH / 2) + d0);
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       bf16_t* base = qkv + r * (3 * D) + which * D + h * DH;
-      const float a0 = bf16_to_f32(base[lane]);
-      const float a1 = bf16_to_f32(base[lane + 64]);
-      const float mean = wave_sum(a0 + a1) * (1.0f / DH);
-      const float d0 = a0 - mean, d1 = a1 - mean;
-      const float rstd = rsqrtf(wave_sum(d0 * d0 + d1 * d1) * (1.0f / DH) + LN_EPS);
-      const float y0 = d0 * rstd * (which ? gk0 : gq0) + (which ? bk0 : bq0);
-      const float y1 = d1 * rstd * (which ? gk1 : gq1) + (which ? bk1 : bq1);
-      base[lane] = f32_to_bf16(y0 * c - y1 * s);
-      base[lane + 64] = f32_to_bf16(y1 * c + y0 * s);
+      const uint2 ulo = *reinterpret_cast<const uint2*>(base + d0);
+      const uint2 uhi = *reinterpret_cast<const uint2*>(base + 64 + d0);
+      float a[4] = {bf16_to_f32((bf16_t)(ulo.x & 0xFFFF)), bf16_to_f32((bf16_t)(ulo.x >> 16)),
+                    bf16_to_f32((bf16_t)(ulo.y & 0xFFFF)), bf16_to_f32((bf16_t)(ulo.y >> 16))};
+      float b[4] = {bf16_to_f32((bf16_t)(uhi.x & 0xFFFF)), bf16_to_f32((bf16_t)(uhi.x >> 16)),
+                    bf16_to_f32((bf16_t)(uhi.y & 0xFFFF)), bf16_to_f32((bf16_t)(uhi.y >> 16))};
+      float sum = (a[0] + a[1]) + (a[2] + a[3]) + (b[0] + b[1]) + (b[2] + b[3]);
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      const float mean = sum * (1.0f / DH);
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] -= mean;
+        b[e] -= mean;
+        sq += a[e] * a[e] + b[e] * b[e];
+      }
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      const float rstd = rsqrtf(sq * (1.0f / DH) + LN_EPS);
+      const float4 g0 = which ? gk0 : gq0, g1 = which ? gk1 : gq1;
+      const float4 e0 = which ? bk0 : bq0, e1 = which ? bk1 : bq1;
+      const float ga[4] = {g0.x, g0.y, g0.z, g0.w}, gb[4] = {g1.x, g1.y, g1.z, g1.w};
+      const float ea[4] = {e0.x, e0.y, e0.z, e0.w}, eb[4] = {e1.x, e1.y, e1.z, e1.w};
+      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+      float lo[4], hi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float y0 = a[e] * rstd * ga[e] + ea[e];
+        const float y1 = b[e] * rstd * gb[e] + eb[e];
+        lo[e] = y0 * cc[e] - y1 * ss[e];
+        hi[e] = y1 * cc[e] + y0 * ss[e];
+      }
+      *reinterpret_cast<uint2*>(base + d0) =
+          make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
+      *reinterpret_cast<uint2*>(base + 64 + d0) =
+          make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
     }
   }
 
-  // v tile -> LDS (row-major; rows past the clip are zero), then transposed out.
-  for (int c = threadIdx.x; c < QK_ROWS * DH / 8; c += 256) {
-    const int rr = c / (DH / 8), kc = c % (DH / 8);
-    const int p = p0 + rr;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (p < len) u = *reinterpret_cast<const uint4*>(qkv + (s0 + p) * (3 * D) + 2 * D + h * DH + kc * 8);
-    *reinterpret_cast<uint4*>(&sv[rr][kc * 8]) = u;
-  }
-  __syncthreads();
-  for (int c = threadIdx.x; c < DH * QK_ROWS / 8; c += 256) {
-    const int d = c / (QK_ROWS / 8), rc = c % (QK_ROWS / 8);
-    if (rc * 8 >= span) continue;
-    uint32_t e[4];
+  // v: each thread transposes one 8 x 8 block (8 positions x 8 dims) in
+  // registers -- output word k of column c takes half c%2 of word c/2 from
+  // rows 2k and 2k+1 (one byte permute each) -- and stores 8 keys of each of
+  // its 8 dims as 16-byte vectors.  Positions past the clip are zeros.
+  {
+    const int rb = threadIdx.x >> 4;           // 16 blocks of 8 positions
+    const int db = threadIdx.x & 15;           // 16 blocks of 8 dims
+    if (rb * 8 < span) {
+      uint4 rows[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      e[q] = (uint32_t)sv[rc * 8 + 2 * q][d] | ((uint32_t)sv[rc * 8 + 2 * q + 1][d] << 16);
-    bf16_t* dst = vt + ((int64_t)h * DH + d) * ld_vt + vt_base[seq] + p0 + rc * 8;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(e[0], e[1], e[2], e[3]);
+      for (int i = 0; i < 8; ++i) {
+        const int p = p0 + rb * 8 + i;
+        rows[i] = (p < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + p) * (3 * D) + 2 * D +
+                                                               h * DH + db * 8)
+                            : make_uint4(0, 0, 0, 0);
+      }
+      bf16_t* dst = vt + ((int64_t)h * DH + db * 8) * ld_vt + vt_base[seq] + p0 + rb * 8;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t* ra = reinterpret_cast<const uint32_t*>(&rows[2 * k]);
+          const uint32_t* rb2 = reinterpret_cast<const uint32_t*>(&rows[2 * k + 1]);
+          w[k] = __builtin_amdgcn_perm(rb2[c >> 1], ra[c >> 1], sel);
+        }
+        *reinterpret_cast<uint4*>(dst + (int64_t)c * ld_vt) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
   }
 }
 
