@@ -21,10 +21,10 @@
 //    four-stage ring of 32-wide K steps (4 x 32 KB) keeps three steps of loads
 //    in flight; one barrier per step.  The stream of steps runs on across the
 //    workgroup's tiles, so the next tile's loads overlap this tile's epilogue.
-//  * gemm_splitk_kernel + splitk_reduce_kernel -- the tiles left after the
-//    last full round, cut into 128 x 128 pieces and split along K so that the
-//    final partial round spreads over every CU (a 256 x 256 tile per CU would
-//    leave most CUs idle for a whole tile time).
+//  * gemm_piece_kernel (+ splitk_reduce_kernel) -- the tiles left after the
+//    last full round, or the whole product when it has fewer 256 x 256 tiles
+//    than CUs, as 128 x 128 pieces split along K when needed so that every CU
+//    is busy (a 256 x 256 tile per CU would leave most CUs idle).
 //
 // Each lane ends up owning one output row and runs of four consecutive
 // columns: the epilogue adds bias / residual / GELU in registers and stores
@@ -154,7 +154,6 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
   const int slot = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
   const int my_tiles = slot < n_big ? (n_big - 1 - slot) / G + 1 : 0;
   const int KT = K / BKS;
-  const int S = my_tiles * KT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -336,34 +335,72 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-// ------------------------------------------------------------- tail (split K)
-// The tiles left after the last full round: each 256 x 256 tile is cut into
-// four 128 x 128 pieces and K into `splits` equal ranges, so that the tail
-// occupies every CU for a short time instead of a few CUs for a whole tile.
-// Each workgroup writes its fp32 partial sums; splitk_reduce_kernel adds the
-// partials of a piece in a fixed order (deterministic) and applies the
-// epilogue.  128 x 128 per workgroup, four wavefronts of 64 x 64, K in steps
-// of 64 through registers (two steps in flight) and one LDS buffer.
-constexpr int SBK = 64;
+// ------------------------------------------------------- 128 x 128 pieces
+// Work the persistent kernel does not cover -- the tiles left after its last
+// full round, or the whole product when there are fewer 256 x 256 tiles than
+// CUs -- is cut into 128 x 128 pieces, and K into `splits` ranges when that
+// is needed to occupy every CU.  A workgroup (four wavefronts of 64 x 64)
+// takes one (piece, split): the same direct-to-LDS ring as the big kernel,
+// 4 stages of 32-wide K steps (16 KB each), so two workgroups fit on a CU and
+// cover each other's waits.  With one split the epilogue is applied directly;
+// otherwise fp32 partial sums go to `part` and splitk_reduce_kernel adds them
+// in a fixed order (deterministic) and applies the epilogue.
 constexpr int PIECE = 128;
+constexpr int PNS = 4;
 
-__global__ __launch_bounds__(256) void gemm_splitk_kernel(
+struct PieceMap {
+  int mode;       // 0: pieces of leftover big tiles t_begin.., 1: a plain grid
+  int t_begin;    // mode 0
+  int tiles_m, tiles_n;
+  int pieces_n;   // mode 1: pieces per row of pieces (N / 128)
+};
+
+__device__ __forceinline__ void piece_coords(int pid, const PieceMap& pm, int64_t& m0, int64_t& n0) {
+  if (pm.mode == 0) {
+    int tm, tn;
+    tile_coords(pm.t_begin + (pid >> 2), pm.tiles_m, pm.tiles_n, tm, tn);
+    m0 = (int64_t)tm * BIG + (pid & 1) * PIECE;
+    n0 = (int64_t)tn * BIG + ((pid >> 1) & 1) * PIECE;
+  } else {
+    // groups of 8 piece rows, column-major inside a group
+    const int per_group = 8 * pm.pieces_n;
+    const int group = pid / per_group;
+    const int pieces_m = (pm.tiles_m * BIG) / PIECE;   // rounded up to whole big tiles
+    const int first = group * 8;
+    const int gsize = min(pieces_m - first, 8);
+    const int r = pid - group * per_group;
+    m0 = (int64_t)(first + r % gsize) * PIECE;
+    n0 = (int64_t)(r / gsize) * PIECE;
+  }
+}
+
+template <Epilogue EPI, bool PARTIAL>
+__global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
-    float* __restrict__ part, int64_t M, int K, int tiles_m, int tiles_n, int t_begin,
-    int splits) {
-  constexpr int CH = PIECE * SBK / 8;        // 16-byte chunks per operand tile
-  __shared__ uint4 sA[CH];
-  __shared__ uint4 sW[CH];
+    const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, float* __restrict__ part,
+    int64_t M, int K, PieceMap pm, int splits) {
+  constexpr int STG = 2 * PIECE * BKS / 8;   // uint4 per stage (16 KB)
+  __shared__ uint4 st0[STG];
+  __shared__ uint4 st1[STG];
+  __shared__ uint4 st2[STG];
+  __shared__ uint4 st3[STG];
+  auto stage = [&](int i) -> uint4* {
+    switch (i & 3) {
+      case 0: return st0;
+      case 1: return st1;
+      case 2: return st2;
+      default: return st3;
+    }
+  };
 
   const int split = blockIdx.x % splits;
-  const int pid = blockIdx.x / splits;       // piece index
-  const int piece = pid & 3;
-  int tm, tn;
-  tile_coords(t_begin + (pid >> 2), tiles_m, tiles_n, tm, tn);
-  const int64_t m0 = (int64_t)tm * BIG + (piece & 1) * PIECE;
-  const int64_t n0 = (int64_t)tn * BIG + (piece >> 1) * PIECE;
+  const int pid = blockIdx.x / splits;
+  int64_t m0, n0;
+  piece_coords(pid, pm, m0, n0);
+  if (m0 >= M) return;   // whole piece past the last row (plain grid rounding)
   const int kc = K / splits;
   const int kb = split * kc;
+  const int KT = kc / BKS;   // multiple of PNS
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -373,32 +410,30 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  const bf16_t* ap[4];
-  const bf16_t* wp[4];
+  // DMA: wave w loads 2 x 16 rows of A and of W per step (rows (w*2+i)*16 + lane/4).
+  const int drow = wave * 32 + (lane >> 2);
+  const int dcol = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
+  const bf16_t* ia[2];
+  const bf16_t* iw[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + i * 256;
-    const int row = c >> 3, col = (c & 7) * 8;
-    ap[i] = A + min<int64_t>(m0 + row, M - 1) * lda + kb + col;
-    wp[i] = W + (n0 + row) * ldw + kb + col;
+  for (int i = 0; i < 2; ++i) {
+    ia[i] = A + min<int64_t>(m0 + drow + 16 * i, M - 1) * lda + kb + dcol;
+    iw[i] = W + (n0 + drow + 16 * i) * ldw + kb + dcol;
   }
-  uint4 ra[2][4], rw[2][4];
-  auto load_regs = [&](int k0, int buf) {
+  int ikt = 0;
+  auto issue = [&](uint4* sp) {
+    const int k0 = min(ikt, KT - 1) * BKS;   // past the end: re-read the last step
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[buf][i] = *reinterpret_cast<const uint4*>(ap[i] + k0);
-      rw[buf][i] = *reinterpret_cast<const uint4*>(wp[i] + k0);
+    for (int i = 0; i < 2; ++i) {
+      dma16(ia[i] + k0, (lds_void*)(sp + (wave * 2 + i) * 64));
+      dma16(iw[i] + k0, (lds_void*)(sp + PIECE * 4 + (wave * 2 + i) * 64));
     }
+    ++ikt;
   };
-  auto store_tiles = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int row = c >> 3, ch = c & 7;
-      sA[row * 8 + (ch ^ (row & 7))] = ra[buf][i];
-      sW[row * 8 + (ch ^ (row & 7))] = rw[buf][i];
-    }
-  };
+
+  const int rsw = (l32 >> 1) & 3;
+  const int wofs = PIECE * 4 + (wn * 64 + l32) * 4;
+  const int aofs = (wm * 64 + l32) * 4;
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -408,54 +443,73 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int steps = kc / SBK;
-  load_regs(0, 0);
-  if (steps > 1) load_regs(SBK, 1);
-  for (int st = 0; st < steps; ++st) {
-    __syncthreads();
-    if (st & 1) store_tiles(1); else store_tiles(0);
-    __syncthreads();
-    if (st + 2 < steps) {
-      if (st & 1) load_regs((st + 2) * SBK, 1); else load_regs((st + 2) * SBK, 0);
+  constexpr int VM = 4 * (PNS - 2);
+  constexpr int WAIT_STEP = (VM & 15) | ((VM >> 4) << 14) | 0x0070;   // vmcnt(8) lgkmcnt(0)
+#pragma unroll
+  for (int i = 0; i < PNS - 1; ++i) issue(stage(i));
+  for (int kt = 0; kt < KT; kt += PNS) {
+#pragma unroll
+    for (int u = 0; u < PNS; ++u) {
+      __builtin_amdgcn_s_waitcnt(WAIT_STEP);
+      __builtin_amdgcn_s_barrier();
+      issue(stage(u + PNS - 1));
+      const uint4* sp = stage(u);
+      bf16x8 fw[2][2], fa[2][2];
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        const int pc = (2 * sl + lhi) ^ rsw;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint4 uw = sp[wofs + i * 128 + pc];
+          fw[sl][i] = *reinterpret_cast<const bf16x8*>(&uw);
+          const uint4 ua = sp[aofs + i * 128 + pc];
+          fa[sl][i] = *reinterpret_cast<const bf16x8*>(&ua);
+        }
+      }
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl][i], fa[sl][j], acc[i][j], 0,
+                                                                0, 0);
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // loads past the last step land before LDS is released
+
+  if constexpr (PARTIAL) {
+    // Partial layout: [pid][split][128 rows][128 cols] fp32.
+    float* dst = part + ((int64_t)pid * splits + split) * (PIECE * PIECE);
 #pragma unroll
-    for (int s = 0; s < SBK / 16; ++s) {
-      const int chunk = 2 * s + lhi;
-      bf16x8 fw[2], fa[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wn * 64 + i * 32 + l32;
-        const uint4 u = sW[row * 8 + (chunk ^ (row & 7))];
-        fw[i] = *reinterpret_cast<const bf16x8*>(&u);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wm * 64 + j * 32 + l32;
-        const uint4 u = sA[row * 8 + (chunk ^ (row & 7))];
-        fa[j] = *reinterpret_cast<const bf16x8*>(&u);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int r = wm * 64 + j * 32 + l32;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * 64 + i * 32 + 8 * q + 4 * lhi;
+          *reinterpret_cast<float4*>(dst + r * PIECE + c) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]);
+        }
     }
-  }
-
-  // Partial layout: [pid][split][128 rows][128 cols] fp32.
-  float* dst = part + ((int64_t)pid * splits + split) * (PIECE * PIECE);
+  } else {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = wm * 64 + j * 32 + l32;
+    for (int i = 0; i < 2; ++i) {
+      const int nw = (int)(n0 + wn * 64 + i * 32);
+      float4 bv[4];
+      load_bias32(bias, nw, lhi, bv);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int64_t m = m0 + wm * 64 + j * 32 + l32;
+        if (m >= M) continue;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = wn * 64 + i * 32 + 8 * q + 4 * lhi;
-        *reinterpret_cast<float4*>(dst + r * PIECE + c) =
-            make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                        acc[i][j][4 * q + 3]);
+        for (int q = 0; q < 4; ++q)
+          store4<EPI>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], acc[i][j][4 * q],
+                      acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
+    }
   }
 }
 
@@ -464,15 +518,14 @@ __global__ __launch_bounds__(256) void gemm_splitk_kernel(
 template <Epilogue EPI>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, void* __restrict__ Cv,
-    int64_t ldc, int64_t M, int tiles_m, int tiles_n, int t_begin, int splits) {
+    int64_t ldc, int64_t M, PieceMap pm, int splits) {
   const int pid = blockIdx.y;
-  const int piece = pid & 3;
-  int tm, tn;
-  tile_coords(t_begin + (pid >> 2), tiles_m, tiles_n, tm, tn);
+  int64_t m0, n0;
+  piece_coords(pid, pm, m0, n0);
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // element in the piece
   const int r = e / PIECE, c = e % PIECE;
-  const int64_t m = (int64_t)tm * BIG + (piece & 1) * PIECE + r;
-  const int n = tn * BIG + (piece >> 1) * PIECE + c;
+  const int64_t m = m0 + r;
+  const int n = (int)n0 + c;
   if (m >= M) return;
   const float* src = part + (int64_t)pid * splits * (PIECE * PIECE) + e;
   float4 s = *reinterpret_cast<const float4*>(src);
@@ -497,6 +550,41 @@ int num_cus() {
   return g_num_cus;
 }
 
+// Split K (into a divisor of K / 128 ranges) as far as the pieces that hold
+// rows stay within two workgroups per CU, and the partial sums of every piece
+// id within the partial buffer.
+int choose_splits(int live_pieces, int grid_pieces, int K, int cus, size_t part_bytes) {
+  const int units = K / (BKS * PNS);
+  int splits = 1;
+  for (int sp = 2; sp <= units; ++sp) {
+    if (units % sp) continue;
+    if ((int64_t)live_pieces * sp > 2 * cus) break;
+    if ((size_t)grid_pieces * sp * PIECE * PIECE * sizeof(float) > part_bytes) break;
+    splits = sp;
+  }
+  return splits;
+}
+
+template <Epilogue EPI>
+hipError_t launch_pieces(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
+                         const float* bias, void* C, int64_t ldc, int64_t M, int K, float* part,
+                         size_t part_bytes, const PieceMap& pm, int live_pieces, int pieces,
+                         int cus, hipStream_t stream) {
+  const int splits = choose_splits(live_pieces, pieces, K, cus, part_bytes);
+  if (splits == 1) {
+    gemm_piece_kernel<EPI, false><<<dim3(pieces), dim3(256), 0, stream>>>(
+        A, lda, W, ldw, bias, C, ldc, part, M, K, pm, 1);
+    return hipGetLastError();
+  }
+  gemm_piece_kernel<EPI, true><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
+      A, lda, W, ldw, bias, C, ldc, part, M, K, pm, splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  splitk_reduce_kernel<EPI><<<dim3(PIECE * PIECE / 1024, pieces), dim3(256), 0, stream>>>(
+      part, bias, C, ldc, M, pm, splits);
+  return hipGetLastError();
+}
+
 template <Epilogue EPI>
 hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, const float* bias,
                     void* C, int64_t ldc, int64_t M, int N, int K, float* part,
@@ -505,41 +593,28 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   const int tiles_n = N / BIG;
   const int tiles = tiles_m * tiles_n;
   const int cus = num_cus();
-  // Full rounds go to the persistent kernel, the remainder to the split-K tail.
+  if (tiles < cus) {
+    // Fewer big tiles than CUs: the whole product as 128 x 128 pieces.
+    PieceMap pm{1, 0, tiles_m, tiles_n, N / PIECE};
+    const int live = (int)((M + PIECE - 1) / PIECE) * (N / PIECE);
+    // piece ids cover whole big-tile rows; ids past M return at once
+    const int grid_pieces = ((tiles_m * BIG) / PIECE) * (N / PIECE);
+    return launch_pieces<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm, live,
+                              grid_pieces, cus, stream);
+  }
+  // Full rounds go to the persistent kernel, the remainder to 128 x 128 pieces.
   const int n_big = (tiles / cus) * cus;
-  if (n_big > 0) {
-    if ((K / BKS) % 10 == 0)
-      gemm_big_kernel<EPI, 5><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
-                                                                   K, tiles_m, tiles_n, n_big);
-    else
-      gemm_big_kernel<EPI, 4><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
-                                                                   K, tiles_m, tiles_n, n_big);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (tiles > n_big) {
-    // Split K so that pieces x splits fills about two workgroups per CU, each
-    // with at least two 64-wide steps, within the partial buffer.
-    const int pieces = 4 * (tiles - n_big);
-    const int kblocks = K / SBK;
-    int splits = 1;
-    for (int sp = 2; sp <= kblocks / 2; ++sp) {
-      if (kblocks % sp) continue;
-      if ((int64_t)pieces * sp > 2 * cus) break;
-      if ((size_t)pieces * sp * PIECE * PIECE * sizeof(float) > part_bytes) break;
-      splits = sp;
-    }
-    if ((size_t)pieces * splits * PIECE * PIECE * sizeof(float) > part_bytes)
-      return hipErrorInvalidValue;
-    gemm_splitk_kernel<<<dim3(pieces * splits), dim3(256), 0, stream>>>(
-        A, lda, W, ldw, part, M, K, tiles_m, tiles_n, n_big, splits);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    splitk_reduce_kernel<EPI><<<dim3(PIECE * PIECE / 1024, pieces), dim3(256), 0, stream>>>(
-        part, bias, C, ldc, M, tiles_m, tiles_n, n_big, splits);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  if ((K / BKS) % 10 == 0)
+    gemm_big_kernel<EPI, 5><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
+                                                                 K, tiles_m, tiles_n, n_big);
+  else
+    gemm_big_kernel<EPI, 4><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
+                                                                 K, tiles_m, tiles_n, n_big);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || tiles == n_big) return e;
+  PieceMap pm{0, n_big, tiles_m, tiles_n, N / PIECE};
+  return launch_pieces<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm,
+                            4 * (tiles - n_big), 4 * (tiles - n_big), cus, stream);
 }
 
 }  // namespace
@@ -548,7 +623,7 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t*
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                        float* part, size_t part_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (N % BIG != 0 || K % (BKS * 8) != 0 || K % SBK != 0) return hipErrorInvalidValue;
+  if (N % BIG != 0 || K % (BKS * 8) != 0) return hipErrorInvalidValue;
   switch (epi) {
     case Epilogue::kBiasBf16:
       return launch_t<Epilogue::kBiasBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes,
