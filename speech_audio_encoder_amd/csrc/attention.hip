@@ -7,16 +7,41 @@
 // "Local encoder windows, recording-wide language context" notes that
 // FlashAttention-style kernels avoid materialising the quadratic score matrix).
 //
-// Work split: a workgroup takes 128 queries of one clip and one head; each of
-// its four wavefronts owns 32 queries and walks the clip's keys 64 at a time.
-// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16,
-// so every lane holds 16 keys of one query: the running max and sum of the
-// online softmax need one cross-lane exchange (lanes l and l ^ 32) per tile.
-// The probabilities feed O^T += V^T P^T straight from registers; V arrives
-// already transposed (per head [dim][key]) and is staged in LDS with its keys
-// permuted inside each group of 16 so that a lane's eight operand keys are
-// contiguous.  Keys past the clip end are masked to -inf in S; their V^T
-// columns (up to the next multiple of 64) are zero.
+// Work split: a workgroup of two wavefronts takes 128 queries of one clip and
+// one head; each wavefront owns 64 queries (two blocks of 32), so every K or
+// V^T fragment read from LDS feeds two v_mfma_f32_32x32x16_bf16.  Scores are
+// computed transposed, S^T = K Q^T, so a lane holds 16 keys of one query per
+// 32-key block: the softmax needs one cross-lane exchange (lanes l, l ^ 32)
+// per tile for the maximum and none for the sum.  Probabilities feed
+// O^T += V^T P^T straight from registers; V arrives transposed per head
+// ([dim][key], keys permuted inside each group of 16 so that a lane's eight
+// operand keys are one 16-byte chunk).
+//
+// Pipeline: K goes global -> LDS in 32-key units (a ring of four) and V^T in
+// 64-key tiles (two buffers) by direct loads (global_load_lds, 16 bytes per
+// lane, swizzle applied on the global side), one barrier per 64 keys.  The
+// scores of unit u + 1 are issued to the matrix cores in the same basic block
+// as unit u's exponentials and products with V, so the VALU work of the
+// softmax overlaps the MFMAs.
+//
+// Softmax reference.  QK-norm bounds every score: after LayerNorm a head
+// vector has norm at most max|gain| * sqrt(128) + |bias|, so |q.k| is bounded
+// by the product of the two norms.  When the launcher is told that this bound
+// keeps scores * log2(e) / sqrt(128) within +-100 (kFixedRef), probabilities
+// are exp2 of the scaled scores against a fixed reference of 0: no running
+// maximum, no rescaling, and fp32 sums cannot overflow.  Otherwise the
+// running maximum is kept lazily: the accumulators are rescaled only when a
+// query's unit maximum exceeds it by more than 8 (log2 units); in between,
+// probabilities are taken against the stale maximum (they stay below 2^8),
+// which leaves the normalised result unchanged.
+//
+// Keys past the clip end: their K rows (read from whatever follows in the qkv
+// buffer, which has 64 rows of slack) are masked to -inf by a select in the
+// clip's last tile; their V^T columns (up to the next multiple of 64) are
+// zero.
+
+#include <algorithm>
+#include <cmath>
 
 #include "common.h"
 #include "kernels.h"
@@ -25,201 +50,328 @@ namespace enc {
 
 namespace {
 
-constexpr int QB = 128;     // queries per workgroup (4 wavefronts x 32)
-constexpr int KB = 64;      // keys per tile
+constexpr int QPW = 64;                // queries per wavefront
+constexpr int NWAVE = 2;               // wavefronts per workgroup
+constexpr int QTILE = QPW * NWAVE;     // queries per workgroup (the plan's tiles)
+constexpr int KT = 64;                 // keys per V^T tile
+constexpr int KU = 32;                 // keys per K unit (one score block)
+constexpr int KU_BYTES = KU * DH * 2;  // 8 KB
+constexpr int VT_BYTES = KT * DH * 2;  // 16 KB
+static_assert(QTILE == 128, "attention tiles of the plan are 128 queries");
 
-// Position of key kappa (0..63) inside an LDS row of the V^T tile: within each
-// group of 16 keys, blocks of 4 are stored in the order 0, 2, 1, 3.
-__device__ __forceinline__ int vperm(int kappa) {
-  const int blk = (kappa >> 2) & 3;
-  const int nb = (blk == 1) ? 2 : (blk == 2 ? 1 : blk);
-  return (kappa & ~15) | (nb << 2) | (kappa & 3);
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from g to LDS byte address lds + 16 * lane (lds is
+// wave-uniform).  Written in asm so that the compiler does not track it: it
+// would otherwise wait for these loads before every LDS read it cannot prove
+// disjoint.  Callers wait with lds_loads_wait() before the barrier that
+// publishes the data.  M0 is not otherwise used by this kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void lds_loads_wait() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ __launch_bounds__(256) void attention_kernel(
+template <bool kFixedRef>
+__global__ __launch_bounds__(128) void attention_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ vt, int64_t ld_vt,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
-    const int32_t* __restrict__ tile_seq,
-    const int32_t* __restrict__ tile_q0, bf16_t* __restrict__ out) {
-  __shared__ uint4 sK[KB * DH / 8];          // [key][16 chunks], swizzled
-  __shared__ uint2 sV[DH * KB / 4];          // [dim][16 half-chunks], permuted+swizzled
+    const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_q0, int n_tiles,
+    int n_items, bf16_t* __restrict__ out) {
+  // K in a ring of four 32-key units, V^T in two 64-key tiles.
+  __shared__ uint4 sK[4][KU * DH / 8];   // [key][16 chunks of 8 dims], swizzled
+  __shared__ uint4 sV[2][DH * KT / 8];   // [dim][8 chunks of 8 keys], swizzled
 
-  const int tile = blockIdx.x;
-  const int h = blockIdx.y;
+  // Hardware block b runs on XCD b % 8; XCD x takes items [x * per, x * per +
+  // per) so that the workgroups resident on one XCD walk the same head's keys.
+  const int per = gridDim.x >> 3;
+  const int item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int h = item / n_tiles;
+  const int tile = item - h * n_tiles;
   const int seq = tile_seq[tile];
   const int64_t s0 = cu[seq];
   const int len = cu[seq + 1] - cu[seq];
   const int q0 = tile_q0[tile];
-  const bf16_t* vbase = vt + (int64_t)h * DH * ld_vt + vt_base[seq];
+  const int nkt = (len + KT - 1) / KT;   // 64-key tiles
+  const int nku = 2 * nkt;               // 32-key units
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  // Q^T fragments for this lane's query, 8 k-steps of 16 dims.
-  static_assert(QB == 4 * 32, "one 32-query block per wavefront");
-  const int qi = q0 + wave * 32 + l32;
-  bf16x8 qf[DH / 16];
-  {
-    const bool ok = qi < len;
-    const bf16_t* qrow = qkv + (s0 + (ok ? qi : 0)) * (3 * D) + h * DH;
+  // Q^T fragments: query block qb, 16-dim step s.
+  bf16x8 qf[2][DH / 16];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = q0 + wave * QPW + qb * 32 + l32;
+    const bool ok = q < len;
+    const bf16_t* qrow = qkv + (s0 + (ok ? q : 0)) * (3 * D) + h * DH + lhi * 8;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
-      uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + s * 16 + lhi * 8) : make_uint4(0, 0, 0, 0);
-      qf[s] = *reinterpret_cast<const bf16x8*>(&u);
+      const uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + s * 16) : make_uint4(0, 0, 0, 0);
+      qf[qb][s] = __builtin_bit_cast(bf16x8, u);
     }
   }
 
-  f32x16 acc_o[DH / 32];
+  // Direct loads.  A K unit is eight 1-KB pieces (keys 4i..4i+3; lane -> key
+  // 4i + lane/16, LDS chunk lane%16 holds global chunk (lane%16) ^ (key%16)),
+  // this wave loads pieces 4*wave..4*wave+3.  A V^T tile is sixteen pieces
+  // (dims 8i..8i+7; lane -> dim 8i + lane/8, LDS chunk lane%8 holds global
+  // chunk (lane%8) ^ ((dim/2)%8)), this wave loads 8*wave..8*wave+7.
+  // Offsets are bytes from the unit's / tile's origin.
+  uint32_t koff[4], voff[8];
 #pragma unroll
-  for (int i = 0; i < DH / 32; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc_o[i][v] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float scale = 0.08838834764831845f * 1.4426950408889634f;   // 1/sqrt(128) * log2(e)
-
-  // Staging: 4 K chunks and 4 V^T chunks (16 B each) per thread per tile.
-  uint4 rk[4], rv[4];
-  auto load_tile = [&](int kv0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int key = c >> 4, kc = c & 15;
-      const int kk = kv0 + key;
-      rk[i] = (kk < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + kk) * (3 * D) + D + h * DH + kc * 8)
-                         : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int d = c >> 3, kc = c & 7;
-      // columns up to roundup(len, 64) exist and are zero past len
-      rv[i] = *reinterpret_cast<const uint4*>(vbase + (int64_t)d * ld_vt + kv0 + kc * 8);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int key = c >> 4, kc = c & 15;
-      sK[key * 16 + (kc ^ (key & 15))] = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + i * 256;
-      const int d = c >> 3, kc = c & 7;
-      // keys kc*8 .. kc*8+7 = two blocks of 4, each to its permuted slot
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int pos = vperm(kc * 8 + half * 4);          // multiple of 4
-        const int chunk = pos >> 3, sub = (pos >> 2) & 1;  // 16-byte chunk, 8-byte half
-        const int slot = ((chunk ^ (d & 7)) << 1) | sub;
-        sV[d * 16 + slot] = half ? make_uint2(rv[i].z, rv[i].w) : make_uint2(rv[i].x, rv[i].y);
-      }
-    }
-  };
-
-  load_tile(0);
-  for (int kv0 = 0; kv0 < len; kv0 += KB) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kv0 + KB < len) load_tile(kv0 + KB);
-
-    // S^T for two blocks of 32 keys.
-    f32x16 sacc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
-#pragma unroll
-      for (int s = 0; s < DH / 16; ++s) {
-        const int key = kb * 32 + l32;
-        const int chunk = 2 * s + lhi;
-        const uint4 u = sK[key * 16 + (chunk ^ (key & 15))];
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&u),
-                                                           qf[s], sacc[kb], 0, 0, 0);
-      }
-    }
-
-    // Online softmax over this tile (lane: one query, 32 of the 64 keys).
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int key = kv0 + kb * 32 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-        const float sv = (key < len) ? sacc[kb][v] * scale : -INFINITY;
-        sacc[kb][v] = sv;
-        tmax = fmaxf(tmax, sv);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    float tsum = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(sacc[kb][v] - m_new);
-        sacc[kb][v] = p;
-        tsum += p;
-      }
-    tsum += __shfl_xor(tsum, 32, 64);
-    l_run = l_run * alpha + tsum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DH / 32; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc_o[i][v] *= alpha;
-
-    // O^T += V^T P^T over four k-steps of 16 keys.
-#pragma unroll
-    for (int kk = 0; kk < KB / 16; ++kk) {
-      const int kb = kk >> 1, v0 = (kk & 1) * 8;
-      uint32_t pk[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pk[j] = pack_bf16x2(sacc[kb][v0 + 2 * j], sacc[kb][v0 + 2 * j + 1]);
-      const bf16x8 pf = *reinterpret_cast<const bf16x8*>(pk);
-#pragma unroll
-      for (int db = 0; db < DH / 32; ++db) {
-        const int d = db * 32 + l32;
-        const int chunk = 2 * kk + lhi;
-        const int slot = (chunk ^ (d & 7)) << 1;
-        const uint2 a = sV[d * 16 + slot];
-        const uint2 b = sV[d * 16 + slot + 1];
-        const uint4 u = make_uint4(a.x, a.y, b.x, b.y);
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(&u),
-                                                            pf, acc_o[db], 0, 0, 0);
-      }
-    }
+  for (int t = 0; t < 4; ++t) {
+    const int key = (wave * 4 + t) * 4 + (lane >> 4);
+    koff[t] = (uint32_t)(key * (3 * D * 2) + (((lane & 15) ^ (key & 15)) * 16));
   }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int d = (wave * 8 + t) * 8 + (lane >> 3);
+    voff[t] = (uint32_t)(d * (uint32_t)ld_vt * 2 + (((lane & 7) ^ ((d >> 1) & 7)) * 16));
+  }
+  const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * D) + D + h * DH);
+  const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)h * DH * ld_vt + vt_base[seq]);
+  const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_void*)&sK[0][0] + wave * 4 * 1024;
+  const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0] + wave * 8 * 1024;
+  // K unit u into ring slot u % 4.  Units past the clip's last one re-load
+  // the last unit into a slot that is never read again (no branch).
+  auto issue_k = [&](int u) __attribute__((always_inline)) {
+    const char* g = kbase + (int64_t)min(u, nku - 1) * KU * (3 * D * 2);
+    const uint32_t l = k_lds + (u & 3) * KU_BYTES;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(g + koff[t], l + t * 1024);
+  };
+  // V^T tile j into buffer j % 2.
+  auto issue_v = [&](int j) __attribute__((always_inline)) {
+    const char* g = vbase + (int64_t)j * KT * 2;
+    const uint32_t l = v_lds + (j & 1) * VT_BYTES;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) dma16(g + voff[t], l + t * 1024);
+  };
 
-  if (qi >= len) return;
-  const float inv = 1.0f / l_run;
-  bf16_t* orow = out + (s0 + qi) * D + h * DH;
+  // Scores arrive in log2 units (k was scaled by log2(e) / sqrt(128)).
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};    // this lane's partial row sums
+
+  f32x16 O[DH / 32][2];
 #pragma unroll
   for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int d = db * 32 + 8 * g + 4 * lhi;
-      *reinterpret_cast<uint2*>(orow + d) =
-          make_uint2(pack_bf16x2(acc_o[db][4 * g] * inv, acc_o[db][4 * g + 1] * inv),
-                     pack_bf16x2(acc_o[db][4 * g + 2] * inv, acc_o[db][4 * g + 3] * inv));
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) O[db][qb][v] = 0.f;
+
+  f32x16 SA[2], SB[2];   // scores of one 32-key unit, per query block
+
+  const int kx = lhi ^ (l32 & 15);          // K chunk swizzle of this lane
+  const int vx = lhi ^ ((l32 >> 1) & 7);    // V^T chunk swizzle of this lane
+
+  // S^T of unit u: 8 k-steps x 2 query blocks.
+  auto qk = [&](f32x16 (&S)[2], int u) __attribute__((always_inline)) {
+    const uint4* sk = sK[u & 3];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) S[qb][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < DH / 16; ++s) {
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, sk[l32 * 16 + ((2 * s) ^ kx)]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], S[qb], 0, 0, 0);
     }
+  };
+
+  // Mask keys past the clip (unit u).  With a running maximum: take the
+  // unit's maximum and rescale the accumulators if some query's maximum grew
+  // by more than 8.
+  auto decide = [&](f32x16 (&S)[2], int u) __attribute__((always_inline)) {
+    const int kv0 = u * KU;
+    if (kv0 + KU > len) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kv0 + 8 * (v >> 2) + 4 * lhi + (v & 3);
+          S[qb][v] = key < len ? S[qb][v] : -INFINITY;
+        }
+    }
+    if constexpr (!kFixedRef) {
+      float mx[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float m = S[qb][0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) m = fmaxf(m, S[qb][v]);
+        mx[qb] = fmaxf(m, __shfl_xor(m, 32, 64));
+      }
+      if (__any(mx[0] > m_run[0] + 8.0f || mx[1] > m_run[1] + 8.0f)) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const float mn = fmaxf(m_run[qb], mx[qb]);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) O[db][qb][v] *= alpha;
+          m_run[qb] = mn;
+        }
+      }
+    }
+  };
+
+  // Probabilities of one unit and O^T += V^T P^T over its two 16-key steps
+  // (kk0, kk0 + 1 of V^T tile j).  Row sums take the bf16 probabilities the
+  // products use (one dot2 per pair).
+  auto expv = [&](f32x16 (&S)[2], int j, int kk0) __attribute__((always_inline)) {
+    const uint4* sv = sV[j & 1];
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      bf16x8 pf[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float nm = kFixedRef ? 0.f : -m_run[qb];
+        uint32_t pk[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          float p0 = S[qb][half * 8 + 2 * jj], p1 = S[qb][half * 8 + 2 * jj + 1];
+          if constexpr (!kFixedRef) {
+            p0 += nm;
+            p1 += nm;
+          }
+          pk[jj] = pack_bf16x2(__builtin_amdgcn_exp2f(p0), __builtin_amdgcn_exp2f(p1));
+          l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[jj]), ones,
+                                                      l_run[qb], false);
+        }
+        pf[qb] = __builtin_bit_cast(bf16x8, pk);
+      }
+      const int kk = kk0 + half;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db) {
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, sv[(db * 32 + l32) * 8 + ((2 * kk) ^ vx)]);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
+      }
+    }
+  };
+
+  // Prologue: K units 0..2 and V^T tile 0; scores of unit 0.
+  issue_k(0);
+  issue_k(1);
+  issue_k(2);
+  issue_v(0);
+  lds_loads_wait();
+  __syncthreads();
+  qk(SA, 0);
+  decide(SA, 0);
+
+  // Tile j (not the last one): units 2j, 2j+1 go through softmax and V while
+  // the scores of units 2j+1 and 2j+2 are computed.  K units 2j+1, 2j+2 and
+  // V^T tile j were loaded during the previous step; this step loads K units
+  // 2j+3, 2j+4 into the slots of 2j-1, 2j and V^T tile j+1 into the buffer
+  // of tile j-1, all read before the barrier.
+#pragma unroll 1
+  for (int j = 0; j + 1 < nkt; ++j) {
+    lds_loads_wait();
+    __syncthreads();
+    issue_k(2 * j + 3);
+    issue_k(2 * j + 4);
+    issue_v(j + 1);
+    qk(SB, 2 * j + 1);
+    expv(SA, j, 0);
+    if constexpr (!kFixedRef) decide(SB, 2 * j + 1);
+    qk(SA, 2 * j + 2);
+    expv(SB, j, 2);
+    // Unit 2j+2 may lie in the last tile: with a fixed reference its mask is
+    // applied below; a running maximum needs it now.
+    if constexpr (!kFixedRef) decide(SA, 2 * j + 2);
+  }
+
+  // Last tile.
+  {
+    const int j = nkt - 1;
+    lds_loads_wait();
+    __syncthreads();
+    if constexpr (kFixedRef) decide(SA, 2 * j);
+    const bool second = j * KT + KU < len;
+    if (second) qk(SB, 2 * j + 1);
+    expv(SA, j, 0);
+    if (second) {
+      decide(SB, 2 * j + 1);
+      expv(SB, j, 2);
+    }
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+    const int q = q0 + wave * QPW + qb * 32 + l32;
+    if (q >= len) continue;
+    const float inv = 1.0f / lt;
+    bf16_t* orow = out + (s0 + q) * D + h * DH;
+#pragma unroll
+    for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = db * 32 + 8 * g + 4 * lhi;
+        *reinterpret_cast<uint2*>(orow + d) =
+            make_uint2(pack_bf16x2(O[db][qb][4 * g] * inv, O[db][qb][4 * g + 1] * inv),
+                       pack_bf16x2(O[db][qb][4 * g + 2] * inv, O[db][qb][4 * g + 3] * inv));
+      }
+  }
 }
 
 }  // namespace
 
+bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g,
+                            const float* k_b) {
+  // Norm bound of a head vector after LayerNorm (sum of squares of the
+  // normalised values <= 128) with gain g and bias b, rotated (norm kept).
+  auto norm_bound = [](const float* g, const float* b) {
+    double gmax = 0.0, bsq = 0.0;
+    for (int i = 0; i < DH; ++i) {
+      gmax = std::max(gmax, std::fabs((double)g[i]));
+      bsq += (double)b[i] * b[i];
+    }
+    return gmax * std::sqrt((double)DH) + std::sqrt(bsq);
+  };
+  // 2^-6 covers bf16 rounding of q and k and fp32 rounding of the products.
+  const double bound = norm_bound(q_g, q_b) * norm_bound(k_g, k_b) * (1.0 + 1.0 / 64);
+  const double log2_range = bound * 1.4426950408889634 / std::sqrt((double)DH);
+  return std::isfinite(log2_range) && log2_range <= 100.0;
+}
+
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
-                            const int32_t* tile_q0, int n_tiles, bf16_t* out,
+                            const int32_t* tile_q0, int n_tiles, bool fixed_ref, bf16_t* out,
                             hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
-  attention_kernel<<<dim3(n_tiles, H), dim3(256), 0, stream>>>(qkv, vt, ld_vt, cu_seq, vt_base,
-                                                               tile_seq, tile_q0, out);
+  // V^T byte offsets inside a tile are 32-bit: 128 rows of ld_vt bf16.
+  if (ld_vt <= 0 || ld_vt % 64 != 0 || (int64_t)DH * ld_vt * 2 >= (int64_t)1 << 31)
+    return hipErrorInvalidValue;
+  const int n_items = n_tiles * H;
+  const int grid = (n_items + 7) / 8 * 8;
+  if (fixed_ref)
+    attention_kernel<true><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
+        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out);
+  else
+    attention_kernel<false><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
+        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out);
   return hipGetLastError();
 }
 

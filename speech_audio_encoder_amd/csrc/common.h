@@ -22,6 +22,9 @@ constexpr int NFFT = 512;
 constexpr int NBIN = 257;
 constexpr int64_t MAX_SAMPLES = 57600000;   // one hour at 16 kHz
 constexpr int MAX_POS = 45000;              // positions of a one-hour clip
+// Scale applied to k after QK-norm and rotation: log2(e) / sqrt(head dim),
+// so that q . k is the softmax exponent in base 2.
+constexpr float K_SCORE_SCALE = 0.12751743082459868f;
 
 typedef uint16_t bf16_t;   // bfloat16 bits in memory
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -32,15 +35,19 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
 
-// Round to nearest, ties to even.  Inputs here are finite.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// Round to nearest, ties to even: gfx950 converts in hardware
+// (v_cvt_pk_bf16_f32, two values per instruction).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_v v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(bf16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

@@ -65,9 +65,12 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, bf16
                             int64_t rows, hipStream_t stream);
 
 // In place on qkv [rows, 3840] bf16, per attention tile (clip tile_seq[i],
-// positions tile_p0[i] .. +127) and head: q <- RoPE(LN_q(q)), k <- RoPE(LN_k(k)),
-// and v copied transposed to vt[h][d][vt_base[b] + p] (ld_vt per d), with
-// zeros for p in [P_b, roundup(P_b, 64)).  cu_seq[b] is clip b's first row.
+// positions tile_p0[i] .. +127) and head: q <- RoPE(LN_q(q)),
+// k <- RoPE(LN_k(k)) * K_SCORE_SCALE,
+// and v copied transposed to vt[h][d][vt_base[b] + c] (ld_vt per d), where
+// column c of each aligned group of 16 holds position 0-3, 8-11, 4-7, 12-15
+// of the group in that order, with zeros for positions in
+// [P_b, roundup(P_b, 64)).  cu_seq[b] is clip b's first row.
 hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* vt_base,
                               const int32_t* tile_seq, const int32_t* tile_p0, int n_tiles,
                               const float* qg, const float* qb, const float* kg, const float* kb,
@@ -91,9 +94,18 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
 // at columns vt_base[b]..., zero past P_b up to a multiple of 64).  Work tile
 // i covers queries [tile_q0[i], min(tile_q0[i] + 128, P_b)) of clip
 // tile_seq[i].  out is bf16 [rows, 1280] with head h in columns h*128...
+// qkv must have 63 readable rows after its last one (their k is masked), and
+// vt's columns hold keys permuted inside each group of 16 as written by
+// launch_qknorm_rope.
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
-                            const int32_t* tile_q0, int n_tiles, bf16_t* out,
+                            const int32_t* tile_q0, int n_tiles, bool fixed_ref, bf16_t* out,
                             hipStream_t stream);
+// fixed_ref may be true only when |q . k| * log2(e) / sqrt(128) <= 100 for
+// every query and key (softmax against a fixed reference instead of a
+// running maximum); attention_fixed_ref_ok decides it from the QK-norm
+// parameters of a layer.
+bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g,
+                            const float* k_b);
 
 }  // namespace enc

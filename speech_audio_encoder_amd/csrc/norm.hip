@@ -169,13 +169,16 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
       const float ga[4] = {g0.x, g0.y, g0.z, g0.w}, gb[4] = {g1.x, g1.y, g1.z, g1.w};
       const float ea[4] = {e0.x, e0.y, e0.z, e0.w}, eb[4] = {e1.x, e1.y, e1.z, e1.w};
       const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+      // k leaves scaled by log2(e) / sqrt(128): the attention kernel's
+      // scores are then directly the exponents of exp2.
+      const float outscale = which ? K_SCORE_SCALE : 1.0f;
       float lo[4], hi[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float y0 = a[e] * rstd * ga[e] + ea[e];
         const float y1 = b[e] * rstd * gb[e] + eb[e];
-        lo[e] = y0 * cc[e] - y1 * ss[e];
-        hi[e] = y1 * cc[e] + y0 * ss[e];
+        lo[e] = (y0 * cc[e] - y1 * ss[e]) * outscale;
+        hi[e] = (y1 * cc[e] + y0 * ss[e]) * outscale;
       }
       *reinterpret_cast<uint2*>(base + d0) =
           make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
@@ -188,14 +191,18 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   // registers -- output word k of column c takes half c%2 of word c/2 from
   // rows 2k and 2k+1 (one byte permute each) -- and stores 8 keys of each of
   // its 8 dims as 16-byte vectors.  Positions past the clip are zeros.
+  // Key order inside each group of 16 columns: positions 0-3, 8-11, 4-7,
+  // 12-15 of the group, so that 8 consecutive columns are the 8 keys one
+  // lane supplies to a 32x32x16 MFMA whose other operand comes from the
+  // accumulator layout of K Q^T (rows 4*(lane/32) + 8g + r).
   {
-    const int rb = threadIdx.x >> 4;           // 16 blocks of 8 positions
+    const int rb = threadIdx.x >> 4;           // 16 blocks of 8 columns
     const int db = threadIdx.x & 15;           // 16 blocks of 8 dims
     if (rb * 8 < span) {
       uint4 rows[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int p = p0 + rb * 8 + i;
+        const int p = p0 + 16 * (rb >> 1) + 4 * (rb & 1) + (i & 3) + 8 * (i >> 2);
         rows[i] = (p < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + p) * (3 * D) + 2 * D +
                                                                h * DH + db * 8)
                             : make_uint4(0, 0, 0, 0);

@@ -177,7 +177,9 @@ Layout layout_for(int64_t rows, int64_t vt_cols) {
   const size_t r = (size_t)std::max<int64_t>(rows, 1);
   l.x = take(r * D * 4);
   l.a = take(r * D * 2);
-  l.qkv = take(r * 3 * D * 2);
+  // 64 rows of slack: attention reads k in whole 64-key tiles past a clip's
+  // last position (those keys are masked).
+  l.qkv = take((r + 64) * 3 * D * 2);
   l.o = take(r * D * 2);
   l.u = take(r * std::max(FF, DIN) * 2);   // also holds the stacked log-mel
   l.ld_vt = std::max<int64_t>(vt_cols, 64);
@@ -189,6 +191,7 @@ Layout layout_for(int64_t rows, int64_t vt_cols) {
 struct LayerW {
   bf16_t *w_qkv, *w_o, *w_up, *w_down;
   float *ln1_g, *ln1_b, *b_qkv, *q_g, *q_b, *k_g, *k_b, *b_o, *ln2_g, *ln2_b, *b_up, *b_down;
+  bool attn_fixed_ref;   // QK-norm bounds the scores: softmax without a running maximum
 };
 
 }  // namespace
@@ -475,6 +478,15 @@ int enc_create(const enc_weights* w, enc_ctx** out) {
   if (e == hipSuccess) e = hipMemcpy(c->rope_sin, rc_sin.data(), rope_bytes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->plan_copied, hipEventDisableTiming);
   if (e == hipSuccess) e = hipDeviceSynchronize();
+  // Per layer: may attention use a fixed softmax reference (bounded scores)?
+  for (int i = 0; i < L && e == hipSuccess; ++i) {
+    LayerW& d = c->layers[i];
+    float qk[4][DH];
+    const float* src[4] = {d.q_g, d.q_b, d.k_g, d.k_b};
+    for (int t = 0; t < 4 && e == hipSuccess; ++t)
+      e = hipMemcpy(qk[t], src[t], sizeof(qk[t]), hipMemcpyDeviceToHost);
+    d.attn_fixed_ref = e == hipSuccess && attention_fixed_ref_ok(qk[0], qk[1], qk[2], qk[3]);
+  }
   if (e != hipSuccess) {
     release(c);
     return hip_fail(e, "enc_create upload");
@@ -579,7 +591,8 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, Lw.q_g, Lw.q_b, Lw.k_g,
                                   Lw.k_b, ctx->rope_cos, ctx->rope_sin, vt, lay.ld_vt, stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
-               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, o, stream));
+               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles,
+                                Lw.attn_fixed_ref, o, stream));
     ENC_LAUNCH(ENC_K_GEMM_O, launch_gemm(Epilogue::kBiasResidualF32, o, D, Lw.w_o, D, Lw.b_o, x,
                                          D, R, D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln2_g, Lw.ln2_b, a, R, stream));

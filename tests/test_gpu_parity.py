@@ -58,7 +58,24 @@ def get_weights(kind):
             _WEIGHTS[kind] = workloads.workload_weights("tiny")
         elif kind == "perturbed":
             _WEIGHTS[kind] = workloads.make_weights(2, bf16=False, perturb=True)
+        elif kind == "sharp":
+            # QK-norm gains x3: scores too large for a fixed softmax reference
+            w = workloads.make_weights(2, bf16=False, perturb=True)
+            for lw in w["layers"]:
+                lw["q_g"] = lw["q_g"] * 3.0
+                lw["k_g"] = lw["k_g"] * 3.0
+            _WEIGHTS[kind] = w
     return _WEIGHTS[kind]
+
+
+def score_log2_bound(lw):
+    """Bound on |q.k| * log2(e) / sqrt(128) implied by the QK-norm parameters
+    (a LayerNorm'd 128-vector has norm <= sqrt(128)), with the 2^-6 margin the
+    library uses to choose a fixed softmax reference (bound <= 100)."""
+    def norm_bound(g, b):
+        return float(np.abs(g).max()) * np.sqrt(128) + float(np.linalg.norm(b))
+    return (norm_bound(lw["q_g"], lw["q_b"]) * norm_bound(lw["k_g"], lw["k_b"])
+            * (1 + 1 / 64) * np.log2(np.e) / np.sqrt(128))
 
 
 def prefix(w, n):
@@ -252,6 +269,26 @@ def test_forward_ragged_perturbed_weights(torch_mod, ctx_for):
         if p:
             ref = oracle.encode(audio[b, :n], w)
             check_embeddings(got[b, :p], ref, f"ragged clip {b} (P={p})")
+
+
+def test_forward_large_qk_gains_running_max(torch_mod, ctx_for):
+    # QK-norm gains large enough that the scores need a running softmax
+    # maximum (the bounded fast path is not allowed); clips spanning several
+    # query and key tiles with ragged tails.
+    torch = torch_mod
+    w = get_weights("sharp")
+    for lw in w["layers"]:
+        assert score_log2_bound(lw) > 100.0
+    for lw in get_weights("perturbed")["layers"]:
+        assert score_log2_bound(lw) <= 100.0
+    lengths = [700_000, 33_000, 16_400]
+    audio, lengths = workloads.custom_audio(lengths, seed=61)
+    got = run_forward(torch, ctx_for("sharp", 2, "f32"), audio, lengths)
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        assert np.all(got[b, p:] == 0.0)
+        ref = oracle.encode(audio[b, :n], w)
+        check_embeddings(got[b, :p], ref, f"large-gain clip {b} (P={p})")
 
 
 def test_forward_batch_invariance(torch_mod, ctx_for):
