@@ -73,6 +73,31 @@ def kernel_bytes(name, rows, lengths):
     }.get(name)
 
 
+def gemm_bytes(name, rows):
+    """Algorithmic HBM bytes of one GEMM launch: A and W read once, C written
+    once (bf16, or fp32 read+write for the residual epilogue)."""
+    mnk = {"gemm_in": (D, DIN, 4), "gemm_qkv": (3 * D, D, 2), "gemm_o": (D, D, 8),
+           "gemm_up": (FF, D, 2), "gemm_down": (D, FF, 8)}.get(name)
+    if mnk is None:
+        return None
+    n, k, c_bytes = mnk
+    return rows * k * 2 + n * k * 2 + rows * n * c_bytes
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of a kernel class from the committed rocprofv3
+    counter summary of this workload, if the kernel's sources are unchanged
+    since the counters were taken (else None)."""
+    from speech_audio_encoder_amd import prof_summary
+    rec = prof_summary.read_traffic(os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md"))
+    if not rec or rec.get("workload") != workload:
+        return None
+    c = rec.get("classes", {}).get(kernel)
+    if not c or c.get("sources_sha256") != prof_summary.source_hashes(kernel):
+        return None
+    return int(round(c["bytes_per_launch"]))
+
+
 def cpu_baseline(audio, lengths, weights, budget_s=12.0):
     """Time the oracle (as it stands) on whole clips until ~budget_s of CPU."""
     import oracle
@@ -187,20 +212,27 @@ def main():
 
     avg_ms = dom_ms / max(n_dom, 1)
     fl = kernel_flops(dom, rows, pos)
+    traffic = measured_traffic(args.workload, dom)
     if fl is not None:
         achieved = fl / (avg_ms / 1000.0) / 1e12
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "avg_launch_ms": round(avg_ms, 5), "launches": n_dom,
                 "flops_per_launch": fl}
+        ab = gemm_bytes(dom, rows)
+        if ab is not None:
+            roof["algorithmic_bytes_per_launch"] = ab
     else:
         by = kernel_bytes(dom, rows, lengths)
         achieved = by / (avg_ms / 1000.0) / 1e9
         roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": None, "avg_launch_ms": round(avg_ms, 5), "launches": n_dom,
+                "traffic": traffic, "avg_launch_ms": round(avg_ms, 5), "launches": n_dom,
                 "bytes_per_launch": by}
+    if traffic is not None:
+        roof["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, " \
+                               "copy-calibrated)"
 
     result = {
         "metric": "audio-seconds encoded/sec (bf16 encoder fwd) + % MFMA peak, 1 MI355X",

@@ -1,0 +1,234 @@
+"""Summaries of rocprofv3 output for the encoder's kernels.
+
+Two reports, written as Markdown under ``profiles/``:
+
+* ``kernels``: per-kernel calls / total / average duration from a
+  ``--kernel-trace`` CSV (``<name>_kernel_trace.csv``);
+* ``traffic``: HBM bytes per dispatch from two ``--pmc`` runs (FETCH_SIZE,
+  WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
+  for a plain device copy of known size (``bench.py --copy-calibration-mib``),
+  grouped by the kernel classes the library times (``enc_profile_kernel``).
+  The report ends with a JSON block that ``bench.py`` reads for the
+  ``traffic`` field of its roofline; each class records the SHA-256 of the
+  sources its kernels are built from, so a changed kernel reports no traffic.
+
+Usage:
+  python -m speech_audio_encoder_amd.prof_summary kernels TRACE_CSV OUT_MD "COMMAND"
+  python -m speech_audio_encoder_amd.prof_summary traffic WORKLOAD FETCH_CSV WRITE_CSV \\
+      COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB OUT_MD "COMMANDS"
+"""
+
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+
+# Kernel class -> sources its kernels come from.
+CLASS_SOURCES = {
+    "frontend": ["frontend.hip", "common.h", "kernels.h"],
+    "gemm_in": ["gemm.hip", "common.h", "kernels.h"],
+    "gemm_qkv": ["gemm.hip", "common.h", "kernels.h"],
+    "gemm_o": ["gemm.hip", "common.h", "kernels.h"],
+    "gemm_up": ["gemm.hip", "common.h", "kernels.h"],
+    "gemm_down": ["gemm.hip", "common.h", "kernels.h"],
+    "layernorm": ["norm.hip", "common.h", "kernels.h"],
+    "qknorm_rope": ["norm.hip", "common.h", "kernels.h"],
+    "attention": ["attention.hip", "common.h", "kernels.h"],
+    "final_norm": ["norm.hip", "common.h", "kernels.h"],
+}
+
+
+def source_hashes(cls):
+    out = {}
+    for name in CLASS_SOURCES[cls]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            out[name] = hashlib.sha256(f.read()).hexdigest()
+    return out
+
+
+def short_name(name):
+    n = re.sub(r"\(anonymous namespace\)::|enc::|^void ", "", name)
+    n = re.sub(r"\(Epilogue\)", "E", n)
+    return re.sub(r"\(.*", "", n) if "<" not in n else re.sub(r">\(.*", ">", n)
+
+
+def epilogue_class(short):
+    """Which GEMM a dispatch belongs to, from its epilogue (E0 bias->bf16:
+    qkv; E1 GELU: up; E2 residual: o and down alternate; E3 fp32: input)."""
+    m = re.search(r"<E(\d)", short)
+    return int(m.group(1)) if m else None
+
+
+def classify(rows):
+    """rows: dicts with Kernel_Name in dispatch order -> list of (class, row).
+    A GEMM call is a contiguous run of dispatches with one epilogue (big-tile
+    kernel, piece kernel, split-K reduce); residual-epilogue runs alternate
+    between the attention output projection and the FFN contraction."""
+    out = []
+    e2_runs = 0
+    prev_e2 = False
+    for r in rows:
+        s = short_name(r["Kernel_Name"])
+        cls, is_e2 = None, False
+        if "logmel" in s:
+            cls = "frontend"
+        elif s.startswith("layernorm"):
+            cls = "layernorm"
+        elif s.startswith("qknorm"):
+            cls = "qknorm_rope"
+        elif s.startswith("attention"):
+            cls = "attention"
+        elif s.startswith("final_norm"):
+            cls = "final_norm"
+        elif "gemm" in s or "splitk" in s:
+            e = epilogue_class(s)
+            if e == 0:
+                cls = "gemm_qkv"
+            elif e == 1:
+                cls = "gemm_up"
+            elif e == 3:
+                cls = "gemm_in"
+            else:
+                is_e2 = True
+                if not prev_e2:
+                    e2_runs += 1
+                cls = "gemm_o" if e2_runs % 2 == 1 else "gemm_down"
+        prev_e2 = is_e2
+        out.append((cls, r))
+    return out
+
+
+def kernels_report(trace_csv, out_md, command):
+    rows = list(csv.DictReader(open(trace_csv)))
+    agg = collections.OrderedDict()
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        agg.setdefault(short_name(r["Kernel_Name"]), []).append(d)
+    tot = sum(sum(v) for v in agg.values())
+    lines = ["# Kernel durations: " + os.path.basename(out_md)[:-3], "",
+             "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | total ms | avg us | share |", "|---|---:|---:|---:|---:|"]
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k}` | {len(v)} | {sum(v) / 1000:.3f} | {sum(v) / len(v):.2f} | "
+                     f"{100 * sum(v) / tot:.1f}% |")
+    # Per kernel class (the units bench.py times with HIP events): a class
+    # launch is one call of the library's launcher, e.g. a GEMM's big-tile
+    # kernel plus its tail pieces and split-K reduce.
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    per = collections.OrderedDict()
+    prev = None
+    for cls, r in classify(rows):
+        if cls is None:
+            prev = None
+            continue
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+        e = per.setdefault(cls, [0.0, 0])
+        e[0] += d
+        if cls != prev or cls in ("layernorm", "frontend", "final_norm", "qknorm_rope",
+                                  "attention"):
+            e[1] += 1
+        prev = cls
+    lines += ["", "Per kernel class (one launch = one call of the library's launcher; "
+              "dispatch durations summed):", "",
+              "| class | launches | avg us per launch |", "|---|---:|---:|"]
+    for cls, (t, n) in per.items():
+        lines.append(f"| {cls} | {n} | {t / max(n, 1):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def _counter(path, counter):
+    rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    key = "Dispatch_Id" if rows and "Dispatch_Id" in rows[0] else None
+    if key:
+        rows.sort(key=lambda r: int(r[key]))
+    return rows
+
+
+def traffic_report(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib,
+                   out_md, commands):
+    copy_bytes = copy_mib * (1 << 20)
+
+    def calib(path, counter):
+        vals = [float(r["Counter_Value"]) for r in _counter(path, counter)
+                if "copy" in r["Kernel_Name"].lower()]
+        vals = [v for v in vals if v > 0.25 * copy_bytes / 1024]   # the 1-GiB copies
+        med = sorted(vals)[len(vals) // 2]
+        return copy_bytes / (med * 1024.0), med
+
+    f_fac, f_med = calib(copy_fetch_csv, "FETCH_SIZE")
+    w_fac, w_med = calib(copy_write_csv, "WRITE_SIZE")
+    per_class = {}
+    for counter, path, fac in (("FETCH_SIZE", fetch_csv, f_fac), ("WRITE_SIZE", write_csv, w_fac)):
+        rows = _counter(path, counter)
+        for cls, r in classify(rows):
+            if cls is None:
+                continue
+            d = per_class.setdefault(cls, {"FETCH_SIZE": [], "WRITE_SIZE": [], "kernels": set()})
+            d[counter].append(float(r["Counter_Value"]) * 1024.0 * fac)
+            d["kernels"].add(short_name(r["Kernel_Name"]))
+    calls = {"frontend": 1, "gemm_in": 1, "final_norm": 1, "layernorm": 2}
+    record = {"workload": workload, "fetch_factor": f_fac, "write_factor": w_fac, "classes": {}}
+    lines = ["# HBM traffic per launch: " + workload, "",
+             "Commands (from the repository root, on one MI355X; each counter in a run",
+             "of its own):", "", "```", commands, "```", "",
+             f"Calibration: a plain {copy_mib} MiB device copy reads {f_med:.0f} KiB on "
+             f"FETCH_SIZE (factor {f_fac:.3f}) and {w_med:.0f} KiB on WRITE_SIZE "
+             f"(factor {w_fac:.3f}); counters below are scaled by those factors.", "",
+             "Per launch of a kernel class = the sum over its dispatches in one step divided "
+             "by the class's launches per step (layers, or 2 x layers for LayerNorm).", "",
+             "| class | kernels | fetch MB/launch | write MB/launch | total MB/launch |",
+             "|---|---|---:|---:|---:|"]
+    n_steps = None
+    for cls, d in per_class.items():
+        if cls == "frontend":
+            n_steps = len(d["FETCH_SIZE"])   # one frontend dispatch per step
+    n_steps = n_steps or 1
+    for cls in CLASS_SOURCES:
+        if cls not in per_class:
+            continue
+        d = per_class[cls]
+        launches_per_step = calls.get(cls)
+        if launches_per_step is None:
+            # per-layer classes: dispatches of the class / kernels per call
+            launches_per_step = max(1, len(d["FETCH_SIZE"]) // n_steps //
+                                    max(1, len(d["kernels"])))
+        elif cls == "layernorm":
+            launches_per_step = len(d["FETCH_SIZE"]) // n_steps
+        n_launch = n_steps * launches_per_step
+        fb = sum(d["FETCH_SIZE"]) / n_launch
+        wb = sum(d["WRITE_SIZE"]) / n_launch
+        lines.append(f"| {cls} | {', '.join(f'`{k}`' for k in sorted(d['kernels']))} | "
+                     f"{fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
+        record["classes"][cls] = {"fetch_bytes": fb, "write_bytes": wb,
+                                  "bytes_per_launch": fb + wb, "sources_sha256": source_hashes(cls)}
+    lines += ["", "Machine-readable record (read by bench.py):", "", "```json",
+              json.dumps(record, indent=1, sort_keys=True), "```"]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def read_traffic(md_path):
+    """The JSON record at the end of a traffic report, or None."""
+    try:
+        text = open(md_path).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    return json.loads(m.group(1)) if m else None
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "kernels":
+        kernels_report(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "traffic":
+        traffic_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
+                       int(sys.argv[7]), sys.argv[8], sys.argv[9])
+    else:
+        sys.exit(__doc__)
