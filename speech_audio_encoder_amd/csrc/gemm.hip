@@ -12,15 +12,15 @@
 // Two kernels share the output tiling (256 x 256 tiles, numbered in groups of
 // four tile rows so that neighbouring tiles share A rows and W columns):
 //
-//  * gemm_big_kernel -- persistent, one workgroup per CU, four wavefronts of
-//    128 x 128 outputs each (16 MFMA 32x32x16 accumulators, held in AGPRs).
-//    It covers every full round of tiles.  Operands go straight from global
+//  * gemm_big_kernel -- persistent, one workgroup per CU, eight wavefronts
+//    of 128 x 64 outputs each in two groups that alternate between running
+//    MFMAs and issuing loads / storing results (see its own comment).  It
+//    covers every full round of tiles.  Operands go straight from global
 //    memory into LDS with global_load_lds_dwordx4 (no register staging; the
 //    XOR swizzle that keeps the MFMA operand reads conflict-free is applied on
-//    the global side by choosing which 16-byte chunk each lane fetches).  A
-//    four-stage ring of 32-wide K steps (4 x 32 KB) keeps three steps of loads
-//    in flight; one barrier per step.  The stream of steps runs on across the
-//    workgroup's tiles, so the next tile's loads overlap this tile's epilogue.
+//    the global side by choosing which 16-byte chunk each lane fetches), in
+//    64-wide K slices of whole 128-byte lines.  The stream of steps runs on
+//    across the workgroup's tiles.
 //  * gemm_piece_kernel (+ splitk_reduce_kernel) -- the tiles left after the
 //    last full round, or the whole product when it has fewer 256 x 256 tiles
 //    than CUs, as 128 x 128 pieces split along K when needed so that every CU
@@ -40,7 +40,7 @@ namespace enc {
 namespace {
 
 constexpr int BIG = 256;    // big tile edge
-constexpr int BKS = 32;     // big kernel K step
+constexpr int BKS = 32;     // piece kernel K step
 constexpr int GROUP_M = 4;  // tile rows per ordering group
 
 // Exact-erf GELU, x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), with erf taken from
@@ -121,200 +121,165 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_void* lds) {
   __builtin_amdgcn_global_load_lds(gptr, lds, 16, 0, 0);
 }
 
-// ----------------------------------------------------------- big (persistent)
-template <Epilogue EPI, int NS>
-__global__ __launch_bounds__(256, 1) void gemm_big_kernel(
+// ------------------------------------------------- big (persistent, 8 waves)
+// 256 x 256 tiles in 64-wide K steps.  Eight wavefronts in two groups of
+// four, one wavefront of each group per SIMD; group g owns output rows
+// 128 g .. 128 g + 127 of the tile and wave q of a group the columns
+// 64 q .. 64 q + 63 (eight 32x32 accumulators, 128 registers).  A slices
+// (256 rows x 64 K, 32 KB) rotate through three LDS slots and W slices
+// through two (160 KB).  Each step has two phases separated by a barrier:
+//   phase 1: group 0 runs its MFMAs on step g; group 1 sends the direct loads
+//            of W for step g+1 (and, at a tile's first step, stores its part
+//            of the previous tile);
+//   phase 2: group 1 runs its MFMAs on step g; group 0 sends the loads of A
+//            for step g+2 (and, at a tile's last step, stores its part).
+// A wavefront that is issuing loads (which can stall for hundreds of cycles
+// when the load path is busy) or storing results is never the one feeding
+// the matrix cores of its SIMD, and the stores of one tile spread over two
+// phases instead of leaving every CU idle at once.
+// Direct load of 16 bytes per lane from sbase + voff to LDS byte address
+// lds + 16 * lane (sbase and lds uniform).  Written in asm so that the
+// compiler does not track it: the kernel waits for these loads explicitly
+// (wait_vm0) before the barrier that publishes a slot, and the compiler would
+// otherwise stall every LDS read it cannot prove disjoint from a slot in
+// flight.  M0 is not used otherwise by this kernel.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_s(const char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int PBK = 64;   // K step of the persistent kernel
+
+template <Epilogue EPI>
+__global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int K,
     int tiles_m, int tiles_n, int n_big) {
-  // Stage layout (uint4 units): A rows 0..255 x 4 chunks, then W rows x 4.
-  constexpr int STG = 2 * BIG * BKS / 8;
-  // NS stages of 32 KB.  Distinct arrays, referenced statically, so the
-  // compiler can tell a DMA into one stage from reads of another and does not
-  // wait on it (unused ones are not allocated).
-  static_assert(NS == 4 || NS == 5, "ring depth");
-  __shared__ uint4 st0[STG];
-  __shared__ uint4 st1[STG];
-  __shared__ uint4 st2[STG];
-  __shared__ uint4 st3[STG];
-  __shared__ uint4 st4[STG];
-  auto stage = [&](int i) -> uint4* {
-    switch (i) {
-      case 0: return st0;
-      case 1: return st1;
-      case 2: return st2;
-      case 3: return st3;
-      default: return st4;
-    }
-  };
+  constexpr int SL = BIG * PBK / 8;   // uint4 per slot (32 KB)
+  __shared__ uint4 sA[3][SL];
+  __shared__ uint4 sW[2][SL];
 
   const int G = gridDim.x;
   const int wg = blockIdx.x;
-  // Hardware block wg runs on XCD wg % 8: give each XCD a contiguous slot range.
   const int slot = (G % 8 == 0) ? (wg % 8) * (G / 8) + wg / 8 : wg;
   const int my_tiles = slot < n_big ? (n_big - 1 - slot) / G + 1 : 0;
-  const int KT = K / BKS;
+  const int KT = K / PBK;
+  const int total = my_tiles * KT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int q = wave & 3;
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  // DMA lane mapping: wavefront load i of wave w covers tile rows
-  // (w*4 + i)*16 + lane/4 (16 rows of 64 B); lane%4 is the physical chunk,
-  // holding logical chunk (lane%4) ^ ((row/2) % 4).
-  const int drow = wave * 64 + (lane >> 2);
-  const int dcol = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
-  // Issue state: tile ir of this workgroup, k step ikt, and the per-lane
-  // source rows of that tile (rows past M re-read row M-1; dropped later).
-  // Past the workgroup's last tile the loads simply repeat that tile's K
-  // range (harmless, and it keeps the step body free of branches).
-  int ir = 0, ikt = 0;
-  const bf16_t* ia[4];
-  const bf16_t* iw[4];
-  auto set_issue_tile = [&]() {
-    int tm, tn;
-    tile_coords(min(ir, my_tiles - 1) * G + slot, tiles_m, tiles_n, tm, tn);
-    const int64_t am = (int64_t)tm * BIG;
-    const int64_t wn0 = (int64_t)tn * BIG;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ia[i] = A + min<int64_t>(am + drow + 16 * i, M - 1) * lda + dcol;
-      iw[i] = W + (wn0 + drow + 16 * i) * ldw + dcol;
-    }
-  };
-  auto issue = [&](uint4* stage) {
-    const int k0 = ikt * BKS;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dma16(ia[i] + k0, (lds_void*)(stage + (wave * 4 + i) * 64));
-      dma16(iw[i] + k0, (lds_void*)(stage + BIG * 4 + (wave * 4 + i) * 64));
-    }
-  };
-  auto advance = [&]() {
-    if (++ikt == KT) {
-      ikt = 0;
-      ++ir;
-      if (ir < my_tiles) set_issue_tile();
-    }
-  };
-
-  // Operand reads: row r of a stage, logical chunk c -> uint4 r*4 + (c ^ ((r/2)%4)).
-  const int rsw = (l32 >> 1) & 3;
-  const int wofs = BIG * 4 + (wn * 128 + l32) * 4;
-  const int aofs = (wm * 128 + l32) * 4;
-
-  f32x16 acc[4][4];
-  // Operand fragments of a whole 32-wide step (two 16-wide slices: 4 of W and
-  // 4 of A each), double-buffered across steps.
-  bf16x8 fb0[16], fb1[16];
-  auto load = [&](const uint4* sp, bf16x8 (&f)[16]) {
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      const int pc = (2 * sl + lhi) ^ rsw;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 u = sp[wofs + i * 128 + pc];
-        f[sl * 8 + i] = *reinterpret_cast<const bf16x8*>(&u);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint4 u = sp[aofs + j * 128 + pc];
-        f[sl * 8 + 4 + j] = *reinterpret_cast<const bf16x8*>(&u);
-      }
-    }
-  };
-  auto mma = [&](const bf16x8 (&f)[16]) {
-#pragma unroll
-    for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[sl * 8 + i], f[sl * 8 + 4 + j],
-                                                              acc[i][j], 0, 0, 0);
-  };
-  // Within one basic block, spread the 16 LDS reads of step g between the 32
-  // MFMAs of step g - 1 (a wave that issues an MFMA can issue an LDS read
-  // while the matrix core works; a burst of reads would leave it idle).  The
-  // 8 DMAs of step g + NS - 1 go out as one burst before the MFMAs: spread
-  // between them they measured slower.
-  auto interleave = [&]() {
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
-    }
-  };
-
-  set_issue_tile();
-#pragma unroll
-  for (int i = 0; i < NS - 1; ++i) {
-    issue(stage(i));
-    advance();
-  }
-  int since_epi = 0;   // steps since the last epilogue (its stores count in vmcnt)
-
-  // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
-  // 6:4, lgkmcnt 11:8); fields not named are left at their maximum.
-  // WAIT_STEP allows the loads of the NS - 2 younger steps (8 DMAs each).
-  constexpr int WAIT_LGKM0 = 0xC07F;                       // lgkmcnt(0)
-  constexpr int VM = 8 * (NS - 2);
-  constexpr int WAIT_STEP = (VM & 15) | ((VM >> 4) << 14) | 0x0070;  // vmcnt(VM) lgkmcnt(0)
-  constexpr int WAIT_EPI = 0xC07F & ~0x0F00;               // vmcnt(63) lgkmcnt(0)
-
-  // One K step (tile-local index u) on stage u % NS: its fragments go to
-  // fb[u % 2] while the MFMAs of the previous step run from the other buffer
-  // (none on a tile's first step), and the loads of the step NS - 1 ahead go
-  // to the stage just freed.  Before the barrier each wave waits for its own
-  // loads of this step (the younger steps stay in flight; just after an
-  // epilogue its stores count too, hence the looser bound) and for its LDS
-  // reads of the previous step, whose stage the new loads overwrite.  The
-  // barrier is the bare s_barrier: a fenced one would also wait for the
-  // younger loads.
-  auto step = [&](int u, bool first) {
-    if (since_epi > 0 && since_epi < NS)
-      __builtin_amdgcn_s_waitcnt(WAIT_EPI);
-    else
-      __builtin_amdgcn_s_waitcnt(WAIT_STEP);
-    __builtin_amdgcn_s_barrier();
-    issue(stage((u + NS - 1) % NS));
-    if (u & 1) load(stage(u % NS), fb1); else load(stage(u % NS), fb0);
-    if (!first) {
-      if (u & 1) mma(fb0); else mma(fb1);
-      interleave();
-    }
-    advance();
-    if (since_epi > 0) ++since_epi;
-  };
-
-  for (int r = 0; r < my_tiles; ++r) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-    // K / 32 is a multiple of 2 * NS: the stage and fragment buffer of every
-    // step are compile-time constants in the unrolled body.
-#pragma unroll
-    for (int u = 0; u < 2 * NS; ++u) step(u, u == 0);
-    for (int kt = 2 * NS; kt < KT; kt += 2 * NS) {
-#pragma unroll
-      for (int u = 0; u < 2 * NS; ++u) step(u, false);
-    }
-    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
-    mma(fb1);
-
+  // Piece t of a slice = rows 8t .. 8t+7; wave q of the loading group fills
+  // pieces 8q .. 8q+7; lane -> row 8t + lane/8, LDS chunk lane%8 of the row
+  // holds global chunk (lane%8) ^ ((row/2)%8).
+  uint32_t off[8];
+  int off_tile = -1;
+  const uint32_t ldsA = (uint32_t)(uintptr_t)(lds_void*)&sA[0][0];
+  const uint32_t ldsW = (uint32_t)(uintptr_t)(lds_void*)&sW[0][0];
+  auto issue = [&](int g, bool is_a) __attribute__((always_inline)) {
+    const int r = g / KT, kt = g - r * KT;
     int tm, tn;
     tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
-    const int64_t mb = (int64_t)tm * BIG + wm * 128 + l32;
-    const int nw = tn * BIG + wn * 128;
+    const int64_t am = (int64_t)tm * BIG;
+    if (is_a) {
+      if (off_tile != r) {   // rows past M re-read row M - 1
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int t = 0; t < 8; ++t) {
+          const int rr = (q * 8 + t) * 8 + (lane >> 3);
+          const int c = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+          const int64_t row = min<int64_t>(am + rr, M - 1) - am;
+          off[t] = (uint32_t)((row * lda + c) * 2);
+        }
+        off_tile = r;
+      }
+      const char* base = reinterpret_cast<const char*>(A + am * lda) + kt * PBK * 2;
+      const uint32_t l = ldsA + (g % 3) * (SL * 16) + q * 8 * 1024;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) dma16_s(base, off[t], l + t * 1024);
+    } else {
+      if (off_tile != -2) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const int rr = (q * 8 + t) * 8 + (lane >> 3);
+          const int c = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+          off[t] = (uint32_t)((rr * ldw + c) * 2);
+        }
+        off_tile = -2;
+      }
+      const char* base =
+          reinterpret_cast<const char*>(W + (int64_t)tn * BIG * ldw) + kt * PBK * 2;
+      const uint32_t l = ldsW + (g & 1) * (SL * 16) + q * 8 * 1024;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) dma16_s(base, off[t], l + t * 1024);
+    }
+  };
+
+  const int rsw = (l32 >> 1) & 7;
+  const int aofs = (grp * 128 + l32) * 8;
+  const int wofs = (q * 64 + l32) * 8;
+
+  f32x16 acc[2][4];
+  bf16x8 f0[6], f1[6];
+  auto load = [&](const uint4* a, const uint4* w, int sl, bf16x8 (&f)[6])
+      __attribute__((always_inline)) {
+    const int pc = (2 * sl + lhi) ^ rsw;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f[i] = __builtin_bit_cast(bf16x8, w[wofs + i * 256 + pc]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[2 + j] = __builtin_bit_cast(bf16x8, a[aofs + j * 256 + pc]);
+  };
+  auto mma = [&](const bf16x8 (&f)[6], bool fresh) __attribute__((always_inline)) {
+    const f32x16 z = {};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], f[2 + j], fresh ? z : acc[i][j],
+                                                            0, 0, 0);
+  };
+  auto interleave = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 6; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+  auto compute = [&](const uint4* a, const uint4* w, bool first) __attribute__((always_inline)) {
+    load(a, w, 1, f1);
+    mma(f0, first);
+    interleave();
+    load(a, w, 2, f0);
+    mma(f1, false);
+    interleave();
+    load(a, w, 3, f1);
+    mma(f0, false);
+    interleave();
+    mma(f1, false);
+  };
+  auto epilogue = [&](int r) __attribute__((always_inline)) {
+    int tm, tn;
+    tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
+    const int64_t mb = (int64_t)tm * BIG + grp * 128 + l32;
+    const int nw = tn * BIG + q * 64;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
       float4 bv[4];
       load_bias32(bias, nw + i * 32, lhi, bv);
 #pragma unroll
@@ -322,16 +287,56 @@ __global__ __launch_bounds__(256, 1) void gemm_big_kernel(
         const int64_t m = mb + j * 32;
         if (m < M) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            store4<EPI>(Cv, ldc, m, nw + i * 32 + 8 * q + 4 * lhi, bv[q], acc[i][j][4 * q],
-                        acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          for (int qq = 0; qq < 4; ++qq)
+            store4<EPI>(Cv, ldc, m, nw + i * 32 + 8 * qq + 4 * lhi, bv[qq], acc[i][j][4 * qq],
+                        acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]);
         }
       }
     }
-    since_epi = 1;
+  };
+
+  // Prologue: A of steps 0 and 1 (group 0), W of step 0 (group 1).
+  if (total > 0) {
+    if (grp == 0) {
+      issue(0, true);
+      if (total > 1) issue(1, true);
+      wait_vm0();
+    } else {
+      issue(0, false);
+      wait_vm0();
+    }
   }
-  // Loads past the last step may still be landing in LDS: drain them before
-  // the workgroup's LDS is released.
+  wg_barrier();
+  for (int g = 0; g < total; ++g) {
+    const int r = g / KT, kt = g - r * KT;
+    const uint4* a = sA[g % 3];
+    const uint4* w = sW[g & 1];
+    // phase 1: group 0 computes, group 1 loads W(g+1)
+    if (grp == 0) {
+      load(a, w, 0, f0);
+      if (kt == 0) compute(a, w, true);
+      else compute(a, w, false);
+    } else {
+      if (g + 1 < total) issue(g + 1, false);
+      if (kt == 0 && r > 0) epilogue(r - 1);
+      load(a, w, 0, f0);
+    }
+    wg_barrier();
+    // phase 2: group 1 computes, group 0 loads A(g+2)
+    if (grp == 1) {
+      if (kt == 0) compute(a, w, true);
+      else compute(a, w, false);
+      wait_vm0();   // W(g+1) landed
+    } else {
+      // A(g+1), issued a step ago, must have landed before the barrier; wait
+      // for it first, so that no count of younger operations is needed.
+      wait_vm0();
+      if (g + 2 < total) issue(g + 2, true);
+      if (kt == KT - 1) epilogue(r);
+    }
+    wg_barrier();
+  }
+  if (grp == 1 && total > 0) epilogue(my_tiles - 1);
   __builtin_amdgcn_s_waitcnt(0);
 }
 
@@ -604,12 +609,8 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   }
   // Full rounds go to the persistent kernel, the remainder to 128 x 128 pieces.
   const int n_big = (tiles / cus) * cus;
-  if ((K / BKS) % 10 == 0)
-    gemm_big_kernel<EPI, 5><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
-                                                                 K, tiles_m, tiles_n, n_big);
-  else
-    gemm_big_kernel<EPI, 4><<<dim3(cus), dim3(256), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M,
-                                                                 K, tiles_m, tiles_n, n_big);
+  gemm_big_kernel<EPI><<<dim3(cus), dim3(512), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M, K,
+                                                            tiles_m, tiles_n, n_big);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tiles == n_big) return e;
   PieceMap pm{0, n_big, tiles_m, tiles_n, N / PIECE};
