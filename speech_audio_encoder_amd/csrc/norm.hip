@@ -97,12 +97,130 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict
 }
 
 // Workgroup: one attention tile (up to 128 positions of one clip) x one head.
-// The wavefronts normalise and rotate q and k of the tile's rows, then each
-// thread transposes an 8 x 8 block of v in registers so that every store is 8
-// consecutive keys of one dim.
+// Grid z = 0 handles q and k, z = 1 v (separate workgroups keep each path's
+// registers low).  q and k: 8 lanes per (row, head); lane j holds dims 8j..8j+7 and
+// 64+8j..64+8j+7, i.e. eight whole rotation pairs, so the rotation is local,
+// every access is a 16-byte vector and a wavefront's access covers whole
+// 128-byte lines; the statistics reduce over the 8 lanes.  v: each thread
+// transposes an 8 x 8 block in registers; the thread map puts the 8 threads
+// that share a dim block on consecutive position blocks, so every store
+// instruction writes whole 128-byte rows of vt.
 // The clip's keys occupy columns [vt_base[b], vt_base[b] + roundup(P_b, 64))
 // of vt; columns past P_b are written as zeros.
 constexpr int QK_ROWS = 128;
+
+__device__ __forceinline__ void unpack8(const uint4 u, float (&f)[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+// q and k of one tile x head: normalise, rotate, scale k (in place).
+__device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t s0, int len, int p0, int h,
+                                        int lane, int wave, const float* __restrict__ qg,
+                                        const float* __restrict__ qb, const float* __restrict__ kg,
+                                        const float* __restrict__ kb,
+                                        const float* __restrict__ rope_cos,
+                                        const float* __restrict__ rope_sin) {
+  const int sub = lane & 7;     // dims 8 sub .. + 7 and 64 + 8 sub .. + 7
+  const int grp = lane >> 3;    // row within the wavefront's 8
+  const int d0 = sub * 8;
+  float gq[2][8], bq[2][8], gk[2][8], bk[2][8];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gq[hh][e] = qg[hh * 64 + d0 + e];
+      bq[hh][e] = qb[hh * 64 + d0 + e];
+      gk[hh][e] = kg[hh * 64 + d0 + e];
+      bk[hh][e] = kb[hh * 64 + d0 + e];
+    }
+
+  // Every load is issued before the first store (rows are updated in place,
+  // so the compiler could not move a later row's loads above an earlier
+  // row's stores).  Rows past the clip re-read row p0 and are not stored.
+  constexpr int NR = QK_ROWS / 32;   // passes of 32 rows (4 wavefronts x 8)
+  uint4 uq[NR][2], uk[NR][2];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int p = p0 + i * 32 + wave * 8 + grp;
+    const int pl = p < len ? p : p0;
+    const bf16_t* base = qkv + (s0 + pl) * (3 * D) + h * DH + d0;
+    uq[i][0] = *reinterpret_cast<const uint4*>(base);
+    uq[i][1] = *reinterpret_cast<const uint4*>(base + 64);
+    uk[i][0] = *reinterpret_cast<const uint4*>(base + D);
+    uk[i][1] = *reinterpret_cast<const uint4*>(base + D + 64);
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    const int p = p0 + i * 32 + wave * 8 + grp;
+    const bool live = p < len;   // uniform over the 8 lanes of the row
+    const int pl = live ? p : p0;
+    const uint4 uq0 = uq[i][0], uq1 = uq[i][1], uk0 = uk[i][0], uk1 = uk[i][1];
+    float cs[8], sn[8];
+    {
+      const float4 c0 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * (DH / 2) + d0);
+      const float4 c1 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * (DH / 2) + d0 + 4);
+      const float4 s0v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * (DH / 2) + d0);
+      const float4 s1v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * (DH / 2) + d0 + 4);
+      cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w;
+      cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
+      sn[0] = s0v.x; sn[1] = s0v.y; sn[2] = s0v.z; sn[3] = s0v.w;
+      sn[4] = s1v.x; sn[5] = s1v.y; sn[6] = s1v.z; sn[7] = s1v.w;
+    }
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      float a[8], b[8];
+      unpack8(which ? uk0 : uq0, a);
+      unpack8(which ? uk1 : uq1, b);
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum += a[e] + b[e];
+#pragma unroll
+      for (int o = 4; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      const float mean = sum * (1.0f / DH);
+      float sq = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        a[e] -= mean;
+        b[e] -= mean;
+        sq += a[e] * a[e] + b[e] * b[e];
+      }
+#pragma unroll
+      for (int o = 4; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      const float rstd = rsqrtf(sq * (1.0f / DH) + LN_EPS);
+      // k leaves scaled by log2(e) / sqrt(128): the attention kernel's
+      // scores are then directly the exponents of exp2.
+      const float outscale = which ? K_SCORE_SCALE : 1.0f;
+      uint32_t lo[4], hi[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float y0[2], y1[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float ga = which ? gk[0][e + t] : gq[0][e + t];
+          const float gb = which ? gk[1][e + t] : gq[1][e + t];
+          const float ea = which ? bk[0][e + t] : bq[0][e + t];
+          const float eb = which ? bk[1][e + t] : bq[1][e + t];
+          const float x0 = a[e + t] * rstd * ga + ea;
+          const float x1 = b[e + t] * rstd * gb + eb;
+          y0[t] = (x0 * cs[e + t] - x1 * sn[e + t]) * outscale;
+          y1[t] = (x1 * cs[e + t] + x0 * sn[e + t]) * outscale;
+        }
+        lo[e / 2] = pack_bf16x2(y0[0], y0[1]);
+        hi[e / 2] = pack_bf16x2(y1[0], y1[1]);
+      }
+      if (live) {
+        bf16_t* base = qkv + (s0 + p) * (3 * D) + which * D + h * DH + d0;
+        *reinterpret_cast<uint4*>(base) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+        *reinterpret_cast<uint4*>(base + 64) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     bf16_t* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
@@ -119,107 +237,45 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  // q and k: 16 lanes per (row, head); lane j of a group holds dims 4j..4j+3
-  // and 64+4j..64+4j+3, i.e. four whole rotation pairs, so the rotation is
-  // local and every access is an 8-byte vector.  A wavefront does 4 rows at a
-  // time; the statistics reduce over the 16 lanes of the group.
-  const int sub = lane & 15;
-  const int grp = lane >> 4;
-  const int d0 = sub * 4;
-  const float4 gq0 = *reinterpret_cast<const float4*>(qg + d0);
-  const float4 gq1 = *reinterpret_cast<const float4*>(qg + 64 + d0);
-  const float4 bq0 = *reinterpret_cast<const float4*>(qb + d0);
-  const float4 bq1 = *reinterpret_cast<const float4*>(qb + 64 + d0);
-  const float4 gk0 = *reinterpret_cast<const float4*>(kg + d0);
-  const float4 gk1 = *reinterpret_cast<const float4*>(kg + 64 + d0);
-  const float4 bk0 = *reinterpret_cast<const float4*>(kb + d0);
-  const float4 bk1 = *reinterpret_cast<const float4*>(kb + 64 + d0);
-
-  for (int rr = wave * 4 + grp; rr < QK_ROWS; rr += 16) {
-    const int p = p0 + rr;
-    if (p >= len) continue;
-    const int64_t r = s0 + p;
-    const float4 c = *reinterpret_cast<const float4*>(rope_cos + (int64_t)p * (DH / 2) + d0);
-    const float4 sn = *reinterpret_cast<const float4*>(rope_sin + (int64_t)p * (DH / 2) + d0);
+  if (blockIdx.z == 0) {
+    qk_part(qkv, s0, len, p0, h, lane, wave, qg, qb, kg, kb, rope_cos, rope_sin);
+    return;
+  }
+  // v thread map: wavefront w covers position blocks 8 (w & 1) .. + 7 and dim
+  // blocks 8 (w >> 1) .. + 7; lane -> (position block lane % 8, dim block
+  // lane / 8).
+  const int vrb = (lane & 7) + 8 * (wave & 1);
+  const int vdb = (lane >> 3) + 8 * (wave >> 1);
+  const bool vblock = vrb * 8 < span;
+  uint4 vrows[8];
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      bf16_t* base = qkv + r * (3 * D) + which * D + h * DH;
-      const uint2 ulo = *reinterpret_cast<const uint2*>(base + d0);
-      const uint2 uhi = *reinterpret_cast<const uint2*>(base + 64 + d0);
-      float a[4] = {bf16_to_f32((bf16_t)(ulo.x & 0xFFFF)), bf16_to_f32((bf16_t)(ulo.x >> 16)),
-                    bf16_to_f32((bf16_t)(ulo.y & 0xFFFF)), bf16_to_f32((bf16_t)(ulo.y >> 16))};
-      float b[4] = {bf16_to_f32((bf16_t)(uhi.x & 0xFFFF)), bf16_to_f32((bf16_t)(uhi.x >> 16)),
-                    bf16_to_f32((bf16_t)(uhi.y & 0xFFFF)), bf16_to_f32((bf16_t)(uhi.y >> 16))};
-      float sum = (a[0] + a[1]) + (a[2] + a[3]) + (b[0] + b[1]) + (b[2] + b[3]);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-      const float mean = sum * (1.0f / DH);
-      float sq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] -= mean;
-        b[e] -= mean;
-        sq += a[e] * a[e] + b[e] * b[e];
-      }
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
-      const float rstd = rsqrtf(sq * (1.0f / DH) + LN_EPS);
-      const float4 g0 = which ? gk0 : gq0, g1 = which ? gk1 : gq1;
-      const float4 e0 = which ? bk0 : bq0, e1 = which ? bk1 : bq1;
-      const float ga[4] = {g0.x, g0.y, g0.z, g0.w}, gb[4] = {g1.x, g1.y, g1.z, g1.w};
-      const float ea[4] = {e0.x, e0.y, e0.z, e0.w}, eb[4] = {e1.x, e1.y, e1.z, e1.w};
-      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
-      // k leaves scaled by log2(e) / sqrt(128): the attention kernel's
-      // scores are then directly the exponents of exp2.
-      const float outscale = which ? K_SCORE_SCALE : 1.0f;
-      float lo[4], hi[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float y0 = a[e] * rstd * ga[e] + ea[e];
-        const float y1 = b[e] * rstd * gb[e] + eb[e];
-        lo[e] = (y0 * cc[e] - y1 * ss[e]) * outscale;
-        hi[e] = (y1 * cc[e] + y0 * ss[e]) * outscale;
-      }
-      *reinterpret_cast<uint2*>(base + d0) =
-          make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
-      *reinterpret_cast<uint2*>(base + 64 + d0) =
-          make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
-    }
+  for (int i = 0; i < 8; ++i) {
+    // Key order inside each group of 16 columns: positions 0-3, 8-11, 4-7,
+    // 12-15 of the group, so that 8 consecutive columns are the 8 keys one
+    // lane supplies to a 32x32x16 MFMA whose other operand comes from the
+    // accumulator layout of K Q^T (rows 4*(lane/32) + 8g + r).
+    const int p = p0 + 16 * (vrb >> 1) + 4 * (vrb & 1) + (i & 3) + 8 * (i >> 2);
+    vrows[i] = (vblock && p < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + p) * (3 * D) +
+                                                                      2 * D + h * DH + vdb * 8)
+                                   : make_uint4(0, 0, 0, 0);
   }
 
-  // v: each thread transposes one 8 x 8 block (8 positions x 8 dims) in
-  // registers -- output word k of column c takes half c%2 of word c/2 from
-  // rows 2k and 2k+1 (one byte permute each) -- and stores 8 keys of each of
-  // its 8 dims as 16-byte vectors.  Positions past the clip are zeros.
-  // Key order inside each group of 16 columns: positions 0-3, 8-11, 4-7,
-  // 12-15 of the group, so that 8 consecutive columns are the 8 keys one
-  // lane supplies to a 32x32x16 MFMA whose other operand comes from the
-  // accumulator layout of K Q^T (rows 4*(lane/32) + 8g + r).
-  {
-    const int rb = threadIdx.x >> 4;           // 16 blocks of 8 columns
-    const int db = threadIdx.x & 15;           // 16 blocks of 8 dims
-    if (rb * 8 < span) {
-      uint4 rows[8];
+  // v: output word k of column c takes half c%2 of word c/2 from rows 2k and
+  // 2k+1 (one byte permute each); 8 keys of each of the block's 8 dims go out
+  // as 16-byte vectors.  Positions past the clip are zeros.
+  if (vblock) {
+    bf16_t* dst = vt + ((int64_t)h * DH + vdb * 8) * ld_vt + vt_base[seq] + p0 + vrb * 8;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int p = p0 + 16 * (rb >> 1) + 4 * (rb & 1) + (i & 3) + 8 * (i >> 2);
-        rows[i] = (p < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + p) * (3 * D) + 2 * D +
-                                                               h * DH + db * 8)
-                            : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t w[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t* ra = reinterpret_cast<const uint32_t*>(&vrows[2 * k]);
+        const uint32_t* rb2 = reinterpret_cast<const uint32_t*>(&vrows[2 * k + 1]);
+        w[k] = __builtin_amdgcn_perm(rb2[c >> 1], ra[c >> 1], sel);
       }
-      bf16_t* dst = vt + ((int64_t)h * DH + db * 8) * ld_vt + vt_base[seq] + p0 + rb * 8;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t w[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t* ra = reinterpret_cast<const uint32_t*>(&rows[2 * k]);
-          const uint32_t* rb2 = reinterpret_cast<const uint32_t*>(&rows[2 * k + 1]);
-          w[k] = __builtin_amdgcn_perm(rb2[c >> 1], ra[c >> 1], sel);
-        }
-        *reinterpret_cast<uint4*>(dst + (int64_t)c * ld_vt) = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+      *reinterpret_cast<uint4*>(dst + (int64_t)c * ld_vt) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }
@@ -264,7 +320,7 @@ hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t*
                               const float* rope_cos, const float* rope_sin, bf16_t* vt,
                               int64_t ld_vt, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
-  qknorm_rope_kernel<<<dim3(n_tiles, H), dim3(256), 0, stream>>>(
+  qknorm_rope_kernel<<<dim3(n_tiles, H, 2), dim3(256), 0, stream>>>(
       qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt);
   return hipGetLastError();
 }
