@@ -9,6 +9,11 @@ the library's stream during the timed steps) and the CPU oracle timed on a
 bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                      [--attention CORE,CONTEXT]
+
+--attention encodes each clip in windows of CORE positions with CONTEXT
+positions of context on each side (500,50 are the serving windows, 375,0 the
+30-second chunks); flops then count the windows' sequences, context included.
 """
 
 import argparse
@@ -33,14 +38,26 @@ DESCRIPTIONS = {
     "tiny": "1 clip x 1.0 s tones, 2-layer encoder",
     "clip30": "1 clip x 30 s tones, 32-layer encoder",
     "batch64": "64 clips x U(5-30 s) tones (variable length, masked), 32-layer encoder",
-    "long10m": "1 clip x 600 s segment mix, 32-layer encoder, full attention",
-    "hour": "1 clip x 3600 s segment mix, 32-layer encoder, full attention",
+    "long10m": "1 clip x 600 s segment mix, 32-layer encoder",
+    "hour": "1 clip x 3600 s segment mix, 32-layer encoder",
 }
 
 
 def positions(n):
     f = 0 if n < 400 else 1 + (n - 400) // 160
     return (f + 7) // 8
+
+
+def sequences(pos, core=0, context=0):
+    """Lengths of the attention sequences the layers run on: whole clips, or
+    each clip's windows (core positions plus context on each side)."""
+    if core == 0:
+        return list(pos)
+    out = []
+    for p in pos:
+        for c0 in range(0, p, core):
+            out.append(min(p, c0 + core + context) - max(0, c0 - context))
+    return out
 
 
 def gemm_flops_per_layer(rows):
@@ -98,7 +115,7 @@ def measured_traffic(workload, kernel):
     return int(round(c["bytes_per_launch"]))
 
 
-def cpu_baseline(audio, lengths, weights, budget_s=12.0):
+def cpu_baseline(audio, lengths, weights, core=0, context=0, budget_s=12.0):
     """Time the oracle (as it stands) on whole clips until ~budget_s of CPU."""
     import oracle
     try:
@@ -111,7 +128,10 @@ def cpu_baseline(audio, lengths, weights, budget_s=12.0):
     for b in order:
         n = int(lengths[b])
         t0 = time.perf_counter()
-        oracle.encode(audio[b, :n], weights)
+        if core:
+            oracle.encode_windows(audio[b, :n], weights, core, context)
+        else:
+            oracle.encode(audio[b, :n], weights)
         spent += time.perf_counter() - t0
         done_samples += n
         clips += 1
@@ -129,6 +149,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="batch64", choices=list(DESCRIPTIONS))
+    ap.add_argument("--attention", default="full",
+                    help="'full' or CORE,CONTEXT for windowed attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every kernel class (extra untimed steps)")
@@ -136,6 +158,11 @@ def main():
                     help="only run a plain device copy of this many MiB (5 times), "
                          "to scale HBM byte counters")
     args = ap.parse_args()
+    core, context = 0, 0
+    if args.attention != "full":
+        core, context = (int(v) for v in args.attention.split(","))
+        if core < 1 or context < 0:
+            ap.error("--attention needs CORE >= 1 and CONTEXT >= 0")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the encoder batch would be split by clips across ranks, which this "
@@ -161,9 +188,11 @@ def main():
     n_layers = len(weights["layers"])
     dtype = "bf16" if workloads.WORKLOADS[args.workload][3] else "f32"
     enc = binding.Encoder(weights, dtype=dtype)
+    if core:
+        enc.set_attention(core, context)
     x = torch.from_numpy(audio).cuda()
     lengths = [int(n) for n in lengths]
-    pos = [positions(n) for n in lengths]
+    pos = sequences([positions(n) for n in lengths], core, context)
     rows = sum(pos)
     _, p_max = binding.enc_shapes(lengths)
     out = torch.empty((len(lengths), p_max, D), dtype=torch.bfloat16, device="cuda")
@@ -251,14 +280,16 @@ def main():
         "mfma_pct_of_peak": round(mfma_pct, 2),
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
                    "clips": len(lengths), "audio_seconds": round(audio_s, 3),
-                   "positions": rows, "layers": n_layers,
+                   "positions": sum(positions(n) for n in lengths), "layer_rows": rows,
+                   "layers": n_layers,
+                   "attention": "full" if not core else f"windows core={core} context={context}",
                    "algorithmic_tflop_per_step": round(total_flops / 1e12, 4)},
         "roofline": roof,
     }
     if breakdown:
         result["kernel_ms_per_step"] = breakdown
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(audio, lengths, weights)
+        result["cpu_baseline"] = cpu_baseline(audio, lengths, weights, core, context)
     enc.close()
     print(json.dumps(result), flush=True)
 

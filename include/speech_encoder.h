@@ -160,6 +160,32 @@ int enc_logmel(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t
 int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                 void* out_embeddings, hipStream_t stream);
 
+/*
+ * enc_set_attention: the attention scope of later enc_forward calls on ctx.
+ * The pages describe the encoder as trained on 30-second chunks and served
+ * with local windows (500 positions of core plus 50 of context on each side,
+ * "Local encoder windows, recording-wide language context"); this call
+ * selects between full-clip attention and such windows.
+ *   mode ENC_ATTN_FULL (default): each clip is one sequence; core and
+ *        context must be 0.
+ *   mode ENC_ATTN_WINDOWS: position p of a clip with P positions belongs to
+ *        window w = floor(p / core).  Window w is encoded as an independent
+ *        input: its sequence is positions [max(0, w*core - context),
+ *        min(P, (w+1)*core + context)) of the clip's stacked features, with
+ *        attention only inside it and rotary positions counted from its
+ *        first position; position p's embedding is the one computed in its own
+ *        window (context positions are computed and discarded).  context = 0
+ *        gives non-overlapping chunks (core = 375 is the pages' 30 seconds);
+ *        core = 500, context = 50 gives the serving windows.
+ *        Requires core >= 1, context >= 0, core + 2*context <= 45,000.
+ * The output layout is unchanged.  Windows with context duplicate the context
+ * rows, so the workspace grows by their share (enc_workspace_bytes reports
+ * the full-attention size).  Host-only; errors: ENC_ERR_ARG.
+ */
+#define ENC_ATTN_FULL 0
+#define ENC_ATTN_WINDOWS 1
+int enc_set_attention(enc_ctx* ctx, int32_t mode, int32_t core, int32_t context);
+
 /* enc_destroy: wait for the context's device work and free it.  NULL is a
  * no-op. */
 void enc_destroy(enc_ctx* ctx);
@@ -172,8 +198,8 @@ int enc_shapes(const int64_t* lengths, int32_t batch, int64_t* f_max, int64_t* p
 
 /*
  * enc_workspace_bytes: host-only.  Device bytes enc_forward's workspace needs
- * for this batch (independent of n_layers >= 1).  Errors: ENC_ERR_ARG,
- * ENC_ERR_TOO_LONG.
+ * for this batch with full-clip attention (independent of n_layers >= 1).
+ * Errors: ENC_ERR_ARG, ENC_ERR_TOO_LONG.
  */
 int enc_workspace_bytes(int32_t n_layers, const int64_t* lengths, int32_t batch, size_t* bytes);
 

@@ -28,5 +28,5 @@ from .frontend import (  # noqa: F401
 )
 from .encoder import (  # noqa: F401
     layer_norm, gelu, rope_tables, apply_rope, attention, encoder_layer,
-    encode_from_logmel, encode, encode_batch, parameter_count,
+    encode_from_logmel, encode, encode_windows, encode_batch, parameter_count,
 )

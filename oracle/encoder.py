@@ -157,6 +157,34 @@ def encode(x, weights, n_layers=None, rows=None):
     return encode_from_logmel(logmel(x), weights, n_layers, rows)
 
 
+def encode_windows(x, weights, core, context, n_layers=None):
+    """Embeddings [P, d] of one clip encoded in local attention windows.
+
+    The encoder is trained on 30-second chunks and served with local windows
+    of 500 positions plus 50 of context on either side ("Nemotron 3.5
+    Transcribe: From Recorded Speech to Dataset Audits", section "Local
+    encoder windows, recording-wide language context").  Position p belongs
+    to window w = p // core; the window's sequence is positions
+    [max(0, w core - context), min(P, (w + 1) core + context)) of the clip's
+    stacked features, encoded on its own (attention inside it, rotary
+    positions from its first position); p takes the row computed in its own
+    window.  context = 0 gives non-overlapping chunks.
+    """
+    feats = logmel(x)
+    n_frames = feats.shape[0]
+    P = position_count(n_frames)
+    d = weights["w_in"].shape[0]
+    out = np.zeros((P, d), dtype=np.float32)
+    for c0 in range(0, P, core):
+        st = max(0, c0 - context)
+        en = min(P, c0 + core + context)
+        # positions st .. en-1 stack frames 8 st .. 8 en - 1 (zeros past the clip)
+        y = encode_from_logmel(feats[8 * st:min(n_frames, 8 * en)], weights, n_layers)
+        c1 = min(P, c0 + core)
+        out[c0:c1] = y[c0 - st:c1 - st]
+    return out
+
+
 def encode_batch(audio, lengths, weights, n_layers=None):
     """[B, P(max length), d] embeddings; each clip encoded alone, rows >= P_b zero."""
     lengths = [int(n) for n in lengths]

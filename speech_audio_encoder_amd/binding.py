@@ -26,8 +26,12 @@ D_MODEL, N_MELS = 1280, 128
 KERNELS = ["frontend", "gemm_in", "layernorm", "gemm_qkv", "qknorm_rope", "attention",
            "gemm_o", "gemm_up", "gemm_down", "final_norm"]
 
-EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_destroy", "enc_shapes",
-           "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
+EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_set_attention", "enc_destroy",
+           "enc_shapes", "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel",
+           "enc_profile_read"]
+
+ENC_ATTN_FULL = 0
+ENC_ATTN_WINDOWS = 1
 
 _LAYER_FIELDS = ["ln1_g", "ln1_b", "w_qkv", "b_qkv", "q_g", "q_b", "k_g", "k_b",
                  "w_o", "b_o", "ln2_g", "ln2_b", "w_up", "b_up", "w_down", "b_down"]
@@ -69,6 +73,8 @@ def load_library(path=LIB_PATH):
                                ctypes.c_void_p, ctypes.c_void_p]
     lib.enc_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.enc_set_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32]
     lib.enc_destroy.argtypes = [ctypes.c_void_p]
     lib.enc_destroy.restype = None
     lib.enc_shapes.argtypes = [i64p, ctypes.c_int32, i64p, i64p]
@@ -197,6 +203,14 @@ def enc_forward_raw(ctx, audio_ptr, lengths, out_ptr, stream_ptr=0):
                                       ctypes.c_void_p(stream_ptr))
 
 
+def enc_set_attention(ctx, mode, core=0, context=0):
+    """Attention scope of later enc_forward calls: ENC_ATTN_FULL, or
+    ENC_ATTN_WINDOWS with `core` positions per window plus `context` on each
+    side."""
+    _check(load_library().enc_set_attention(ctypes.c_void_p(ctx), int(mode), int(core),
+                                            int(context)))
+
+
 def enc_profile_kernel(ctx, name_or_id):
     kid = KERNELS.index(name_or_id) if isinstance(name_or_id, str) else int(name_or_id)
     _check(load_library().enc_profile_kernel(ctypes.c_void_p(ctx), kid))
@@ -221,6 +235,14 @@ class Encoder:
 
     def forward(self, audio, lengths, out=None):
         return enc_forward(self.ctx, audio, lengths, out)
+
+    def set_attention(self, core=None, context=0):
+        """Full-clip attention (core None) or windows of `core` positions with
+        `context` positions of context on each side."""
+        if core is None:
+            enc_set_attention(self.ctx, ENC_ATTN_FULL, 0, 0)
+        else:
+            enc_set_attention(self.ctx, ENC_ATTN_WINDOWS, core, context)
 
     def close(self):
         if self.ctx:

@@ -77,10 +77,17 @@ hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t*
                               const float* rope_cos, const float* rope_sin, bf16_t* vt,
                               int64_t ld_vt, hipStream_t stream);
 
-// out[b, p, :] = LN_f(x[cu_seq[b] + p, :]) for p < P_b, else 0; bf16 output
-// of shape [batch, p_max, 1280].
+// out[b, p, :] = LN_f(x[s, :]) for p < P_b, else 0, with s = cu_seq[b] + p,
+// or src_rows[cu_seq[b] + p] when src_rows is not NULL; bf16 output of shape
+// [batch, p_max, 1280].
 hipError_t launch_final_norm(const float* x, const float* g, const float* b, const int32_t* cu_seq,
-                             int batch, int64_t p_max, bf16_t* out, hipStream_t stream);
+                             const int32_t* src_rows, int batch, int64_t p_max, bf16_t* out,
+                             hipStream_t stream);
+
+// dst[r, :] = src[rows[r], :] for r < n, rows of 1024 bf16 (the stacked
+// features of overlapping attention windows).
+hipError_t launch_gather_rows(const bf16_t* src, const int32_t* rows, int64_t n, bf16_t* dst,
+                              hipStream_t stream);
 
 // Element conversions used when weights are copied into the context.
 hipError_t launch_to_bf16(const void* src, bool src_is_bf16, bf16_t* dst, int64_t n,

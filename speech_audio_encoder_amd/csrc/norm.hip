@@ -74,8 +74,10 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict__ x,
                                                          const float* __restrict__ g,
                                                          const float* __restrict__ b,
-                                                         const int32_t* __restrict__ cu, int batch,
-                                                         int64_t p_max, bf16_t* __restrict__ out) {
+                                                         const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ src_rows,
+                                                         int batch, int64_t p_max,
+                                                         bf16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= (int64_t)batch * p_max) return;
@@ -88,8 +90,9 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict
       *reinterpret_cast<uint2*>(dst + (i * 64 + lane) * 4) = make_uint2(0u, 0u);
     return;
   }
+  const int64_t row = (int64_t)cu[bi] + p;
   float4 o[5];
-  ln_row_1280(x + ((int64_t)cu[bi] + p) * D, g, b, lane, o);
+  ln_row_1280(x + (src_rows ? (int64_t)src_rows[row] : row) * D, g, b, lane, o);
 #pragma unroll
   for (int i = 0; i < 5; ++i)
     *reinterpret_cast<uint2*>(dst + (i * 64 + lane) * 4) =
@@ -280,6 +283,21 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   }
 }
 
+// dst[r, :] = src[rows[r], :] for rows of 1024 bf16 (one wavefront per row,
+// 32 bytes per lane).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* __restrict__ src,
+                                                          const int32_t* __restrict__ rows,
+                                                          int64_t n, bf16_t* __restrict__ dst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const uint4* s = reinterpret_cast<const uint4*>(src + (int64_t)rows[r] * DIN) + lane * 2;
+  uint4* d = reinterpret_cast<uint4*>(dst + r * DIN) + lane * 2;
+  const uint4 a = s[0], b2 = s[1];
+  d[0] = a;
+  d[1] = b2;
+}
+
 __global__ void to_bf16_kernel(const void* __restrict__ src, int src_is_bf16,
                                bf16_t* __restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -306,11 +324,19 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, bf16
 }
 
 hipError_t launch_final_norm(const float* x, const float* g, const float* b, const int32_t* cu_seq,
+                             const int32_t* src_rows,
                              int batch, int64_t p_max, bf16_t* out, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * p_max;
   if (rows == 0) return hipSuccess;
   final_norm_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(
-      x, g, b, cu_seq, batch, p_max, out);
+      x, g, b, cu_seq, src_rows, batch, p_max, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const bf16_t* src, const int32_t* rows, int64_t n, bf16_t* dst,
+                              hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  gather_rows_kernel<<<dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream>>>(src, rows, n, dst);
   return hipGetLastError();
 }
 

@@ -102,29 +102,41 @@ bool build_frontend_tables(FrontendTables* t) {
 }
 
 // -------------------------------------------------------------- launch plan
+// Attention scope (enc_set_attention): core == 0 means whole clips.
+struct AttnScope {
+  int32_t core = 0;
+  int32_t context = 0;
+};
+
 struct Plan {
   int batch = 0;
   int64_t f_max = 0, p_max = 0;
-  int64_t rows = 0;                 // sum of P_b
+  int64_t rows = 0;                 // sum of P_b: clip rows, packed by clip
+  int64_t vrows = 0;                // rows the layers run on (> rows only if windows overlap)
   std::vector<int32_t> n_frames;    // [batch]
-  std::vector<int32_t> frame_base;  // [batch]  8 * cu_seq[b]
-  std::vector<int32_t> cu_seq;      // [batch + 1]
-  std::vector<int32_t> vt_base;     // [batch]  first V^T column of each clip
-  int64_t vt_cols = 0;              // sum of roundup(P_b, 64)
+  std::vector<int32_t> frame_base;  // [batch]  8 * cu_clip[b]
+  std::vector<int32_t> cu_clip;     // [batch + 1] first clip row of each clip
+  std::vector<int32_t> cu_seq;      // [n_seq + 1] first row of each attention sequence
+  std::vector<int32_t> vt_base;     // [n_seq]  first V^T column of each sequence
+  int64_t vt_cols = 0;              // sum of roundup(sequence length, 64)
   std::vector<int32_t> tile_seq, tile_q0;
+  // Overlapping windows only: clip row of each layer row, and layer row of
+  // each clip row's own window.
+  std::vector<int32_t> gather_src;  // [vrows]
+  std::vector<int32_t> out_src;     // [rows]
 };
 
 constexpr int ATT_QB = 128;
 
-int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles) {
+int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles,
+              const AttnScope& scope = AttnScope()) {
   if (!lengths) return fail(ENC_ERR_ARG, "lengths is NULL");
   if (batch < 1) return fail(ENC_ERR_ARG, "batch must be >= 1");
   p->batch = batch;
   p->n_frames.resize(batch);
   p->frame_base.resize(batch);
-  p->cu_seq.resize(batch + 1);
-  p->vt_base.resize(batch);
-  int64_t nmax = 0, rows = 0, vcols = 0;
+  p->cu_clip.resize(batch + 1);
+  int64_t nmax = 0, rows = 0;
   for (int b = 0; b < batch; ++b) {
     const int64_t n = lengths[b];
     if (n < 0) return fail(ENC_ERR_ARG, "lengths[" + std::to_string(b) + "] is negative");
@@ -134,25 +146,63 @@ int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles) {
     nmax = std::max(nmax, n);
     const int64_t f = frames_of(n);
     p->n_frames[b] = (int32_t)f;
-    p->cu_seq[b] = (int32_t)rows;
+    p->cu_clip[b] = (int32_t)rows;
     p->frame_base[b] = (int32_t)(rows * STACK);
-    p->vt_base[b] = (int32_t)vcols;
     rows += positions_of(f);
-    vcols += (positions_of(f) + 63) / 64 * 64;
   }
-  p->vt_cols = vcols;
-  p->cu_seq[batch] = (int32_t)rows;
+  p->cu_clip[batch] = (int32_t)rows;
   if (rows * STACK > INT32_MAX) return fail(ENC_ERR_TOO_LONG, "batch has too many frames");
   p->rows = rows;
   p->f_max = frames_of(nmax);
   p->p_max = positions_of(p->f_max);
+
+  // Attention sequences: whole clips, or each clip's windows.
+  p->cu_seq.clear();
+  p->gather_src.clear();
+  p->out_src.clear();
+  const bool overlap = scope.core > 0 && scope.context > 0;
+  if (overlap) p->out_src.assign(rows, 0);
+  int64_t vrows = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t P = p->cu_clip[b + 1] - p->cu_clip[b];
+    if (scope.core == 0) {
+      p->cu_seq.push_back(p->cu_clip[b]);
+      vrows += P;
+      continue;
+    }
+    for (int64_t c0 = 0; c0 < P; c0 += scope.core) {
+      const int64_t st = std::max<int64_t>(0, c0 - scope.context);
+      const int64_t en = std::min<int64_t>(P, c0 + scope.core + scope.context);
+      if (!overlap) {
+        p->cu_seq.push_back((int32_t)(p->cu_clip[b] + st));
+        vrows += en - st;
+        continue;
+      }
+      p->cu_seq.push_back((int32_t)vrows);
+      for (int64_t j = st; j < en; ++j) p->gather_src.push_back((int32_t)(p->cu_clip[b] + j));
+      for (int64_t j = c0; j < std::min(P, c0 + scope.core); ++j)
+        p->out_src[p->cu_clip[b] + j] = (int32_t)(vrows + j - st);
+      vrows += en - st;
+    }
+  }
+  if (vrows * 8 > INT32_MAX) return fail(ENC_ERR_TOO_LONG, "batch has too many positions");
+  p->vrows = vrows;
+  p->cu_seq.push_back((int32_t)vrows);
+  const int n_seq = (int)p->cu_seq.size() - 1;
+  p->vt_base.resize(n_seq);
+  int64_t vcols = 0;
+  for (int s = 0; s < n_seq; ++s) {
+    p->vt_base[s] = (int32_t)vcols;
+    vcols += (p->cu_seq[s + 1] - p->cu_seq[s] + 63) / 64 * 64;
+  }
+  p->vt_cols = vcols;
   p->tile_seq.clear();
   p->tile_q0.clear();
   if (with_tiles) {
-    for (int b = 0; b < batch; ++b) {
-      const int len = p->cu_seq[b + 1] - p->cu_seq[b];
+    for (int s = 0; s < n_seq; ++s) {
+      const int len = p->cu_seq[s + 1] - p->cu_seq[s];
       for (int q0 = 0; q0 < len; q0 += ATT_QB) {
-        p->tile_seq.push_back(b);
+        p->tile_seq.push_back(s);
         p->tile_q0.push_back(q0);
       }
     }
@@ -218,6 +268,7 @@ struct enc_ctx {
   bool plan_pending = false;
   hipStream_t last_stream = nullptr;
   bool has_last_stream = false;
+  AttnScope scope;          // attention scope of enc_forward (enc_set_attention)
   int prof_kernel = -1;
   std::vector<hipEvent_t> prof_events;   // pairs
   size_t prof_used = 0;
@@ -521,7 +572,7 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                 void* out_embeddings, hipStream_t stream) {
   if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
   Plan p;
-  int rc = make_plan(lengths, batch, &p, true);
+  int rc = make_plan(lengths, batch, &p, true, ctx->scope);
   if (rc != ENC_OK) return rc;
   int64_t nmax = 0;
   for (int b = 0; b < batch; ++b) nmax = std::max(nmax, lengths[b]);
@@ -531,7 +582,7 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   if (p.p_max == 0) return ENC_OK;
 
   // Memory admission before any launch.
-  const Layout lay = layout_for(p.rows, p.vt_cols);
+  const Layout lay = layout_for(p.vrows, p.vt_cols);
   if (const char* cap = std::getenv("ENC_WORKSPACE_CAP_BYTES")) {
     const unsigned long long lim = std::strtoull(cap, nullptr, 10);
     if ((unsigned long long)lay.total > lim)
@@ -566,7 +617,7 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
 
   std::vector<int32_t*> dev;
   if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.cu_seq, &p.vt_base, &p.tile_seq,
-                              &p.tile_q0},
+                              &p.tile_q0, &p.cu_clip, &p.gather_src, &p.out_src},
                         &dev, stream)) != ENC_OK)
     return rc;
   const int32_t* d_nf = dev[0];
@@ -575,11 +626,23 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   const int32_t* d_vb = dev[3];
   const int32_t* d_ts = dev[4];
   const int32_t* d_tq = dev[5];
-  const int64_t R = p.rows;
+  const int32_t* d_clip = dev[6];
+  const bool overlap = !p.gather_src.empty();
+  const int32_t* d_gather = overlap ? dev[7] : nullptr;
+  const int32_t* d_outsrc = overlap ? dev[8] : nullptr;
+  const int64_t R = p.vrows;
   const int n_tiles = (int)p.tile_seq.size();
 
-  ENC_LAUNCH(ENC_K_FRONTEND, launch_logmel_stacked(audio, nmax, d_nf, d_fb, batch, R * STACK,
-                                                   ctx->tables, stk, stream));
+  // Stacked features of the clips (packed by clip); with overlapping windows
+  // they are gathered into window order (context rows repeated) first.
+  if (overlap) {
+    ENC_LAUNCH(ENC_K_FRONTEND, launch_logmel_stacked(audio, nmax, d_nf, d_fb, batch,
+                                                     p.rows * STACK, ctx->tables, o, stream));
+    ENC_LAUNCH(ENC_K_FRONTEND, launch_gather_rows(o, d_gather, R, stk, stream));
+  } else {
+    ENC_LAUNCH(ENC_K_FRONTEND, launch_logmel_stacked(audio, nmax, d_nf, d_fb, batch, R * STACK,
+                                                     ctx->tables, stk, stream));
+  }
   ENC_LAUNCH(ENC_K_GEMM_IN, launch_gemm(Epilogue::kBiasF32, stk, DIN, ctx->w_in, DIN, ctx->b_in, x,
                                         D, R, D, DIN, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
   for (int li = 0; li < ctx->n_layers; ++li) {
@@ -601,8 +664,24 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
     ENC_LAUNCH(ENC_K_GEMM_DOWN, launch_gemm(Epilogue::kBiasResidualF32, u, FF, Lw.w_down, FF,
                                             Lw.b_down, x, D, R, D, FF, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
   }
-  ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_cu, batch, p.p_max,
-                                                 (bf16_t*)out_embeddings, stream));
+  ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_clip, d_outsrc,
+                                                 batch, p.p_max, (bf16_t*)out_embeddings, stream));
+  return ENC_OK;
+}
+
+int enc_set_attention(enc_ctx* ctx, int32_t mode, int32_t core, int32_t context) {
+  if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  if (mode == ENC_ATTN_FULL) {
+    if (core != 0 || context != 0)
+      return fail(ENC_ERR_ARG, "ENC_ATTN_FULL takes core = 0 and context = 0");
+    ctx->scope = AttnScope();
+    return ENC_OK;
+  }
+  if (mode != ENC_ATTN_WINDOWS) return fail(ENC_ERR_ARG, "unknown attention mode");
+  if (core < 1 || context < 0 || (int64_t)core + 2 * (int64_t)context > MAX_POS)
+    return fail(ENC_ERR_ARG, "windows need core >= 1, context >= 0, core + 2 context <= 45000");
+  ctx->scope.core = core;
+  ctx->scope.context = context;
   return ENC_OK;
 }
 

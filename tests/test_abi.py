@@ -88,4 +88,5 @@ def test_null_context_is_rejected(lib):
     arr = (ctypes.c_int64 * 1)(16000)
     assert lib.enc_forward(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
     assert lib.enc_logmel(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
+    assert lib.enc_set_attention(None, binding.ENC_ATTN_WINDOWS, 500, 50) == binding.ENC_ERR_ARG
     lib.enc_destroy(None)   # no-op

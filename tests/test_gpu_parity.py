@@ -345,3 +345,89 @@ def test_forward_all_clips_too_short(torch_mod, ctx_for):
     out = enc.forward(to_dev(torch, audio), lengths)
     torch.cuda.synchronize()
     assert tuple(out.shape) == (2, 0, 1280)
+
+
+# ------------------------------------------------------- attention windows
+def window_segment(audio, st, en):
+    """Samples whose frames are exactly frames 8 st .. 8 en - 1 of a clip."""
+    return audio[160 * 8 * st:min(len(audio), 160 * (8 * en - 1) + 400)]
+
+
+@pytest.mark.parametrize("core,context", [(375, 0), (500, 50), (13, 5), (200, 64)])
+def test_forward_windows_ragged(core, context, torch_mod, binding_mod):
+    # Chunks (context 0) and overlapping windows against the oracle's windowed
+    # encoder, on clips spanning several windows with ragged last windows, a
+    # clip shorter than one window, a one-position clip and an empty clip.
+    torch = torch_mod
+    w = get_weights("perturbed")
+    lengths = [1_400_000, 700_000, 33_000, 400, 0]
+    audio, lengths = workloads.custom_audio(lengths, seed=83)
+    say(f"windows core={core} context={context}")
+    enc = binding_mod.Encoder(w, dtype="f32")
+    try:
+        enc.set_attention(core, context)
+        got = run_forward(torch, enc, audio, lengths)
+    finally:
+        enc.close()
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        assert np.all(got[b, p:] == 0.0), f"clip {b}: padded rows not zero"
+        if p:
+            ref = oracle.encode_windows(audio[b, :n], w, core, context)
+            check_embeddings(got[b, :p], ref, f"windows {core}/{context} clip {b} (P={p})")
+
+
+def test_forward_windows_scope_switch(torch_mod, binding_mod):
+    # The scope is a context setting: full, windows, full again on one context
+    # (the workspace is sized for the larger, overlapping plan in between).
+    torch = torch_mod
+    w = get_weights("perturbed")
+    audio, lengths = workloads.custom_audio([300_000, 90_000], seed=85)
+    enc = binding_mod.Encoder(w, dtype="f32")
+    try:
+        full = run_forward(torch, enc, audio, lengths)
+        enc.set_attention(60, 20)
+        win = run_forward(torch, enc, audio, lengths)
+        enc.set_attention(None)
+        full2 = run_forward(torch, enc, audio, lengths)
+        with pytest.raises(binding_mod.EncoderError):
+            enc.set_attention(0, 0)
+        with pytest.raises(binding_mod.EncoderError):
+            enc.set_attention(10, -1)
+        with pytest.raises(binding_mod.EncoderError):
+            enc.set_attention(44_000, 501)
+    finally:
+        enc.close()
+    np.testing.assert_array_equal(full, full2)
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        check_embeddings(full[b, :p], oracle.encode(audio[b, :n], w), f"full clip {b}")
+        check_embeddings(win[b, :p], oracle.encode_windows(audio[b, :n], w, 60, 20),
+                         f"windows 60/20 clip {b}")
+
+
+def test_forward_hour_windows_sampled(torch_mod, binding_mod):
+    # The hour-long recording in the serving windows (500 core + 50 context)
+    # at full depth in bf16: the first, a middle and the last window against
+    # the oracle run on the window's own samples, plus final-LN moments of
+    # every row.
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("hour")
+    w = get_weights("bf16")
+    enc = binding_mod.Encoder(w, dtype="bf16")
+    try:
+        enc.set_attention(500, 50)
+        got = run_forward(torch, enc, audio, lengths)
+    finally:
+        enc.close()
+    P = 45_000
+    assert got.shape == (1, P, 1280)
+    var = got[0].var(axis=1)
+    assert np.abs(got[0].mean(axis=1)).max() < 1e-2 and np.abs(var - 1.0).max() < 2e-2
+    for c0 in (0, 22_500, 44_500):
+        st, en = max(0, c0 - 50), min(P, c0 + 550)
+        say(f"oracle hour window at {c0} (32 layers, {en - st} rows)")
+        ref = oracle.encode(window_segment(audio[0], st, en), w)
+        assert ref.shape[0] == en - st
+        check_embeddings(got[0, c0:c0 + 500], ref[c0 - st:c0 - st + 500],
+                         f"hour window {c0 // 500}")

@@ -303,3 +303,42 @@ def test_row_subset_matches_full_layer():
     rows = np.array([0, 3, 9])
     np.testing.assert_allclose(oracle.encode_from_logmel(feats, w, rows=rows), full[rows],
                                rtol=1e-5, atol=1e-5)
+
+
+# ----------------------------------------------------------------- windows
+def _segment(audio, st, en):
+    """Audio whose frames are exactly frames 8 st .. 8 en - 1 of the clip
+    (fewer at the clip's end): frame t covers samples [160 t, 160 t + 400)."""
+    s0 = 160 * 8 * st
+    s1 = 160 * (8 * en - 1) + 400
+    return audio[s0:min(len(audio), s1)]
+
+
+def test_windows_whole_clip_is_full_encoder():
+    w = small_weights(n_layers=2)
+    audio, _ = workloads.custom_audio([23_000], seed=71)
+    x = audio[0]
+    full = oracle.encode(x, w)
+    assert np.array_equal(oracle.encode_windows(x, w, core=full.shape[0], context=0), full)
+    assert np.array_equal(oracle.encode_windows(x, w, core=10 ** 6, context=7), full)
+
+
+@pytest.mark.parametrize("core,context", [(5, 0), (4, 2), (3, 5)])
+def test_windows_equal_encoder_on_audio_segments(core, context):
+    # Independent route: each window's sequence re-derived from the waveform
+    # (its samples cut out and encoded as a clip of its own), not from the
+    # clip's features.
+    w = small_weights(n_layers=2)
+    audio, _ = workloads.custom_audio([31_000], seed=73)   # 193 frames, 25 positions
+    x = audio[0]
+    P = oracle.position_count(oracle.frame_count(len(x)))
+    got = oracle.encode_windows(x, w, core, context)
+    assert got.shape == (P, w["w_in"].shape[0])
+    for c0 in range(0, P, core):
+        st, en = max(0, c0 - context), min(P, c0 + core + context)
+        ref = oracle.encode(_segment(x, st, en), w)
+        assert ref.shape[0] == en - st
+        c1 = min(P, c0 + core)
+        np.testing.assert_allclose(got[c0:c1], ref[c0 - st:c1 - st], rtol=0, atol=1e-5)
+    # windows change the result (attention scope), so a wrong scope would show
+    assert not np.allclose(got, oracle.encode(x, w), atol=1e-3)
