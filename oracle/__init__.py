@@ -30,3 +30,7 @@ from .encoder import (  # noqa: F401
     layer_norm, gelu, rope_tables, apply_rope, attention, encoder_layer,
     encode_from_logmel, encode, encode_windows, encode_batch, parameter_count,
 )
+from .fusion import (  # noqa: F401
+    speaker_kernel, speaker_indicators, speaker_features, fuse_speakers, connector,
+    encode_fused,
+)

@@ -207,3 +207,56 @@ def workload_weights(name, n_layers=None, perturb=False):
     _, _, depth, bf16 = WORKLOADS[name]
     return make_weights(depth if n_layers is None else n_layers, bf16=bf16,
                         perturb=perturb)
+
+
+# ------------------------------------------------- speaker activity, connector
+N_SPEAKERS = 8
+LLM_DIM = 2688
+
+
+def speaker_activity(n_positions, seed, max_speakers=4):
+    """Synthetic speaker-activity probabilities [n_positions, 8] float32 on the
+    80 ms grid: a conversation of 1-4 speakers in turns of 1-8 s (12-100
+    positions), with occasional overlap of a second speaker; active slots
+    draw probabilities U(0.6, 1.0), inactive ones U(0.0, 0.4), and a few
+    positions sit near the 0.5 threshold (U(0.45, 0.55))."""
+    rng = np.random.default_rng((seed, 9))
+    act = rng.uniform(0.0, 0.4, (n_positions, N_SPEAKERS)).astype(np.float32)
+    n_spk = int(rng.integers(1, max_speakers + 1))
+    slots = rng.choice(N_SPEAKERS, n_spk, replace=False)
+    p = 0
+    while p < n_positions:
+        turn = int(rng.integers(12, 101))
+        who = int(rng.choice(slots))
+        end = min(n_positions, p + turn)
+        act[p:end, who] = rng.uniform(0.6, 1.0, end - p)
+        if n_spk > 1 and rng.uniform() < 0.3:
+            other = int(rng.choice([s for s in slots if s != who]))
+            o0 = int(rng.integers(p, end))
+            act[o0:end, other] = rng.uniform(0.6, 1.0, end - o0)
+        p = end
+    near = rng.uniform(size=n_positions) < 0.02
+    act[near] = rng.uniform(0.45, 0.55, (int(near.sum()), N_SPEAKERS))
+    return act
+
+
+def make_connector_weights(bf16=True, perturb=False, d=D_MODEL, out_dim=LLM_DIM,
+                           seed=WEIGHT_SEED):
+    """Random-init speaker LayerNorm (gain 1, bias 0; N(1, 0.1^2) and
+    N(0, 0.1^2) draws with perturb) and connector (N(0, 0.02^2) weights,
+    zero or N(0, 0.1^2) bias), speaker-kernel scale 1."""
+    def rng(tid):
+        return np.random.default_rng((seed, 1000, tid))
+    g = np.ones(N_SPEAKERS, np.float32)
+    b = np.zeros(N_SPEAKERS, np.float32)
+    bc = np.zeros(out_dim, np.float32)
+    if perturb:
+        g = (1.0 + 0.1 * rng(0).standard_normal(N_SPEAKERS)).astype(np.float32)
+        b = (0.1 * rng(1).standard_normal(N_SPEAKERS)).astype(np.float32)
+        bc = (0.1 * rng(3).standard_normal(out_dim)).astype(np.float32)
+    w = (WEIGHT_STD * rng(2).standard_normal((out_dim, d))).astype(np.float32)
+    cw = {"spk_ln_g": g, "spk_ln_b": b, "w_conn": w, "b_conn": bc, "speaker_scale": 1.0}
+    if bf16:
+        for k in ("spk_ln_g", "spk_ln_b", "w_conn", "b_conn"):
+            cw[k] = round_bf16(cw[k])
+    return cw
