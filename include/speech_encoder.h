@@ -186,6 +186,65 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
 #define ENC_ATTN_WINDOWS 1
 int enc_set_attention(enc_ctx* ctx, int32_t mode, int32_t core, int32_t context);
 
+/*
+ * Speaker fusion and identity connector.  The page's section "How audio and
+ * speakers reach the language model" adds speaker activity to the ASR
+ * states before the language model: activity of up to eight speaker slots,
+ * aligned to the encoder's 80 ms grid, is thresholded at 0.5, normalised by a
+ * learned LayerNorm over the slots and mapped to width 1,280 by a fixed
+ * sinusoidal speaker kernel (saved scale 1); the sum keeps the positions and
+ * the width.  One learned linear map (no temporal downsampling) then takes
+ * the fused states to the language model's width (2,688 in the section "What
+ * the 52 backbone blocks actually do").  The formulas did not survive the
+ * page's extraction; this library reads them as:
+ *   b    = [a > 0.5] per slot (a = activity probability, fp32 compare)
+ *   n    = LayerNorm(b) over the 8 slots (biased variance, eps 1e-5, gain, bias)
+ *   K    = scale * [sin(s w_i), cos(s w_i)] interleaved over columns 2i, 2i+1,
+ *          s = slot index 0..7, w_i = 10000^(-2i/1280) (the sinusoid table of
+ *          the original Transformer with the slot index as position)
+ *   fused = H + n K,   z = fused W_c^T + b_c
+ * with H the encoder output (final LayerNorm included).
+ */
+#define ENC_SPEAKERS 8
+#define ENC_LLM_DIM 2688
+
+typedef struct enc_connector_weights {
+  int32_t abi_version;    /* must be ENC_ABI_VERSION                          */
+  int32_t dtype;          /* ENC_F32 or ENC_BF16, for every tensor            */
+  int32_t out_dim;        /* language-model width: a multiple of 128, 128..65536 */
+  float speaker_scale;    /* scale of the fixed speaker kernel (1 in the release) */
+  const void* spk_ln_g;   /* DEVICE [8]            speaker LayerNorm gain      */
+  const void* spk_ln_b;   /* DEVICE [8]            and bias                    */
+  const void* w_conn;     /* DEVICE [out_dim, 1280] connector weight          */
+  const void* b_conn;     /* DEVICE [out_dim]       connector bias            */
+} enc_connector_weights;
+
+/*
+ * enc_set_connector: copy speaker-fusion and connector weights into ctx
+ * (w_conn to bf16, the rest to fp32; the kernel table is built on the host in
+ * float64 and rounded once to fp32), replacing any earlier set.  Synchronous.
+ * Errors: ENC_ERR_ARG (NULL, wrong abi_version, unknown dtype, bad out_dim,
+ * non-finite scale), ENC_ERR_NOMEM, ENC_ERR_HIP.
+ */
+int enc_set_connector(enc_ctx* ctx, const enc_connector_weights* w);
+
+/*
+ * enc_forward_fused: waveform and speaker activity to language-model input
+ * rows: the encoder as in enc_forward (same attention scope), then speaker
+ * fusion and the connector.
+ *   audio, lengths  as for enc_logmel.
+ *   activity  DEVICE fp32 [R, 8], R = sum_b P_b: the rows of clip b are
+ *             R_b = sum_{b' < b} P_b' .. R_b + P_b - 1 (clips packed in order,
+ *             no padding), row R_b + p holds the activity of the 8 slots at
+ *             position p (80 ms grid).
+ *   out       DEVICE bf16 [R, out_dim], packed the same way.
+ * Requires an earlier enc_set_connector.  Errors: as enc_forward, and
+ * ENC_ERR_ARG when no connector is set or activity/out is NULL with R > 0.
+ * R = 0 (every clip shorter than 400 samples) writes nothing.
+ */
+int enc_forward_fused(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                      const float* activity, void* out, hipStream_t stream);
+
 /* enc_destroy: wait for the context's device work and free it.  NULL is a
  * no-op. */
 void enc_destroy(enc_ctx* ctx);
@@ -208,7 +267,7 @@ const char* enc_last_error(void);
 
 /*
  * Kernel timing for measurement.  enc_profile_kernel(ctx, id) brackets every
- * launch of kernel class id (ENC_K_*) made by later enc_forward calls with a
+ * launch of kernel class id (ENC_K_*) made by later enc_forward(_fused) calls with a
  * pair of HIP events on the call's stream; id = -1 turns this off.
  * enc_profile_read(ctx, &launches, &total_ms) waits for those events and
  * returns the number of bracketed launches and their summed duration, then
@@ -224,7 +283,9 @@ const char* enc_last_error(void);
 #define ENC_K_GEMM_UP 7
 #define ENC_K_GEMM_DOWN 8
 #define ENC_K_FINAL_NORM 9
-#define ENC_K_COUNT 10
+#define ENC_K_SPEAKER_FUSE 10   /* enc_forward_fused: final norm + speaker fusion */
+#define ENC_K_CONNECTOR 11      /* enc_forward_fused: connector GEMM              */
+#define ENC_K_COUNT 12
 int enc_profile_kernel(enc_ctx* ctx, int32_t kernel_id);
 int enc_profile_read(enc_ctx* ctx, int64_t* launches, double* total_ms);
 

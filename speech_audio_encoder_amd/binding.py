@@ -24,11 +24,11 @@ ENC_ABI_VERSION = 1
 D_MODEL, N_MELS = 1280, 128
 
 KERNELS = ["frontend", "gemm_in", "layernorm", "gemm_qkv", "qknorm_rope", "attention",
-           "gemm_o", "gemm_up", "gemm_down", "final_norm"]
+           "gemm_o", "gemm_up", "gemm_down", "final_norm", "speaker_fuse", "connector"]
 
-EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_set_attention", "enc_destroy",
-           "enc_shapes", "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel",
-           "enc_profile_read"]
+EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_set_attention", "enc_set_connector",
+           "enc_forward_fused", "enc_destroy", "enc_shapes", "enc_workspace_bytes",
+           "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
 
 ENC_ATTN_FULL = 0
 ENC_ATTN_WINDOWS = 1
@@ -47,6 +47,13 @@ class EncWeights(ctypes.Structure):
                 ("w_in", ctypes.c_void_p), ("b_in", ctypes.c_void_p),
                 ("layers", ctypes.POINTER(EncLayerWeights)),
                 ("lnf_g", ctypes.c_void_p), ("lnf_b", ctypes.c_void_p)]
+
+
+class EncConnectorWeights(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("out_dim", ctypes.c_int32), ("speaker_scale", ctypes.c_float),
+                ("spk_ln_g", ctypes.c_void_p), ("spk_ln_b", ctypes.c_void_p),
+                ("w_conn", ctypes.c_void_p), ("b_conn", ctypes.c_void_p)]
 
 
 class EncoderError(RuntimeError):
@@ -75,6 +82,9 @@ def load_library(path=LIB_PATH):
                                 ctypes.c_void_p, ctypes.c_void_p]
     lib.enc_set_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32]
+    lib.enc_set_connector.argtypes = [ctypes.c_void_p, ctypes.POINTER(EncConnectorWeights)]
+    lib.enc_forward_fused.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.enc_destroy.argtypes = [ctypes.c_void_p]
     lib.enc_destroy.restype = None
     lib.enc_shapes.argtypes = [i64p, ctypes.c_int32, i64p, i64p]
@@ -195,6 +205,60 @@ def enc_forward(ctx, audio, lengths, out=None, stream=None):
     return out
 
 
+def packed_rows(lengths):
+    """Rows of the clip-packed layout: sum over clips of ceil(F_b / 8)."""
+    total = 0
+    for n in lengths:
+        n = int(n)
+        f = 0 if n < 400 else 1 + (n - 400) // 160
+        total += (f + 7) // 8
+    return total
+
+
+def enc_set_connector(ctx, cw, dtype="bf16", device="cuda"):
+    """Speaker-fusion and connector weights from a dict with spk_ln_g [8],
+    spk_ln_b [8], w_conn [out_dim, 1280], b_conn [out_dim] and optionally
+    speaker_scale (default 1)."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    keep = []
+
+    def dev(a):
+        t = torch.as_tensor(np.asarray(a, dtype=np.float32)) if not torch.is_tensor(a) else a
+        t = t.to(device=device, dtype=tdt).contiguous()
+        keep.append(t)
+        return ctypes.c_void_p(t.data_ptr())
+
+    w = EncConnectorWeights(abi_version=ENC_ABI_VERSION,
+                            dtype=ENC_BF16 if dtype == "bf16" else ENC_F32,
+                            out_dim=int(np.shape(cw["w_conn"])[0]),
+                            speaker_scale=float(cw.get("speaker_scale", 1.0)),
+                            spk_ln_g=dev(cw["spk_ln_g"]), spk_ln_b=dev(cw["spk_ln_b"]),
+                            w_conn=dev(cw["w_conn"]), b_conn=dev(cw["b_conn"]))
+    torch.cuda.synchronize()
+    _check(load_library().enc_set_connector(ctypes.c_void_p(ctx), ctypes.byref(w)))
+    del keep
+    return w.out_dim
+
+
+def enc_forward_fused(ctx, audio, lengths, activity, out_dim, out=None, stream=None):
+    """Language-model input rows: audio cuda fp32 [B, N_max] and activity cuda
+    fp32 [R, 8] (clips packed) -> bf16 [R, out_dim], R = packed_rows(lengths)."""
+    import torch
+    arr, ptr = _lengths_array(lengths)
+    rows = packed_rows(arr)
+    if tuple(activity.shape) != (rows, 8) or activity.dtype != torch.float32 \
+            or not activity.is_contiguous():
+        raise ValueError(f"activity must be contiguous float32 [{rows}, 8]")
+    if out is None:
+        out = torch.empty((rows, out_dim), dtype=torch.bfloat16, device=audio.device)
+    _check(load_library().enc_forward_fused(
+        ctypes.c_void_p(ctx), ctypes.c_void_p(audio.data_ptr()), ptr, len(arr),
+        ctypes.c_void_p(activity.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        _stream_handle(stream)))
+    return out
+
+
 def enc_forward_raw(ctx, audio_ptr, lengths, out_ptr, stream_ptr=0):
     """enc_forward with raw pointers; returns the status code (tests)."""
     arr, ptr = _lengths_array(lengths)
@@ -235,6 +299,12 @@ class Encoder:
 
     def forward(self, audio, lengths, out=None):
         return enc_forward(self.ctx, audio, lengths, out)
+
+    def set_connector(self, cw, dtype="bf16"):
+        self.out_dim = enc_set_connector(self.ctx, cw, dtype=dtype)
+
+    def forward_fused(self, audio, lengths, activity, out=None):
+        return enc_forward_fused(self.ctx, audio, lengths, activity, self.out_dim, out)
 
     def set_attention(self, core=None, context=0):
         """Full-clip attention (core None) or windows of `core` positions with

@@ -22,6 +22,7 @@ constexpr int NFFT = 512;
 constexpr int NBIN = 257;
 constexpr int64_t MAX_SAMPLES = 57600000;   // one hour at 16 kHz
 constexpr int MAX_POS = 45000;              // positions of a one-hour clip
+constexpr int NSPK = 8;                     // speaker slots of the activity input
 // Scale applied to k after QK-norm and rotation: log2(e) / sqrt(head dim),
 // so that q . k is the softmax exponent in base 2.
 constexpr float K_SCORE_SCALE = 0.12751743082459868f;

@@ -618,13 +618,9 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
                             4 * (tiles - n_big), 4 * (tiles - n_big), cus, stream);
 }
 
-}  // namespace
-
-hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
+hipError_t launch_cols(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                        float* part, size_t part_bytes, hipStream_t stream) {
-  if (M == 0) return hipSuccess;
-  if (N % BIG != 0 || K % (BKS * 8) != 0) return hipErrorInvalidValue;
   switch (epi) {
     case Epilogue::kBiasBf16:
       return launch_t<Epilogue::kBiasBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes,
@@ -640,6 +636,26 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t*
                                           stream);
   }
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
+                       const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
+                       float* part, size_t part_bytes, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  if (N <= 0 || N % PIECE != 0 || K % (BKS * 8) != 0) return hipErrorInvalidValue;
+  // Whole 256-column tiles first; a last strip of 128 columns (N % 256 == 128)
+  // is a product of its own on the piece kernel.
+  const int n_main = N / BIG * BIG;
+  hipError_t e = hipSuccess;
+  if (n_main > 0) e = launch_cols(epi, A, lda, W, ldw, bias, C, ldc, M, n_main, K, part, part_bytes,
+                                  stream);
+  if (e != hipSuccess || n_main == N) return e;
+  const size_t c_elem = (epi == Epilogue::kBiasBf16 || epi == Epilogue::kBiasGeluBf16) ? 2 : 4;
+  return launch_cols(epi, A, lda, W + (int64_t)n_main * ldw, ldw, bias + n_main,
+                     (char*)C + (size_t)n_main * c_elem, ldc, M, N - n_main, K, part, part_bytes,
+                     stream);
 }
 
 }  // namespace enc

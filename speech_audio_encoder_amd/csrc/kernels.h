@@ -43,7 +43,7 @@ hipError_t launch_logmel_stacked(const float* audio, int64_t audio_stride, const
 
 // -------------------------------------------------------------------- GEMM
 // C[M, N] (op)= A[M, K] * W[N, K]^T + bias[N]; A, W bf16 row-major
-// (K contiguous), fp32 accumulation.  N % 256 == 0, K % 256 == 0.
+// (K contiguous), fp32 accumulation.  N % 128 == 0, K % 256 == 0.
 // `part` is scratch for split-K partial sums (GEMM_PARTIAL_BYTES suffices);
 // calls on one stream may share it.
 enum class Epilogue {
@@ -83,6 +83,15 @@ hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t*
 hipError_t launch_final_norm(const float* x, const float* g, const float* b, const int32_t* cu_seq,
                              const int32_t* src_rows, int batch, int64_t p_max, bf16_t* out,
                              hipStream_t stream);
+
+// Speaker fusion into the connector's operand: out[r, :] (bf16, [rows, 1280])
+// = LN_f(x[s, :]) + sum_j n_j spk_tab[j, :] with s = src_rows ? src_rows[r] : r
+// and n = LN_spk(act[r, :] > 0.5) over the NSPK slots (act fp32 [rows, NSPK],
+// spk_tab fp32 [NSPK, 1280]).
+hipError_t launch_speaker_fuse(const float* x, const float* g, const float* b,
+                               const int32_t* src_rows, int64_t rows, const float* act,
+                               const float* spk_g, const float* spk_b, const float* spk_tab,
+                               bf16_t* out, hipStream_t stream);
 
 // dst[r, :] = src[rows[r], :] for r < n, rows of 1024 bf16 (the stacked
 // features of overlapping attention windows).

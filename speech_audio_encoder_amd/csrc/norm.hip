@@ -298,6 +298,66 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const bf16_t* __restri
   d[1] = b2;
 }
 
+// Speaker-activity fusion, section "How audio and speakers reach the language
+// model": the activity of the 8 speaker slots is thresholded at 0.5 (1 where
+// > 0.5), normalised by a LayerNorm over the slots, mapped to width 1280 by a
+// fixed sinusoidal table and added to the encoder states.  Row r of the
+// clip-packed output: y = LN_f(x[s]) + sum_j n_j tab[j], n = LN_spk(act[r] > 0.5),
+// s = src_rows ? src_rows[r] : r; bf16 output (the connector GEMM's operand).
+// The 8 x 1280 table is staged in LDS once per workgroup of FUSE_ROWS rows;
+// each lane then reads its own 20 columns of the 8 rows as 16-byte vectors.
+constexpr int FUSE_ROWS = 32;
+
+__global__ __launch_bounds__(256) void speaker_fuse_kernel(
+    const float* __restrict__ x, const float* __restrict__ g, const float* __restrict__ b,
+    const int32_t* __restrict__ src_rows, int64_t rows, const float* __restrict__ act,
+    const float* __restrict__ sg, const float* __restrict__ sb, const float* __restrict__ tab,
+    bf16_t* __restrict__ out) {
+  __shared__ float4 stab[NSPK * D / 4];
+  for (int i = threadIdx.x; i < NSPK * D / 4; i += 256)
+    stab[i] = reinterpret_cast<const float4*>(tab)[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int k = 0; k < FUSE_ROWS / 4; ++k) {
+    const int64_t r = (int64_t)blockIdx.x * FUSE_ROWS + k * 4 + wave;
+    if (r >= rows) break;
+    float4 o[5];
+    ln_row_1280(x + (src_rows ? (int64_t)src_rows[r] : r) * D, g, b, lane, o);
+    const float4 a0 = *reinterpret_cast<const float4*>(act + r * NSPK);
+    const float4 a1 = *reinterpret_cast<const float4*>(act + r * NSPK + 4);
+    float n[NSPK] = {a0.x > 0.5f ? 1.f : 0.f, a0.y > 0.5f ? 1.f : 0.f, a0.z > 0.5f ? 1.f : 0.f,
+                     a0.w > 0.5f ? 1.f : 0.f, a1.x > 0.5f ? 1.f : 0.f, a1.y > 0.5f ? 1.f : 0.f,
+                     a1.z > 0.5f ? 1.f : 0.f, a1.w > 0.5f ? 1.f : 0.f};
+    float mean = 0.f;
+#pragma unroll
+    for (int j = 0; j < NSPK; ++j) mean += n[j];
+    mean *= 1.0f / NSPK;
+    float var = 0.f;
+#pragma unroll
+    for (int j = 0; j < NSPK; ++j) {
+      n[j] -= mean;
+      var += n[j] * n[j];
+    }
+    const float rstd = rsqrtf(var * (1.0f / NSPK) + LN_EPS);
+#pragma unroll
+    for (int j = 0; j < NSPK; ++j) n[j] = n[j] * rstd * sg[j] + sb[j];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+#pragma unroll
+      for (int j = 0; j < NSPK; ++j) {
+        const float4 t = stab[j * (D / 4) + i * 64 + lane];
+        o[i].x = fmaf(n[j], t.x, o[i].x);
+        o[i].y = fmaf(n[j], t.y, o[i].y);
+        o[i].z = fmaf(n[j], t.z, o[i].z);
+        o[i].w = fmaf(n[j], t.w, o[i].w);
+      }
+      *reinterpret_cast<uint2*>(out + r * D + (i * 64 + lane) * 4) =
+          make_uint2(pack_bf16x2(o[i].x, o[i].y), pack_bf16x2(o[i].z, o[i].w));
+    }
+  }
+}
+
 __global__ void to_bf16_kernel(const void* __restrict__ src, int src_is_bf16,
                                bf16_t* __restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -330,6 +390,16 @@ hipError_t launch_final_norm(const float* x, const float* g, const float* b, con
   if (rows == 0) return hipSuccess;
   final_norm_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(
       x, g, b, cu_seq, src_rows, batch, p_max, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_speaker_fuse(const float* x, const float* g, const float* b,
+                               const int32_t* src_rows, int64_t rows, const float* act,
+                               const float* spk_g, const float* spk_b, const float* spk_tab,
+                               bf16_t* out, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  speaker_fuse_kernel<<<dim3((unsigned)((rows + FUSE_ROWS - 1) / FUSE_ROWS)), dim3(256), 0,
+                        stream>>>(x, g, b, src_rows, rows, act, spk_g, spk_b, spk_tab, out);
   return hipGetLastError();
 }
 

@@ -269,6 +269,11 @@ struct enc_ctx {
   hipStream_t last_stream = nullptr;
   bool has_last_stream = false;
   AttnScope scope;          // attention scope of enc_forward (enc_set_attention)
+  // Speaker fusion + connector (enc_set_connector); conn_dim == 0 if unset.
+  void* conn_mem = nullptr;
+  bf16_t* w_conn = nullptr;
+  float *b_conn = nullptr, *spk_g = nullptr, *spk_b = nullptr, *spk_tab = nullptr;
+  int conn_dim = 0;
   int prof_kernel = -1;
   std::vector<hipEvent_t> prof_events;   // pairs
   size_t prof_used = 0;
@@ -287,6 +292,7 @@ void release(enc_ctx* c) {
   (void)hipFree(c->gemm_part);
   (void)hipFree(c->ws);
   (void)hipFree(c->plan_dev);
+  (void)hipFree(c->conn_mem);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
   if (c->plan_copied) (void)hipEventDestroy(c->plan_copied);
   for (hipEvent_t e : c->prof_events) (void)hipEventDestroy(e);
@@ -568,8 +574,13 @@ int enc_logmel(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t
   return ENC_OK;
 }
 
-int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
-                void* out_embeddings, hipStream_t stream) {
+namespace {
+
+// The encoder on a batch, then either the final norm into the padded
+// embedding layout (fused == false) or speaker fusion and the connector into
+// clip-packed language-model rows (fused == true).
+int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                void* out, const float* activity, bool fused, hipStream_t stream) {
   if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
   Plan p;
   int rc = make_plan(lengths, batch, &p, true, ctx->scope);
@@ -577,7 +588,13 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   int64_t nmax = 0;
   for (int b = 0; b < batch; ++b) nmax = std::max(nmax, lengths[b]);
   if (nmax > 0 && !audio) return fail(ENC_ERR_ARG, "audio is NULL");
-  if (p.p_max > 0 && !out_embeddings) return fail(ENC_ERR_ARG, "out_embeddings is NULL");
+  if (fused) {
+    if (ctx->conn_dim == 0) return fail(ENC_ERR_ARG, "no connector weights (enc_set_connector)");
+    if (p.rows > 0 && !activity) return fail(ENC_ERR_ARG, "activity is NULL");
+    if (p.rows > 0 && !out) return fail(ENC_ERR_ARG, "out is NULL");
+  } else if (p.p_max > 0 && !out) {
+    return fail(ENC_ERR_ARG, "out_embeddings is NULL");
+  }
   if ((rc = check_device(ctx)) != ENC_OK) return rc;
   if (p.p_max == 0) return ENC_OK;
 
@@ -664,8 +681,92 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
     ENC_LAUNCH(ENC_K_GEMM_DOWN, launch_gemm(Epilogue::kBiasResidualF32, u, FF, Lw.w_down, FF,
                                             Lw.b_down, x, D, R, D, FF, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
   }
-  ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_clip, d_outsrc,
-                                                 batch, p.p_max, (bf16_t*)out_embeddings, stream));
+  if (!fused) {
+    ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_clip, d_outsrc,
+                                                   batch, p.p_max, (bf16_t*)out, stream));
+    return ENC_OK;
+  }
+  // Fused states (bf16, clip-packed) go where the LayerNorm output lived.
+  ENC_LAUNCH(ENC_K_SPEAKER_FUSE,
+             launch_speaker_fuse(x, ctx->lnf_g, ctx->lnf_b, d_outsrc, p.rows, activity, ctx->spk_g,
+                                 ctx->spk_b, ctx->spk_tab, a, stream));
+  ENC_LAUNCH(ENC_K_CONNECTOR,
+             launch_gemm(Epilogue::kBiasBf16, a, D, ctx->w_conn, D, ctx->b_conn, out,
+                         ctx->conn_dim, p.rows, ctx->conn_dim, D, ctx->gemm_part,
+                         GEMM_PARTIAL_BYTES, stream));
+  return ENC_OK;
+}
+
+}  // namespace
+
+int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                void* out_embeddings, hipStream_t stream) {
+  return run_forward(ctx, audio, lengths, batch, out_embeddings, nullptr, false, stream);
+}
+
+int enc_forward_fused(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                      const float* activity, void* out, hipStream_t stream) {
+  return run_forward(ctx, audio, lengths, batch, out, activity, true, stream);
+}
+
+int enc_set_connector(enc_ctx* ctx, const enc_connector_weights* w) {
+  if (!ctx || !w) return fail(ENC_ERR_ARG, "NULL argument");
+  if (w->abi_version != ENC_ABI_VERSION)
+    return fail(ENC_ERR_ARG, "abi_version " + std::to_string(w->abi_version) + " != " +
+                                 std::to_string(ENC_ABI_VERSION));
+  if (w->dtype != ENC_F32 && w->dtype != ENC_BF16) return fail(ENC_ERR_ARG, "unknown dtype");
+  if (w->out_dim < 128 || w->out_dim > 65536 || w->out_dim % 128 != 0)
+    return fail(ENC_ERR_ARG, "out_dim must be a multiple of 128 in [128, 65536]");
+  if (!std::isfinite(w->speaker_scale)) return fail(ENC_ERR_ARG, "speaker_scale is not finite");
+  if (!w->spk_ln_g || !w->spk_ln_b || !w->w_conn || !w->b_conn)
+    return fail(ENC_ERR_ARG, "NULL weight tensor");
+  int rc = check_device(ctx);
+  if (rc != ENC_OK) return rc;
+  hipError_t e = hipDeviceSynchronize();   // the old set may still be in use
+  if (e != hipSuccess) return hip_fail(e, "device synchronize");
+  (void)hipFree(ctx->conn_mem);
+  ctx->conn_mem = nullptr;
+  ctx->conn_dim = 0;
+  const size_t n_w = (size_t)w->out_dim * D;
+  const size_t n_v = (size_t)w->out_dim + 2 * NSPK + (size_t)NSPK * D;
+  const size_t w_bytes = align_up(n_w * 2, 256);
+  void* mem = nullptr;
+  if (hipMalloc(&mem, w_bytes + n_v * 4) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ENC_ERR_NOMEM, "connector weight allocation failed");
+  }
+  bf16_t* wc = (bf16_t*)mem;
+  float* v = (float*)((char*)mem + w_bytes);
+  float* tab = v;                       // [NSPK, D], 16-byte aligned
+  float* bc = tab + (size_t)NSPK * D;
+  float* sg = bc + w->out_dim;
+  float* sb = sg + NSPK;
+  const bool bf = w->dtype == ENC_BF16;
+  // Fixed speaker kernel: slot s, columns 2i / 2i+1 = sin / cos(s * 10000^(-2i/D)).
+  std::vector<float> host_tab((size_t)NSPK * D);
+  for (int sl = 0; sl < NSPK; ++sl)
+    for (int i = 0; i < D / 2; ++i) {
+      const double ang = (double)sl * std::pow(10000.0, -2.0 * i / D);
+      host_tab[(size_t)sl * D + 2 * i] = (float)(w->speaker_scale * std::sin(ang));
+      host_tab[(size_t)sl * D + 2 * i + 1] = (float)(w->speaker_scale * std::cos(ang));
+    }
+  if ((e = launch_to_bf16(w->w_conn, bf, wc, (int64_t)n_w, nullptr)) != hipSuccess ||
+      (e = launch_to_f32(w->b_conn, bf, bc, w->out_dim, nullptr)) != hipSuccess ||
+      (e = launch_to_f32(w->spk_ln_g, bf, sg, NSPK, nullptr)) != hipSuccess ||
+      (e = launch_to_f32(w->spk_ln_b, bf, sb, NSPK, nullptr)) != hipSuccess ||
+      (e = hipMemcpy(tab, host_tab.data(), host_tab.size() * 4, hipMemcpyHostToDevice)) !=
+          hipSuccess ||
+      (e = hipDeviceSynchronize()) != hipSuccess) {
+    (void)hipFree(mem);
+    return hip_fail(e, "connector weight copy");
+  }
+  ctx->conn_mem = mem;
+  ctx->w_conn = wc;
+  ctx->b_conn = bc;
+  ctx->spk_g = sg;
+  ctx->spk_b = sb;
+  ctx->spk_tab = tab;
+  ctx->conn_dim = w->out_dim;
   return ENC_OK;
 }
 

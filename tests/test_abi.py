@@ -89,4 +89,11 @@ def test_null_context_is_rejected(lib):
     assert lib.enc_forward(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
     assert lib.enc_logmel(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
     assert lib.enc_set_attention(None, binding.ENC_ATTN_WINDOWS, 500, 50) == binding.ENC_ERR_ARG
+    assert lib.enc_set_connector(None, None) == binding.ENC_ERR_ARG
+    assert lib.enc_forward_fused(None, None, arr, 1, None, None, None) == binding.ENC_ERR_ARG
     lib.enc_destroy(None)   # no-op
+
+
+def test_packed_rows_closed_form():
+    assert binding.packed_rows([0, 399, 400, 559, 560, 1680, 57_600_000]) == \
+        0 + 0 + 1 + 1 + 1 + 2 + 45_000

@@ -431,3 +431,122 @@ def test_forward_hour_windows_sampled(torch_mod, binding_mod):
         assert ref.shape[0] == en - st
         check_embeddings(got[0, c0:c0 + 500], ref[c0 - st:c0 - st + 500],
                          f"hour window {c0 // 500}")
+
+
+# ------------------------------------------- speaker fusion and connector
+_CONN = {}
+
+
+def get_connector(kind):
+    if kind not in _CONN:
+        if kind == "bf16":
+            _CONN[kind] = workloads.make_connector_weights(bf16=True)
+        else:
+            _CONN[kind] = workloads.make_connector_weights(bf16=False, perturb=True)
+    return _CONN[kind]
+
+
+def clip_activity(lengths, seed):
+    """Per-clip synthetic activity, packed by clip, plus exact-threshold rows."""
+    acts = []
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        a = workloads.speaker_activity(p, seed=seed + b)
+        if p > 3:
+            a[1] = 0.5                                   # exactly at the threshold: off
+            a[2] = np.nextafter(np.float32(0.5), np.float32(1))   # just above: on
+        acts.append(a)
+    return acts
+
+
+def run_fused(torch, enc, audio, lengths, acts):
+    rows = sum(a.shape[0] for a in acts)
+    act = torch.from_numpy(np.concatenate(acts) if rows else np.zeros((0, 8), np.float32)).cuda()
+    out = torch.full((rows, enc.out_dim), float("nan"), dtype=torch.bfloat16, device="cuda")
+    enc.forward_fused(to_dev(torch, audio), lengths, act.contiguous(), out=out)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("windows", [None, (500, 50), (375, 0)])
+def test_forward_fused_ragged(windows, torch_mod, binding_mod):
+    # Encoder + speaker fusion + connector (N = 2688: ten 256-wide tiles and a
+    # 128-wide strip) on a ragged batch with perturbed weights, against the
+    # oracle per clip; clips packed in order, no padding.
+    torch = torch_mod
+    w = get_weights("perturbed")
+    cw = get_connector("perturbed")
+    lengths = [1_400_000, 33_000, 400, 0, 16_000]
+    audio, lengths = workloads.custom_audio(lengths, seed=91)
+    acts = clip_activity(lengths, seed=92)
+    enc = binding_mod.Encoder(w, dtype="f32")
+    try:
+        enc.set_connector(cw, dtype="f32")
+        assert enc.out_dim == 2688
+        if windows:
+            enc.set_attention(*windows)
+        got = run_fused(torch, enc, audio, lengths, acts)
+    finally:
+        enc.close()
+    r0 = 0
+    for b, n in enumerate(lengths):
+        p = acts[b].shape[0]
+        if p:
+            ref = oracle.encode_fused(audio[b, :n], w, acts[b], cw, windows=windows)
+            check_embeddings(got[r0:r0 + p], ref, f"fused {windows} clip {b} (P={p})")
+        r0 += p
+    assert r0 == got.shape[0]
+
+
+def test_forward_fused_batch64_full_depth(torch_mod, binding_mod):
+    # The 64-clip batch at full depth in bf16 through fusion and connector;
+    # two sampled clips against the oracle, every row finite.
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("batch64")
+    w = get_weights("bf16")
+    cw = get_connector("bf16")
+    acts = clip_activity(lengths, seed=300)
+    enc = binding_mod.Encoder(w, dtype="bf16")
+    try:
+        enc.set_connector(cw)
+        got = run_fused(torch, enc, audio, lengths, acts)
+    finally:
+        enc.close()
+    assert np.all(np.isfinite(got))
+    starts = np.concatenate([[0], np.cumsum([a.shape[0] for a in acts])])
+    for b in (int(np.argmin(lengths)), 42):
+        say(f"oracle fused batch64 clip {b}")
+        ref = oracle.encode_fused(audio[b, :lengths[b]], w, acts[b], cw)
+        check_embeddings(got[starts[b]:starts[b + 1]], ref, f"fused batch64 clip {b}")
+
+
+def test_forward_fused_errors(torch_mod, binding_mod):
+    torch = torch_mod
+    w = get_weights("tiny")
+    audio, lengths = workloads.workload_audio("tiny")
+    enc = binding_mod.Encoder(prefix(w, 2), dtype="f32")
+    try:
+        enc.out_dim = 2688
+        act = torch.zeros((13, 8), dtype=torch.float32, device="cuda")
+        with pytest.raises(binding_mod.EncoderError):      # no connector set
+            enc.forward_fused(to_dev(torch, audio), lengths, act)
+        bad = dict(get_connector("perturbed"))
+        bad["w_conn"] = bad["w_conn"][:200]
+        bad["b_conn"] = bad["b_conn"][:200]
+        with pytest.raises(binding_mod.EncoderError):      # out_dim not a multiple of 128
+            enc.set_connector(bad, dtype="f32")
+        # a narrower connector (one 128-wide strip only) works
+        small = dict(get_connector("perturbed"))
+        small["w_conn"] = small["w_conn"][:128]
+        small["b_conn"] = small["b_conn"][:128]
+        enc.set_connector(small, dtype="f32")
+        acts = clip_activity(lengths, seed=5)
+        got = run_fused(torch, enc, audio, lengths, acts)
+        ref = oracle.encode_fused(audio[0], prefix(w, 2), acts[0], small)
+        check_embeddings(got, ref, "fused out_dim 128")
+        # too-short clips: no rows, nothing written, no error
+        empty = run_fused(torch, enc, np.zeros((2, 399), np.float32), [10, 399],
+                          [np.zeros((0, 8), np.float32)] * 2)
+        assert empty.shape == (0, 128)
+    finally:
+        enc.close()
