@@ -9,7 +9,10 @@ the library's stream during the timed steps) and the CPU oracle timed on a
 bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                      [--attention CORE,CONTEXT]
+                      [--attention CORE,CONTEXT] [--fused]
+
+--fused runs the encoder through speaker fusion and the 1280 -> 2688 connector
+(synthetic speaker activity) instead of stopping at the embeddings.
 
 --attention encodes each clip in windows of CORE positions with CONTEXT
 positions of context on each side (500,50 are the serving windows, 375,0 the
@@ -31,6 +34,7 @@ from speech_audio_encoder_amd import workloads  # noqa: E402
 
 SAMPLE_RATE = 16000
 D, FF, DIN, H, DH = 1280, 5120, 1024, 10, 128
+LLM = 2688                     # language-model width (connector output)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
@@ -68,14 +72,16 @@ def attention_flops_per_layer(pos):
     return sum(4 * p * p * DH * H for p in pos)
 
 
-def kernel_flops(name, rows, pos):
-    """Algorithmic MFMA flops of one launch of a kernel class."""
+def kernel_flops(name, rows, pos, clip_rows=None):
+    """Algorithmic MFMA flops of one launch of a kernel class (rows: the
+    layers' rows; clip_rows: the clips' positions, which the connector maps)."""
     return {
         "gemm_in": 2 * rows * D * DIN,
         "gemm_qkv": 2 * rows * 3 * D * D,
         "gemm_o": 2 * rows * D * D,
         "gemm_up": 2 * rows * D * FF,
         "gemm_down": 2 * rows * FF * D,
+        "connector": 2 * (rows if clip_rows is None else clip_rows) * D * LLM,
         "attention": attention_flops_per_layer(pos),
     }.get(name)
 
@@ -151,6 +157,8 @@ def main():
     ap.add_argument("--workload", default="batch64", choices=list(DESCRIPTIONS))
     ap.add_argument("--attention", default="full",
                     help="'full' or CORE,CONTEXT for windowed attention")
+    ap.add_argument("--fused", action="store_true",
+                    help="encoder + speaker fusion + connector (language-model input rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every kernel class (extra untimed steps)")
@@ -195,18 +203,33 @@ def main():
     pos = sequences([positions(n) for n in lengths], core, context)
     rows = sum(pos)
     _, p_max = binding.enc_shapes(lengths)
-    out = torch.empty((len(lengths), p_max, D), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
+    clip_pos = [positions(n) for n in lengths]
+    if args.fused:
+        cw = workloads.make_connector_weights(bf16=True)
+        enc.set_connector(cw)
+        acts = np.concatenate([workloads.speaker_activity(p, seed=400 + b)
+                               for b, p in enumerate(clip_pos)])
+        act_dev = torch.from_numpy(acts).cuda()
+        out = torch.empty((sum(clip_pos), LLM), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            enc.forward_fused(x, lengths, act_dev, out=out)
+    else:
+        out = torch.empty((len(lengths), p_max, D), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            enc.forward(x, lengths, out=out)
 
     for _ in range(args.warmup):
-        enc.forward(x, lengths, out=out)
+        step()
     torch.cuda.synchronize()
 
     breakdown = {}
     if args.breakdown:
         for kname in binding.KERNELS:
             binding.enc_profile_kernel(enc.ctx, kname)
-            enc.forward(x, lengths, out=out)
+            step()
             n, ms = binding.enc_profile_read(enc.ctx)
             breakdown[kname] = {"launches": n, "ms": round(ms, 4)}
         binding.enc_profile_kernel(enc.ctx, -1)
@@ -224,7 +247,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        enc.forward(x, lengths, out=out)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -237,10 +260,12 @@ def main():
     value = audio_s / (ms_per_step / 1000.0)
     total_flops = (n_layers * (gemm_flops_per_layer(rows) + attention_flops_per_layer(pos))
                    + 2 * rows * D * DIN)
+    if args.fused:
+        total_flops += 2 * sum(clip_pos) * D * LLM
     mfma_pct = 100.0 * total_flops / (ms_per_step / 1000.0) / (PEAK_BF16_TFLOPS * 1e12)
 
     avg_ms = dom_ms / max(n_dom, 1)
-    fl = kernel_flops(dom, rows, pos)
+    fl = kernel_flops(dom, rows, pos, sum(clip_pos))
     traffic = measured_traffic(args.workload, dom)
     if fl is not None:
         achieved = fl / (avg_ms / 1000.0) / 1e12
@@ -283,6 +308,8 @@ def main():
                    "positions": sum(positions(n) for n in lengths), "layer_rows": rows,
                    "layers": n_layers,
                    "attention": "full" if not core else f"windows core={core} context={context}",
+                   "output": "fused + connector rows [R, 2688]" if args.fused
+                   else "embeddings [B, P_max, 1280]",
                    "algorithmic_tflop_per_step": round(total_flops / 1e12, 4)},
         "roofline": roof,
     }

@@ -41,6 +41,8 @@ CLASS_SOURCES = {
     "qknorm_rope": ["norm.hip", "common.h", "kernels.h"],
     "attention": ["attention.hip", "common.h", "kernels.h"],
     "final_norm": ["norm.hip", "common.h", "kernels.h"],
+    "speaker_fuse": ["norm.hip", "common.h", "kernels.h"],
+    "connector": ["gemm.hip", "common.h", "kernels.h"],
 }
 
 
@@ -60,7 +62,8 @@ def short_name(name):
 
 def epilogue_class(short):
     """Which GEMM a dispatch belongs to, from its epilogue (E0 bias->bf16:
-    qkv; E1 GELU: up; E2 residual: o and down alternate; E3 fp32: input)."""
+    qkv, or the connector after the speaker fusion; E1 GELU: up; E2 residual:
+    o and down alternate; E3 fp32: input)."""
     m = re.search(r"<E(\d)", short)
     return int(m.group(1)) if m else None
 
@@ -73,11 +76,16 @@ def classify(rows):
     out = []
     e2_runs = 0
     prev_e2 = False
+    after_fuse = False
     for r in rows:
         s = short_name(r["Kernel_Name"])
         cls, is_e2 = None, False
-        if "logmel" in s:
+        if "logmel" in s or "gather_rows" in s:
             cls = "frontend"
+            after_fuse = False
+        elif s.startswith("speaker_fuse"):
+            cls = "speaker_fuse"
+            after_fuse = True
         elif s.startswith("layernorm"):
             cls = "layernorm"
         elif s.startswith("qknorm"):
@@ -89,7 +97,7 @@ def classify(rows):
         elif "gemm" in s or "splitk" in s:
             e = epilogue_class(s)
             if e == 0:
-                cls = "gemm_qkv"
+                cls = "connector" if after_fuse else "gemm_qkv"
             elif e == 1:
                 cls = "gemm_up"
             elif e == 3:
@@ -130,8 +138,8 @@ def kernels_report(trace_csv, out_md, command):
         d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
         e = per.setdefault(cls, [0.0, 0])
         e[0] += d
-        if cls != prev or cls in ("layernorm", "frontend", "final_norm", "qknorm_rope",
-                                  "attention"):
+        if cls != prev or cls in ("layernorm", "final_norm", "qknorm_rope", "attention",
+                                  "speaker_fuse"):
             e[1] += 1
         prev = cls
     lines += ["", "Per kernel class (one launch = one call of the library's launcher; "
@@ -173,7 +181,8 @@ def traffic_report(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_cs
             d = per_class.setdefault(cls, {"FETCH_SIZE": [], "WRITE_SIZE": [], "kernels": set()})
             d[counter].append(float(r["Counter_Value"]) * 1024.0 * fac)
             d["kernels"].add(short_name(r["Kernel_Name"]))
-    calls = {"frontend": 1, "gemm_in": 1, "final_norm": 1, "layernorm": 2}
+    calls = {"frontend": 1, "gemm_in": 1, "final_norm": 1, "speaker_fuse": 1, "connector": 1,
+             "layernorm": 2}
     record = {"workload": workload, "fetch_factor": f_fac, "write_factor": w_fac, "classes": {}}
     lines = ["# HBM traffic per launch: " + workload, "",
              "Commands (from the repository root, on one MI355X; each counter in a run",
@@ -185,11 +194,9 @@ def traffic_report(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_cs
              "by the class's launches per step (layers, or 2 x layers for LayerNorm).", "",
              "| class | kernels | fetch MB/launch | write MB/launch | total MB/launch |",
              "|---|---|---:|---:|---:|"]
-    n_steps = None
-    for cls, d in per_class.items():
-        if cls == "frontend":
-            n_steps = len(d["FETCH_SIZE"])   # one frontend dispatch per step
-    n_steps = n_steps or 1
+    # one log-mel dispatch per step
+    n_steps = sum(1 for r in _counter(fetch_csv, "FETCH_SIZE")
+                  if "logmel" in short_name(r["Kernel_Name"])) or 1
     for cls in CLASS_SOURCES:
         if cls not in per_class:
             continue
