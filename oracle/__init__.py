@@ -34,3 +34,4 @@ from .fusion import (  # noqa: F401
     speaker_kernel, speaker_indicators, speaker_features, fuse_speakers, connector,
     encode_fused,
 )
+from . import fp8  # noqa: F401

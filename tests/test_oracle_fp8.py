@@ -1,0 +1,128 @@
+"""Pins of the FP8 (E4M3, per-tensor scales) oracle, CPU only.
+
+The E4M3 rounding is pinned to the format's definition (OCP FP8: bias 7, 3
+mantissa bits, largest finite 448, subnormals down to 2^-9) by brute force
+over its value grid; the quantized linear map reduces to the plain linear map
+when every operand is on the grid; the FP8 layer's structure is pinned to the
+unquantized layer through its calibration mode.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8
+from speech_audio_encoder_amd import workloads
+
+
+def e4m3_grid():
+    """Every finite non-negative E4M3 value with its mantissa bits, from the
+    format definition."""
+    vals, mant = [0.0], [0]
+    for m in range(1, 8):                        # subnormals m/8 * 2^-6
+        vals.append(m / 8 * 2.0 ** -6)
+        mant.append(m)
+    for e in range(1, 16):                       # normals (1 + m/8) 2^(e-7)
+        for m in range(8):
+            if e == 15 and m == 7:               # the NaN code
+                continue
+            vals.append((1 + m / 8) * 2.0 ** (e - 7))
+            mant.append(m)
+    return np.array(vals), np.array(mant)
+
+
+def test_grid_landmarks():
+    g, _ = e4m3_grid()
+    assert g.max() == 448.0 and g[g > 0].min() == 2.0 ** -9
+    assert 2.0 ** -6 in g and len(g) == 127
+    assert np.array_equal(fp8.e4m3(g.astype(np.float32)), g)
+    assert np.array_equal(fp8.e4m3(-g.astype(np.float32)), -g)
+
+
+def test_rounding_is_nearest_ties_to_even_brute_force():
+    g, mant = e4m3_grid()
+    rng = np.random.default_rng(0)
+    mids = (g[1:] + g[:-1]) / 2
+    xs = np.concatenate([rng.uniform(0, 448, 20000), rng.uniform(0, 0.05, 20000), mids,
+                         np.nextafter(mids.astype(np.float32), np.float32(0)),
+                         np.nextafter(mids.astype(np.float32), np.float32(1000))]).astype(np.float32)
+    got = fp8.e4m3(xs)
+    for x, y in zip(xs.astype(np.float64), got.astype(np.float64)):
+        d = np.abs(g - x)
+        best = np.nonzero(d == d.min())[0]
+        if len(best) == 1:
+            assert y == g[best[0]], (x, y)
+        else:                                    # a tie: the even mantissa wins
+            even = [i for i in best if mant[i] % 2 == 0]
+            assert len(even) == 1 and y == g[even[0]], (x, y)
+
+
+def test_saturation_and_sign():
+    x = np.array([448.0, 449.0, 464.0, 500.0, 1e30, -1e30, -470.0], np.float32)
+    assert fp8.e4m3(x).tolist() == [448, 448, 448, 448, 448, -448, -448]
+
+
+def test_quantize_with_power_of_two_scale_is_exact_on_grid():
+    g, _ = e4m3_grid()
+    v = np.concatenate([g, -g]).astype(np.float32) * np.float32(0.25)
+    assert np.array_equal(fp8.quantize(v, 0.25), np.concatenate([g, -g]))
+
+
+def test_weight_scale_and_zero_matrix():
+    w = np.array([[0.5, -2.0], [1.0, 0.25]], np.float32)
+    assert fp8.weight_scale(w) == np.float32(2.0) / np.float32(448)
+    assert fp8.weight_scale(np.zeros((3, 3), np.float32)) == 1.0
+    q, s = fp8.quantize_weight(w)
+    assert np.abs(q).max() == 448.0 and s == np.float32(2.0) / np.float32(448)
+    assert np.array_equal(fp8.scales_from_amax([[0.0, 896.0]]), np.float32([[1.0, 2.0]]))
+
+
+def test_linear_fp8_reduces_to_linear_on_grid():
+    # operands already on the E4M3 grid under power-of-two scales: the FP8
+    # map is the plain linear map (torch's)
+    g, _ = e4m3_grid()
+    rng = np.random.default_rng(1)
+    pick = g[(g > 0.01) & (g < 100)]
+    x = (rng.choice(pick, (7, 64)) * rng.choice([-1, 1], (7, 64))).astype(np.float32) * 0.5
+    wq = (rng.choice(pick, (48, 64)) * rng.choice([-1, 1], (48, 64))).astype(np.float32)
+    b = rng.normal(size=48).astype(np.float32)
+    got = fp8.linear_fp8(x, wq, np.float32(0.125), b, np.float32(0.5))
+    ref = torch.nn.functional.linear(torch.from_numpy(x).double(),
+                                     torch.from_numpy(wq * 0.125).double(),
+                                     torch.from_numpy(b).double()).numpy()
+    assert np.allclose(got, ref, rtol=1e-6, atol=1e-5)
+
+
+def small_weights():
+    return workloads.make_weights(2, bf16=False, perturb=True, d=256, dh=128, ffn=1024)
+
+
+def test_calibration_mode_is_the_unquantized_layer():
+    w = small_weights()
+    x = np.random.default_rng(2).normal(size=(19, 256)).astype(np.float32)
+    rec = []
+    got = fp8.encoder_layer_fp8(x, w["layers"][0], None, None, record=rec)
+    assert np.allclose(got, oracle.encoder_layer(x, w["layers"][0]), atol=1e-5)
+    t = torch.from_numpy(x)
+    ln1 = torch.nn.functional.layer_norm(t, (256,), torch.from_numpy(w["layers"][0]["ln1_g"]),
+                                         torch.from_numpy(w["layers"][0]["ln1_b"]), eps=1e-5)
+    assert len(rec) == 4 and rec[0] == pytest.approx(float(ln1.abs().max()), rel=1e-5)
+    assert all(r > 0 for r in rec)
+
+
+def test_fp8_encoder_close_to_unquantized_and_calibration():
+    w = small_weights()
+    audio, _ = workloads.custom_audio([24_000, 9_000], seed=3)
+    clips = [audio[0], audio[1, :9_000]]
+    amax = fp8.calibrate(clips, w)
+    assert amax.shape == (2, 4) and np.all(amax > 0)
+    scales = fp8.scales_from_amax(amax)
+    ref = oracle.encode(clips[0], w)
+    got = fp8.encode_fp8(clips[0], w, scales)
+    rel = np.abs(got - ref).max() / np.abs(ref).max()
+    assert 1e-4 < rel < 0.15      # quantized, but close
+    # scales far too small saturate everything: a different result
+    bad = fp8.encode_fp8(clips[0], w, scales * 1e-3)
+    assert np.abs(bad - ref).max() > 3 * np.abs(got - ref).max()
+    assert fp8.encode_fp8(np.zeros(300, np.float32), w, scales).shape == (0, 256)
