@@ -9,10 +9,14 @@ the library's stream during the timed steps) and the CPU oracle timed on a
 bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                      [--attention CORE,CONTEXT] [--fused]
+                      [--attention CORE,CONTEXT] [--fused] [--precision bf16|fp8]
 
 --fused runs the encoder through speaker fusion and the 1280 -> 2688 connector
 (synthetic speaker activity) instead of stopping at the embeddings.
+
+--precision fp8 runs the four linear maps of every layer on E4M3 codes with
+per-tensor scales (input scales from the library's calibration on the same
+batch, untimed); GEMM flops are then priced at the fp8 MFMA peak.
 
 --attention encodes each clip in windows of CORE positions with CONTEXT
 positions of context on each side (500,50 are the serving windows, 375,0 the
@@ -36,6 +40,7 @@ SAMPLE_RATE = 16000
 D, FF, DIN, H, DH = 1280, 5120, 1024, 10, 128
 LLM = 2688                     # language-model width (connector output)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0
 
 DESCRIPTIONS = {
@@ -96,15 +101,17 @@ def kernel_bytes(name, rows, lengths):
     }.get(name)
 
 
-def gemm_bytes(name, rows):
+def gemm_bytes(name, rows, fp8=False):
     """Algorithmic HBM bytes of one GEMM launch: A and W read once, C written
-    once (bf16, or fp32 read+write for the residual epilogue)."""
+    once (bf16, E4M3 for the FP8 path's GELU output, or fp32 read+write for
+    the residual epilogue)."""
     mnk = {"gemm_in": (D, DIN, 4), "gemm_qkv": (3 * D, D, 2), "gemm_o": (D, D, 8),
-           "gemm_up": (FF, D, 2), "gemm_down": (D, FF, 8)}.get(name)
+           "gemm_up": (FF, D, 1 if fp8 else 2), "gemm_down": (D, FF, 8)}.get(name)
     if mnk is None:
         return None
     n, k, c_bytes = mnk
-    return rows * k * 2 + n * k * 2 + rows * n * c_bytes
+    ab = 1 if fp8 and name != "gemm_in" else 2
+    return rows * k * ab + n * k * ab + rows * n * c_bytes
 
 
 def measured_traffic(workload, kernel):
@@ -159,6 +166,8 @@ def main():
                     help="'full' or CORE,CONTEXT for windowed attention")
     ap.add_argument("--fused", action="store_true",
                     help="encoder + speaker fusion + connector (language-model input rows)")
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"],
+                    help="linear maps of the layers in bf16 or FP8 (E4M3, per-tensor scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true",
                     help="also time every kernel class (extra untimed steps)")
@@ -205,6 +214,10 @@ def main():
     _, p_max = binding.enc_shapes(lengths)
     stream = torch.cuda.current_stream()
     clip_pos = [positions(n) for n in lengths]
+    fp8 = args.precision == "fp8"
+    if fp8:
+        amax = enc.calibrate(x, lengths)
+        enc.set_precision("fp8", binding.scales_from_amax(amax))
     if args.fused:
         cw = workloads.make_connector_weights(bf16=True)
         enc.set_connector(cw)
@@ -262,19 +275,27 @@ def main():
                    + 2 * rows * D * DIN)
     if args.fused:
         total_flops += 2 * sum(clip_pos) * D * LLM
-    mfma_pct = 100.0 * total_flops / (ms_per_step / 1000.0) / (PEAK_BF16_TFLOPS * 1e12)
+    if fp8:
+        # layer GEMMs at the fp8 peak, attention and the bf16 products at the bf16 peak
+        f8_flops = n_layers * gemm_flops_per_layer(rows)
+        peak_time = (f8_flops / PEAK_FP8_TFLOPS + (total_flops - f8_flops) / PEAK_BF16_TFLOPS) / 1e12
+        mfma_pct = 100.0 * peak_time / (ms_per_step / 1000.0)
+    else:
+        mfma_pct = 100.0 * total_flops / (ms_per_step / 1000.0) / (PEAK_BF16_TFLOPS * 1e12)
 
     avg_ms = dom_ms / max(n_dom, 1)
     fl = kernel_flops(dom, rows, pos, sum(clip_pos))
     traffic = measured_traffic(args.workload, dom)
     if fl is not None:
         achieved = fl / (avg_ms / 1000.0) / 1e12
+        peak = PEAK_FP8_TFLOPS if fp8 and dom in ("gemm_qkv", "gemm_o", "gemm_up",
+                                                  "gemm_down") else PEAK_BF16_TFLOPS
         roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic if not fp8 else None,
                 "avg_launch_ms": round(avg_ms, 5), "launches": n_dom,
                 "flops_per_launch": fl}
-        ab = gemm_bytes(dom, rows)
+        ab = gemm_bytes(dom, rows, fp8)
         if ab is not None:
             roof["algorithmic_bytes_per_launch"] = ab
     else:
@@ -300,7 +321,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8-e4m3 layer GEMMs, bf16 attention" if fp8 else "bf16",
         "data": "synthetic",
         "mfma_pct_of_peak": round(mfma_pct, 2),
         "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}",
@@ -308,6 +329,7 @@ def main():
                    "positions": sum(positions(n) for n in lengths), "layer_rows": rows,
                    "layers": n_layers,
                    "attention": "full" if not core else f"windows core={core} context={context}",
+                   "precision": args.precision,
                    "output": "fused + connector rows [R, 2688]" if args.fused
                    else "embeddings [B, P_max, 1280]",
                    "algorithmic_tflop_per_step": round(total_flops / 1e12, 4)},

@@ -245,6 +245,50 @@ int enc_set_connector(enc_ctx* ctx, const enc_connector_weights* w);
 int enc_forward_fused(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                       const float* activity, void* out, hipStream_t stream);
 
+/*
+ * FP8 variant.  The nemotron-transcribe skill page, section "Precision
+ * selection", describes an FP8 release (a ModelOpt export) with a quantized
+ * audio encoder; the Dataset Audits page, section "The long-audio memory
+ * budget is not just the KV cache", keeps the ASR projections in FP8.  This
+ * library reads that as the per-tensor FP8 scheme:
+ *   - the four linear maps of every layer (QKV, attention output, FFN up,
+ *     FFN down) multiply E4M3 codes (OCP FP8, largest value 448) with fp32
+ *     accumulation: y = (q_x . q_w) * fp32(s_x * s_w) + b;
+ *   - weight codes q_w = e4m3(sat(w * fp32(1 / s_w))), s_w = amax|w| / 448,
+ *     from the context's bf16 copy of each matrix (s_w = 1 for a zero matrix);
+ *   - input codes q_x = e4m3(sat(x * fp32(1 / s_x))) with one static scale s_x
+ *     per linear map (a calibration result: amax / 448 over calibration data);
+ *     the producers (LayerNorm, attention, the FFN's GELU) write the codes;
+ *   - the input projection, attention, the norms and the connector stay as in
+ *     the bf16 encoder.
+ * e4m3() rounds to nearest even; sat() clamps to [-448, 448].
+ */
+#define ENC_PREC_BF16 0
+#define ENC_PREC_FP8 1
+
+/*
+ * enc_set_precision: the precision of later enc_forward(_fused) calls.
+ *   ENC_PREC_BF16 (default): input_scales is ignored (may be NULL).
+ *   ENC_PREC_FP8: input_scales is a HOST float array [n_layers][4], the input
+ *   scales s_x of (QKV, attention output, FFN up, FFN down) of each layer,
+ *   each positive and finite.  The first FP8 call quantizes the weights
+ *   (synchronous; 631 MB of codes for 32 layers kept in the context).
+ * Errors: ENC_ERR_ARG, ENC_ERR_NOMEM, ENC_ERR_HIP.
+ */
+int enc_set_precision(enc_ctx* ctx, int32_t precision, const float* input_scales);
+
+/*
+ * enc_calibrate: run the bf16 encoder on a batch (as enc_forward, same
+ * attention scope, no output) and return in amax (HOST float [n_layers][4])
+ * the largest magnitude of the input of each quantizable linear map: the
+ * LayerNorm outputs feeding QKV and FFN up, the attention output and the
+ * GELU output, as the bf16 values those maps read.  Synchronous.  Input
+ * scales for enc_set_precision are amax / 448 (merge several batches by
+ * taking the maximum).  Errors: as enc_forward.
+ */
+int enc_calibrate(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                  float* amax, hipStream_t stream);
+
 /* enc_destroy: wait for the context's device work and free it.  NULL is a
  * no-op. */
 void enc_destroy(enc_ctx* ctx);

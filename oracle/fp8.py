@@ -21,7 +21,13 @@ given; this oracle takes the plainest reading, the per-tensor FP8 scheme
   * y = (q_x . q_w) * fp32(s_x * s_w) + b, accumulated exactly here (float64)
     and in fp32 on the GPU;
   * the input projection, attention itself, the norms and the rotation stay
-    as in the bf16 encoder.
+    as in the bf16 encoder, whose matrix-product and attention operands are
+    bf16: the stacked log-mel features and W_in of the input projection, and
+    q, k, v (the QKV product's output as stored, q and k again after
+    normalisation and rotation) are rounded to bf16 here.  The unquantized
+    oracle can leave that rounding to its tolerance; this one cannot,
+    because every E4M3 code is a decision taken on values computed from
+    those operands, and both sides must take it in the same precision.
 """
 
 import numpy as np
@@ -98,16 +104,18 @@ def encoder_layer_fp8(x, lw, qw, scales, record=None):
         wq, s_w = qw[name]
         return linear_fp8(inp, wq, s_w, lw[bname], scales[i])
 
+    # bf16 attention operands, except in calibration (the unquantized model)
+    op = (lambda t: t) if record is not None else round_bf16
     h = layer_norm(x, lw["ln1_g"], lw["ln1_b"])
-    qkv = lin(h, 0, "w_qkv", "b_qkv")
+    qkv = op(lin(h, 0, "w_qkv", "b_qkv"))
     cos, sin = rope_tables(x.shape[0], dh)
     heads = []
     for hh in range(nh):
         q = qkv[:, hh * dh:(hh + 1) * dh]
         k = qkv[:, d + hh * dh:d + (hh + 1) * dh]
         v = qkv[:, 2 * d + hh * dh:2 * d + (hh + 1) * dh]
-        q = apply_rope(layer_norm(q, lw["q_g"], lw["q_b"]), cos, sin)
-        k = apply_rope(layer_norm(k, lw["k_g"], lw["k_b"]), cos, sin)
+        q = op(apply_rope(layer_norm(q, lw["q_g"], lw["q_b"]), cos, sin))
+        k = op(apply_rope(layer_norm(k, lw["k_g"], lw["k_b"]), cos, sin))
         heads.append(attention(q, k, v))
     o = np.concatenate(heads, axis=1)
     x = x + lin(o, 1, "w_o", "b_o")
@@ -117,8 +125,9 @@ def encoder_layer_fp8(x, lw, qw, scales, record=None):
 
 
 def _stacked_input(x, weights):
-    feats = stack_frames(logmel(x))
-    return linear(feats, weights["w_in"], weights["b_in"])
+    """Input projection on bf16 operands (stacked features and W_in)."""
+    feats = round_bf16(stack_frames(logmel(x)))
+    return linear(feats, round_bf16(weights["w_in"]), weights["b_in"])
 
 
 def encode_fp8(x, weights, input_scales, n_layers=None, qw=None):

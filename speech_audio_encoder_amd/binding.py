@@ -27,8 +27,12 @@ KERNELS = ["frontend", "gemm_in", "layernorm", "gemm_qkv", "qknorm_rope", "atten
            "gemm_o", "gemm_up", "gemm_down", "final_norm", "speaker_fuse", "connector"]
 
 EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_set_attention", "enc_set_connector",
-           "enc_forward_fused", "enc_destroy", "enc_shapes", "enc_workspace_bytes",
-           "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
+           "enc_forward_fused", "enc_set_precision", "enc_calibrate", "enc_destroy", "enc_shapes",
+           "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
+
+ENC_PREC_BF16 = 0
+ENC_PREC_FP8 = 1
+E4M3_MAX = 448.0
 
 ENC_ATTN_FULL = 0
 ENC_ATTN_WINDOWS = 1
@@ -85,6 +89,10 @@ def load_library(path=LIB_PATH):
     lib.enc_set_connector.argtypes = [ctypes.c_void_p, ctypes.POINTER(EncConnectorWeights)]
     lib.enc_forward_fused.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.enc_set_precision.argtypes = [ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_float)]
+    lib.enc_calibrate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
+                                  ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]
     lib.enc_destroy.argtypes = [ctypes.c_void_p]
     lib.enc_destroy.restype = None
     lib.enc_shapes.argtypes = [i64p, ctypes.c_int32, i64p, i64p]
@@ -259,6 +267,33 @@ def enc_forward_fused(ctx, audio, lengths, activity, out_dim, out=None, stream=N
     return out
 
 
+def enc_set_precision(ctx, precision, input_scales=None):
+    """ENC_PREC_BF16, or ENC_PREC_FP8 with input scales [n_layers, 4] (QKV, O,
+    up, down inputs of each layer)."""
+    ptr = None
+    if input_scales is not None:
+        arr = np.ascontiguousarray(input_scales, dtype=np.float32).reshape(-1)
+        ptr = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    _check(load_library().enc_set_precision(ctypes.c_void_p(ctx), int(precision), ptr))
+
+
+def enc_calibrate(ctx, audio, lengths, n_layers, stream=None):
+    """amax [n_layers, 4] of the quantizable linear maps' inputs on one batch."""
+    arr, ptr = _lengths_array(lengths)
+    out = np.zeros(n_layers * 4, dtype=np.float32)
+    _check(load_library().enc_calibrate(ctypes.c_void_p(ctx), ctypes.c_void_p(audio.data_ptr()),
+                                        ptr, len(arr),
+                                        out.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                        _stream_handle(stream)))
+    return out.reshape(n_layers, 4)
+
+
+def scales_from_amax(amax):
+    """Input scales amax / 448 (1 where amax is 0), float32."""
+    a = np.asarray(amax, dtype=np.float32)
+    return np.where(a > 0, a / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+
+
 def enc_forward_raw(ctx, audio_ptr, lengths, out_ptr, stream_ptr=0):
     """enc_forward with raw pointers; returns the status code (tests)."""
     arr, ptr = _lengths_array(lengths)
@@ -293,6 +328,7 @@ class Encoder:
 
     def __init__(self, weights, dtype="bf16", device="cuda"):
         self.ctx = enc_create(weights, dtype=dtype, device=device)
+        self.n_layers = len(weights["layers"])
 
     def logmel(self, audio, lengths, out=None):
         return enc_logmel(self.ctx, audio, lengths, out)
@@ -305,6 +341,14 @@ class Encoder:
 
     def forward_fused(self, audio, lengths, activity, out=None):
         return enc_forward_fused(self.ctx, audio, lengths, activity, self.out_dim, out)
+
+    def set_precision(self, precision, input_scales=None):
+        """"bf16", or "fp8" with input scales [n_layers, 4]."""
+        enc_set_precision(self.ctx, ENC_PREC_FP8 if precision == "fp8" else ENC_PREC_BF16,
+                          input_scales)
+
+    def calibrate(self, audio, lengths):
+        return enc_calibrate(self.ctx, audio, lengths, self.n_layers)
 
     def set_attention(self, core=None, context=0):
         """Full-clip attention (core None) or windows of `core` positions with

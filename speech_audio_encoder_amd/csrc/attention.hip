@@ -84,7 +84,7 @@ __global__ __launch_bounds__(128) void attention_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ vt, int64_t ld_vt,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
     const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_q0, int n_tiles,
-    int n_items, bf16_t* __restrict__ out) {
+    int n_items, void* __restrict__ out, float out_scale) {
   // K in a ring of four 32-key units, V^T in two 64-key tiles.
   __shared__ uint4 sK[4][KU * DH / 8];   // [key][16 chunks of 8 dims], swizzled
   __shared__ uint4 sV[2][DH * KT / 8];   // [dim][8 chunks of 8 keys], swizzled
@@ -323,7 +323,22 @@ __global__ __launch_bounds__(128) void attention_kernel(
     const int q = q0 + wave * QPW + qb * 32 + l32;
     if (q >= len) continue;
     const float inv = 1.0f / lt;
-    bf16_t* orow = out + (s0 + q) * D + h * DH;
+    if (out_scale > 0.0f) {
+      // E4M3 codes of the output times out_scale (the FP8 output projection's input)
+      uint8_t* orow = reinterpret_cast<uint8_t*>(out) + (s0 + q) * D + h * DH;
+#pragma unroll
+      for (int db = 0; db < DH / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * lhi;
+          const float sc = inv * out_scale;
+          *reinterpret_cast<uint32_t*>(orow + d) =
+              pack_fp8x4(O[db][qb][4 * g] * sc, O[db][qb][4 * g + 1] * sc,
+                         O[db][qb][4 * g + 2] * sc, O[db][qb][4 * g + 3] * sc);
+        }
+      continue;
+    }
+    bf16_t* orow = reinterpret_cast<bf16_t*>(out) + (s0 + q) * D + h * DH;
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
@@ -358,8 +373,8 @@ bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g
 
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
-                            const int32_t* tile_q0, int n_tiles, bool fixed_ref, bf16_t* out,
-                            hipStream_t stream) {
+                            const int32_t* tile_q0, int n_tiles, bool fixed_ref, void* out,
+                            float out_scale, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   // V^T byte offsets inside a tile are 32-bit: 128 rows of ld_vt bf16.
   if (ld_vt <= 0 || ld_vt % 64 != 0 || (int64_t)DH * ld_vt * 2 >= (int64_t)1 << 31)
@@ -368,10 +383,10 @@ hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
   const int grid = (n_items + 7) / 8 * 8;
   if (fixed_ref)
     attention_kernel<true><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
-        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out);
+        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale);
   else
     attention_kernel<false><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
-        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out);
+        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale);
   return hipGetLastError();
 }
 

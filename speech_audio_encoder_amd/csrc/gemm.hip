@@ -77,14 +77,25 @@ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int
 
 // Apply the epilogue to four consecutive columns n..n+3 of row m; bv holds
 // their biases.
-template <Epilogue EPI>
+// The FP8 path first multiplies the accumulators by alpha (the product of the
+// two operand scales); kBiasGeluFp8 scales its result by oscale and stores
+// E4M3 codes (ldc in bytes).
+template <Epilogue EPI, bool F8>
 __device__ __forceinline__ void store4(void* __restrict__ Cv, int64_t ldc, int64_t m, int n,
-                                       float4 bv, float a0, float a1, float a2, float a3) {
+                                       float4 bv, float alpha, float oscale, float a0, float a1,
+                                       float a2, float a3) {
+  if constexpr (F8) {
+    a0 *= alpha; a1 *= alpha; a2 *= alpha; a3 *= alpha;
+  }
   float o0 = a0 + bv.x, o1 = a1 + bv.y, o2 = a2 + bv.z, o3 = a3 + bv.w;
-  if constexpr (EPI == Epilogue::kBiasGeluBf16) {
+  if constexpr (EPI == Epilogue::kBiasGeluBf16 || EPI == Epilogue::kBiasGeluFp8) {
     o0 = gelu_erf(o0); o1 = gelu_erf(o1); o2 = gelu_erf(o2); o3 = gelu_erf(o3);
   }
-  if constexpr (EPI == Epilogue::kBiasBf16 || EPI == Epilogue::kBiasGeluBf16) {
+  if constexpr (EPI == Epilogue::kBiasGeluFp8) {
+    uint8_t* C = reinterpret_cast<uint8_t*>(Cv);
+    *reinterpret_cast<uint32_t*>(C + m * ldc + n) =
+        pack_fp8x4(o0 * oscale, o1 * oscale, o2 * oscale, o3 * oscale);
+  } else if constexpr (EPI == Epilogue::kBiasBf16 || EPI == Epilogue::kBiasGeluBf16) {
     bf16_t* C = reinterpret_cast<bf16_t*>(Cv);
     *reinterpret_cast<uint2*>(C + m * ldc + n) = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
   } else {
@@ -161,11 +172,16 @@ __device__ __forceinline__ void wg_barrier() {
 
 constexpr int PBK = 64;   // K step of the persistent kernel
 
-template <Epilogue EPI>
+// F8: A and W hold E4M3 codes and every length along K (K, lda, ldw) is given
+// in units of two codes, so the data movement below is the bf16 one byte for
+// byte; one 64-code MFMA step takes the two consecutive 16-byte fragments a
+// lane would feed to two bf16 steps (A and W use the same assignment of
+// bytes to k, so every product pairs the right codes).
+template <Epilogue EPI, bool F8>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int K,
-    int tiles_m, int tiles_n, int n_big) {
+    int tiles_m, int tiles_n, int n_big, float alpha, float oscale) {
   constexpr int SL = BIG * PBK / 8;   // uint4 per slot (32 KB)
   __shared__ uint4 sA[3][SL];
   __shared__ uint4 sW[2][SL];
@@ -187,46 +203,90 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 
   // Piece t of a slice = rows 8t .. 8t+7; wave q of the loading group fills
   // pieces 8q .. 8q+7; lane -> row 8t + lane/8, LDS chunk lane%8 of the row
-  // holds global chunk (lane%8) ^ ((row/2)%8).
-  uint32_t off[8];
-  int off_tile = -1;
+  // holds global chunk (lane%8) ^ ((row/2)%8).  Rows past M (last row tile
+  // only) re-read row M-1.
+  //   bf16: the eight per-lane offsets are kept in registers (recomputed when
+  //         the A tile changes).
+  //   FP8:  its larger fragments leave no registers for them: with
+  //         row = 64q + 8t' + lane/8 (t' = t - 8q) the swizzle depends only on
+  //         the parity of t' and on lane/16, so two offsets are computed per
+  //         call and the 8t'-row step goes into the uniform base address.
   const uint32_t ldsA = (uint32_t)(uintptr_t)(lds_void*)&sA[0][0];
   const uint32_t ldsW = (uint32_t)(uintptr_t)(lds_void*)&sW[0][0];
+  uint32_t off[8];
+  int off_tile = -1;
   auto issue = [&](int g, bool is_a) __attribute__((always_inline)) {
     const int r = g / KT, kt = g - r * KT;
     int tm, tn;
     tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
     const int64_t am = (int64_t)tm * BIG;
-    if (is_a) {
-      if (off_tile != r) {   // rows past M re-read row M - 1
+    if constexpr (!F8) {
+      if (is_a) {
+        if (off_tile != r) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int rr = (q * 8 + t) * 8 + (lane >> 3);
-          const int c = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
-          const int64_t row = min<int64_t>(am + rr, M - 1) - am;
-          off[t] = (uint32_t)((row * lda + c) * 2);
+          for (int t = 0; t < 8; ++t) {
+            const int rr = (q * 8 + t) * 8 + (lane >> 3);
+            const int c = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+            const int64_t row = min<int64_t>(am + rr, M - 1) - am;
+            off[t] = (uint32_t)((row * lda + c) * 2);
+          }
+          off_tile = r;
         }
-        off_tile = r;
+        const char* base = reinterpret_cast<const char*>(A + am * lda) + kt * PBK * 2;
+        const uint32_t l = ldsA + (g % 3) * (SL * 16) + q * 8 * 1024;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dma16_s(base, off[t], l + t * 1024);
+      } else {
+        if (off_tile != -2) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int rr = (q * 8 + t) * 8 + (lane >> 3);
+            const int c = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
+            off[t] = (uint32_t)((rr * ldw + c) * 2);
+          }
+          off_tile = -2;
+        }
+        const char* base =
+            reinterpret_cast<const char*>(W + (int64_t)tn * BIG * ldw) + kt * PBK * 2;
+        const uint32_t l = ldsW + (g & 1) * (SL * 16) + q * 8 * 1024;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dma16_s(base, off[t], l + t * 1024);
       }
+      return;
+    }
+    // FP8 (the empty asm keeps the offsets from being hoisted out of the loop,
+    // where they would be spilled and reloaded through memory)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int rl = q * 64 + (ln >> 3);
+    const int sw = ln >> 4;
+    const int ce = ((ln & 7) ^ sw) * 8;
+    const int co = ((ln & 7) ^ (sw + 4)) * 8;
+    if (is_a) {
       const char* base = reinterpret_cast<const char*>(A + am * lda) + kt * PBK * 2;
       const uint32_t l = ldsA + (g % 3) * (SL * 16) + q * 8 * 1024;
+      if (am + BIG <= M) {
+        const uint32_t ve = (uint32_t)((rl * lda + ce) * 2);
+        const uint32_t vo = (uint32_t)((rl * lda + co) * 2);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) dma16_s(base, off[t], l + t * 1024);
-    } else {
-      if (off_tile != -2) {
+        for (int t = 0; t < 8; ++t)
+          dma16_s(base + (int64_t)t * 16 * lda, (t & 1) ? vo : ve, l + t * 1024);
+      } else {
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int rr = (q * 8 + t) * 8 + (lane >> 3);
-          const int c = ((lane & 7) ^ ((rr >> 1) & 7)) * 8;
-          off[t] = (uint32_t)((rr * ldw + c) * 2);
+          const int64_t row = min<int64_t>(am + rl + 8 * t, M - 1) - am;
+          dma16_s(base, (uint32_t)((row * lda + ((t & 1) ? co : ce)) * 2), l + t * 1024);
         }
-        off_tile = -2;
       }
+    } else {
       const char* base =
           reinterpret_cast<const char*>(W + (int64_t)tn * BIG * ldw) + kt * PBK * 2;
       const uint32_t l = ldsW + (g & 1) * (SL * 16) + q * 8 * 1024;
+      const uint32_t ve = (uint32_t)((rl * ldw + ce) * 2);
+      const uint32_t vo = (uint32_t)((rl * ldw + co) * 2);
 #pragma unroll
-      for (int t = 0; t < 8; ++t) dma16_s(base, off[t], l + t * 1024);
+      for (int t = 0; t < 8; ++t)
+        dma16_s(base + (int64_t)t * 16 * ldw, (t & 1) ? vo : ve, l + t * 1024);
     }
   };
 
@@ -273,6 +333,58 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     interleave();
     mma(f1, false);
   };
+  // FP8: code step ks covers bf16 steps 2 ks and 2 ks + 1; a fragment is the
+  // two 16-byte chunks of those steps.  Step 1's fragments are read while
+  // step 0's MFMAs run, each A fragment only after the two MFMAs that use
+  // the previous one, so that at most one step plus two fragments are live.
+  auto ld8 = [&](const uint4* base, int ofs, int ks) __attribute__((always_inline)) {
+    const i32x4 lo = __builtin_bit_cast(i32x4, base[ofs + ((4 * ks + lhi) ^ rsw)]);
+    const i32x4 hi = __builtin_bit_cast(i32x4, base[ofs + ((4 * ks + 2 + lhi) ^ rsw)]);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  i32x8 gw0, gw1, ga[4];
+  auto mma8 = [&](const i32x8& w0, const i32x8& w1, const i32x8& aj, int j, bool fresh)
+      __attribute__((always_inline)) {
+    const f32x16 z = {};
+    acc[0][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w0, aj, fresh ? z : acc[0][j], 0,
+                                                                0, 0, 0, 0, 0);
+    acc[1][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w1, aj, fresh ? z : acc[1][j], 0,
+                                                                0, 0, 0, 0, 0);
+  };
+  auto compute8 = [&](const uint4* a, const uint4* w, bool first) __attribute__((always_inline)) {
+    const i32x8 nw0 = ld8(w, wofs, 1);
+    const i32x8 nw1 = ld8(w, wofs + 256, 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mma8(gw0, gw1, ga[j], j, first);
+      ga[j] = ld8(a, aofs + j * 256, 1);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mma8(nw0, nw1, ga[j], j, false);
+    // order: next W reads; per A fragment two MFMAs then its replacement's
+    // reads; then the second step's eight MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  };
+  auto preload = [&](const uint4* a, const uint4* w) __attribute__((always_inline)) {
+    if constexpr (F8) {
+      gw0 = ld8(w, wofs, 0);
+      gw1 = ld8(w, wofs + 256, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ga[j] = ld8(a, aofs + j * 256, 0);
+    } else {
+      load(a, w, 0, f0);
+    }
+  };
+  auto step = [&](const uint4* a, const uint4* w, bool first) __attribute__((always_inline)) {
+    if constexpr (F8) compute8(a, w, first);
+    else compute(a, w, first);
+  };
   auto epilogue = [&](int r) __attribute__((always_inline)) {
     int tm, tn;
     tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
@@ -288,8 +400,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         if (m < M) {
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq)
-            store4<EPI>(Cv, ldc, m, nw + i * 32 + 8 * qq + 4 * lhi, bv[qq], acc[i][j][4 * qq],
-                        acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]);
+            store4<EPI, F8>(Cv, ldc, m, nw + i * 32 + 8 * qq + 4 * lhi, bv[qq], alpha, oscale,
+                            acc[i][j][4 * qq], acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2],
+                            acc[i][j][4 * qq + 3]);
         }
       }
     }
@@ -313,19 +426,19 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const uint4* w = sW[g & 1];
     // phase 1: group 0 computes, group 1 loads W(g+1)
     if (grp == 0) {
-      load(a, w, 0, f0);
-      if (kt == 0) compute(a, w, true);
-      else compute(a, w, false);
+      preload(a, w);
+      if (kt == 0) step(a, w, true);
+      else step(a, w, false);
     } else {
       if (g + 1 < total) issue(g + 1, false);
       if (kt == 0 && r > 0) epilogue(r - 1);
-      load(a, w, 0, f0);
+      preload(a, w);
     }
     wg_barrier();
     // phase 2: group 1 computes, group 0 loads A(g+2)
     if (grp == 1) {
-      if (kt == 0) compute(a, w, true);
-      else compute(a, w, false);
+      if (kt == 0) step(a, w, true);
+      else step(a, w, false);
       wait_vm0();   // W(g+1) landed
     } else {
       // A(g+1), issued a step ago, must have landed before the barrier; wait
@@ -379,11 +492,11 @@ __device__ __forceinline__ void piece_coords(int pid, const PieceMap& pm, int64_
   }
 }
 
-template <Epilogue EPI, bool PARTIAL>
+template <Epilogue EPI, bool PARTIAL, bool F8>
 __global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, float* __restrict__ part,
-    int64_t M, int K, PieceMap pm, int splits) {
+    int64_t M, int K, PieceMap pm, int splits, float alpha, float oscale) {
   constexpr int STG = 2 * PIECE * BKS / 8;   // uint4 per stage (16 KB)
   __shared__ uint4 st0[STG];
   __shared__ uint4 st1[STG];
@@ -471,14 +584,30 @@ __global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
           fa[sl][i] = *reinterpret_cast<const bf16x8*>(&ua);
         }
       }
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
+      if constexpr (F8) {
+        // one 64-code step: the two 16-byte fragments of the bf16 steps
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl][i], fa[sl][j], acc[i][j], 0,
-                                                                0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                __builtin_shufflevector(__builtin_bit_cast(i32x4, fw[0][i]),
+                                        __builtin_bit_cast(i32x4, fw[1][i]), 0, 1, 2, 3, 4, 5, 6,
+                                        7),
+                __builtin_shufflevector(__builtin_bit_cast(i32x4, fa[0][j]),
+                                        __builtin_bit_cast(i32x4, fa[1][j]), 0, 1, 2, 3, 4, 5, 6,
+                                        7),
+                acc[i][j], 0, 0, 0, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl][i], fa[sl][j], acc[i][j],
+                                                                  0, 0, 0);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // loads past the last step land before LDS is released
@@ -511,7 +640,7 @@ __global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
         if (m >= M) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          store4<EPI>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], acc[i][j][4 * q],
+          store4<EPI, F8>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], alpha, oscale, acc[i][j][4 * q],
                       acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
       }
     }
@@ -520,10 +649,10 @@ __global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
 
 // Sum the split partials of each piece (split order 0, 1, ...) and apply the
 // epilogue.  One thread per 4 consecutive columns.
-template <Epilogue EPI>
+template <Epilogue EPI, bool F8>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const float* __restrict__ part, const float* __restrict__ bias, void* __restrict__ Cv,
-    int64_t ldc, int64_t M, PieceMap pm, int splits) {
+    int64_t ldc, int64_t M, PieceMap pm, int splits, float alpha, float oscale) {
   const int pid = blockIdx.y;
   int64_t m0, n0;
   piece_coords(pid, pm, m0, n0);
@@ -538,7 +667,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)k * (PIECE * PIECE));
     s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
   }
-  store4<EPI>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), s.x, s.y, s.z, s.w);
+  store4<EPI, F8>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), alpha, oscale, s.x,
+                  s.y, s.z, s.w);
 }
 
 int g_num_cus = 0;
@@ -570,30 +700,30 @@ int choose_splits(int live_pieces, int grid_pieces, int K, int cus, size_t part_
   return splits;
 }
 
-template <Epilogue EPI>
+template <Epilogue EPI, bool F8>
 hipError_t launch_pieces(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                          const float* bias, void* C, int64_t ldc, int64_t M, int K, float* part,
                          size_t part_bytes, const PieceMap& pm, int live_pieces, int pieces,
-                         int cus, hipStream_t stream) {
+                         int cus, float alpha, float oscale, hipStream_t stream) {
   const int splits = choose_splits(live_pieces, pieces, K, cus, part_bytes);
   if (splits == 1) {
-    gemm_piece_kernel<EPI, false><<<dim3(pieces), dim3(256), 0, stream>>>(
-        A, lda, W, ldw, bias, C, ldc, part, M, K, pm, 1);
+    gemm_piece_kernel<EPI, false, F8><<<dim3(pieces), dim3(256), 0, stream>>>(
+        A, lda, W, ldw, bias, C, ldc, part, M, K, pm, 1, alpha, oscale);
     return hipGetLastError();
   }
-  gemm_piece_kernel<EPI, true><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
-      A, lda, W, ldw, bias, C, ldc, part, M, K, pm, splits);
+  gemm_piece_kernel<EPI, true, F8><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
+      A, lda, W, ldw, bias, C, ldc, part, M, K, pm, splits, alpha, oscale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  splitk_reduce_kernel<EPI><<<dim3(PIECE * PIECE / 1024, pieces), dim3(256), 0, stream>>>(
-      part, bias, C, ldc, M, pm, splits);
+  splitk_reduce_kernel<EPI, F8><<<dim3(PIECE * PIECE / 1024, pieces), dim3(256), 0, stream>>>(
+      part, bias, C, ldc, M, pm, splits, alpha, oscale);
   return hipGetLastError();
 }
 
-template <Epilogue EPI>
+template <Epilogue EPI, bool F8>
 hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, const float* bias,
                     void* C, int64_t ldc, int64_t M, int N, int K, float* part,
-                    size_t part_bytes, hipStream_t stream) {
+                    size_t part_bytes, float alpha, float oscale, hipStream_t stream) {
   const int tiles_m = (int)((M + BIG - 1) / BIG);
   const int tiles_n = N / BIG;
   const int tiles = tiles_m * tiles_n;
@@ -604,38 +734,64 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
     const int live = (int)((M + PIECE - 1) / PIECE) * (N / PIECE);
     // piece ids cover whole big-tile rows; ids past M return at once
     const int grid_pieces = ((tiles_m * BIG) / PIECE) * (N / PIECE);
-    return launch_pieces<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm, live,
-                              grid_pieces, cus, stream);
+    return launch_pieces<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm, live,
+                                  grid_pieces, cus, alpha, oscale, stream);
   }
   // Full rounds go to the persistent kernel, the remainder to 128 x 128 pieces.
   const int n_big = (tiles / cus) * cus;
-  gemm_big_kernel<EPI><<<dim3(cus), dim3(512), 0, stream>>>(A, lda, W, ldw, bias, C, ldc, M, K,
-                                                            tiles_m, tiles_n, n_big);
+  gemm_big_kernel<EPI, F8><<<dim3(cus), dim3(512), 0, stream>>>(
+      A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big, alpha, oscale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tiles == n_big) return e;
   PieceMap pm{0, n_big, tiles_m, tiles_n, N / PIECE};
-  return launch_pieces<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm,
-                            4 * (tiles - n_big), 4 * (tiles - n_big), cus, stream);
+  return launch_pieces<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm,
+                                4 * (tiles - n_big), 4 * (tiles - n_big), cus, alpha, oscale,
+                                stream);
 }
 
+template <bool F8>
 hipError_t launch_cols(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
-                       float* part, size_t part_bytes, hipStream_t stream) {
+                       float* part, size_t part_bytes, float alpha, float oscale,
+                       hipStream_t stream) {
   switch (epi) {
     case Epilogue::kBiasBf16:
-      return launch_t<Epilogue::kBiasBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes,
-                                           stream);
+      return launch_t<Epilogue::kBiasBf16, F8>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
+                                               part_bytes, alpha, oscale, stream);
     case Epilogue::kBiasGeluBf16:
-      return launch_t<Epilogue::kBiasGeluBf16>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
-                                               part_bytes, stream);
+      return launch_t<Epilogue::kBiasGeluBf16, F8>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
+                                                   part_bytes, alpha, oscale, stream);
     case Epilogue::kBiasResidualF32:
-      return launch_t<Epilogue::kBiasResidualF32>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
-                                                  part_bytes, stream);
+      return launch_t<Epilogue::kBiasResidualF32, F8>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
+                                                      part_bytes, alpha, oscale, stream);
     case Epilogue::kBiasF32:
-      return launch_t<Epilogue::kBiasF32>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes,
-                                          stream);
+      return launch_t<Epilogue::kBiasF32, F8>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
+                                              part_bytes, alpha, oscale, stream);
+    case Epilogue::kBiasGeluFp8:
+      if constexpr (F8)
+        return launch_t<Epilogue::kBiasGeluFp8, true>(A, lda, W, ldw, bias, C, ldc, M, N, K, part,
+                                                      part_bytes, alpha, oscale, stream);
+      break;
   }
   return hipErrorInvalidValue;
+}
+
+// Whole 256-column tiles first; a last strip of 128 columns (N % 256 == 128)
+// is a product of its own on the piece kernel.  c_elem: bytes per C element.
+template <bool F8>
+hipError_t launch_split_n(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W,
+                          int64_t ldw, const float* bias, void* C, int64_t ldc, int64_t M, int N,
+                          int K, float* part, size_t part_bytes, float alpha, float oscale,
+                          size_t c_elem, hipStream_t stream) {
+  const int n_main = N / BIG * BIG;
+  hipError_t e = hipSuccess;
+  if (n_main > 0)
+    e = launch_cols<F8>(epi, A, lda, W, ldw, bias, C, ldc, M, n_main, K, part, part_bytes, alpha,
+                        oscale, stream);
+  if (e != hipSuccess || n_main == N) return e;
+  return launch_cols<F8>(epi, A, lda, W + (int64_t)n_main * ldw, ldw, bias + n_main,
+                         (char*)C + (size_t)n_main * c_elem, ldc, M, N - n_main, K, part,
+                         part_bytes, alpha, oscale, stream);
 }
 
 }  // namespace
@@ -644,18 +800,27 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t*
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                        float* part, size_t part_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (N <= 0 || N % PIECE != 0 || K % (BKS * 8) != 0) return hipErrorInvalidValue;
-  // Whole 256-column tiles first; a last strip of 128 columns (N % 256 == 128)
-  // is a product of its own on the piece kernel.
-  const int n_main = N / BIG * BIG;
-  hipError_t e = hipSuccess;
-  if (n_main > 0) e = launch_cols(epi, A, lda, W, ldw, bias, C, ldc, M, n_main, K, part, part_bytes,
-                                  stream);
-  if (e != hipSuccess || n_main == N) return e;
+  if (N <= 0 || N % PIECE != 0 || K % (BKS * 8) != 0 || epi == Epilogue::kBiasGeluFp8)
+    return hipErrorInvalidValue;
   const size_t c_elem = (epi == Epilogue::kBiasBf16 || epi == Epilogue::kBiasGeluBf16) ? 2 : 4;
-  return launch_cols(epi, A, lda, W + (int64_t)n_main * ldw, ldw, bias + n_main,
-                     (char*)C + (size_t)n_main * c_elem, ldc, M, N - n_main, K, part, part_bytes,
-                     stream);
+  return launch_split_n<false>(epi, A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes, 1.0f,
+                               1.0f, c_elem, stream);
+}
+
+hipError_t launch_gemm_fp8(Epilogue epi, const uint8_t* A, int64_t lda, const uint8_t* W,
+                           int64_t ldw, float alpha, float out_scale, const float* bias, void* C,
+                           int64_t ldc, int64_t M, int N, int K, float* part, size_t part_bytes,
+                           hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  // Codes are moved as pairs (bf16-sized units): K / 2 must be a multiple of
+  // the piece kernel's split unit (BKS * PNS) and the strides even.
+  if (N <= 0 || N % PIECE != 0 || K % (2 * BKS * PNS) != 0 || (lda & 1) || (ldw & 1) ||
+      epi == Epilogue::kBiasGeluBf16)
+    return hipErrorInvalidValue;
+  const size_t c_elem = epi == Epilogue::kBiasGeluFp8 ? 1 : epi == Epilogue::kBiasBf16 ? 2 : 4;
+  return launch_split_n<true>(epi, reinterpret_cast<const bf16_t*>(A), lda / 2,
+                              reinterpret_cast<const bf16_t*>(W), ldw / 2, bias, C, ldc, M, N,
+                              K / 2, part, part_bytes, alpha, out_scale, c_elem, stream);
 }
 
 }  // namespace enc

@@ -51,6 +51,7 @@ enum class Epilogue {
   kBiasGeluBf16,      // C (bf16)  = gelu(acc + bias)
   kBiasResidualF32,   // C (fp32) += acc + bias
   kBiasF32,           // C (fp32)  = acc + bias
+  kBiasGeluFp8,       // C (E4M3)  = q(gelu(acc + bias) * out_scale)   (FP8 path only)
 };
 
 constexpr size_t GEMM_PARTIAL_BYTES = (size_t)2 * 512 * 128 * 128 * sizeof(float);
@@ -63,6 +64,18 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t*
 // y[r, :] = LN(x[r, :]) * g + b over d = 1280, fp32 statistics, bf16 output.
 hipError_t launch_layernorm(const float* x, const float* g, const float* b, bf16_t* y,
                             int64_t rows, hipStream_t stream);
+// The same with E4M3 output: y8[r, :] = q(LN(x[r, :]) * g + b) * out_scale).
+hipError_t launch_layernorm_fp8(const float* x, const float* g, const float* b, float out_scale,
+                                uint8_t* y8, int64_t rows, hipStream_t stream);
+
+// amax[slot] = max(amax[slot], max |x|) over n bf16 values (n % 8 == 0);
+// amax holds non-negative floats, so their bit patterns order as integers.
+hipError_t launch_amax_bf16(const bf16_t* x, int64_t n, float* amax, hipStream_t stream);
+// Per-tensor E4M3 quantization of a bf16 matrix: s = amax / 448 (1 if amax is
+// 0) is read from *amax and written to *scale; q = e4m3(sat(w * (1 / s))).
+hipError_t launch_quantize_fp8(const bf16_t* w, int64_t n, const float* amax, float* scale,
+                               uint8_t* q, hipStream_t stream);
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
 
 // In place on qkv [rows, 3840] bf16, per attention tile (clip tile_seq[i],
 // positions tile_p0[i] .. +127) and head: q <- RoPE(LN_q(q)),
@@ -83,6 +96,16 @@ hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t*
 hipError_t launch_final_norm(const float* x, const float* g, const float* b, const int32_t* cu_seq,
                              const int32_t* src_rows, int batch, int64_t p_max, bf16_t* out,
                              hipStream_t stream);
+
+// FP8 variant: A [M, K] and W [N, K] hold E4M3 codes (row strides lda, ldw in
+// bytes, both even; K % 128 == 0, N % 128 == 0); C (op)= acc * alpha + bias
+// with the epilogues above (kBiasGeluFp8 writes E4M3 codes of
+// gelu(.) * out_scale, saturated at +-448); ldc counts elements of C (bytes
+// for E4M3 output).
+hipError_t launch_gemm_fp8(Epilogue epi, const uint8_t* A, int64_t lda, const uint8_t* W,
+                           int64_t ldw, float alpha, float out_scale, const float* bias, void* C,
+                           int64_t ldc, int64_t M, int N, int K, float* part, size_t part_bytes,
+                           hipStream_t stream);
 
 // Speaker fusion into the connector's operand: out[r, :] (bf16, [rows, 1280])
 // = LN_f(x[s, :]) + sum_j n_j spk_tab[j, :] with s = src_rows ? src_rows[r] : r
@@ -109,14 +132,16 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
 // 1280-column groups of qkv [rows, 3840]; v comes transposed from vt (clip b
 // at columns vt_base[b]..., zero past P_b up to a multiple of 64).  Work tile
 // i covers queries [tile_q0[i], min(tile_q0[i] + 128, P_b)) of clip
-// tile_seq[i].  out is bf16 [rows, 1280] with head h in columns h*128...
+// tile_seq[i].  out is bf16 [rows, 1280] with head h in columns h*128..., or,
+// when out_scale > 0, E4M3 codes of the output times out_scale (saturated at
+// +-448), one byte per element in the same layout.
 // qkv must have 63 readable rows after its last one (their k is masked), and
 // vt's columns hold keys permuted inside each group of 16 as written by
 // launch_qknorm_rope.
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
-                            const int32_t* tile_q0, int n_tiles, bool fixed_ref, bf16_t* out,
-                            hipStream_t stream);
+                            const int32_t* tile_q0, int n_tiles, bool fixed_ref, void* out,
+                            float out_scale, hipStream_t stream);
 // fixed_ref may be true only when |q . k| * log2(e) / sqrt(128) <= 100 for
 // every query and key (softmax against a fixed reference instead of a
 // running maximum); attention_fixed_ref_ok decides it from the QK-norm

@@ -13,6 +13,8 @@
 // All of these are HBM-bound: one wavefront per row (or per row and head),
 // statistics in fp32 registers with wavefront shuffles, vector loads/stores.
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -69,6 +71,80 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
     *reinterpret_cast<uint2*>(y + r * D + c) =
         make_uint2(pack_bf16x2(o[i].x, o[i].y), pack_bf16x2(o[i].z, o[i].w));
   }
+}
+
+// LayerNorm with E4M3 output (the FP8 linear maps' input): codes of
+// LN(x) * g + b times out_scale, saturated at +-448.
+__global__ __launch_bounds__(256) void layernorm_fp8_kernel(const float* __restrict__ x,
+                                                            const float* __restrict__ g,
+                                                            const float* __restrict__ b,
+                                                            float out_scale,
+                                                            uint8_t* __restrict__ y8,
+                                                            int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float4 o[5];
+  ln_row_1280(x + r * D, g, b, lane, o);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int c = (i * 64 + lane) * 4;
+    *reinterpret_cast<uint32_t*>(y8 + r * D + c) =
+        pack_fp8x4(o[i].x * out_scale, o[i].y * out_scale, o[i].z * out_scale,
+                   o[i].w * out_scale);
+  }
+}
+
+// Largest magnitude of a bf16 tensor, merged into *amax (calibration).
+__global__ __launch_bounds__(256) void amax_bf16_kernel(const bf16_t* __restrict__ x, int64_t n8,
+                                                        float* __restrict__ amax) {
+  __shared__ float part[4];
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      m = fmaxf(m, fabsf(__uint_as_float(w[k] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(w[k] & 0xffff0000u)));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
+  }
+}
+
+// Per-tensor E4M3 codes of a bf16 matrix under s = amax / 448.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const bf16_t* __restrict__ w,
+                                                           int64_t n8,
+                                                           const float* __restrict__ amax,
+                                                           float* __restrict__ scale,
+                                                           uint8_t* __restrict__ q) {
+  const float a = *amax;
+  const float s = a > 0.0f ? a / E4M3_MAX : 1.0f;
+  const float r = 1.0f / s;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i == 0) *scale = s;
+  if (i >= n8) return;
+  const uint4 v = reinterpret_cast<const uint4*>(w)[i];
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    out[k] = pack_fp8x4(__uint_as_float(u[2 * k] << 16) * r,
+                        __uint_as_float(u[2 * k] & 0xffff0000u) * r,
+                        __uint_as_float(u[2 * k + 1] << 16) * r,
+                        __uint_as_float(u[2 * k + 1] & 0xffff0000u) * r);
+  reinterpret_cast<uint2*>(q)[i] = make_uint2(out[0], out[1]);
+}
+
+__global__ void fill_f32_kernel(float* __restrict__ p, float v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
 }
 
 __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict__ x,
@@ -380,6 +456,38 @@ hipError_t launch_layernorm(const float* x, const float* g, const float* b, bf16
                             int64_t rows, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   layernorm_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(x, g, b, y, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_layernorm_fp8(const float* x, const float* g, const float* b, float out_scale,
+                                uint8_t* y8, int64_t rows, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  layernorm_fp8_kernel<<<dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream>>>(
+      x, g, b, out_scale, y8, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16(const bf16_t* x, int64_t n, float* amax, hipStream_t stream) {
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  if (n == 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  const unsigned grid = (unsigned)std::min<int64_t>((n8 + 255) / 256, 2048);
+  amax_bf16_kernel<<<dim3(grid), dim3(256), 0, stream>>>(x, n8, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const bf16_t* w, int64_t n, const float* amax, float* scale,
+                               uint8_t* q, hipStream_t stream) {
+  if (n % 8 != 0 || n == 0) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  quantize_fp8_kernel<<<dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream>>>(w, n8, amax,
+                                                                                   scale, q);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  fill_f32_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(p, v, n);
   return hipGetLastError();
 }
 

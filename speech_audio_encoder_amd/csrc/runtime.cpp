@@ -242,6 +242,13 @@ struct LayerW {
   bf16_t *w_qkv, *w_o, *w_up, *w_down;
   float *ln1_g, *ln1_b, *b_qkv, *q_g, *q_b, *k_g, *k_b, *b_o, *ln2_g, *ln2_b, *b_up, *b_down;
   bool attn_fixed_ref;   // QK-norm bounds the scores: softmax without a running maximum
+  // FP8 variant: E4M3 codes of the four matrices (QKV, O, up, down), their
+  // scales, the input scales and the derived GEMM factors.
+  uint8_t* q8[4] = {nullptr, nullptr, nullptr, nullptr};
+  float s_w[4] = {1, 1, 1, 1};
+  float s_x[4] = {1, 1, 1, 1};
+  float alpha[4] = {1, 1, 1, 1};   // fp32(s_x * s_w)
+  float r_x[4] = {1, 1, 1, 1};     // fp32(1 / s_x): scale of the producer's codes
 };
 
 }  // namespace
@@ -274,6 +281,11 @@ struct enc_ctx {
   bf16_t* w_conn = nullptr;
   float *b_conn = nullptr, *spk_g = nullptr, *spk_b = nullptr, *spk_tab = nullptr;
   int conn_dim = 0;
+  // Precision of the layers' linear maps (enc_set_precision).
+  int precision = ENC_PREC_BF16;
+  void* fp8_mem = nullptr;   // E4M3 weight codes (all layers)
+  float* amax_dev = nullptr; // [n_layers * 4] calibration / weight amax slots
+  float* scale_dev = nullptr;
   int prof_kernel = -1;
   std::vector<hipEvent_t> prof_events;   // pairs
   size_t prof_used = 0;
@@ -293,6 +305,8 @@ void release(enc_ctx* c) {
   (void)hipFree(c->ws);
   (void)hipFree(c->plan_dev);
   (void)hipFree(c->conn_mem);
+  (void)hipFree(c->fp8_mem);
+  (void)hipFree(c->amax_dev);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
   if (c->plan_copied) (void)hipEventDestroy(c->plan_copied);
   for (hipEvent_t e : c->prof_events) (void)hipEventDestroy(e);
@@ -388,6 +402,8 @@ struct ProfScope {
     c->prof_used = idx + 2;
   }
 };
+
+constexpr int K_UNTIMED = 1 << 20;   // launches no kernel class brackets (calibration)
 
 #define ENC_LAUNCH(id, call)                                  \
   do {                                                        \
@@ -579,9 +595,67 @@ namespace {
 // The encoder on a batch, then either the final norm into the padded
 // embedding layout (fused == false) or speaker fusion and the connector into
 // clip-packed language-model rows (fused == true).
+int ensure_amax(enc_ctx* c) {
+  if (c->amax_dev) return ENC_OK;
+  // amax and scale slots: 4 per layer each
+  if (hipMalloc((void**)&c->amax_dev, (size_t)c->n_layers * 8 * sizeof(float)) != hipSuccess) {
+    c->amax_dev = nullptr;
+    (void)hipGetLastError();
+    return fail(ENC_ERR_NOMEM, "amax slot allocation failed");
+  }
+  c->scale_dev = c->amax_dev + (size_t)c->n_layers * 4;
+  return ENC_OK;
+}
+
+// E4M3 codes of every layer's four matrices from the context's bf16 copies:
+// per matrix, amax -> s_w = amax / 448 -> codes of w / s_w (synchronous).
+int prepare_fp8_weights(enc_ctx* c) {
+  int rc = ensure_amax(c);
+  if (rc != ENC_OK) return rc;
+  const size_t per_layer = (size_t)3 * D * D + (size_t)D * D + 2 * (size_t)FF * D;
+  void* mem = nullptr;
+  if (hipMalloc(&mem, per_layer * c->n_layers) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(ENC_ERR_NOMEM, "fp8 weight allocation failed");
+  }
+  const int64_t sizes[4] = {(int64_t)3 * D * D, (int64_t)D * D, (int64_t)FF * D, (int64_t)D * FF};
+  hipError_t e = launch_fill_f32(c->amax_dev, 0.0f, (int64_t)c->n_layers * 4, nullptr);
+  uint8_t* q = (uint8_t*)mem;
+  for (int li = 0; li < c->n_layers && e == hipSuccess; ++li) {
+    LayerW& L = c->layers[li];
+    const bf16_t* src[4] = {L.w_qkv, L.w_o, L.w_up, L.w_down};
+    for (int k = 0; k < 4 && e == hipSuccess; ++k) {
+      float* am = c->amax_dev + 4 * li + k;
+      if ((e = launch_amax_bf16(src[k], sizes[k], am, nullptr)) != hipSuccess) break;
+      e = launch_quantize_fp8(src[k], sizes[k], am, c->scale_dev + 4 * li + k, q, nullptr);
+      L.q8[k] = q;
+      q += sizes[k];
+    }
+  }
+  std::vector<float> sw((size_t)c->n_layers * 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess)
+    e = hipMemcpy(sw.data(), c->scale_dev, sw.size() * sizeof(float), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) {
+    (void)hipFree(mem);
+    for (LayerW& L : c->layers)
+      for (int k = 0; k < 4; ++k) L.q8[k] = nullptr;
+    return hip_fail(e, "fp8 weight quantization");
+  }
+  for (int li = 0; li < c->n_layers; ++li)
+    for (int k = 0; k < 4; ++k) c->layers[li].s_w[k] = sw[4 * li + k];
+  c->fp8_mem = mem;
+  return ENC_OK;
+}
+
+enum class Tail { kEmbeddings, kFused, kCalibrate };
+
 int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
-                void* out, const float* activity, bool fused, hipStream_t stream) {
+                void* out, const float* activity, Tail tail, hipStream_t stream) {
   if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  const bool fused = tail == Tail::kFused;
+  const bool calib = tail == Tail::kCalibrate;
+  const bool fp8 = ctx->precision == ENC_PREC_FP8 && !calib;
   Plan p;
   int rc = make_plan(lengths, batch, &p, true, ctx->scope);
   if (rc != ENC_OK) return rc;
@@ -592,7 +666,7 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
     if (ctx->conn_dim == 0) return fail(ENC_ERR_ARG, "no connector weights (enc_set_connector)");
     if (p.rows > 0 && !activity) return fail(ENC_ERR_ARG, "activity is NULL");
     if (p.rows > 0 && !out) return fail(ENC_ERR_ARG, "out is NULL");
-  } else if (p.p_max > 0 && !out) {
+  } else if (!calib && p.p_max > 0 && !out) {
     return fail(ENC_ERR_ARG, "out_embeddings is NULL");
   }
   if ((rc = check_device(ctx)) != ENC_OK) return rc;
@@ -662,25 +736,61 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   }
   ENC_LAUNCH(ENC_K_GEMM_IN, launch_gemm(Epilogue::kBiasF32, stk, DIN, ctx->w_in, DIN, ctx->b_in, x,
                                         D, R, D, DIN, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+  uint8_t* a8 = (uint8_t*)a;   // E4M3 operands of the FP8 path reuse the bf16 buffers
+  uint8_t* o8 = (uint8_t*)o;
+  uint8_t* u8 = (uint8_t*)u;
+  float* amax = ctx->amax_dev;
   for (int li = 0; li < ctx->n_layers; ++li) {
     const LayerW& Lw = ctx->layers[li];
-    ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln1_g, Lw.ln1_b, a, R, stream));
-    ENC_LAUNCH(ENC_K_GEMM_QKV, launch_gemm(Epilogue::kBiasBf16, a, D, Lw.w_qkv, D, Lw.b_qkv, qkv,
-                                           3 * D, R, 3 * D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+    if (fp8) {
+      ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm_fp8(x, Lw.ln1_g, Lw.ln1_b, Lw.r_x[0], a8, R,
+                                                       stream));
+      ENC_LAUNCH(ENC_K_GEMM_QKV,
+                 launch_gemm_fp8(Epilogue::kBiasBf16, a8, D, Lw.q8[0], D, Lw.alpha[0], 0.0f,
+                                 Lw.b_qkv, qkv, 3 * D, R, 3 * D, D, ctx->gemm_part,
+                                 GEMM_PARTIAL_BYTES, stream));
+    } else {
+      ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln1_g, Lw.ln1_b, a, R, stream));
+      if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(a, R * D, amax + 4 * li + 0, stream));
+      ENC_LAUNCH(ENC_K_GEMM_QKV, launch_gemm(Epilogue::kBiasBf16, a, D, Lw.w_qkv, D, Lw.b_qkv,
+                                             qkv, 3 * D, R, 3 * D, D, ctx->gemm_part,
+                                             GEMM_PARTIAL_BYTES, stream));
+    }
     ENC_LAUNCH(ENC_K_QKNORM_ROPE,
                launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, Lw.q_g, Lw.q_b, Lw.k_g,
                                   Lw.k_b, ctx->rope_cos, ctx->rope_sin, vt, lay.ld_vt, stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
                launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles,
-                                Lw.attn_fixed_ref, o, stream));
+                                Lw.attn_fixed_ref, o, fp8 ? Lw.r_x[1] : 0.0f, stream));
+    if (fp8) {
+      ENC_LAUNCH(ENC_K_GEMM_O,
+                 launch_gemm_fp8(Epilogue::kBiasResidualF32, o8, D, Lw.q8[1], D, Lw.alpha[1],
+                                 0.0f, Lw.b_o, x, D, R, D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES,
+                                 stream));
+      ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm_fp8(x, Lw.ln2_g, Lw.ln2_b, Lw.r_x[2], a8, R,
+                                                       stream));
+      ENC_LAUNCH(ENC_K_GEMM_UP,
+                 launch_gemm_fp8(Epilogue::kBiasGeluFp8, a8, D, Lw.q8[2], D, Lw.alpha[2],
+                                 Lw.r_x[3], Lw.b_up, u8, FF, R, FF, D, ctx->gemm_part,
+                                 GEMM_PARTIAL_BYTES, stream));
+      ENC_LAUNCH(ENC_K_GEMM_DOWN,
+                 launch_gemm_fp8(Epilogue::kBiasResidualF32, u8, FF, Lw.q8[3], FF, Lw.alpha[3],
+                                 0.0f, Lw.b_down, x, D, R, D, FF, ctx->gemm_part,
+                                 GEMM_PARTIAL_BYTES, stream));
+      continue;
+    }
+    if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(o, R * D, amax + 4 * li + 1, stream));
     ENC_LAUNCH(ENC_K_GEMM_O, launch_gemm(Epilogue::kBiasResidualF32, o, D, Lw.w_o, D, Lw.b_o, x,
                                          D, R, D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln2_g, Lw.ln2_b, a, R, stream));
+    if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(a, R * D, amax + 4 * li + 2, stream));
     ENC_LAUNCH(ENC_K_GEMM_UP, launch_gemm(Epilogue::kBiasGeluBf16, a, D, Lw.w_up, D, Lw.b_up, u,
                                           FF, R, FF, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+    if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(u, R * FF, amax + 4 * li + 3, stream));
     ENC_LAUNCH(ENC_K_GEMM_DOWN, launch_gemm(Epilogue::kBiasResidualF32, u, FF, Lw.w_down, FF,
                                             Lw.b_down, x, D, R, D, FF, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
   }
+  if (calib) return ENC_OK;
   if (!fused) {
     ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_clip, d_outsrc,
                                                    batch, p.p_max, (bf16_t*)out, stream));
@@ -701,12 +811,60 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
 
 int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                 void* out_embeddings, hipStream_t stream) {
-  return run_forward(ctx, audio, lengths, batch, out_embeddings, nullptr, false, stream);
+  return run_forward(ctx, audio, lengths, batch, out_embeddings, nullptr, Tail::kEmbeddings,
+                     stream);
 }
 
 int enc_forward_fused(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                       const float* activity, void* out, hipStream_t stream) {
-  return run_forward(ctx, audio, lengths, batch, out, activity, true, stream);
+  return run_forward(ctx, audio, lengths, batch, out, activity, Tail::kFused, stream);
+}
+
+int enc_calibrate(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                  float* amax_out, hipStream_t stream) {
+  if (!ctx || !amax_out) return fail(ENC_ERR_ARG, "NULL argument");
+  int rc = check_device(ctx);
+  if (rc != ENC_OK) return rc;
+  if ((rc = ensure_amax(ctx)) != ENC_OK) return rc;
+  const int64_t n = (int64_t)ctx->n_layers * 4;
+  // Slots start at 0 (a fill kernel, so that the call can sit in a captured graph).
+  hipError_t e = launch_fill_f32(ctx->amax_dev, 0.0f, n, stream);
+  if (e != hipSuccess) return hip_fail(e, "amax fill");
+  rc = run_forward(ctx, audio, lengths, batch, nullptr, nullptr, Tail::kCalibrate, stream);
+  if (rc != ENC_OK) return rc;
+  if ((e = hipMemcpyAsync(amax_out, ctx->amax_dev, n * sizeof(float), hipMemcpyDeviceToHost,
+                          stream)) != hipSuccess ||
+      (e = hipStreamSynchronize(stream)) != hipSuccess)
+    return hip_fail(e, "amax copy");
+  return ENC_OK;
+}
+
+int enc_set_precision(enc_ctx* ctx, int32_t precision, const float* input_scales) {
+  if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  if (precision == ENC_PREC_BF16) {
+    ctx->precision = ENC_PREC_BF16;
+    return ENC_OK;
+  }
+  if (precision != ENC_PREC_FP8) return fail(ENC_ERR_ARG, "unknown precision");
+  if (!input_scales) return fail(ENC_ERR_ARG, "input_scales is NULL");
+  for (int i = 0; i < ctx->n_layers * 4; ++i)
+    if (!(input_scales[i] > 0.0f) || !std::isfinite(input_scales[i]) ||
+        !std::isfinite(1.0f / input_scales[i]))
+      return fail(ENC_ERR_ARG, "input_scales[" + std::to_string(i) + "] is not a positive "
+                               "finite scale");
+  int rc = check_device(ctx);
+  if (rc != ENC_OK) return rc;
+  if (!ctx->fp8_mem && (rc = prepare_fp8_weights(ctx)) != ENC_OK) return rc;
+  for (int li = 0; li < ctx->n_layers; ++li) {
+    LayerW& L = ctx->layers[li];
+    for (int k = 0; k < 4; ++k) {
+      L.s_x[k] = input_scales[4 * li + k];
+      L.alpha[k] = L.s_x[k] * L.s_w[k];
+      L.r_x[k] = 1.0f / L.s_x[k];
+    }
+  }
+  ctx->precision = ENC_PREC_FP8;
+  return ENC_OK;
 }
 
 int enc_set_connector(enc_ctx* ctx, const enc_connector_weights* w) {

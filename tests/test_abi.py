@@ -90,6 +90,8 @@ def test_null_context_is_rejected(lib):
     assert lib.enc_logmel(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
     assert lib.enc_set_attention(None, binding.ENC_ATTN_WINDOWS, 500, 50) == binding.ENC_ERR_ARG
     assert lib.enc_set_connector(None, None) == binding.ENC_ERR_ARG
+    assert lib.enc_set_precision(None, binding.ENC_PREC_BF16, None) == binding.ENC_ERR_ARG
+    assert lib.enc_calibrate(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
     assert lib.enc_forward_fused(None, None, arr, 1, None, None, None) == binding.ENC_ERR_ARG
     lib.enc_destroy(None)   # no-op
 

@@ -116,13 +116,17 @@ def check_logmel(got, audio, lengths):
     return worst
 
 
-def check_embeddings(got, ref, label):
+def check_embeddings(got, ref, label, tol=EMB_REL_TOL, mean_tol=None):
     got = np.asarray(got, dtype=np.float32)
     err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    mean = float(np.abs(got - ref).mean()) if ref.size else 0.0
     scale = float(np.abs(ref).max()) if ref.size else 1.0
-    say(f"{label}: max abs err {err:.4e}, max |ref| {scale:.3f}, ratio {err / scale:.3e}")
+    say(f"{label}: max abs err {err:.4e}, max |ref| {scale:.3f}, ratio {err / scale:.3e}, "
+        f"mean ratio {mean / scale:.3e}")
     assert np.all(np.isfinite(got))
-    assert err <= EMB_REL_TOL * scale, f"{label}: {err:.3e} > {EMB_REL_TOL} * {scale:.3f}"
+    assert err <= tol * scale, f"{label}: {err:.3e} > {tol} * {scale:.3f}"
+    if mean_tol is not None:
+        assert mean <= mean_tol * scale, f"{label}: mean {mean:.3e} > {mean_tol} * {scale:.3f}"
 
 
 # ------------------------------------------------------------------ log-mel
@@ -548,5 +552,130 @@ def test_forward_fused_errors(torch_mod, binding_mod):
         empty = run_fused(torch, enc, np.zeros((2, 399), np.float32), [10, 399],
                           [np.zeros((0, 8), np.float32)] * 2)
         assert empty.shape == (0, 128)
+    finally:
+        enc.close()
+
+
+# ------------------------------------------------------------- FP8 variant
+# Input amax per linear map (QKV, O, up, down) used as fixed test scales on
+# both sides: a little above what calibration of these random weights finds
+# (4.9, 3.2, 4.9, 3.6), so that few inputs saturate.
+FP8_AMAX = np.array([5.0, 3.5, 5.0, 4.0], np.float32)
+
+
+def fp8_tolerance(n_layers):
+    """(max, mean) bounds relative to max|oracle| for the FP8 path at this
+    depth: twice the largest move of the FP8 oracle itself under log-mel
+    changes of +-1e-4 (tests/golden/fp8_spread.txt, written by
+    fp8_spread.py there from the oracle alone).  E4M3 codes are rounding
+    decisions, so upstream differences of rounding size flip some of them and
+    the flips propagate; the two sides can agree only up to that spread."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fp8_spread.txt")
+    rows = np.loadtxt(path, comments="#", ndmin=2)
+    sel = rows[rows[:, 0] == n_layers]
+    assert len(sel), f"no FP8 spread recorded for {n_layers} layers"
+    return 2.0 * float(sel[:, 1].max()), 2.0 * float(sel[:, 2].max())
+
+
+def fp8_scales(n_layers):
+    return np.tile(FP8_AMAX / np.float32(448.0), (n_layers, 1)).astype(np.float32)
+
+
+def test_forward_fp8_ragged(torch_mod, binding_mod):
+    from oracle import fp8
+    torch = torch_mod
+    w = get_weights("perturbed")
+    lengths = [700_000, 33_000, 16_400, 400, 0]
+    audio, lengths = workloads.custom_audio(lengths, seed=97)
+    scales = fp8_scales(2)
+    enc = binding_mod.Encoder(w, dtype="f32")
+    try:
+        bf = run_forward(torch, enc, audio, lengths)
+        enc.set_precision("fp8", scales)
+        got = run_forward(torch, enc, audio, lengths)
+        np.testing.assert_array_equal(got, run_forward(torch, enc, audio, lengths))
+        enc.set_precision("bf16")
+        bf2 = run_forward(torch, enc, audio, lengths)
+    finally:
+        enc.close()
+    np.testing.assert_array_equal(bf, bf2)          # switching back restores bf16 exactly
+    qw = fp8.prepare_fp8(w)
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        assert np.all(got[b, p:] == 0.0)
+        if p:
+            ref = fp8.encode_fp8(audio[b, :n], w, scales, qw=qw)
+            check_embeddings(got[b, :p], ref, f"fp8 clip {b} (P={p})", *fp8_tolerance(2))
+            q_vs_bf = float(np.abs(got[b, :p] - bf[b, :p]).max() / np.abs(ref).max())
+            say(f"fp8 vs bf16 GPU clip {b}: {q_vs_bf:.3e}")
+            assert q_vs_bf > 0.0
+
+
+def test_forward_fp8_batch64_full_depth(torch_mod, binding_mod):
+    from oracle import fp8
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("batch64")
+    w = get_weights("bf16")
+    scales = fp8_scales(32)
+    enc = binding_mod.Encoder(w, dtype="bf16")
+    try:
+        enc.set_precision("fp8", scales)
+        got = run_forward(torch, enc, audio, lengths)
+    finally:
+        enc.close()
+    assert np.all(np.isfinite(got))
+    for b in (int(np.argmin(lengths)), 42):
+        p = oracle.position_count(oracle.frame_count(lengths[b]))
+        say(f"oracle fp8 batch64 clip {b}")
+        ref = fp8.encode_fp8(audio[b, :lengths[b]], w, scales)
+        check_embeddings(got[b, :p], ref, f"fp8 batch64 clip {b}", *fp8_tolerance(32))
+
+
+def test_calibrate_matches_oracle(torch_mod, binding_mod):
+    from oracle import fp8
+    torch = torch_mod
+    w = get_weights("perturbed")
+    audio, lengths = workloads.custom_audio([700_000, 33_000, 16_400, 0], seed=61)
+    enc = binding_mod.Encoder(w, dtype="f32")
+    try:
+        enc.set_attention(200, 20)     # calibration follows the attention scope
+        amax_w = enc.calibrate(to_dev(torch, audio), lengths)
+        enc.set_attention(None)
+        amax = enc.calibrate(to_dev(torch, audio), lengths)
+        again = enc.calibrate(to_dev(torch, audio), lengths)
+    finally:
+        enc.close()
+    np.testing.assert_array_equal(amax, again)
+    ref = fp8.calibrate([audio[b, :n] for b, n in enumerate(lengths)], w)
+    rel = np.abs(amax - ref) / ref
+    say(f"calibration amax rel diff max {rel.max():.3e}")
+    assert amax.shape == (2, 4) and rel.max() < 2e-2
+    # windows are independent inputs: the oracle calibrated on each window's
+    # own samples
+    segs = []
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        for c0 in range(0, p, 200):
+            segs.append(window_segment(audio[b, :n], max(0, c0 - 20), min(p, c0 + 220)))
+    ref_w = fp8.calibrate(segs, w)
+    rel_w = np.abs(amax_w - ref_w) / ref_w
+    say(f"windowed calibration amax rel diff max {rel_w.max():.3e}")
+    assert rel_w.max() < 2e-2
+
+
+def test_fp8_errors(torch_mod, binding_mod):
+    enc = binding_mod.Encoder(prefix(get_weights("tiny"), 2), dtype="f32")
+    try:
+        with pytest.raises(binding_mod.EncoderError):
+            binding_mod.enc_set_precision(enc.ctx, binding_mod.ENC_PREC_FP8, None)
+        bad = fp8_scales(2)
+        bad[1, 2] = -1.0
+        with pytest.raises(binding_mod.EncoderError):
+            enc.set_precision("fp8", bad)
+        bad[1, 2] = np.inf
+        with pytest.raises(binding_mod.EncoderError):
+            enc.set_precision("fp8", bad)
+        with pytest.raises(binding_mod.EncoderError):
+            binding_mod.enc_set_precision(enc.ctx, 7, fp8_scales(2))
     finally:
         enc.close()
