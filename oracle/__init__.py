@@ -35,3 +35,4 @@ from .fusion import (  # noqa: F401
     encode_fused,
 )
 from . import fp8  # noqa: F401
+from . import ctc  # noqa: F401

@@ -260,3 +260,33 @@ def make_connector_weights(bf16=True, perturb=False, d=D_MODEL, out_dim=LLM_DIM,
         for k in ("spk_ln_g", "spk_ln_b", "w_conn", "b_conn"):
             cw[k] = round_bf16(cw[k])
     return cw
+
+
+# ------------------------------------------------------ CTC timestamp adapter
+CTC_CLASSES = 23_863      # 23,862 tokens + blank
+CTC_HEAD_DIM = 80         # 16 heads over width 1,280
+CTC_FFN = 1_280
+
+
+def make_ctc_weights(bf16=True, perturb=False, d=D_MODEL, dh=CTC_HEAD_DIM, ffn=CTC_FFN,
+                     n_layers=2, n_classes=CTC_CLASSES, seed=WEIGHT_SEED):
+    """Random-init adapter weights: upsampling taps w_conv [2, d, d] and
+    b_conv [d], n_layers layer dicts (the encoder's keys, head width dh, FFN
+    width ffn), lnf_g / lnf_b, projection w_out [n_classes, d], b_out.
+    Draws as make_weights (N(0, 0.02^2) matrices; gains 1 / biases 0, or
+    perturbed), from seeds (seed, 2000 + layer, tensor id)."""
+    def tensor(layer, tid, kind, shape):
+        key = (seed, 2000 + layer + 1, tid)
+        if perturb and not kind.startswith("w_"):
+            key = key + (1,)
+        a = _draw(kind, shape, np.random.default_rng(key), perturb)
+        return round_bf16(a, inplace=True) if bf16 else a
+
+    cw = {"w_conv": tensor(-1, 0, "w_conv", (2, d, d)), "b_conv": tensor(-1, 1, "bias_d", (d,)),
+          "lnf_g": tensor(-1, 2, "gain", (d,)), "lnf_b": tensor(-1, 3, "bias_d", (d,)),
+          "w_out": tensor(-1, 4, "w_out", (n_classes, d)),
+          "b_out": tensor(-1, 5, "bias_c", (n_classes,)), "layers": []}
+    for layer in range(n_layers):
+        cw["layers"].append({name: tensor(layer, tid, kind, _shape(kind, d, dh, ffn, 0))
+                             for name, kind, tid in _LAYER_TENSORS})
+    return cw
