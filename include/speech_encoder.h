@@ -289,6 +289,64 @@ int enc_set_precision(enc_ctx* ctx, int32_t precision, const float* input_scales
 int enc_calibrate(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                   float* amax, hipStream_t stream);
 
+/*
+ * CTC timestamp adapter.  The Dataset Audits page, section "4. Use alignment
+ * and audio questions as supporting evidence", describes a ~50M-parameter
+ * adapter on the unfused ASR states (width 1,280, 80 ms grid): a stride-two
+ * transposed convolution to a 40 ms grid, two Transformer layers with 16
+ * heads, and a projection to 23,862 tokens plus the CTC blank, whose frame
+ * probabilities forced alignment consumes.  This library reads it as:
+ *   - input: the encoder output (final LayerNorm included, before fusion);
+ *   - upsampling: kernel 2, stride 2: frame 2t + j = H[t] W_j^T + b_conv;
+ *   - layers: the encoder's block type with 16 heads of width 80 (QK-norm
+ *     over 80 dims, rotation of pairs (i, i + 40) at the frame's position on
+ *     the 40 ms grid, bidirectional attention over the whole clip) and a
+ *     feed-forward width of 1,280 (53.5M parameters in all, the stated ~50M);
+ *   - a final LayerNorm, the projection, log-softmax over the classes.
+ */
+typedef struct enc_ctc_weights {
+  int32_t abi_version;              /* must be ENC_ABI_VERSION                   */
+  int32_t dtype;                    /* ENC_F32 or ENC_BF16, for every tensor     */
+  int32_t n_layers;                 /* 1..8 (2 in the release)                   */
+  int32_t n_classes;                /* 2..1048576 (23,863: 23,862 tokens + blank) */
+  const void* w_conv;               /* DEVICE [2, 1280, 1280]: tap j, [out, in]  */
+  const void* b_conv;               /* DEVICE [1280]                             */
+  const enc_layer_weights* layers;  /* HOST array [n_layers] of DEVICE tensors with
+                                       head width 80: q_g, q_b, k_g, k_b [80];
+                                       w_qkv [3840, 1280] (head h of q/k/v in rows
+                                       80 h ..); w_o, w_up, w_down [1280, 1280];
+                                       b_up [1280]; the rest as for the encoder */
+  const void* lnf_g;                /* DEVICE [1280] final LayerNorm              */
+  const void* lnf_b;                /* DEVICE [1280]                             */
+  const void* w_out;                /* DEVICE [n_classes, 1280]                  */
+  const void* b_out;                /* DEVICE [n_classes]                        */
+} enc_ctc_weights;
+
+/*
+ * enc_set_ctc: copy adapter weights into ctx (matrices to bf16, vectors to
+ * fp32, q/k/v heads into 128-wide slots whose extra dims are zero), replacing
+ * any earlier set.  Synchronous.  Errors: ENC_ERR_ARG, ENC_ERR_NOMEM,
+ * ENC_ERR_HIP.
+ */
+int enc_set_ctc(enc_ctx* ctx, const enc_ctc_weights* w);
+
+/*
+ * enc_forward_ctc: waveform to CTC log-probabilities: the encoder as in
+ * enc_forward (same attention scope and precision), then the adapter (its
+ * attention always over the whole clip).
+ *   audio, lengths  as for enc_logmel.
+ *   out_logprobs  DEVICE fp32 [2 R, n_classes], R = sum_b P_b: clip b's frames
+ *                 are rows 2 R_b .. 2 R_b + 2 P_b - 1 (R_b = sum_{b' < b} P_b'),
+ *                 frame f at f x 40 ms; each row is log-probabilities over the
+ *                 classes (blank last, as the weights order them).
+ * The adapter keeps its own workspace (about 250 KB per encoder position,
+ * most of it the padded logits).  Requires an earlier enc_set_ctc.  Errors: as
+ * enc_forward, and ENC_ERR_ARG without adapter weights or with a NULL output
+ * and R > 0.  R = 0 writes nothing.
+ */
+int enc_forward_ctc(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                    float* out_logprobs, hipStream_t stream);
+
 /* enc_destroy: wait for the context's device work and free it.  NULL is a
  * no-op. */
 void enc_destroy(enc_ctx* ctx);
@@ -329,7 +387,9 @@ const char* enc_last_error(void);
 #define ENC_K_FINAL_NORM 9
 #define ENC_K_SPEAKER_FUSE 10   /* enc_forward_fused: final norm + speaker fusion */
 #define ENC_K_CONNECTOR 11      /* enc_forward_fused: connector GEMM              */
-#define ENC_K_COUNT 12
+#define ENC_K_CTC 12            /* enc_forward_ctc: upsampling and adapter layers */
+#define ENC_K_CTC_OUT 13        /* enc_forward_ctc: final norm, projection, log-softmax */
+#define ENC_K_COUNT 14
 int enc_profile_kernel(enc_ctx* ctx, int32_t kernel_id);
 int enc_profile_read(enc_ctx* ctx, int64_t* launches, double* total_ms);
 

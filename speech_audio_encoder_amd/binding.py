@@ -24,10 +24,12 @@ ENC_ABI_VERSION = 1
 D_MODEL, N_MELS = 1280, 128
 
 KERNELS = ["frontend", "gemm_in", "layernorm", "gemm_qkv", "qknorm_rope", "attention",
-           "gemm_o", "gemm_up", "gemm_down", "final_norm", "speaker_fuse", "connector"]
+           "gemm_o", "gemm_up", "gemm_down", "final_norm", "speaker_fuse", "connector", "ctc",
+           "ctc_out"]
 
 EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_set_attention", "enc_set_connector",
-           "enc_forward_fused", "enc_set_precision", "enc_calibrate", "enc_destroy", "enc_shapes",
+           "enc_forward_fused", "enc_set_precision", "enc_calibrate", "enc_set_ctc",
+           "enc_forward_ctc", "enc_destroy", "enc_shapes",
            "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
 
 ENC_PREC_BF16 = 0
@@ -58,6 +60,15 @@ class EncConnectorWeights(ctypes.Structure):
                 ("out_dim", ctypes.c_int32), ("speaker_scale", ctypes.c_float),
                 ("spk_ln_g", ctypes.c_void_p), ("spk_ln_b", ctypes.c_void_p),
                 ("w_conn", ctypes.c_void_p), ("b_conn", ctypes.c_void_p)]
+
+
+class EncCtcWeights(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("n_classes", ctypes.c_int32),
+                ("w_conv", ctypes.c_void_p), ("b_conv", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(EncLayerWeights)),
+                ("lnf_g", ctypes.c_void_p), ("lnf_b", ctypes.c_void_p),
+                ("w_out", ctypes.c_void_p), ("b_out", ctypes.c_void_p)]
 
 
 class EncoderError(RuntimeError):
@@ -93,6 +104,9 @@ def load_library(path=LIB_PATH):
                                       ctypes.POINTER(ctypes.c_float)]
     lib.enc_calibrate.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
                                   ctypes.POINTER(ctypes.c_float), ctypes.c_void_p]
+    lib.enc_set_ctc.argtypes = [ctypes.c_void_p, ctypes.POINTER(EncCtcWeights)]
+    lib.enc_forward_ctc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p]
     lib.enc_destroy.argtypes = [ctypes.c_void_p]
     lib.enc_destroy.restype = None
     lib.enc_shapes.argtypes = [i64p, ctypes.c_int32, i64p, i64p]
@@ -294,6 +308,50 @@ def scales_from_amax(amax):
     return np.where(a > 0, a / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
 
 
+def enc_set_ctc(ctx, cw, dtype="bf16", device="cuda"):
+    """Timestamp-adapter weights from a dict: w_conv [2, 1280, 1280] (tap,
+    out, in), b_conv, layers (encoder-style dicts at head width 80), lnf_g,
+    lnf_b, w_out [n_classes, 1280], b_out.  Returns n_classes."""
+    import torch
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    keep = []
+
+    def dev(a):
+        t = torch.as_tensor(np.asarray(a, dtype=np.float32)) if not torch.is_tensor(a) else a
+        t = t.to(device=device, dtype=tdt).contiguous()
+        keep.append(t)
+        return ctypes.c_void_p(t.data_ptr())
+
+    layers = (EncLayerWeights * len(cw["layers"]))()
+    for i, lw in enumerate(cw["layers"]):
+        for name in _LAYER_FIELDS:
+            setattr(layers[i], name, dev(lw[name]))
+    n_classes = int(np.shape(cw["w_out"])[0])
+    w = EncCtcWeights(abi_version=ENC_ABI_VERSION, dtype=ENC_BF16 if dtype == "bf16" else ENC_F32,
+                      n_layers=len(cw["layers"]), n_classes=n_classes,
+                      w_conv=dev(cw["w_conv"]), b_conv=dev(cw["b_conv"]), layers=layers,
+                      lnf_g=dev(cw["lnf_g"]), lnf_b=dev(cw["lnf_b"]), w_out=dev(cw["w_out"]),
+                      b_out=dev(cw["b_out"]))
+    torch.cuda.synchronize()
+    _check(load_library().enc_set_ctc(ctypes.c_void_p(ctx), ctypes.byref(w)))
+    del keep
+    return n_classes
+
+
+def enc_forward_ctc(ctx, audio, lengths, n_classes, out=None, stream=None):
+    """CTC log-probabilities: audio cuda fp32 [B, N_max] -> fp32 [2 R, n_classes],
+    clips packed in order (R = packed_rows(lengths))."""
+    import torch
+    arr, ptr = _lengths_array(lengths)
+    rows = 2 * packed_rows(arr)
+    if out is None:
+        out = torch.empty((rows, n_classes), dtype=torch.float32, device=audio.device)
+    _check(load_library().enc_forward_ctc(ctypes.c_void_p(ctx), ctypes.c_void_p(audio.data_ptr()),
+                                          ptr, len(arr), ctypes.c_void_p(out.data_ptr()),
+                                          _stream_handle(stream)))
+    return out
+
+
 def enc_forward_raw(ctx, audio_ptr, lengths, out_ptr, stream_ptr=0):
     """enc_forward with raw pointers; returns the status code (tests)."""
     arr, ptr = _lengths_array(lengths)
@@ -341,6 +399,12 @@ class Encoder:
 
     def forward_fused(self, audio, lengths, activity, out=None):
         return enc_forward_fused(self.ctx, audio, lengths, activity, self.out_dim, out)
+
+    def set_ctc(self, cw, dtype="bf16"):
+        self.n_classes = enc_set_ctc(self.ctx, cw, dtype=dtype)
+
+    def forward_ctc(self, audio, lengths, out=None):
+        return enc_forward_ctc(self.ctx, audio, lengths, self.n_classes, out)
 
     def set_precision(self, precision, input_scales=None):
         """"bf16", or "fp8" with input scales [n_layers, 4]."""

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(128) void attention_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ vt, int64_t ld_vt,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
     const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_q0, int n_tiles,
-    int n_items, void* __restrict__ out, float out_scale) {
+    int n_items, void* __restrict__ out, float out_scale, int hd, int dh_out) {
   // K in a ring of four 32-key units, V^T in two 64-key tiles.
   __shared__ uint4 sK[4][KU * DH / 8];   // [key][16 chunks of 8 dims], swizzled
   __shared__ uint4 sV[2][DH * KT / 8];   // [dim][8 chunks of 8 keys], swizzled
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(128) void attention_kernel(
   for (int qb = 0; qb < 2; ++qb) {
     const int q = q0 + wave * QPW + qb * 32 + l32;
     const bool ok = q < len;
-    const bf16_t* qrow = qkv + (s0 + (ok ? q : 0)) * (3 * D) + h * DH + lhi * 8;
+    const bf16_t* qrow = qkv + (s0 + (ok ? q : 0)) * (3 * hd) + h * DH + lhi * 8;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
       const uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + s * 16) : make_uint4(0, 0, 0, 0);
@@ -133,21 +133,21 @@ __global__ __launch_bounds__(128) void attention_kernel(
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int key = (wave * 4 + t) * 4 + (lane >> 4);
-    koff[t] = (uint32_t)(key * (3 * D * 2) + (((lane & 15) ^ (key & 15)) * 16));
+    koff[t] = (uint32_t)(key * (3 * hd * 2) + (((lane & 15) ^ (key & 15)) * 16));
   }
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int d = (wave * 8 + t) * 8 + (lane >> 3);
     voff[t] = (uint32_t)(d * (uint32_t)ld_vt * 2 + (((lane & 7) ^ ((d >> 1) & 7)) * 16));
   }
-  const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * D) + D + h * DH);
+  const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + hd + h * DH);
   const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)h * DH * ld_vt + vt_base[seq]);
   const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_void*)&sK[0][0] + wave * 4 * 1024;
   const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0] + wave * 8 * 1024;
   // K unit u into ring slot u % 4.  Units past the clip's last one re-load
   // the last unit into a slot that is never read again (no branch).
   auto issue_k = [&](int u) __attribute__((always_inline)) {
-    const char* g = kbase + (int64_t)min(u, nku - 1) * KU * (3 * D * 2);
+    const char* g = kbase + (int64_t)min(u, nku - 1) * KU * (3 * hd * 2);
     const uint32_t l = k_lds + (u & 3) * KU_BYTES;
 #pragma unroll
     for (int t = 0; t < 4; ++t) dma16(g + koff[t], l + t * 1024);
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(128) void attention_kernel(
     const float inv = 1.0f / lt;
     if (out_scale > 0.0f) {
       // E4M3 codes of the output times out_scale (the FP8 output projection's input)
-      uint8_t* orow = reinterpret_cast<uint8_t*>(out) + (s0 + q) * D + h * DH;
+      uint8_t* orow = reinterpret_cast<uint8_t*>(out) + (s0 + q) * hd + h * DH;
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
@@ -338,12 +338,16 @@ __global__ __launch_bounds__(128) void attention_kernel(
         }
       continue;
     }
-    bf16_t* orow = reinterpret_cast<bf16_t*>(out) + (s0 + q) * D + h * DH;
+    // rows of n_heads x dh_out: a head narrower than its 128-wide slot
+    // (dims >= dh_out are zero) stores only its own dims
+    bf16_t* orow = reinterpret_cast<bf16_t*>(out) + (s0 + q) * (int64_t)(n_items / n_tiles) * dh_out +
+                   h * dh_out;
 #pragma unroll
     for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db * 32 + 8 * g + 4 * lhi;
+        if (d >= dh_out) continue;
         *reinterpret_cast<uint2*>(orow + d) =
             make_uint2(pack_bf16x2(O[db][qb][4 * g] * inv, O[db][qb][4 * g + 1] * inv),
                        pack_bf16x2(O[db][qb][4 * g + 2] * inv, O[db][qb][4 * g + 3] * inv));
@@ -354,39 +358,45 @@ __global__ __launch_bounds__(128) void attention_kernel(
 }  // namespace
 
 bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g,
-                            const float* k_b) {
+                            const float* k_b, int dh) {
   // Norm bound of a head vector after LayerNorm (sum of squares of the
   // normalised values <= 128) with gain g and bias b, rotated (norm kept).
-  auto norm_bound = [](const float* g, const float* b) {
+  auto norm_bound = [dh](const float* g, const float* b) {
     double gmax = 0.0, bsq = 0.0;
-    for (int i = 0; i < DH; ++i) {
+    for (int i = 0; i < dh; ++i) {
       gmax = std::max(gmax, std::fabs((double)g[i]));
       bsq += (double)b[i] * b[i];
     }
-    return gmax * std::sqrt((double)DH) + std::sqrt(bsq);
+    return gmax * std::sqrt((double)dh) + std::sqrt(bsq);
   };
   // 2^-6 covers bf16 rounding of q and k and fp32 rounding of the products.
   const double bound = norm_bound(q_g, q_b) * norm_bound(k_g, k_b) * (1.0 + 1.0 / 64);
-  const double log2_range = bound * 1.4426950408889634 / std::sqrt((double)DH);
+  const double log2_range = bound * 1.4426950408889634 / std::sqrt((double)dh);
   return std::isfinite(log2_range) && log2_range <= 100.0;
 }
 
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
-                            const int32_t* tile_q0, int n_tiles, bool fixed_ref, void* out,
-                            float out_scale, hipStream_t stream) {
+                            const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
+                            bool fixed_ref, void* out, float out_scale, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   // V^T byte offsets inside a tile are 32-bit: 128 rows of ld_vt bf16.
   if (ld_vt <= 0 || ld_vt % 64 != 0 || (int64_t)DH * ld_vt * 2 >= (int64_t)1 << 31)
     return hipErrorInvalidValue;
-  const int n_items = n_tiles * H;
+  if (n_heads < 1 || head_dim < 4 || head_dim > DH || head_dim % 4 != 0 ||
+      (out_scale > 0.0f && head_dim != DH))
+    return hipErrorInvalidValue;
+  const int n_items = n_tiles * n_heads;
+  const int hd = n_heads * DH;
   const int grid = (n_items + 7) / 8 * 8;
   if (fixed_ref)
     attention_kernel<true><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
-        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale);
+        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale, hd,
+        head_dim);
   else
     attention_kernel<false><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
-        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale);
+        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale, hd,
+        head_dim);
   return hipGetLastError();
 }
 

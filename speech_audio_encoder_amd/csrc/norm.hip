@@ -14,6 +14,7 @@
 // statistics in fp32 registers with wavefront shuffles, vector loads/stores.
 
 #include <algorithm>
+#include <cmath>
 
 #include "common.h"
 #include "kernels.h"
@@ -198,24 +199,32 @@ __device__ __forceinline__ void unpack8(const uint4 u, float (&f)[8]) {
 }
 
 // q and k of one tile x head: normalise, rotate, scale k (in place).
-__device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t s0, int len, int p0, int h,
-                                        int lane, int wave, const float* __restrict__ qg,
+// HALF = half the head width (rotation pairs (i, i + HALF)): 64 for the
+// encoder's heads, 40 for the timestamp adapter's (head slots stay 128 wide,
+// dims 2 HALF .. 127 are zero and untouched).  ldq: row stride of qkv, hd:
+// offset of the k block within a row (heads x 128), kscale: factor on k.
+template <int HALF>
+__device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t ldq, int hd, int64_t s0,
+                                        int len, int p0, int h, int lane, int wave,
+                                        const float* __restrict__ qg,
                                         const float* __restrict__ qb, const float* __restrict__ kg,
                                         const float* __restrict__ kb,
                                         const float* __restrict__ rope_cos,
-                                        const float* __restrict__ rope_sin) {
-  const int sub = lane & 7;     // dims 8 sub .. + 7 and 64 + 8 sub .. + 7
+                                        const float* __restrict__ rope_sin, float kscale) {
+  constexpr float INV_DH = 1.0f / (2 * HALF);
+  const int sub = lane & 7;     // dims 8 sub .. + 7 and HALF + 8 sub .. + 7
   const int grp = lane >> 3;    // row within the wavefront's 8
-  const int d0 = sub * 8;
+  const bool act = sub < HALF / 8;   // lanes past the head width idle
+  const int d0 = (act ? sub : 0) * 8;
   float gq[2][8], bq[2][8], gk[2][8], bk[2][8];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      gq[hh][e] = qg[hh * 64 + d0 + e];
-      bq[hh][e] = qb[hh * 64 + d0 + e];
-      gk[hh][e] = kg[hh * 64 + d0 + e];
-      bk[hh][e] = kb[hh * 64 + d0 + e];
+      gq[hh][e] = qg[hh * HALF + d0 + e];
+      bq[hh][e] = qb[hh * HALF + d0 + e];
+      gk[hh][e] = kg[hh * HALF + d0 + e];
+      bk[hh][e] = kb[hh * HALF + d0 + e];
     }
 
   // Every load is issued before the first store (rows are updated in place,
@@ -227,11 +236,11 @@ __device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t s0, in
   for (int i = 0; i < NR; ++i) {
     const int p = p0 + i * 32 + wave * 8 + grp;
     const int pl = p < len ? p : p0;
-    const bf16_t* base = qkv + (s0 + pl) * (3 * D) + h * DH + d0;
+    const bf16_t* base = qkv + (s0 + pl) * ldq + h * DH + d0;
     uq[i][0] = *reinterpret_cast<const uint4*>(base);
-    uq[i][1] = *reinterpret_cast<const uint4*>(base + 64);
-    uk[i][0] = *reinterpret_cast<const uint4*>(base + D);
-    uk[i][1] = *reinterpret_cast<const uint4*>(base + D + 64);
+    uq[i][1] = *reinterpret_cast<const uint4*>(base + HALF);
+    uk[i][0] = *reinterpret_cast<const uint4*>(base + hd);
+    uk[i][1] = *reinterpret_cast<const uint4*>(base + hd + HALF);
   }
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
@@ -241,10 +250,10 @@ __device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t s0, in
     const uint4 uq0 = uq[i][0], uq1 = uq[i][1], uk0 = uk[i][0], uk1 = uk[i][1];
     float cs[8], sn[8];
     {
-      const float4 c0 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * (DH / 2) + d0);
-      const float4 c1 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * (DH / 2) + d0 + 4);
-      const float4 s0v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * (DH / 2) + d0);
-      const float4 s1v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * (DH / 2) + d0 + 4);
+      const float4 c0 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * HALF + d0);
+      const float4 c1 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * HALF + d0 + 4);
+      const float4 s0v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * HALF + d0);
+      const float4 s1v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * HALF + d0 + 4);
       cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w;
       cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
       sn[0] = s0v.x; sn[1] = s0v.y; sn[2] = s0v.z; sn[3] = s0v.w;
@@ -258,9 +267,10 @@ __device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t s0, in
       float sum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum += a[e] + b[e];
+      if (!act) sum = 0.f;
 #pragma unroll
       for (int o = 4; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-      const float mean = sum * (1.0f / DH);
+      const float mean = sum * INV_DH;
       float sq = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -268,12 +278,13 @@ __device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t s0, in
         b[e] -= mean;
         sq += a[e] * a[e] + b[e] * b[e];
       }
+      if (!act) sq = 0.f;
 #pragma unroll
       for (int o = 4; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
-      const float rstd = rsqrtf(sq * (1.0f / DH) + LN_EPS);
-      // k leaves scaled by log2(e) / sqrt(128): the attention kernel's
-      // scores are then directly the exponents of exp2.
-      const float outscale = which ? K_SCORE_SCALE : 1.0f;
+      const float rstd = rsqrtf(sq * INV_DH + LN_EPS);
+      // k leaves scaled by log2(e) / sqrt(head width): the attention
+      // kernel's scores are then directly the exponents of exp2.
+      const float outscale = which ? kscale : 1.0f;
       uint32_t lo[4], hi[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -292,21 +303,24 @@ __device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t s0, in
         lo[e / 2] = pack_bf16x2(y0[0], y0[1]);
         hi[e / 2] = pack_bf16x2(y1[0], y1[1]);
       }
-      if (live) {
-        bf16_t* base = qkv + (s0 + p) * (3 * D) + which * D + h * DH + d0;
+      if (live && act) {
+        bf16_t* base = qkv + (s0 + p) * ldq + which * hd + h * DH + d0;
         *reinterpret_cast<uint4*>(base) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-        *reinterpret_cast<uint4*>(base + 64) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        *reinterpret_cast<uint4*>(base + HALF) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       }
     }
   }
 }
 
+template <int HALF>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     bf16_t* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
     const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_p0,
     const float* __restrict__ qg, const float* __restrict__ qb, const float* __restrict__ kg,
     const float* __restrict__ kb, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, bf16_t* __restrict__ vt, int64_t ld_vt) {
+    const float* __restrict__ rope_sin, bf16_t* __restrict__ vt, int64_t ld_vt, int hd,
+    float kscale) {
+  const int64_t ldq = 3 * (int64_t)hd;
   const int h = blockIdx.y;
   const int seq = tile_seq[blockIdx.x];
   const int p0 = tile_p0[blockIdx.x];
@@ -317,7 +331,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   const int wave = threadIdx.x >> 6;
 
   if (blockIdx.z == 0) {
-    qk_part(qkv, s0, len, p0, h, lane, wave, qg, qb, kg, kb, rope_cos, rope_sin);
+    qk_part<HALF>(qkv, ldq, hd, s0, len, p0, h, lane, wave, qg, qb, kg, kb, rope_cos, rope_sin,
+                  kscale);
     return;
   }
   // v thread map: wavefront w covers position blocks 8 (w & 1) .. + 7 and dim
@@ -334,8 +349,8 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     // lane supplies to a 32x32x16 MFMA whose other operand comes from the
     // accumulator layout of K Q^T (rows 4*(lane/32) + 8g + r).
     const int p = p0 + 16 * (vrb >> 1) + 4 * (vrb & 1) + (i & 3) + 8 * (i >> 2);
-    vrows[i] = (vblock && p < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + p) * (3 * D) +
-                                                                      2 * D + h * DH + vdb * 8)
+    vrows[i] = (vblock && p < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + p) * ldq +
+                                                                      2 * hd + h * DH + vdb * 8)
                                    : make_uint4(0, 0, 0, 0);
   }
 
@@ -434,6 +449,50 @@ __global__ __launch_bounds__(256) void speaker_fuse_kernel(
   }
 }
 
+// Log-softmax of each row over its first n entries: one workgroup per row
+// keeps a running maximum and sum of exponentials (rescaled when the maximum
+// grows), merges the 256 partial pairs, then writes z - max - log(sum).
+__global__ __launch_bounds__(256) void log_softmax_kernel(const float* __restrict__ z,
+                                                          int64_t ldz, int n,
+                                                          float* __restrict__ out) {
+  __shared__ float pm[4], ps[4];
+  const float* zr = z + (int64_t)blockIdx.x * ldz;
+  float m = -INFINITY, sum = 0.0f;
+  for (int i = threadIdx.x; i < n; i += 256) {
+    const float v = zr[i];
+    if (v > m) {
+      sum = sum * __expf(m - v) + 1.0f;
+      m = v;
+    } else {
+      sum += __expf(v - m);
+    }
+  }
+  auto merge = [](float& m1, float& s1, float m2, float s2) {
+    const float mm = fmaxf(m1, m2);
+    if (mm == -INFINITY) return;
+    s1 = s1 * __expf(m1 - mm) + s2 * __expf(m2 - mm);
+    m1 = mm;
+  };
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(sum, o, 64);
+    merge(m, sum, m2, s2);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    pm[threadIdx.x >> 6] = m;
+    ps[threadIdx.x >> 6] = sum;
+  }
+  __syncthreads();
+  m = pm[0];
+  sum = ps[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) merge(m, sum, pm[w], ps[w]);
+  const float lse = m + __logf(sum);
+  float* orow = out + (int64_t)blockIdx.x * n;
+  for (int i = threadIdx.x; i < n; i += 256) orow[i] = zr[i] - lse;
+}
+
 __global__ void to_bf16_kernel(const void* __restrict__ src, int src_is_bf16,
                                bf16_t* __restrict__ dst, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -485,6 +544,14 @@ hipError_t launch_quantize_fp8(const bf16_t* w, int64_t n, const float* amax, fl
   return hipGetLastError();
 }
 
+hipError_t launch_log_softmax(const float* z, int64_t ldz, int64_t rows, int n, float* out,
+                              hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  if (n < 1 || ldz < n || rows > 0x7fffffff) return hipErrorInvalidValue;
+  log_softmax_kernel<<<dim3((unsigned)rows), dim3(256), 0, stream>>>(z, ldz, n, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   fill_f32_kernel<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream>>>(p, v, n);
@@ -520,12 +587,25 @@ hipError_t launch_gather_rows(const bf16_t* src, const int32_t* rows, int64_t n,
 
 hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* vt_base,
                               const int32_t* tile_seq, const int32_t* tile_p0, int n_tiles,
-                              const float* qg, const float* qb, const float* kg, const float* kb,
-                              const float* rope_cos, const float* rope_sin, bf16_t* vt,
-                              int64_t ld_vt, hipStream_t stream) {
+                              int n_heads, int head_dim, const float* qg, const float* qb,
+                              const float* kg, const float* kb, const float* rope_cos,
+                              const float* rope_sin, bf16_t* vt, int64_t ld_vt,
+                              hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
-  qknorm_rope_kernel<<<dim3(n_tiles, H, 2), dim3(256), 0, stream>>>(
-      qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt);
+  if (n_heads < 1) return hipErrorInvalidValue;
+  const int hd = n_heads * DH;
+  // log2(e) / sqrt(head width)
+  const float kscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  if (head_dim == DH)
+    qknorm_rope_kernel<DH / 2><<<dim3(n_tiles, n_heads, 2), dim3(256), 0, stream>>>(
+        qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt,
+        hd, kscale);
+  else if (head_dim == 80)
+    qknorm_rope_kernel<40><<<dim3(n_tiles, n_heads, 2), dim3(256), 0, stream>>>(
+        qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt,
+        hd, kscale);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -124,7 +124,15 @@ struct Plan {
   // each clip row's own window.
   std::vector<int32_t> gather_src;  // [vrows]
   std::vector<int32_t> out_src;     // [rows]
+  // Timestamp adapter (40 ms grid): clip b's 2 P_b frames are one sequence.
+  std::vector<int32_t> a_cu, a_vt_base, a_tile_seq, a_tile_q0;
+  int64_t a_vt_cols = 0;
+  std::vector<int32_t> all_rows;    // {0, rows}: the whole batch as one packed block
 };
+
+// V^T columns and attention tiles of sequences starting at cu[0..n].
+void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* vt_base, int64_t* vt_cols,
+               std::vector<int32_t>* tile_seq, std::vector<int32_t>* tile_q0);
 
 constexpr int ATT_QB = 128;
 
@@ -207,7 +215,31 @@ int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles,
       }
     }
   }
+  // Adapter sequences: every clip whole, at twice the positions.
+  p->all_rows = {0, (int32_t)rows};
+  p->a_cu.resize(batch + 1);
+  for (int b = 0; b <= batch; ++b) p->a_cu[b] = 2 * p->cu_clip[b];
+  seq_tiles(p->a_cu, &p->a_vt_base, &p->a_vt_cols, &p->a_tile_seq, &p->a_tile_q0);
   return ENC_OK;
+}
+
+void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* vt_base, int64_t* vt_cols,
+               std::vector<int32_t>* tile_seq, std::vector<int32_t>* tile_q0) {
+  const int n = (int)cu.size() - 1;
+  vt_base->resize(n);
+  tile_seq->clear();
+  tile_q0->clear();
+  int64_t cols = 0;
+  for (int s = 0; s < n; ++s) {
+    const int len = cu[s + 1] - cu[s];
+    (*vt_base)[s] = (int32_t)cols;
+    cols += (len + 63) / 64 * 64;
+    for (int q0 = 0; q0 < len; q0 += ATT_QB) {
+      tile_seq->push_back(s);
+      tile_q0->push_back(q0);
+    }
+  }
+  *vt_cols = cols;
 }
 
 // Workspace layout for `rows` packed positions (offsets in bytes).
@@ -251,6 +283,22 @@ struct LayerW {
   float r_x[4] = {1, 1, 1, 1};     // fp32(1 / s_x): scale of the producer's codes
 };
 
+// Timestamp adapter: 16 heads of 80 in 128-wide slots (QKV rows and bias
+// padded with zeros), projection rows padded to a multiple of 128.
+constexpr int CTC_HEADS = 16;
+constexpr int CTC_DH = 80;
+constexpr int CTC_HD = CTC_HEADS * DH;   // width of a q / k / v block in slots
+
+struct CtcW {
+  void* mat = nullptr;    // bf16 matrices
+  void* vec = nullptr;    // fp32 vectors and tables
+  bf16_t *w_conv = nullptr, *w_out = nullptr;
+  float *b_conv2 = nullptr, *lnf_g = nullptr, *lnf_b = nullptr, *b_out = nullptr;
+  float *rope_cos = nullptr, *rope_sin = nullptr;   // [2 MAX_POS][CTC_DH / 2]
+  std::vector<LayerW> layers;
+  int n_classes = 0, n_pad = 0;
+};
+
 }  // namespace
 
 struct enc_ctx {
@@ -281,6 +329,10 @@ struct enc_ctx {
   bf16_t* w_conn = nullptr;
   float *b_conn = nullptr, *spk_g = nullptr, *spk_b = nullptr, *spk_tab = nullptr;
   int conn_dim = 0;
+  // Timestamp adapter (enc_set_ctc) and its workspace.
+  CtcW* ctc = nullptr;
+  void* ctc_ws = nullptr;
+  size_t ctc_ws_bytes = 0;
   // Precision of the layers' linear maps (enc_set_precision).
   int precision = ENC_PREC_BF16;
   void* fp8_mem = nullptr;   // E4M3 weight codes (all layers)
@@ -306,6 +358,12 @@ void release(enc_ctx* c) {
   (void)hipFree(c->plan_dev);
   (void)hipFree(c->conn_mem);
   (void)hipFree(c->fp8_mem);
+  if (c->ctc) {
+    (void)hipFree(c->ctc->mat);
+    (void)hipFree(c->ctc->vec);
+    delete c->ctc;
+  }
+  (void)hipFree(c->ctc_ws);
   (void)hipFree(c->amax_dev);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
   if (c->plan_copied) (void)hipEventDestroy(c->plan_copied);
@@ -558,7 +616,7 @@ int enc_create(const enc_weights* w, enc_ctx** out) {
     const float* src[4] = {d.q_g, d.q_b, d.k_g, d.k_b};
     for (int t = 0; t < 4 && e == hipSuccess; ++t)
       e = hipMemcpy(qk[t], src[t], sizeof(qk[t]), hipMemcpyDeviceToHost);
-    d.attn_fixed_ref = e == hipSuccess && attention_fixed_ref_ok(qk[0], qk[1], qk[2], qk[3]);
+    d.attn_fixed_ref = e == hipSuccess && attention_fixed_ref_ok(qk[0], qk[1], qk[2], qk[3], DH);
   }
   if (e != hipSuccess) {
     release(c);
@@ -648,13 +706,105 @@ int prepare_fp8_weights(enc_ctx* c) {
   return ENC_OK;
 }
 
-enum class Tail { kEmbeddings, kFused, kCalibrate };
+enum class Tail { kEmbeddings, kFused, kCalibrate, kCtc };
+
+// Adapter workspace for `rows` adapter frames (offsets in bytes).
+struct CtcLayout {
+  size_t x, a, qkv, vt, o, u, z, total;
+  int64_t ld_vt;
+};
+
+CtcLayout ctc_layout_for(int64_t rows, int64_t vt_cols, int n_pad) {
+  CtcLayout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  const size_t r = (size_t)rows;
+  l.x = take(r * D * 4);
+  l.a = take(r * D * 2);
+  l.qkv = take((r + 64) * 3 * CTC_HD * 2);   // 64 rows of slack for whole key tiles
+  l.ld_vt = std::max<int64_t>(vt_cols, 64);
+  l.vt = take((size_t)CTC_HD * l.ld_vt * 2);
+  l.o = take(r * D * 2);
+  l.u = take(r * D * 2);
+  l.z = take(r * (size_t)n_pad * 4);
+  l.total = off;
+  return l;
+}
+
+// The timestamp adapter on clip-packed encoder states h [rows, 1280] (bf16):
+// upsampling to 2 rows per position, its layers, final LayerNorm, projection
+// and log-softmax into out [2 rows, n_classes].
+int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_cu,
+                const int32_t* d_vb, const int32_t* d_ts, const int32_t* d_tq, float* out,
+                hipStream_t stream) {
+  const CtcW& W = *ctx->ctc;
+  const int64_t R = 2 * p.rows;
+  if (R == 0) return ENC_OK;
+  const CtcLayout lay = ctc_layout_for(R, p.a_vt_cols, W.n_pad);
+  if (lay.total > ctx->ctc_ws_bytes) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    (void)hipFree(ctx->ctc_ws);
+    ctx->ctc_ws = nullptr;
+    ctx->ctc_ws_bytes = 0;
+    if (hipMalloc(&ctx->ctc_ws, lay.total) != hipSuccess) {
+      ctx->ctc_ws = nullptr;
+      (void)hipGetLastError();
+      return fail(ENC_ERR_NOMEM, "adapter workspace allocation of " + std::to_string(lay.total) +
+                                     " bytes failed");
+    }
+    ctx->ctc_ws_bytes = lay.total;
+  }
+  char* ws = (char*)ctx->ctc_ws;
+  float* x = (float*)(ws + lay.x);
+  bf16_t* a = (bf16_t*)(ws + lay.a);
+  bf16_t* qkv = (bf16_t*)(ws + lay.qkv);
+  bf16_t* vt = (bf16_t*)(ws + lay.vt);
+  bf16_t* o = (bf16_t*)(ws + lay.o);
+  bf16_t* u = (bf16_t*)(ws + lay.u);
+  float* z = (float*)(ws + lay.z);
+  const int n_tiles = (int)p.a_tile_seq.size();
+  // Upsampling: [rows, 2 x 1280] row-major is [2 rows, 1280] (frame 2t + j).
+  ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasF32, h, D, W.w_conv, D, W.b_conv2, x, 2 * D,
+                                    p.rows, 2 * D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+  for (const LayerW& L : W.layers) {
+    ENC_LAUNCH(ENC_K_CTC, launch_layernorm(x, L.ln1_g, L.ln1_b, a, R, stream));
+    ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasBf16, a, D, L.w_qkv, D, L.b_qkv, qkv,
+                                      3 * CTC_HD, R, 3 * CTC_HD, D, ctx->gemm_part,
+                                      GEMM_PARTIAL_BYTES, stream));
+    ENC_LAUNCH(ENC_K_CTC,
+               launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, CTC_HEADS, CTC_DH, L.q_g,
+                                  L.q_b, L.k_g, L.k_b, W.rope_cos, W.rope_sin, vt, lay.ld_vt,
+                                  stream));
+    ENC_LAUNCH(ENC_K_CTC,
+               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, CTC_HEADS,
+                                CTC_DH, L.attn_fixed_ref, o, 0.0f, stream));
+    ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasResidualF32, o, D, L.w_o, D, L.b_o, x, D, R,
+                                      D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+    ENC_LAUNCH(ENC_K_CTC, launch_layernorm(x, L.ln2_g, L.ln2_b, a, R, stream));
+    ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasGeluBf16, a, D, L.w_up, D, L.b_up, u, D, R,
+                                      D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+    ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasResidualF32, u, D, L.w_down, D, L.b_down, x,
+                                      D, R, D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+  }
+  ENC_LAUNCH(ENC_K_CTC_OUT, launch_layernorm(x, W.lnf_g, W.lnf_b, a, R, stream));
+  ENC_LAUNCH(ENC_K_CTC_OUT, launch_gemm(Epilogue::kBiasF32, a, D, W.w_out, D, W.b_out, z, W.n_pad,
+                                        R, W.n_pad, D, ctx->gemm_part, GEMM_PARTIAL_BYTES,
+                                        stream));
+  ENC_LAUNCH(ENC_K_CTC_OUT, launch_log_softmax(z, W.n_pad, R, W.n_classes, out, stream));
+  return ENC_OK;
+}
 
 int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                 void* out, const float* activity, Tail tail, hipStream_t stream) {
   if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
   const bool fused = tail == Tail::kFused;
   const bool calib = tail == Tail::kCalibrate;
+  const bool ctc = tail == Tail::kCtc;
   const bool fp8 = ctx->precision == ENC_PREC_FP8 && !calib;
   Plan p;
   int rc = make_plan(lengths, batch, &p, true, ctx->scope);
@@ -665,6 +815,9 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   if (fused) {
     if (ctx->conn_dim == 0) return fail(ENC_ERR_ARG, "no connector weights (enc_set_connector)");
     if (p.rows > 0 && !activity) return fail(ENC_ERR_ARG, "activity is NULL");
+    if (p.rows > 0 && !out) return fail(ENC_ERR_ARG, "out is NULL");
+  } else if (ctc) {
+    if (!ctx->ctc) return fail(ENC_ERR_ARG, "no adapter weights (enc_set_ctc)");
     if (p.rows > 0 && !out) return fail(ENC_ERR_ARG, "out is NULL");
   } else if (!calib && p.p_max > 0 && !out) {
     return fail(ENC_ERR_ARG, "out_embeddings is NULL");
@@ -708,7 +861,8 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
 
   std::vector<int32_t*> dev;
   if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.cu_seq, &p.vt_base, &p.tile_seq,
-                              &p.tile_q0, &p.cu_clip, &p.gather_src, &p.out_src},
+                              &p.tile_q0, &p.cu_clip, &p.gather_src, &p.out_src, &p.a_cu,
+                              &p.a_vt_base, &p.a_tile_seq, &p.a_tile_q0, &p.all_rows},
                         &dev, stream)) != ENC_OK)
     return rc;
   const int32_t* d_nf = dev[0];
@@ -757,10 +911,11 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                              GEMM_PARTIAL_BYTES, stream));
     }
     ENC_LAUNCH(ENC_K_QKNORM_ROPE,
-               launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, Lw.q_g, Lw.q_b, Lw.k_g,
-                                  Lw.k_b, ctx->rope_cos, ctx->rope_sin, vt, lay.ld_vt, stream));
+               launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, H, DH, Lw.q_g, Lw.q_b,
+                                  Lw.k_g, Lw.k_b, ctx->rope_cos, ctx->rope_sin, vt, lay.ld_vt,
+                                  stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
-               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles,
+               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, H, DH,
                                 Lw.attn_fixed_ref, o, fp8 ? Lw.r_x[1] : 0.0f, stream));
     if (fp8) {
       ENC_LAUNCH(ENC_K_GEMM_O,
@@ -791,6 +946,12 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                             Lw.b_down, x, D, R, D, FF, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
   }
   if (calib) return ENC_OK;
+  if (ctc) {
+    // Encoder states, clip-packed bf16, into the LayerNorm buffer.
+    ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, dev[13], d_outsrc,
+                                                   1, p.rows, a, stream));
+    return run_adapter(ctx, p, a, dev[9], dev[10], dev[11], dev[12], (float*)out, stream);
+  }
   if (!fused) {
     ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_clip, d_outsrc,
                                                    batch, p.p_max, (bf16_t*)out, stream));
@@ -818,6 +979,163 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
 int enc_forward_fused(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                       const float* activity, void* out, hipStream_t stream) {
   return run_forward(ctx, audio, lengths, batch, out, activity, Tail::kFused, stream);
+}
+
+int enc_forward_ctc(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                    float* out_logprobs, hipStream_t stream) {
+  return run_forward(ctx, audio, lengths, batch, out_logprobs, nullptr, Tail::kCtc, stream);
+}
+
+int enc_set_ctc(enc_ctx* ctx, const enc_ctc_weights* w) {
+  if (!ctx || !w) return fail(ENC_ERR_ARG, "NULL argument");
+  if (w->abi_version != ENC_ABI_VERSION)
+    return fail(ENC_ERR_ARG, "abi_version " + std::to_string(w->abi_version) + " != " +
+                                 std::to_string(ENC_ABI_VERSION));
+  if (w->dtype != ENC_F32 && w->dtype != ENC_BF16) return fail(ENC_ERR_ARG, "unknown dtype");
+  if (w->n_layers < 1 || w->n_layers > 8) return fail(ENC_ERR_ARG, "n_layers must be in 1..8");
+  if (w->n_classes < 2 || w->n_classes > (1 << 20))
+    return fail(ENC_ERR_ARG, "n_classes must be in 2..1048576");
+  if (!w->w_conv || !w->b_conv || !w->layers || !w->lnf_g || !w->lnf_b || !w->w_out || !w->b_out)
+    return fail(ENC_ERR_ARG, "NULL weight tensor");
+  for (int i = 0; i < w->n_layers; ++i) {
+    const enc_layer_weights& L = w->layers[i];
+    const void* ptrs[] = {L.ln1_g, L.ln1_b, L.w_qkv, L.b_qkv, L.q_g, L.q_b, L.k_g, L.k_b,
+                          L.w_o, L.b_o, L.ln2_g, L.ln2_b, L.w_up, L.b_up, L.w_down, L.b_down};
+    for (const void* q : ptrs)
+      if (!q) return fail(ENC_ERR_ARG, "NULL tensor in adapter layer " + std::to_string(i));
+  }
+  int rc = check_device(ctx);
+  if (rc != ENC_OK) return rc;
+  hipError_t e = hipDeviceSynchronize();   // an earlier set may still be in use
+  if (e != hipSuccess) return hip_fail(e, "device synchronize");
+  if (ctx->ctc) {
+    (void)hipFree(ctx->ctc->mat);
+    (void)hipFree(ctx->ctc->vec);
+    delete ctx->ctc;
+    ctx->ctc = nullptr;
+  }
+  CtcW* W = new (std::nothrow) CtcW();
+  if (!W) return fail(ENC_ERR_NOMEM, "host allocation failed");
+  const int L = w->n_layers;
+  W->n_classes = w->n_classes;
+  W->n_pad = (w->n_classes + 127) / 128 * 128;
+  const size_t per_layer_mat = (size_t)3 * CTC_HD * D + 3 * (size_t)D * D;
+  const size_t n_mat = 2 * (size_t)D * D + L * per_layer_mat + (size_t)W->n_pad * D;
+  const size_t per_layer_vec = 2 * D + 3 * CTC_HD + 4 * CTC_DH + D + 2 * D + D + D;
+  const size_t n_rope = (size_t)2 * MAX_POS * (CTC_DH / 2);
+  const size_t n_vec = 2 * D + 2 * D + (size_t)W->n_pad + L * per_layer_vec + 2 * n_rope;
+  auto drop = [&](int code, const std::string& msg) {
+    (void)hipFree(W->mat);
+    (void)hipFree(W->vec);
+    delete W;
+    return fail(code, msg);
+  };
+  if (hipMalloc(&W->mat, n_mat * 2) != hipSuccess || hipMalloc(&W->vec, n_vec * 4) != hipSuccess) {
+    (void)hipGetLastError();
+    return drop(ENC_ERR_NOMEM, "adapter weight allocation failed");
+  }
+  // Zeros first: the slots' padding dims and the projection's padding rows.
+  if ((e = hipMemset(W->mat, 0, n_mat * 2)) != hipSuccess ||
+      (e = hipMemset(W->vec, 0, n_vec * 4)) != hipSuccess)
+    return drop(ENC_ERR_HIP, std::string("adapter weight clear: ") + hipGetErrorString(e));
+  const bool bf = w->dtype == ENC_BF16;
+  const size_t esz = bf ? 2 : 4;
+  auto at = [&](const void* base, size_t elems) { return (const void*)((const char*)base + elems * esz); };
+  bf16_t* pm = (bf16_t*)W->mat;
+  float* pv = (float*)W->vec;
+  e = hipSuccess;
+  auto mat = [&](const void* src, size_t n, bf16_t* dst) {
+    if (e == hipSuccess) e = launch_to_bf16(src, bf, dst, (int64_t)n, nullptr);
+  };
+  auto vec = [&](const void* src, size_t n, float* dst) {
+    if (e == hipSuccess) e = launch_to_f32(src, bf, dst, (int64_t)n, nullptr);
+  };
+  W->w_conv = pm;  // [2 x 1280 out, 1280 in]: GEMM rows j * 1280 + o
+  mat(w->w_conv, 2 * (size_t)D * D, pm);
+  pm += 2 * (size_t)D * D;
+  W->b_conv2 = pv;
+  vec(w->b_conv, D, pv);
+  vec(w->b_conv, D, pv + D);
+  pv += 2 * D;
+  W->lnf_g = pv;
+  vec(w->lnf_g, D, pv);
+  pv += D;
+  W->lnf_b = pv;
+  vec(w->lnf_b, D, pv);
+  pv += D;
+  W->layers.resize(L);
+  for (int i = 0; i < L; ++i) {
+    const enc_layer_weights& S = w->layers[i];
+    LayerW& T = W->layers[i];
+    T.w_qkv = pm;
+    T.b_qkv = pv;
+    // head h of block q / k / v: source rows blk 1280 + 80 h .. + 79 go to
+    // slot rows blk (16 x 128) + 128 h .. + 79
+    for (int blk = 0; blk < 3; ++blk)
+      for (int h = 0; h < CTC_HEADS; ++h) {
+        const size_t srow = (size_t)blk * D + (size_t)h * CTC_DH;
+        const size_t drow = (size_t)blk * CTC_HD + (size_t)h * DH;
+        mat(at(S.w_qkv, srow * D), (size_t)CTC_DH * D, pm + drow * D);
+        vec(at(S.b_qkv, srow), CTC_DH, pv + drow);
+      }
+    pm += (size_t)3 * CTC_HD * D;
+    pv += 3 * CTC_HD;
+    T.w_o = pm;
+    mat(S.w_o, (size_t)D * D, pm);
+    pm += (size_t)D * D;
+    T.w_up = pm;
+    mat(S.w_up, (size_t)D * D, pm);
+    pm += (size_t)D * D;
+    T.w_down = pm;
+    mat(S.w_down, (size_t)D * D, pm);
+    pm += (size_t)D * D;
+    float** vecs[] = {&T.ln1_g, &T.ln1_b, &T.b_o, &T.ln2_g, &T.ln2_b, &T.b_up, &T.b_down};
+    const void* vsrc[] = {S.ln1_g, S.ln1_b, S.b_o, S.ln2_g, S.ln2_b, S.b_up, S.b_down};
+    for (int k = 0; k < 7; ++k) {
+      *vecs[k] = pv;
+      vec(vsrc[k], D, pv);
+      pv += D;
+    }
+    float** qk[] = {&T.q_g, &T.q_b, &T.k_g, &T.k_b};
+    const void* qsrc[] = {S.q_g, S.q_b, S.k_g, S.k_b};
+    for (int k = 0; k < 4; ++k) {
+      *qk[k] = pv;
+      vec(qsrc[k], CTC_DH, pv);
+      pv += CTC_DH;
+    }
+  }
+  W->w_out = pm;
+  mat(w->w_out, (size_t)w->n_classes * D, pm);
+  pm += (size_t)W->n_pad * D;
+  W->b_out = pv;
+  vec(w->b_out, (size_t)w->n_classes, pv);
+  pv += W->n_pad;
+  // Rotation tables at head width 80 for up to two frames per encoder position.
+  W->rope_cos = pv;
+  W->rope_sin = pv + n_rope;
+  std::vector<float> tc((size_t)n_rope), ts((size_t)n_rope);
+  for (int p = 0; p < 2 * MAX_POS; ++p)
+    for (int i = 0; i < CTC_DH / 2; ++i) {
+      const double ang = (double)p * std::pow(10000.0, -(double)i / (CTC_DH / 2));
+      tc[(size_t)p * (CTC_DH / 2) + i] = (float)std::cos(ang);
+      ts[(size_t)p * (CTC_DH / 2) + i] = (float)std::sin(ang);
+    }
+  if (e == hipSuccess) e = hipMemcpy(W->rope_cos, tc.data(), n_rope * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(W->rope_sin, ts.data(), n_rope * 4, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  for (int i = 0; i < L && e == hipSuccess; ++i) {
+    LayerW& T = W->layers[i];
+    float qk[4][CTC_DH];
+    const float* src[4] = {T.q_g, T.q_b, T.k_g, T.k_b};
+    for (int t = 0; t < 4 && e == hipSuccess; ++t)
+      e = hipMemcpy(qk[t], src[t], sizeof(qk[t]), hipMemcpyDeviceToHost);
+    T.attn_fixed_ref =
+        e == hipSuccess && attention_fixed_ref_ok(qk[0], qk[1], qk[2], qk[3], CTC_DH);
+  }
+  if (e != hipSuccess) return drop(ENC_ERR_HIP, std::string("adapter weight copy: ") +
+                                                    hipGetErrorString(e));
+  ctx->ctc = W;
+  return ENC_OK;
 }
 
 int enc_calibrate(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,

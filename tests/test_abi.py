@@ -92,6 +92,8 @@ def test_null_context_is_rejected(lib):
     assert lib.enc_set_connector(None, None) == binding.ENC_ERR_ARG
     assert lib.enc_set_precision(None, binding.ENC_PREC_BF16, None) == binding.ENC_ERR_ARG
     assert lib.enc_calibrate(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
+    assert lib.enc_set_ctc(None, None) == binding.ENC_ERR_ARG
+    assert lib.enc_forward_ctc(None, None, arr, 1, None, None) == binding.ENC_ERR_ARG
     assert lib.enc_forward_fused(None, None, arr, 1, None, None, None) == binding.ENC_ERR_ARG
     lib.enc_destroy(None)   # no-op
 

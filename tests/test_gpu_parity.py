@@ -679,3 +679,105 @@ def test_fp8_errors(torch_mod, binding_mod):
             binding_mod.enc_set_precision(enc.ctx, 7, fp8_scales(2))
     finally:
         enc.close()
+
+
+# ---------------------------------------------------- CTC timestamp adapter
+_CTC = {}
+
+
+def get_ctc(kind):
+    if kind not in _CTC:
+        if kind == "full":
+            _CTC[kind] = workloads.make_ctc_weights(bf16=True)
+        else:   # perturbed, a small vocabulary (the oracle's projection stays quick)
+            _CTC[kind] = workloads.make_ctc_weights(bf16=False, perturb=True, n_classes=1000)
+    return _CTC[kind]
+
+
+def check_logprobs(got, ref, label):
+    """Log-probabilities: per-row centred values (log-softmax is the logits up
+    to a per-row shift) to the embedding bound, and every row normalised."""
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape
+    lse = np.log(np.exp(got).sum(axis=1))
+    say(f"{label}: max |log sum p| {np.abs(lse).max():.2e}")
+    assert np.abs(lse).max() < 1e-4
+    gc = got - got.mean(axis=1, keepdims=True)
+    rc = ref - ref.mean(axis=1, keepdims=True)
+    check_embeddings(gc, rc, label)
+
+
+def run_ctc(torch, enc, audio, lengths):
+    rows = 2 * sum(oracle.position_count(oracle.frame_count(n)) for n in lengths)
+    out = torch.full((rows, enc.n_classes), float("nan"), dtype=torch.float32, device="cuda")
+    enc.forward_ctc(to_dev(torch, audio), lengths, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_forward_ctc_ragged(torch_mod, binding_mod):
+    # encoder (perturbed, 2 layers) + adapter (perturbed, 1000 classes) on a
+    # ragged batch: a clip spanning several attention tiles on the 40 ms grid,
+    # short clips, a one-position clip (two frames) and an empty clip
+    from oracle import ctc
+    torch = torch_mod
+    w = get_weights("perturbed")
+    cw = get_ctc("small")
+    lengths = [700_000, 33_000, 16_400, 400, 0]
+    audio, lengths = workloads.custom_audio(lengths, seed=101)
+    enc = binding_mod.Encoder(w, dtype="f32")
+    try:
+        enc.set_ctc(cw, dtype="f32")
+        got = run_ctc(torch, enc, audio, lengths)
+        again = run_ctc(torch, enc, audio, lengths)
+    finally:
+        enc.close()
+    np.testing.assert_array_equal(got, again)
+    r0 = 0
+    for b, n in enumerate(lengths):
+        f = 2 * oracle.position_count(oracle.frame_count(n))
+        if f:
+            ref = ctc.ctc_logprobs(audio[b, :n], w, cw)
+            check_logprobs(got[r0:r0 + f], ref, f"ctc clip {b} ({f} frames)")
+        r0 += f
+    assert r0 == got.shape[0]
+
+
+def test_forward_ctc_batch64_full_vocabulary(torch_mod, binding_mod):
+    # the 64-clip batch at full depth in bf16 with the full 23,863-way
+    # adapter; the shortest clip and clip 42 against the oracle
+    from oracle import ctc
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("batch64")
+    w = get_weights("bf16")
+    cw = get_ctc("full")
+    enc = binding_mod.Encoder(w, dtype="bf16")
+    try:
+        enc.set_ctc(cw)
+        assert enc.n_classes == 23_863
+        got = run_ctc(torch, enc, audio, lengths)
+    finally:
+        enc.close()
+    frames = [2 * oracle.position_count(oracle.frame_count(n)) for n in lengths]
+    starts = np.concatenate([[0], np.cumsum(frames)])
+    assert got.shape == (starts[-1], 23_863) and np.all(np.isfinite(got))
+    for b in (int(np.argmin(lengths)), 42):
+        say(f"oracle ctc batch64 clip {b}")
+        ref = ctc.ctc_logprobs(audio[b, :lengths[b]], w, cw)
+        check_logprobs(got[starts[b]:starts[b + 1]], ref, f"ctc batch64 clip {b}")
+
+
+def test_forward_ctc_errors(torch_mod, binding_mod):
+    torch = torch_mod
+    audio, lengths = workloads.workload_audio("tiny")
+    enc = binding_mod.Encoder(prefix(get_weights("tiny"), 2), dtype="f32")
+    try:
+        enc.n_classes = 1000
+        with pytest.raises(binding_mod.EncoderError):   # no adapter weights
+            enc.forward_ctc(to_dev(torch, audio), lengths)
+        enc.set_ctc(get_ctc("small"), dtype="f32")
+        out = enc.forward_ctc(to_dev(torch, np.zeros((2, 399), np.float32)), [10, 399])
+        torch.cuda.synchronize()
+        assert tuple(out.shape) == (0, 1000)
+    finally:
+        enc.close()
