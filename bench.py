@@ -9,10 +9,14 @@ the library's stream during the timed steps) and the CPU oracle timed on a
 bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                      [--attention CORE,CONTEXT] [--fused] [--precision bf16|fp8]
+                      [--attention CORE,CONTEXT] [--fused | --ctc] [--precision bf16|fp8]
 
 --fused runs the encoder through speaker fusion and the 1280 -> 2688 connector
 (synthetic speaker activity) instead of stopping at the embeddings.
+
+--ctc runs the encoder and the CTC timestamp adapter (upsampling to the 40 ms
+grid, two 16-head layers, 23,863-way projection, log-softmax) instead of
+stopping at the embeddings; flops count the adapter at its real head width.
 
 --precision fp8 runs the four linear maps of every layer on E4M3 codes with
 per-tensor scales (input scales from the library's calibration on the same
@@ -67,6 +71,19 @@ def sequences(pos, core=0, context=0):
         for c0 in range(0, p, core):
             out.append(min(p, c0 + core + context) - max(0, c0 - context))
     return out
+
+
+CTC_CLASSES, CTC_HEADS, CTC_DH, CTC_FFN = 23_863, 16, 80, 1280
+
+
+def ctc_flops(clip_pos):
+    """Algorithmic flops of the timestamp adapter on clips of P_b positions
+    (2 P_b frames each): upsampling, two layers at head width 80, projection."""
+    frames = [2 * p for p in clip_pos]
+    r = sum(frames)
+    layer = (2 * r * (3 * D * D + D * D + 2 * D * CTC_FFN)
+             + sum(4 * f * f * CTC_DH * CTC_HEADS for f in frames))
+    return 2 * sum(clip_pos) * D * 2 * D + 2 * layer + 2 * r * D * CTC_CLASSES
 
 
 def gemm_flops_per_layer(rows):
@@ -166,6 +183,8 @@ def main():
                     help="'full' or CORE,CONTEXT for windowed attention")
     ap.add_argument("--fused", action="store_true",
                     help="encoder + speaker fusion + connector (language-model input rows)")
+    ap.add_argument("--ctc", action="store_true",
+                    help="encoder + CTC timestamp adapter (log-probabilities on the 40 ms grid)")
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"],
                     help="linear maps of the layers in bf16 or FP8 (E4M3, per-tensor scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -218,7 +237,13 @@ def main():
     if fp8:
         amax = enc.calibrate(x, lengths)
         enc.set_precision("fp8", binding.scales_from_amax(amax))
-    if args.fused:
+    if args.ctc:
+        enc.set_ctc(workloads.make_ctc_weights(bf16=True))
+        out = torch.empty((2 * sum(clip_pos), enc.n_classes), dtype=torch.float32, device="cuda")
+
+        def step():
+            enc.forward_ctc(x, lengths, out=out)
+    elif args.fused:
         cw = workloads.make_connector_weights(bf16=True)
         enc.set_connector(cw)
         acts = np.concatenate([workloads.speaker_activity(p, seed=400 + b)
@@ -252,7 +277,10 @@ def main():
     # it is bracketed with HIP events on the library's stream during the timed steps.
     dom = "gemm_up"
     if breakdown:
-        dom = max(breakdown, key=lambda k: breakdown[k]["ms"])
+        # the slowest class that has a roofline model (flops or bytes)
+        known = [k for k in breakdown if kernel_flops(k, 1, [1]) is not None
+                 or kernel_bytes(k, 1, [1]) is not None]
+        dom = max(known, key=lambda k: breakdown[k]["ms"])
     binding.enc_profile_kernel(enc.ctx, dom)
 
     torch.cuda.synchronize()
@@ -275,6 +303,8 @@ def main():
                    + 2 * rows * D * DIN)
     if args.fused:
         total_flops += 2 * sum(clip_pos) * D * LLM
+    if args.ctc:
+        total_flops += ctc_flops(clip_pos)
     if fp8:
         # layer GEMMs at the fp8 peak, attention and the bf16 products at the bf16 peak
         f8_flops = n_layers * gemm_flops_per_layer(rows)
@@ -331,6 +361,7 @@ def main():
                    "attention": "full" if not core else f"windows core={core} context={context}",
                    "precision": args.precision,
                    "output": "fused + connector rows [R, 2688]" if args.fused
+                   else "CTC log-probabilities [2R, 23863] fp32" if args.ctc
                    else "embeddings [B, P_max, 1280]",
                    "algorithmic_tflop_per_step": round(total_flops / 1e12, 4)},
         "roofline": roof,
