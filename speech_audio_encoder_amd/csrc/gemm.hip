@@ -686,14 +686,15 @@ int num_cus() {
 }
 
 // Split K (into a divisor of K / 128 ranges) as far as the pieces that hold
-// rows stay within two workgroups per CU, and the partial sums of every piece
-// id within the partial buffer.
+// rows stay within one workgroup per CU (measured: two per CU, with twice the
+// partial sums to write and reduce, was 2% slower per encoder step), and the
+// partial sums of every piece id within the partial buffer.
 int choose_splits(int live_pieces, int grid_pieces, int K, int cus, size_t part_bytes) {
   const int units = K / (BKS * PNS);
   int splits = 1;
   for (int sp = 2; sp <= units; ++sp) {
     if (units % sp) continue;
-    if ((int64_t)live_pieces * sp > 2 * cus) break;
+    if ((int64_t)live_pieces * sp > cus) break;
     if ((size_t)grid_pieces * sp * PIECE * PIECE * sizeof(float) > part_bytes) break;
     splits = sp;
   }
