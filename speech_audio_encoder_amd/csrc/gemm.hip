@@ -207,7 +207,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   // only) re-read row M-1.
   //   bf16: the eight per-lane offsets are kept in registers (recomputed when
   //         the A tile changes).
-  //   FP8:  its larger fragments leave no registers for them: with
+  //   FP8 and the bf16-output epilogue (whose lane exchanges need the
+  //         registers): offsets computed per call: with
   //         row = 64q + 8t' + lane/8 (t' = t - 8q) the swizzle depends only on
   //         the parity of t' and on lane/16, so two offsets are computed per
   //         call and the 8t'-row step goes into the uniform base address.
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     int tm, tn;
     tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
     const int64_t am = (int64_t)tm * BIG;
-    if constexpr (!F8) {
+    if constexpr (!F8 && EPI != Epilogue::kBiasBf16) {
       if (is_a) {
         if (off_tile != r) {
 #pragma unroll
@@ -390,6 +391,60 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
     const int64_t mb = (int64_t)tm * BIG + grp * 128 + l32;
     const int nw = tn * BIG + q * 64;
+    // (measured: the bf16 GELU output, which also needs its load offsets
+    // cached for registers' sake, is faster with the plain stores below)
+    if constexpr (EPI == Epilogue::kBiasBf16 || EPI == Epilogue::kBiasGeluFp8) {
+      // Narrow outputs: lanes l and l + 32 hold the same row, columns
+      // 8 qq + 0..3 and 8 qq + 4..7.  Exchanging the packed chunks of qq = 2p
+      // and 2p + 1 between the two halves (v_permlane32_swap) leaves each lane
+      // 8 consecutive columns, so half as many, twice as wide stores.
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float4 bv[4];
+        load_bias32(bias, nw + i * 32, lhi, bv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t m = mb + j * 32;
+          uint32_t pk[4][2];
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v = acc[i][j][4 * qq + e];
+              if constexpr (F8) v *= alpha;
+              o[e] = v + (e == 0 ? bv[qq].x : e == 1 ? bv[qq].y : e == 2 ? bv[qq].z : bv[qq].w);
+              if constexpr (EPI != Epilogue::kBiasBf16) o[e] = gelu_erf(o[e]);
+            }
+            if constexpr (EPI == Epilogue::kBiasGeluFp8) {
+              pk[qq][0] = pack_fp8x4(o[0] * oscale, o[1] * oscale, o[2] * oscale, o[3] * oscale);
+              pk[qq][1] = 0;
+            } else {
+              pk[qq][0] = pack_bf16x2(o[0], o[1]);
+              pk[qq][1] = pack_bf16x2(o[2], o[3]);
+            }
+          }
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int n = nw + i * 32 + 16 * p + 8 * lhi;
+            const auto s0 = __builtin_amdgcn_permlane32_swap(pk[2 * p][0], pk[2 * p + 1][0],
+                                                             false, false);
+            if constexpr (EPI == Epilogue::kBiasGeluFp8) {
+              if (m < M)
+                *reinterpret_cast<uint2*>(reinterpret_cast<uint8_t*>(Cv) + m * ldc + n) =
+                    make_uint2(s0[0], s0[1]);
+            } else {
+              const auto s1 = __builtin_amdgcn_permlane32_swap(pk[2 * p][1], pk[2 * p + 1][1],
+                                                               false, false);
+              if (m < M)
+                *reinterpret_cast<uint4*>(reinterpret_cast<bf16_t*>(Cv) + m * ldc + n) =
+                    make_uint4(s0[0], s1[0], s0[1], s1[1]);
+            }
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       float4 bv[4];
