@@ -4,6 +4,11 @@ Two reports, written as Markdown under ``profiles/``:
 
 * ``kernels``: per-kernel calls / total / average duration from a
   ``--kernel-trace`` CSV (``<name>_kernel_trace.csv``);
+* ``mfma``: matrix-core use per kernel class from one ``--pmc`` run of
+  SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE and the MFMA op counters
+  (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F8, add+mul ops / 512): busy share of
+  all SIMDs' cycles while the GPU was active, and executed MFMA flops over
+  the dispatch durations against the dtype's dense peak;
 * ``traffic``: HBM bytes per dispatch from two ``--pmc`` runs (FETCH_SIZE,
   WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
   for a plain device copy of known size (``bench.py --copy-calibration-mib``),
@@ -14,6 +19,7 @@ Two reports, written as Markdown under ``profiles/``:
 
 Usage:
   python -m speech_audio_encoder_amd.prof_summary kernels TRACE_CSV OUT_MD "COMMAND"
+  python -m speech_audio_encoder_amd.prof_summary mfma COUNTER_CSV AGENT_CSV OUT_MD "COMMAND" [SKIP]
   python -m speech_audio_encoder_amd.prof_summary traffic WORKLOAD FETCH_CSV WRITE_CSV \\
       COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB OUT_MD "COMMANDS"
 """
@@ -62,8 +68,8 @@ def short_name(name):
 
 def epilogue_class(short):
     """Which GEMM a dispatch belongs to, from its epilogue (E0 bias->bf16:
-    qkv, or the connector after the speaker fusion; E1 GELU: up; E2 residual:
-    o and down alternate; E3 fp32: input)."""
+    qkv, or the connector after the speaker fusion; E1 GELU and E4 GELU to
+    E4M3: up; E2 residual: o and down alternate; E3 fp32: input)."""
     m = re.search(r"<E(\d)", short)
     return int(m.group(1)) if m else None
 
@@ -98,7 +104,7 @@ def classify(rows):
             e = epilogue_class(s)
             if e == 0:
                 cls = "connector" if after_fuse else "gemm_qkv"
-            elif e == 1:
+            elif e in (1, 4):
                 cls = "gemm_up"
             elif e == 3:
                 cls = "gemm_in"
@@ -110,6 +116,32 @@ def classify(rows):
         prev_e2 = is_e2
         out.append((cls, r))
     return out
+
+
+SINGLE_KERNEL = ("layernorm", "final_norm", "qknorm_rope", "attention", "speaker_fuse")
+
+
+def _dur_us(r):
+    return (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+
+
+def class_launches(rows):
+    """rows in dispatch order -> {class: (its dispatches, launches)}: a
+    launch is a run of consecutive dispatches of one class (a GEMM's big-tile
+    kernel, tail pieces and split-K reduce), or each dispatch of a class whose
+    launcher issues one kernel."""
+    per = collections.OrderedDict()
+    prev = None
+    for cls, r in classify(rows):
+        if cls is None:
+            prev = None
+            continue
+        e = per.setdefault(cls, [[], 0])
+        e[0].append(r)
+        if cls != prev or cls in SINGLE_KERNEL:
+            e[1] += 1
+        prev = cls
+    return per
 
 
 def kernels_report(trace_csv, out_md, command):
@@ -129,24 +161,66 @@ def kernels_report(trace_csv, out_md, command):
     # launch is one call of the library's launcher, e.g. a GEMM's big-tile
     # kernel plus its tail pieces and split-K reduce.
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-    per = collections.OrderedDict()
-    prev = None
-    for cls, r in classify(rows):
-        if cls is None:
-            prev = None
-            continue
-        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-        e = per.setdefault(cls, [0.0, 0])
-        e[0] += d
-        if cls != prev or cls in ("layernorm", "final_norm", "qknorm_rope", "attention",
-                                  "speaker_fuse"):
-            e[1] += 1
-        prev = cls
+    per = collections.OrderedDict(
+        (cls, [sum(_dur_us(r) for r in rs), n]) for cls, (rs, n) in class_launches(rows).items())
     lines += ["", "Per kernel class (one launch = one call of the library's launcher; "
               "dispatch durations summed):", "",
               "| class | launches | avg us per launch |", "|---|---:|---:|"]
     for cls, (t, n) in per.items():
         lines.append(f"| {cls} | {n} | {t / max(n, 1):.2f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+# Dense MFMA peaks of one MI355X (TFLOP/s), per operand type.
+MFMA_PEAK = {"bf16": 2500.0, "fp8": 5000.0}
+MOPS = {"bf16": "SQ_INSTS_VALU_MFMA_MOPS_BF16", "fp8": "SQ_INSTS_VALU_MFMA_MOPS_F8"}
+
+
+def mfma_report(counter_csv, agent_csv, out_md, command, skip=0):
+    """Per kernel class: MFMA busy share and executed MFMA throughput.
+
+    SQ_VALU_MFMA_BUSY_CYCLES counts per SIMD and GRBM_GUI_ACTIVE per XCD;
+    rocprofv3 sums each over its instances, so the busy share is
+    busy / (gui_active / n_xcd * n_simd).  The op counters count add and mul
+    operations / 512, so executed flops = ops * 512 (padding rows and masked
+    attention tiles included: the MFMAs a kernel issues, not the algorithm's
+    count).  skip: encoder passes (each opens with its log-mel dispatch) to
+    leave out at the start, e.g. an untimed calibration pass."""
+    agent = [r for r in csv.DictReader(open(agent_csv)) if int(r.get("Simd_Count") or 0) > 0][0]
+    n_simd, n_xcd = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+    disp = collections.OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        d = disp.setdefault(int(r["Dispatch_Id"]), dict(r))
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    rows = sorted(disp.values(), key=lambda r: int(r["Start_Timestamp"]))
+    if skip:
+        starts = [i for i, r in enumerate(rows) if "logmel" in short_name(r["Kernel_Name"])]
+        rows = rows[starts[skip]:] if len(starts) > skip else []
+    types = [t for t in MOPS if MOPS[t] in rows[0]] if rows else []
+    lines = ["# MFMA use per kernel class: " + os.path.basename(out_md)[:-3], "",
+             "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+             f"Agent: {agent.get('Name', '')}, {n_simd} SIMDs in {n_xcd} XCDs.  MFMA busy = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs x SIMDs), summed over the "
+             "class's dispatches; executed TFLOP = MFMA ops x 512 from the op counters; "
+             "TFLOP/s = executed flops / summed dispatch durations (counter collection "
+             "serialises dispatches, so short kernels read slightly low).", "",
+             "| class | launches | avg us | MFMA busy | " +
+             " | ".join(f"{t} TFLOP/launch" for t in types) + " | TFLOP/s | % of peak |",
+             "|---|---:|---:|---:|" + "---:|" * len(types) + "---:|---:|"]
+    for cls, (rs, n) in class_launches(rows).items():
+        busy = sum(r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for r in rs)
+        gui = sum(r.get("GRBM_GUI_ACTIVE", 0.0) for r in rs)
+        t_s = sum(_dur_us(r) for r in rs) / 1e6
+        fl = {t: sum(r.get(MOPS[t], 0.0) for r in rs) * 512 for t in types}
+        share = 100.0 * busy / (gui / n_xcd * n_simd) if gui else 0.0
+        rate = sum(fl.values()) / t_s / 1e12 if t_s else 0.0
+        # peak of the dominant operand type
+        dom = max(types, key=lambda t: fl[t]) if types and sum(fl.values()) else None
+        pct = f"{100 * rate / MFMA_PEAK[dom]:.1f}% {dom}" if dom else "-"
+        lines.append(f"| {cls} | {n} | {1e6 * t_s / max(n, 1):.1f} | {share:.1f}% | " +
+                     " | ".join(f"{fl[t] / max(n, 1) / 1e12:.4f}" for t in types) +
+                     f" | {rate:.1f} | {pct} |")
     with open(out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -234,6 +308,9 @@ def read_traffic(md_path):
 if __name__ == "__main__":
     if sys.argv[1] == "kernels":
         kernels_report(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "mfma":
+        mfma_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
+                    int(sys.argv[6]) if len(sys.argv) > 6 else 0)
     elif sys.argv[1] == "traffic":
         traffic_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                        int(sys.argv[7]), sys.argv[8], sys.argv[9])

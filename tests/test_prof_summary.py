@@ -36,3 +36,42 @@ def test_every_class_has_sources():
     for cls in prof_summary.CLASS_SOURCES:
         h = prof_summary.source_hashes(cls)
         assert h and all(len(v) == 64 for v in h.values())
+
+
+def test_classify_fp8_layer_and_launch_counts():
+    # the FP8 FFN up writes E4M3 codes (epilogue 4); it must not open a
+    # residual run, or up and down would be taken for o and down
+    fp8_layer = [k("layernorm_fp8_kernel"), gemm(0), k("qknorm_rope_kernel"),
+                 k("attention_kernel<true>"), gemm(2), k("layernorm_fp8_kernel"), gemm(4),
+                 gemm(2), gemm(2, True)]
+    rows = [k("logmel_kernel<true>"), gemm(3)] + fp8_layer * 2
+    got = [c for c, _ in prof_summary.classify(rows)]
+    one = ["layernorm", "gemm_qkv", "qknorm_rope", "attention", "gemm_o", "layernorm",
+           "gemm_up", "gemm_down", "gemm_down"]
+    assert got == ["frontend", "gemm_in"] + one * 2
+    per = prof_summary.class_launches(rows)
+    assert {c: n for c, (_, n) in per.items()} == {
+        "frontend": 1, "gemm_in": 1, "layernorm": 4, "gemm_qkv": 2, "qknorm_rope": 2,
+        "attention": 2, "gemm_o": 2, "gemm_up": 2, "gemm_down": 2}
+    assert len(per["gemm_down"][0]) == 4
+
+
+def test_mfma_report_busy_share(tmp_path):
+    # one GEMM dispatch, 1,024 SIMDs in 8 XCDs: GRBM_GUI_ACTIVE summed over the
+    # XCDs is 8 x 1000 cycles, busy cycles summed over the SIMDs 512,000 ->
+    # half the matrix-core cycles; 1e9 MOPS x 512 flops over 1 ms
+    agent = tmp_path / "agent.csv"
+    agent.write_text("Name,Simd_Count,Num_Xcc\ngfx950,1024,8\n")
+    ctr = tmp_path / "ctr.csv"
+    name = '"void enc::(anonymous namespace)::gemm_big_kernel<(enc::Epilogue)1, false>(int)"'
+    lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"]
+    for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 512000), ("GRBM_GUI_ACTIVE", 8000),
+                 ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e9)):
+        lines.append(f"1,{name},{c},{v},0,1000000")
+    ctr.write_text("\n".join(lines) + "\n")
+    out = tmp_path / "m.md"
+    prof_summary.mfma_report(str(ctr), str(agent), str(out), "cmd")
+    row = [ln for ln in out.read_text().splitlines() if ln.startswith("| gemm_up")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1] == "1" and cells[3] == "50.0%"
+    assert cells[4] == "0.5120" and cells[5] == "512.0" and cells[6] == "20.5% bf16"
