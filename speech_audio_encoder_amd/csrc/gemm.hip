@@ -45,21 +45,21 @@ constexpr int GROUP_M = 4;  // tile rows per ordering group
 
 // Exact-erf GELU, x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), with erf taken from
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-// erf(z) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+// erf(z) = 1 - P(t) exp(-z^2), P(t) = a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5,
 // t = 1 / (1 + p z), z >= 0, absolute error below 1.5e-7 -- far below the
-// bf16 rounding of the output -- at one reciprocal, one exponential and five
-// fused multiply-adds instead of a general-purpose erf.
+// bf16 rounding of the output.  With z = |x| / sqrt 2 both signs of x give
+// x Phi(x) = max(x, 0) - 0.5 |x| P(t) exp(-x^2 / 2), which takes one
+// reciprocal, one exponential (exp2 of -x^2 log2(e) / 2) and eleven other
+// operations (the 0.5 is folded into the coefficients).
 __device__ __forceinline__ float gelu_erf(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  const float e = 1.0f - poly * __expf(-z * z);      // erf(|x| / sqrt 2)
-  const float phi2 = x >= 0.0f ? 1.0f + e : 1.0f - e;  // 2 Phi(x)
-  return 0.5f * x * phi2;
+  const float a = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, a, 1.0f));
+  float p = fmaf(0.5f * 1.061405429f, t, 0.5f * -1.453152027f);
+  p = fmaf(p, t, 0.5f * 1.421413741f);
+  p = fmaf(p, t, 0.5f * -0.284496736f);
+  p = fmaf(p, t, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(x * (x * -0.72134752044448170f));
+  return fmaf(-(a * t) * p, e, x > 0.0f ? x : 0.0f);
 }
 
 // Big-tile coordinates of tile t: groups of GROUP_M tile rows, column-major

@@ -449,7 +449,12 @@ struct ProfScope {
     idx = c->prof_used;
     while (c->prof_events.size() < idx + 2) {
       hipEvent_t ev;
-      if (hipEventCreate(&ev) != hipSuccess) { on = false; return; }
+      // Timing only: no system-scope fence, whose L2 writeback and
+      // invalidation would stall and cool the caches for the bracketed launch.
+      if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) {
+        on = false;
+        return;
+      }
       c->prof_events.push_back(ev);
     }
     (void)hipEventRecord(c->prof_events[idx], s);
