@@ -7,9 +7,11 @@
 // "Local encoder windows, recording-wide language context" notes that
 // FlashAttention-style kernels avoid materialising the quadratic score matrix).
 //
-// Work split: a workgroup of two wavefronts takes 128 queries of one clip and
-// one head; each wavefront owns 64 queries (two blocks of 32), so every K or
-// V^T fragment read from LDS feeds two v_mfma_f32_32x32x16_bf16.  Scores are
+// Work split: a workgroup takes 128 queries of one clip and one head, either
+// as two wavefronts of 64 queries (two blocks of 32, so every K or V^T
+// fragment read from LDS feeds two v_mfma_f32_32x32x16_bf16) or, for short
+// sequences, as four wavefronts of 32 queries (half the registers per
+// wavefront, so two wavefronts share a SIMD and cover each other's waits).  Scores are
 // computed transposed, S^T = K Q^T, so a lane holds 16 keys of one query per
 // 32-key block: the softmax needs one cross-lane exchange (lanes l, l ^ 32)
 // per tile for the maximum and none for the sum.  Probabilities feed
@@ -50,14 +52,16 @@ namespace enc {
 
 namespace {
 
-constexpr int QPW = 64;                // queries per wavefront
-constexpr int NWAVE = 2;               // wavefronts per workgroup
-constexpr int QTILE = QPW * NWAVE;     // queries per workgroup (the plan's tiles)
+constexpr int QTILE = 128;             // queries per workgroup (the plan's tiles)
 constexpr int KT = 64;                 // keys per V^T tile
 constexpr int KU = 32;                 // keys per K unit (one score block)
 constexpr int KU_BYTES = KU * DH * 2;  // 8 KB
 constexpr int VT_BYTES = KT * DH * 2;  // 16 KB
-static_assert(QTILE == 128, "attention tiles of the plan are 128 queries");
+// Below this many keys per sequence the launcher takes the four-wavefront
+// form (one 32-query block per wavefront, half the registers, two wavefronts
+// per SIMD to cover each other's load waits); longer sequences keep two
+// wavefronts of two blocks, whose K and V^T fragments feed two MFMAs each.
+constexpr int SHORT_SEQ = 1024;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -79,8 +83,9 @@ __device__ __forceinline__ void lds_loads_wait() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool kFixedRef>
-__global__ __launch_bounds__(128) void attention_kernel(
+// QB: 32-query blocks per wavefront (2: two wavefronts per workgroup; 1: four).
+template <bool kFixedRef, int QB>
+__global__ __launch_bounds__(64 * (4 / QB)) void attention_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ vt, int64_t ld_vt,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
     const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_q0, int n_tiles,
@@ -102,6 +107,10 @@ __global__ __launch_bounds__(128) void attention_kernel(
   const int q0 = tile_q0[tile];
   const int nkt = (len + KT - 1) / KT;   // 64-key tiles
   const int nku = 2 * nkt;               // 32-key units
+  constexpr int QPW = 32 * QB;           // queries per wavefront
+  constexpr int NW = QTILE / QPW;        // wavefronts per workgroup
+  constexpr int KP = 8 / NW;             // 1-KB pieces of a K unit per wavefront
+  constexpr int VP = 16 / NW;            // 1-KB pieces of a V^T tile per wavefront
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -110,9 +119,9 @@ __global__ __launch_bounds__(128) void attention_kernel(
   const int lhi = lane >> 5;
 
   // Q^T fragments: query block qb, 16-dim step s.
-  bf16x8 qf[2][DH / 16];
+  bf16x8 qf[QB][DH / 16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int q = q0 + wave * QPW + qb * 32 + l32;
     const bool ok = q < len;
     const bf16_t* qrow = qkv + (s0 + (ok ? q : 0)) * (3 * hd) + h * DH + lhi * 8;
@@ -125,70 +134,74 @@ __global__ __launch_bounds__(128) void attention_kernel(
 
   // Direct loads.  A K unit is eight 1-KB pieces (keys 4i..4i+3; lane -> key
   // 4i + lane/16, LDS chunk lane%16 holds global chunk (lane%16) ^ (key%16)),
-  // this wave loads pieces 4*wave..4*wave+3.  A V^T tile is sixteen pieces
-  // (dims 8i..8i+7; lane -> dim 8i + lane/8, LDS chunk lane%8 holds global
-  // chunk (lane%8) ^ ((dim/2)%8)), this wave loads 8*wave..8*wave+7.
-  // Offsets are bytes from the unit's / tile's origin.
-  uint32_t koff[4], voff[8];
+  // this wave loads pieces KP*wave..KP*wave+KP-1.  A V^T tile is sixteen
+  // pieces (dims 8i..8i+7; lane -> dim 8i + lane/8, LDS chunk lane%8 holds
+  // global chunk (lane%8) ^ ((dim/2)%8)), this wave loads VP*wave..
+  // VP*wave+VP-1.  Offsets are bytes from the unit's / tile's origin.
+  uint32_t koff[KP], voff[VP];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int key = (wave * 4 + t) * 4 + (lane >> 4);
+  for (int t = 0; t < KP; ++t) {
+    const int key = (wave * KP + t) * 4 + (lane >> 4);
     koff[t] = (uint32_t)(key * (3 * hd * 2) + (((lane & 15) ^ (key & 15)) * 16));
   }
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int d = (wave * 8 + t) * 8 + (lane >> 3);
+  for (int t = 0; t < VP; ++t) {
+    const int d = (wave * VP + t) * 8 + (lane >> 3);
     voff[t] = (uint32_t)(d * (uint32_t)ld_vt * 2 + (((lane & 7) ^ ((d >> 1) & 7)) * 16));
   }
   const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + hd + h * DH);
   const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)h * DH * ld_vt + vt_base[seq]);
-  const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_void*)&sK[0][0] + wave * 4 * 1024;
-  const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0] + wave * 8 * 1024;
+  const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_void*)&sK[0][0] + wave * KP * 1024;
+  const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0] + wave * VP * 1024;
   // K unit u into ring slot u % 4.  Units past the clip's last one re-load
   // the last unit into a slot that is never read again (no branch).
   auto issue_k = [&](int u) __attribute__((always_inline)) {
     const char* g = kbase + (int64_t)min(u, nku - 1) * KU * (3 * hd * 2);
     const uint32_t l = k_lds + (u & 3) * KU_BYTES;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dma16(g + koff[t], l + t * 1024);
+    for (int t = 0; t < KP; ++t) dma16(g + koff[t], l + t * 1024);
   };
   // V^T tile j into buffer j % 2.
   auto issue_v = [&](int j) __attribute__((always_inline)) {
     const char* g = vbase + (int64_t)j * KT * 2;
     const uint32_t l = v_lds + (j & 1) * VT_BYTES;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) dma16(g + voff[t], l + t * 1024);
+    for (int t = 0; t < VP; ++t) dma16(g + voff[t], l + t * 1024);
   };
 
   // Scores arrive in log2 units (k was scaled by log2(e) / sqrt(128)).
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};    // this lane's partial row sums
+  float m_run[QB], l_run[QB];     // running maxima; this lane's partial row sums
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+  }
 
-  f32x16 O[DH / 32][2];
+  f32x16 O[DH / 32][QB];
 #pragma unroll
   for (int db = 0; db < DH / 32; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) O[db][qb][v] = 0.f;
 
-  f32x16 SA[2], SB[2];   // scores of one 32-key unit, per query block
+  f32x16 SA[QB], SB[QB];   // scores of one 32-key unit, per query block
 
   const int kx = lhi ^ (l32 & 15);          // K chunk swizzle of this lane
   const int vx = lhi ^ ((l32 >> 1) & 7);    // V^T chunk swizzle of this lane
 
   // S^T of unit u: 8 k-steps x 2 query blocks.
-  auto qk = [&](f32x16 (&S)[2], int u) __attribute__((always_inline)) {
+  auto qk = [&](f32x16 (&S)[QB], int u) __attribute__((always_inline)) {
     const uint4* sk = sK[u & 3];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) S[qb][v] = 0.f;
 #pragma unroll
     for (int s = 0; s < DH / 16; ++s) {
       const bf16x8 kf = __builtin_bit_cast(bf16x8, sk[l32 * 16 + ((2 * s) ^ kx)]);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
         S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], S[qb], 0, 0, 0);
     }
   };
@@ -196,11 +209,11 @@ __global__ __launch_bounds__(128) void attention_kernel(
   // Mask keys past the clip (unit u).  With a running maximum: take the
   // unit's maximum and rescale the accumulators if some query's maximum grew
   // by more than 8.
-  auto decide = [&](f32x16 (&S)[2], int u) __attribute__((always_inline)) {
+  auto decide = [&](f32x16 (&S)[QB], int u) __attribute__((always_inline)) {
     const int kv0 = u * KU;
     if (kv0 + KU > len) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kv0 + 8 * (v >> 2) + 4 * lhi + (v & 3);
@@ -208,17 +221,19 @@ __global__ __launch_bounds__(128) void attention_kernel(
         }
     }
     if constexpr (!kFixedRef) {
-      float mx[2];
+      float mx[QB];
+      bool grew = false;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         float m = S[qb][0];
 #pragma unroll
         for (int v = 1; v < 16; ++v) m = fmaxf(m, S[qb][v]);
         mx[qb] = fmaxf(m, __shfl_xor(m, 32, 64));
+        grew = grew || mx[qb] > m_run[qb] + 8.0f;
       }
-      if (__any(mx[0] > m_run[0] + 8.0f || mx[1] > m_run[1] + 8.0f)) {
+      if (__any(grew)) {
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        for (int qb = 0; qb < QB; ++qb) {
           const float mn = fmaxf(m_run[qb], mx[qb]);
           const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
           l_run[qb] *= alpha;
@@ -235,15 +250,15 @@ __global__ __launch_bounds__(128) void attention_kernel(
   // Probabilities of one unit and O^T += V^T P^T over its two 16-key steps
   // (kk0, kk0 + 1 of V^T tile j).  Row sums take the bf16 probabilities the
   // products use (one dot2 per pair).
-  auto expv = [&](f32x16 (&S)[2], int j, int kk0) __attribute__((always_inline)) {
+  auto expv = [&](f32x16 (&S)[QB], int j, int kk0) __attribute__((always_inline)) {
     const uint4* sv = sV[j & 1];
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      bf16x8 pf[2];
+      bf16x8 pf[QB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         const float nm = kFixedRef ? 0.f : -m_run[qb];
         uint32_t pk[4];
 #pragma unroll
@@ -264,7 +279,7 @@ __global__ __launch_bounds__(128) void attention_kernel(
       for (int db = 0; db < DH / 32; ++db) {
         const bf16x8 vf = __builtin_bit_cast(bf16x8, sv[(db * 32 + l32) * 8 + ((2 * kk) ^ vx)]);
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < QB; ++qb)
           O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
       }
     }
@@ -318,7 +333,7 @@ __global__ __launch_bounds__(128) void attention_kernel(
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
     const int q = q0 + wave * QPW + qb * 32 + l32;
     if (q >= len) continue;
@@ -378,7 +393,8 @@ bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
                             const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
-                            bool fixed_ref, void* out, float out_scale, hipStream_t stream) {
+                            int max_len, bool fixed_ref, void* out, float out_scale,
+                            hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   // V^T byte offsets inside a tile are 32-bit: 128 rows of ld_vt bf16.
   if (ld_vt <= 0 || ld_vt % 64 != 0 || (int64_t)DH * ld_vt * 2 >= (int64_t)1 << 31)
@@ -389,15 +405,15 @@ hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
   const int n_items = n_tiles * n_heads;
   const int hd = n_heads * DH;
   const int grid = (n_items + 7) / 8 * 8;
-  if (fixed_ref)
-    attention_kernel<true><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
-        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale, hd,
-        head_dim);
-  else
-    attention_kernel<false><<<dim3(grid), dim3(QTILE / QPW * 64), 0, stream>>>(
-        qkv, vt, ld_vt, cu_seq, vt_base, tile_seq, tile_q0, n_tiles, n_items, out, out_scale, hd,
-        head_dim);
-  return hipGetLastError();
+  auto go = [&](auto kernel, int threads) {
+    kernel<<<dim3(grid), dim3(threads), 0, stream>>>(qkv, vt, ld_vt, cu_seq, vt_base, tile_seq,
+                                                     tile_q0, n_tiles, n_items, out, out_scale,
+                                                     hd, head_dim);
+    return hipGetLastError();
+  };
+  if (max_len < SHORT_SEQ)
+    return fixed_ref ? go(attention_kernel<true, 1>, 256) : go(attention_kernel<false, 1>, 256);
+  return fixed_ref ? go(attention_kernel<true, 2>, 128) : go(attention_kernel<false, 2>, 128);
 }
 
 }  // namespace enc
