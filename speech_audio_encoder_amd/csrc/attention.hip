@@ -7,11 +7,12 @@
 // "Local encoder windows, recording-wide language context" notes that
 // FlashAttention-style kernels avoid materialising the quadratic score matrix).
 //
-// Work split: a workgroup takes 128 queries of one clip and one head, either
-// as two wavefronts of 64 queries (two blocks of 32, so every K or V^T
-// fragment read from LDS feeds two v_mfma_f32_32x32x16_bf16) or, for short
-// sequences, as four wavefronts of 32 queries (half the registers per
-// wavefront, so two wavefronts share a SIMD and cover each other's waits).  Scores are
+// Work split: a workgroup of four wavefronts takes 128 queries of one clip
+// and one head, 32 queries per wavefront.  (Two wavefronts of 64 queries, in
+// which every K or V^T fragment read from LDS feeds two MFMAs, need twice the
+// accumulator registers and leave one wavefront per SIMD; with 32 queries two
+// wavefronts share each SIMD and cover each other's load waits, which
+// measured faster from 5 s clips to one hour.)  Scores are
 // computed transposed, S^T = K Q^T, so a lane holds 16 keys of one query per
 // 32-key block: the softmax needs one cross-lane exchange (lanes l, l ^ 32)
 // per tile for the maximum and none for the sum.  Probabilities feed
@@ -57,11 +58,11 @@ constexpr int KT = 64;                 // keys per V^T tile
 constexpr int KU = 32;                 // keys per K unit (one score block)
 constexpr int KU_BYTES = KU * DH * 2;  // 8 KB
 constexpr int VT_BYTES = KT * DH * 2;  // 16 KB
-// Below this many keys per sequence the launcher takes the four-wavefront
-// form (one 32-query block per wavefront, half the registers, two wavefronts
-// per SIMD to cover each other's load waits); longer sequences keep two
-// wavefronts of two blocks, whose K and V^T fragments feed two MFMAs each.
-constexpr int SHORT_SEQ = 1024;
+constexpr int QB = 1;                  // 32-query blocks per wavefront
+constexpr int QPW = 32 * QB;           // queries per wavefront
+constexpr int NW = QTILE / QPW;        // wavefronts per workgroup
+constexpr int KP = 8 / NW;             // 1-KB pieces of a K unit per wavefront
+constexpr int VP = 16 / NW;            // 1-KB pieces of a V^T tile per wavefront
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -83,9 +84,8 @@ __device__ __forceinline__ void lds_loads_wait() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// QB: 32-query blocks per wavefront (2: two wavefronts per workgroup; 1: four).
-template <bool kFixedRef, int QB>
-__global__ __launch_bounds__(64 * (4 / QB)) void attention_kernel(
+template <bool kFixedRef>
+__global__ __launch_bounds__(64 * NW) void attention_kernel(
     const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ vt, int64_t ld_vt,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
     const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_q0, int n_tiles,
@@ -107,10 +107,6 @@ __global__ __launch_bounds__(64 * (4 / QB)) void attention_kernel(
   const int q0 = tile_q0[tile];
   const int nkt = (len + KT - 1) / KT;   // 64-key tiles
   const int nku = 2 * nkt;               // 32-key units
-  constexpr int QPW = 32 * QB;           // queries per wavefront
-  constexpr int NW = QTILE / QPW;        // wavefronts per workgroup
-  constexpr int KP = 8 / NW;             // 1-KB pieces of a K unit per wavefront
-  constexpr int VP = 16 / NW;            // 1-KB pieces of a V^T tile per wavefront
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -393,8 +389,7 @@ bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
                             const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
-                            int max_len, bool fixed_ref, void* out, float out_scale,
-                            hipStream_t stream) {
+                            bool fixed_ref, void* out, float out_scale, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   // V^T byte offsets inside a tile are 32-bit: 128 rows of ld_vt bf16.
   if (ld_vt <= 0 || ld_vt % 64 != 0 || (int64_t)DH * ld_vt * 2 >= (int64_t)1 << 31)
@@ -405,15 +400,11 @@ hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
   const int n_items = n_tiles * n_heads;
   const int hd = n_heads * DH;
   const int grid = (n_items + 7) / 8 * 8;
-  auto go = [&](auto kernel, int threads) {
-    kernel<<<dim3(grid), dim3(threads), 0, stream>>>(qkv, vt, ld_vt, cu_seq, vt_base, tile_seq,
-                                                     tile_q0, n_tiles, n_items, out, out_scale,
-                                                     hd, head_dim);
-    return hipGetLastError();
-  };
-  if (max_len < SHORT_SEQ)
-    return fixed_ref ? go(attention_kernel<true, 1>, 256) : go(attention_kernel<false, 1>, 256);
-  return fixed_ref ? go(attention_kernel<true, 2>, 128) : go(attention_kernel<false, 2>, 128);
+  auto kernel = fixed_ref ? attention_kernel<true> : attention_kernel<false>;
+  kernel<<<dim3(grid), dim3(64 * NW), 0, stream>>>(qkv, vt, ld_vt, cu_seq, vt_base, tile_seq,
+                                                   tile_q0, n_tiles, n_items, out, out_scale, hd,
+                                                   head_dim);
+  return hipGetLastError();
 }
 
 }  // namespace enc

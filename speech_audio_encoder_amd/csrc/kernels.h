@@ -152,13 +152,11 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
 // +-448), one byte per element in the same layout.
 // qkv must have 63 readable rows after its last one (their k is masked), and
 // vt's columns hold keys permuted inside each group of 16 as written by
-// launch_qknorm_rope.  max_len (the longest sequence) only picks the kernel
-// form; any value gives the same result.
+// launch_qknorm_rope.
 hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
                             const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
                             const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
-                            int max_len, bool fixed_ref, void* out, float out_scale,
-                            hipStream_t stream);
+                            bool fixed_ref, void* out, float out_scale, hipStream_t stream);
 // fixed_ref may be true only when |q . k| * log2(e) / sqrt(128) <= 100 for
 // every query and key (softmax against a fixed reference instead of a
 // running maximum); attention_fixed_ref_ok decides it from the QK-norm

@@ -223,13 +223,6 @@ int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles,
   return ENC_OK;
 }
 
-// Longest sequence of offsets cu.
-int max_seq(const std::vector<int32_t>& cu) {
-  int m = 0;
-  for (size_t s = 0; s + 1 < cu.size(); ++s) m = std::max(m, cu[s + 1] - cu[s]);
-  return m;
-}
-
 void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* vt_base, int64_t* vt_cols,
                std::vector<int32_t>* tile_seq, std::vector<int32_t>* tile_q0) {
   const int n = (int)cu.size() - 1;
@@ -794,7 +787,7 @@ int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_c
                                   stream));
     ENC_LAUNCH(ENC_K_CTC,
                launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, CTC_HEADS,
-                                CTC_DH, max_seq(p.a_cu), L.attn_fixed_ref, o, 0.0f, stream));
+                                CTC_DH, L.attn_fixed_ref, o, 0.0f, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasResidualF32, o, D, L.w_o, D, L.b_o, x, D, R,
                                       D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_layernorm(x, L.ln2_g, L.ln2_b, a, R, stream));
@@ -928,8 +921,7 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                   stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
                launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, H, DH,
-                                max_seq(p.cu_seq), Lw.attn_fixed_ref, o,
-                                fp8 ? Lw.r_x[1] : 0.0f, stream));
+                                Lw.attn_fixed_ref, o, fp8 ? Lw.r_x[1] : 0.0f, stream));
     if (fp8) {
       ENC_LAUNCH(ENC_K_GEMM_O,
                  launch_gemm_fp8(Epilogue::kBiasResidualF32, o8, D, Lw.q8[1], D, Lw.alpha[1],
