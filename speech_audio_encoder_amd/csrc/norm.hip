@@ -188,6 +188,7 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict
 // The clip's keys occupy columns [vt_base[b], vt_base[b] + roundup(P_b, 64))
 // of vt; columns past P_b are written as zeros.
 constexpr int QK_ROWS = 128;
+constexpr int QK_HEAD_GROUPS = 5;   // measured: 2 heads per group for 10 heads
 
 __device__ __forceinline__ void unpack8(const uint4 u, float (&f)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -198,24 +199,30 @@ __device__ __forceinline__ void unpack8(const uint4 u, float (&f)[8]) {
   }
 }
 
-// q and k of one tile x head: normalise, rotate, scale k (in place).
+// q and k of 32 positions (8 per wavefront, 8 lanes per position) over all
+// heads: normalise, rotate, scale k (in place).  The QK-norm gains and biases
+// (shared by the heads) and the position's rotation table row are loaded once
+// and serve every head; the next head's q and k are loaded while the current
+// one is computed.
 // HALF = half the head width (rotation pairs (i, i + HALF)): 64 for the
 // encoder's heads, 40 for the timestamp adapter's (head slots stay 128 wide,
 // dims 2 HALF .. 127 are zero and untouched).  ldq: row stride of qkv, hd:
 // offset of the k block within a row (heads x 128), kscale: factor on k.
 template <int HALF>
-__device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t ldq, int hd, int64_t s0,
-                                        int len, int p0, int h, int lane, int wave,
+__device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, int hd, int h0,
+                                        int h1, int64_t s0, int len, int p, int lane,
                                         const float* __restrict__ qg,
                                         const float* __restrict__ qb, const float* __restrict__ kg,
                                         const float* __restrict__ kb,
                                         const float* __restrict__ rope_cos,
                                         const float* __restrict__ rope_sin, float kscale) {
+  if (h0 >= h1) return;          // an empty group (heads not divisible)
   constexpr float INV_DH = 1.0f / (2 * HALF);
   const int sub = lane & 7;     // dims 8 sub .. + 7 and HALF + 8 sub .. + 7
-  const int grp = lane >> 3;    // row within the wavefront's 8
   const bool act = sub < HALF / 8;   // lanes past the head width idle
   const int d0 = (act ? sub : 0) * 8;
+  const bool live = p < len;    // uniform over the 8 lanes of the row
+  const int pl = live ? p : 0;  // rows past the clip read row 0 and store nothing
   float gq[2][8], bq[2][8], gk[2][8], bk[2][8];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
@@ -226,44 +233,36 @@ __device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t ldq, i
       gk[hh][e] = kg[hh * HALF + d0 + e];
       bk[hh][e] = kb[hh * HALF + d0 + e];
     }
-
-  // Every load is issued before the first store (rows are updated in place,
-  // so the compiler could not move a later row's loads above an earlier
-  // row's stores).  Rows past the clip re-read row p0 and are not stored.
-  constexpr int NR = QK_ROWS / 32;   // passes of 32 rows (4 wavefronts x 8)
-  uint4 uq[NR][2], uk[NR][2];
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int p = p0 + i * 32 + wave * 8 + grp;
-    const int pl = p < len ? p : p0;
-    const bf16_t* base = qkv + (s0 + pl) * ldq + h * DH + d0;
-    uq[i][0] = *reinterpret_cast<const uint4*>(base);
-    uq[i][1] = *reinterpret_cast<const uint4*>(base + HALF);
-    uk[i][0] = *reinterpret_cast<const uint4*>(base + hd);
-    uk[i][1] = *reinterpret_cast<const uint4*>(base + hd + HALF);
+  float cs[8], sn[8];
+  {
+    const float4 c0 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * HALF + d0);
+    const float4 c1 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * HALF + d0 + 4);
+    const float4 s0v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * HALF + d0);
+    const float4 s1v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * HALF + d0 + 4);
+    cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w;
+    cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
+    sn[0] = s0v.x; sn[1] = s0v.y; sn[2] = s0v.z; sn[3] = s0v.w;
+    sn[4] = s1v.x; sn[5] = s1v.y; sn[6] = s1v.z; sn[7] = s1v.w;
   }
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-    const int p = p0 + i * 32 + wave * 8 + grp;
-    const bool live = p < len;   // uniform over the 8 lanes of the row
-    const int pl = live ? p : p0;
-    const uint4 uq0 = uq[i][0], uq1 = uq[i][1], uk0 = uk[i][0], uk1 = uk[i][1];
-    float cs[8], sn[8];
-    {
-      const float4 c0 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * HALF + d0);
-      const float4 c1 = *reinterpret_cast<const float4*>(rope_cos + (int64_t)pl * HALF + d0 + 4);
-      const float4 s0v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * HALF + d0);
-      const float4 s1v = *reinterpret_cast<const float4*>(rope_sin + (int64_t)pl * HALF + d0 + 4);
-      cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w;
-      cs[4] = c1.x; cs[5] = c1.y; cs[6] = c1.z; cs[7] = c1.w;
-      sn[0] = s0v.x; sn[1] = s0v.y; sn[2] = s0v.z; sn[3] = s0v.w;
-      sn[4] = s1v.x; sn[5] = s1v.y; sn[6] = s1v.z; sn[7] = s1v.w;
-    }
+  bf16_t* row = qkv + (s0 + pl) * ldq + d0;
+  // u[0..1]: q dims d0.. and HALF + d0..; u[2..3]: the same of k
+  auto load = [&](int h, uint4 (&u)[4]) __attribute__((always_inline)) {
+    const bf16_t* base = row + h * DH;
+    u[0] = *reinterpret_cast<const uint4*>(base);
+    u[1] = *reinterpret_cast<const uint4*>(base + HALF);
+    u[2] = *reinterpret_cast<const uint4*>(base + hd);
+    u[3] = *reinterpret_cast<const uint4*>(base + hd + HALF);
+  };
+  uint4 cur[4], nxt[4];
+  load(h0, cur);
+#pragma unroll 1
+  for (int h = h0; h < h1; ++h) {
+    if (h + 1 < h1) load(h + 1, nxt);
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       float a[8], b[8];
-      unpack8(which ? uk0 : uq0, a);
-      unpack8(which ? uk1 : uq1, b);
+      unpack8(cur[2 * which], a);
+      unpack8(cur[2 * which + 1], b);
       float sum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum += a[e] + b[e];
@@ -304,11 +303,13 @@ __device__ __forceinline__ void qk_part(bf16_t* __restrict__ qkv, int64_t ldq, i
         hi[e / 2] = pack_bf16x2(y1[0], y1[1]);
       }
       if (live && act) {
-        bf16_t* base = qkv + (s0 + p) * ldq + which * hd + h * DH + d0;
+        bf16_t* base = row + which * hd + h * DH;
         *reinterpret_cast<uint4*>(base) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         *reinterpret_cast<uint4*>(base + HALF) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       }
     }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cur[t] = nxt[t];
   }
 }
 
@@ -319,22 +320,35 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
     const float* __restrict__ qg, const float* __restrict__ qb, const float* __restrict__ kg,
     const float* __restrict__ kb, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, bf16_t* __restrict__ vt, int64_t ld_vt, int hd,
-    float kscale) {
+    int n_tiles, int n_heads, int hgroups, float kscale) {
   const int64_t ldq = 3 * (int64_t)hd;
-  const int h = blockIdx.y;
-  const int seq = tile_seq[blockIdx.x];
-  const int p0 = tile_p0[blockIdx.x];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  // Blocks [0, n_qk): q and k of a quarter tile (32 positions) for one of
+  // `hgroups` groups of heads; then one block per tile x head for v.
+  constexpr int QUARTERS = QK_ROWS / 32;
+  const int n_qk = n_tiles * QUARTERS * hgroups;
+  if ((int)blockIdx.x < n_qk) {
+    const int hg = blockIdx.x % hgroups;
+    const int tq = blockIdx.x / hgroups;
+    const int t = tq / QUARTERS;
+    const int seq = tile_seq[t];
+    const int len = cu[seq + 1] - cu[seq];
+    const int p = tile_p0[t] + (tq % QUARTERS) * 32 + wave * 8 + (lane >> 3);
+    if (__builtin_amdgcn_readfirstlane(p - (lane >> 3)) >= len) return;   // no live row
+    const int per = (n_heads + hgroups - 1) / hgroups;
+    qk_rows<HALF>(qkv, ldq, hd, hg * per, min(n_heads, (hg + 1) * per), cu[seq], len, p, lane,
+                  qg, qb, kg, kb, rope_cos, rope_sin, kscale);
+    return;
+  }
+  const int vb = blockIdx.x - n_qk;
+  const int h = vb % n_heads;
+  const int tile = vb / n_heads;
+  const int seq = tile_seq[tile];
+  const int p0 = tile_p0[tile];
   const int64_t s0 = cu[seq];
   const int len = cu[seq + 1] - cu[seq];
   const int span = min(QK_ROWS, ((len + 63) & ~63) - p0);   // rows incl. zero padding
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-
-  if (blockIdx.z == 0) {
-    qk_part<HALF>(qkv, ldq, hd, s0, len, p0, h, lane, wave, qg, qb, kg, kb, rope_cos, rope_sin,
-                  kscale);
-    return;
-  }
   // v thread map: wavefront w covers position blocks 8 (w & 1) .. + 7 and dim
   // blocks 8 (w >> 1) .. + 7; lane -> (position block lane % 8, dim block
   // lane / 8).
@@ -596,14 +610,21 @@ hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t*
   const int hd = n_heads * DH;
   // log2(e) / sqrt(head width)
   const float kscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
+  // the heads are split into QK_HEAD_GROUPS groups, one q/k block per group
+  // and quarter tile (the gains and the rotation table row are loaded once
+  // per group)
+  const int hgroups = std::min(n_heads, QK_HEAD_GROUPS);
+  const int64_t blocks =
+      (int64_t)n_tiles * (QK_ROWS / 32) * hgroups + (int64_t)n_tiles * n_heads;
+  if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (head_dim == DH)
-    qknorm_rope_kernel<DH / 2><<<dim3(n_tiles, n_heads, 2), dim3(256), 0, stream>>>(
+    qknorm_rope_kernel<DH / 2><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt,
-        hd, kscale);
+        hd, n_tiles, n_heads, hgroups, kscale);
   else if (head_dim == 80)
-    qknorm_rope_kernel<40><<<dim3(n_tiles, n_heads, 2), dim3(256), 0, stream>>>(
+    qknorm_rope_kernel<40><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
         qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt,
-        hd, kscale);
+        hd, n_tiles, n_heads, hgroups, kscale);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
