@@ -220,6 +220,23 @@ def test_forward_batch64_sampled_clips(torch_mod, ctx_for):
         check_embeddings(got[b, :pos[b]], ref, f"batch64 clip {b}")
 
 
+def test_forward_many_clips_offsets_in_global_memory(torch_mod, ctx_for):
+    # Batches of more than 2,048 clips take the frontend's search for a frame's
+    # clip through global memory instead of its LDS copy of the offsets.
+    torch = torch_mod
+    n_clips = 2100
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(1300, 6000, size=n_clips)
+    audio, lengths = workloads.custom_audio(lengths, seed=78)
+    got = run_forward(torch, ctx_for("tiny", 2, "f32"), audio, lengths)
+    pos = [oracle.position_count(oracle.frame_count(int(n))) for n in lengths]
+    assert got.shape == (n_clips, max(pos), 1280)
+    for b in (0, 1, 2046, 2047, 2048, 2049, n_clips - 1):
+        ref = oracle.encode(audio[b, :lengths[b]], get_weights("tiny"))
+        assert np.all(got[b, pos[b]:] == 0.0)
+        check_embeddings(got[b, :pos[b]], ref, f"clip {b} of {n_clips}")
+
+
 def test_forward_long10m_two_layers(torch_mod, ctx_for):
     torch = torch_mod
     audio, lengths = workloads.workload_audio("long10m")
