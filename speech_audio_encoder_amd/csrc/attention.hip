@@ -16,11 +16,12 @@
 // computed transposed, S^T = K Q^T, so a lane holds 16 keys of one query per
 // 32-key block: the softmax needs one cross-lane exchange (lanes l, l ^ 32)
 // per tile for the maximum and none for the sum.  Probabilities feed
-// O^T += V^T P^T straight from registers; V arrives transposed per head
-// ([dim][key], keys permuted inside each group of 16 so that a lane's eight
-// operand keys are one 16-byte chunk).
+// O^T += V^T P^T straight from registers.  V stays in the qkv rows as the QKV
+// product wrote it ([key][dim]); its V^T operands come from the row-major LDS
+// tile through the transposing LDS read (ds_read_b64_tr_b16), whose addresses
+// also pick the keys in the order of the probabilities' accumulator layout.
 //
-// Pipeline: K goes global -> LDS in 32-key units (a ring of four) and V^T in
+// Pipeline: K goes global -> LDS in 32-key units (a ring of four) and V in
 // 64-key tiles (two buffers) by direct loads (global_load_lds, 16 bytes per
 // lane, swizzle applied on the global side), one barrier per 64 keys.  The
 // scores of unit u + 1 are issued to the matrix cores in the same basic block
@@ -40,8 +41,7 @@
 //
 // Keys past the clip end: their K rows (read from whatever follows in the qkv
 // buffer, which has 64 rows of slack) are masked to -inf by a select in the
-// clip's last tile; their V^T columns (up to the next multiple of 64) are
-// zero.
+// clip's last tile; their V rows repeat the clip's last row (probability 0).
 
 #include <algorithm>
 #include <cmath>
@@ -65,6 +65,8 @@ constexpr int KP = 8 / NW;             // 1-KB pieces of a K unit per wavefront
 constexpr int VP = 16 / NW;            // 1-KB pieces of a V^T tile per wavefront
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
 // 16 bytes per lane from g to LDS byte address lds + 16 * lane (lds is
 // wave-uniform).  Written in asm so that the compiler does not track it: it
@@ -86,13 +88,12 @@ __device__ __forceinline__ void lds_loads_wait() {
 
 template <bool kFixedRef>
 __global__ __launch_bounds__(64 * NW) void attention_kernel(
-    const bf16_t* __restrict__ qkv, const bf16_t* __restrict__ vt, int64_t ld_vt,
-    const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
+    const bf16_t* __restrict__ qkv, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_q0, int n_tiles,
     int n_items, void* __restrict__ out, float out_scale, int hd, int dh_out) {
-  // K in a ring of four 32-key units, V^T in two 64-key tiles.
+  // K in a ring of four 32-key units, V in two 64-key tiles.
   __shared__ uint4 sK[4][KU * DH / 8];   // [key][16 chunks of 8 dims], swizzled
-  __shared__ uint4 sV[2][DH * KT / 8];   // [dim][8 chunks of 8 keys], swizzled
+  __shared__ uint4 sV[2][KT * DH / 8];   // [key][16 chunks of 8 dims], swizzled
 
   // Hardware block b runs on XCD b % 8; XCD x takes items [x * per, x * per +
   // per) so that the workgroups resident on one XCD walk the same head's keys.
@@ -128,13 +129,13 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     }
   }
 
-  // Direct loads.  A K unit is eight 1-KB pieces (keys 4i..4i+3; lane -> key
-  // 4i + lane/16, LDS chunk lane%16 holds global chunk (lane%16) ^ (key%16)),
-  // this wave loads pieces KP*wave..KP*wave+KP-1.  A V^T tile is sixteen
-  // pieces (dims 8i..8i+7; lane -> dim 8i + lane/8, LDS chunk lane%8 holds
-  // global chunk (lane%8) ^ ((dim/2)%8)), this wave loads VP*wave..
-  // VP*wave+VP-1.  Offsets are bytes from the unit's / tile's origin.
-  uint32_t koff[KP], voff[VP];
+  // Direct loads, in 1-KB pieces of four key rows (lane -> key 4i + lane/16,
+  // LDS chunk lane%16 of the row).  A K unit is eight pieces, LDS chunk c of
+  // key k holding global chunk c ^ (k%16); this wave loads pieces
+  // KP*wave..KP*wave+KP-1.  A V tile is sixteen pieces, LDS chunk c of key k
+  // holding global chunk c ^ 4(k%4); this wave loads VP*wave..VP*wave+VP-1.
+  // Offsets are bytes from the unit's / tile's first key row.
+  uint32_t koff[KP], vchunk[VP];
 #pragma unroll
   for (int t = 0; t < KP; ++t) {
     const int key = (wave * KP + t) * 4 + (lane >> 4);
@@ -142,11 +143,11 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   }
 #pragma unroll
   for (int t = 0; t < VP; ++t) {
-    const int d = (wave * VP + t) * 8 + (lane >> 3);
-    voff[t] = (uint32_t)(d * (uint32_t)ld_vt * 2 + (((lane & 7) ^ ((d >> 1) & 7)) * 16));
+    const int key = (wave * VP + t) * 4 + (lane >> 4);
+    vchunk[t] = (uint32_t)(((lane & 15) ^ (4 * (key & 3))) * 16);
   }
   const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + hd + h * DH);
-  const char* vbase = reinterpret_cast<const char*>(vt + (int64_t)h * DH * ld_vt + vt_base[seq]);
+  const char* vbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + 2 * hd + h * DH);
   const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_void*)&sK[0][0] + wave * KP * 1024;
   const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0] + wave * VP * 1024;
   // K unit u into ring slot u % 4.  Units past the clip's last one re-load
@@ -157,12 +158,16 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 #pragma unroll
     for (int t = 0; t < KP; ++t) dma16(g + koff[t], l + t * 1024);
   };
-  // V^T tile j into buffer j % 2.
+  // V tile j (keys 64 j ..) into buffer j % 2.  Keys past the clip take the
+  // clip's last row: their probability is exactly 0, and a row of the clip is
+  // finite whatever lies beyond it.
   auto issue_v = [&](int j) __attribute__((always_inline)) {
-    const char* g = vbase + (int64_t)j * KT * 2;
     const uint32_t l = v_lds + (j & 1) * VT_BYTES;
 #pragma unroll
-    for (int t = 0; t < VP; ++t) dma16(g + voff[t], l + t * 1024);
+    for (int t = 0; t < VP; ++t) {
+      const int key = min(j * KT + (wave * VP + t) * 4 + (lane >> 4), len - 1);
+      dma16(vbase + (int64_t)key * (3 * hd * 2) + vchunk[t], l + t * 1024);
+    }
   };
 
   // Scores arrive in log2 units (k was scaled by log2(e) / sqrt(128)).
@@ -184,7 +189,19 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   f32x16 SA[QB], SB[QB];   // scores of one 32-key unit, per query block
 
   const int kx = lhi ^ (l32 & 15);          // K chunk swizzle of this lane
-  const int vx = lhi ^ ((l32 >> 1) & 7);    // V^T chunk swizzle of this lane
+  // V^T operands come from the row-major V tile through ds_read_b64_tr_b16:
+  // within each group of 16 lanes, lane 4a + e receives element e of the
+  // 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12.  Lane 4j + a
+  // of group g addresses key row 4 (g/2) + j (+ 8 for the second read) at
+  // dims 16 (g%2) + 4a .. + 3 of the 32-dim block, so lane l receives dim
+  // l%32 of keys 4 lhi + 0..3 and 8 + 4 lhi + 0..3 -- the keys whose
+  // probabilities it holds in the accumulator layout of K Q^T (rows
+  // 8 (v/4) + 4 lhi + v%4).
+  const int tr_j = (lane & 15) >> 2;
+  const uint32_t tr_off =
+      (uint32_t)((4 * (lane >> 5) + tr_j) * (DH * 2) + ((((lane >> 4) & 1) * 2 + ((lane & 3) >> 1)) << 4) +
+                 ((lane & 1) << 3));
+  const uint32_t v_lds0 = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0];
 
   // S^T of unit u: 8 k-steps x 2 query blocks.
   auto qk = [&](f32x16 (&S)[QB], int u) __attribute__((always_inline)) {
@@ -247,7 +264,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   // (kk0, kk0 + 1 of V^T tile j).  Row sums take the bf16 probabilities the
   // products use (one dot2 per pair).
   auto expv = [&](f32x16 (&S)[QB], int j, int kk0) __attribute__((always_inline)) {
-    const uint4* sv = sV[j & 1];
+    const uint32_t sv = v_lds0 + (j & 1) * VT_BYTES;
     typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
     const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -273,7 +290,13 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
       const int kk = kk0 + half;
 #pragma unroll
       for (int db = 0; db < DH / 32; ++db) {
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, sv[(db * 32 + l32) * 8 + ((2 * kk) ^ vx)]);
+        // chunk 4 db + q of key row k sits at 4 (db ^ (k%4)) + q, and k%4 = tr_j
+        const uint32_t at = sv + kk * 16 * (DH * 2) + tr_off + ((db ^ tr_j) << 6);
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)at);
+        const v4i16 hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(at + 8 * DH * 2));
+        const bf16x8 vf =
+            __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           O[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], O[db][qb], 0, 0, 0);
@@ -386,14 +409,10 @@ bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g
   return std::isfinite(log2_range) && log2_range <= 100.0;
 }
 
-hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
-                            const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
+hipError_t launch_attention(const bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
                             const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
                             bool fixed_ref, void* out, float out_scale, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
-  // V^T byte offsets inside a tile are 32-bit: 128 rows of ld_vt bf16.
-  if (ld_vt <= 0 || ld_vt % 64 != 0 || (int64_t)DH * ld_vt * 2 >= (int64_t)1 << 31)
-    return hipErrorInvalidValue;
   if (n_heads < 1 || head_dim < 4 || head_dim > DH || head_dim % 4 != 0 ||
       (out_scale > 0.0f && head_dim != DH))
     return hipErrorInvalidValue;
@@ -401,9 +420,8 @@ hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
   const int hd = n_heads * DH;
   const int grid = (n_items + 7) / 8 * 8;
   auto kernel = fixed_ref ? attention_kernel<true> : attention_kernel<false>;
-  kernel<<<dim3(grid), dim3(64 * NW), 0, stream>>>(qkv, vt, ld_vt, cu_seq, vt_base, tile_seq,
-                                                   tile_q0, n_tiles, n_items, out, out_scale, hd,
-                                                   head_dim);
+  kernel<<<dim3(grid), dim3(64 * NW), 0, stream>>>(qkv, cu_seq, tile_seq, tile_q0, n_tiles,
+                                                   n_items, out, out_scale, hd, head_dim);
   return hipGetLastError();
 }
 

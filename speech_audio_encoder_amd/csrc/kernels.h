@@ -84,23 +84,18 @@ hipError_t launch_log_softmax(const float* z, int64_t ldz, int64_t rows, int n, 
 
 // In place on qkv [rows, 3840] bf16, per attention tile (clip tile_seq[i],
 // positions tile_p0[i] .. +127) and head: q <- RoPE(LN_q(q)),
-// k <- RoPE(LN_k(k)) * K_SCORE_SCALE,
-// and v copied transposed to vt[h][d][vt_base[b] + c] (ld_vt per d), where
-// column c of each aligned group of 16 holds position 0-3, 8-11, 4-7, 12-15
-// of the group in that order, with zeros for positions in
-// [P_b, roundup(P_b, 64)).  cu_seq[b] is clip b's first row.
+// k <- RoPE(LN_k(k)) * K_SCORE_SCALE, in place.  cu_seq[b] is clip b's first
+// row.
 // Head slots are 128 wide for every head width: qkv rows hold q, k, v blocks
 // of n_heads x 128 (row stride 3 x n_heads x 128); with head_dim 80 (the
 // timestamp adapter) dims 80..127 of a slot are zero and stay zero, the
 // statistics cover the 80 dims, the rotation pairs (i, i + 40) and k is
 // scaled by log2(e) / sqrt(80).  rope tables hold head_dim / 2 entries per
 // position.  head_dim: 128 or 80.
-hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* vt_base,
-                              const int32_t* tile_seq, const int32_t* tile_p0, int n_tiles,
-                              int n_heads, int head_dim, const float* qg, const float* qb,
-                              const float* kg, const float* kb, const float* rope_cos,
-                              const float* rope_sin, bf16_t* vt, int64_t ld_vt,
-                              hipStream_t stream);
+hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
+                              const int32_t* tile_p0, int n_tiles, int n_heads, int head_dim,
+                              const float* qg, const float* qb, const float* kg, const float* kb,
+                              const float* rope_cos, const float* rope_sin, hipStream_t stream);
 
 // out[b, p, :] = LN_f(x[s, :]) for p < P_b, else 0, with s = cu_seq[b] + p,
 // or src_rows[cu_seq[b] + p] when src_rows is not NULL; bf16 output of shape
@@ -140,21 +135,18 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
                          hipStream_t stream);
 
 // --------------------------------------------------------------- attention
-// Bidirectional softmax attention per clip and head.  q, k are the first two
+// Bidirectional softmax attention per clip and head.  q, k, v are the three
 // (n_heads x 128)-column groups of qkv [rows, 3 x n_heads x 128] (1280 for
-// the encoder's ten heads); v comes transposed from vt (clip b
-// at columns vt_base[b]..., zero past P_b up to a multiple of 64).  Work tile
+// the encoder's ten heads), q and k as launch_qknorm_rope leaves them.  Work tile
 // i covers queries [tile_q0[i], min(tile_q0[i] + 128, P_b)) of clip
 // tile_seq[i].  out is bf16 [rows, n_heads x head_dim] with head h in columns
 // h*head_dim... (head_dim <= 128: a narrower head's slot has zero dims past
 // head_dim, which are not stored), or,
 // when out_scale > 0, E4M3 codes of the output times out_scale (saturated at
 // +-448), one byte per element in the same layout.
-// qkv must have 63 readable rows after its last one (their k is masked), and
-// vt's columns hold keys permuted inside each group of 16 as written by
-// launch_qknorm_rope.
-hipError_t launch_attention(const bf16_t* qkv, const bf16_t* vt, int64_t ld_vt,
-                            const int32_t* cu_seq, const int32_t* vt_base, const int32_t* tile_seq,
+// k is read in whole 64-key tiles past a clip's end (those keys are masked),
+// so qkv must have 63 readable rows after its last one.
+hipError_t launch_attention(const bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
                             const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
                             bool fixed_ref, void* out, float out_scale, hipStream_t stream);
 // fixed_ref may be true only when |q . k| * log2(e) / sqrt(128) <= 100 for

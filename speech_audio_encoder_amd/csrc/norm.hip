@@ -315,77 +315,27 @@ __device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, i
 
 template <int HALF>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
-    bf16_t* __restrict__ qkv, const int32_t* __restrict__ cu, const int32_t* __restrict__ vt_base,
+    bf16_t* __restrict__ qkv, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_p0,
     const float* __restrict__ qg, const float* __restrict__ qb, const float* __restrict__ kg,
     const float* __restrict__ kb, const float* __restrict__ rope_cos,
-    const float* __restrict__ rope_sin, bf16_t* __restrict__ vt, int64_t ld_vt, int hd,
-    int n_tiles, int n_heads, int hgroups, float kscale) {
+    const float* __restrict__ rope_sin, int hd, int n_heads, int hgroups, float kscale) {
   const int64_t ldq = 3 * (int64_t)hd;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  // Blocks [0, n_qk): q and k of a quarter tile (32 positions) for one of
-  // `hgroups` groups of heads; then one block per tile x head for v.
+  // Block b: q and k of a quarter tile (32 positions) for one of `hgroups`
+  // groups of heads.
   constexpr int QUARTERS = QK_ROWS / 32;
-  const int n_qk = n_tiles * QUARTERS * hgroups;
-  if ((int)blockIdx.x < n_qk) {
-    const int hg = blockIdx.x % hgroups;
-    const int tq = blockIdx.x / hgroups;
-    const int t = tq / QUARTERS;
-    const int seq = tile_seq[t];
-    const int len = cu[seq + 1] - cu[seq];
-    const int p = tile_p0[t] + (tq % QUARTERS) * 32 + wave * 8 + (lane >> 3);
-    if (__builtin_amdgcn_readfirstlane(p - (lane >> 3)) >= len) return;   // no live row
-    const int per = (n_heads + hgroups - 1) / hgroups;
-    qk_rows<HALF>(qkv, ldq, hd, hg * per, min(n_heads, (hg + 1) * per), cu[seq], len, p, lane,
-                  qg, qb, kg, kb, rope_cos, rope_sin, kscale);
-    return;
-  }
-  const int vb = blockIdx.x - n_qk;
-  const int h = vb % n_heads;
-  const int tile = vb / n_heads;
-  const int seq = tile_seq[tile];
-  const int p0 = tile_p0[tile];
-  const int64_t s0 = cu[seq];
+  const int hg = blockIdx.x % hgroups;
+  const int tq = blockIdx.x / hgroups;
+  const int t = tq / QUARTERS;
+  const int seq = tile_seq[t];
   const int len = cu[seq + 1] - cu[seq];
-  const int span = min(QK_ROWS, ((len + 63) & ~63) - p0);   // rows incl. zero padding
-  // v thread map: wavefront w covers position blocks 8 (w & 1) .. + 7 and dim
-  // blocks 8 (w >> 1) .. + 7; lane -> (position block lane % 8, dim block
-  // lane / 8).
-  const int vrb = (lane & 7) + 8 * (wave & 1);
-  const int vdb = (lane >> 3) + 8 * (wave >> 1);
-  const bool vblock = vrb * 8 < span;
-  uint4 vrows[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // Key order inside each group of 16 columns: positions 0-3, 8-11, 4-7,
-    // 12-15 of the group, so that 8 consecutive columns are the 8 keys one
-    // lane supplies to a 32x32x16 MFMA whose other operand comes from the
-    // accumulator layout of K Q^T (rows 4*(lane/32) + 8g + r).
-    const int p = p0 + 16 * (vrb >> 1) + 4 * (vrb & 1) + (i & 3) + 8 * (i >> 2);
-    vrows[i] = (vblock && p < len) ? *reinterpret_cast<const uint4*>(qkv + (s0 + p) * ldq +
-                                                                      2 * hd + h * DH + vdb * 8)
-                                   : make_uint4(0, 0, 0, 0);
-  }
-
-  // v: output word k of column c takes half c%2 of word c/2 from rows 2k and
-  // 2k+1 (one byte permute each); 8 keys of each of the block's 8 dims go out
-  // as 16-byte vectors.  Positions past the clip are zeros.
-  if (vblock) {
-    bf16_t* dst = vt + ((int64_t)h * DH + vdb * 8) * ld_vt + vt_base[seq] + p0 + vrb * 8;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t w[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t* ra = reinterpret_cast<const uint32_t*>(&vrows[2 * k]);
-        const uint32_t* rb2 = reinterpret_cast<const uint32_t*>(&vrows[2 * k + 1]);
-        w[k] = __builtin_amdgcn_perm(rb2[c >> 1], ra[c >> 1], sel);
-      }
-      *reinterpret_cast<uint4*>(dst + (int64_t)c * ld_vt) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
+  const int p = tile_p0[t] + (tq % QUARTERS) * 32 + wave * 8 + (lane >> 3);
+  if (__builtin_amdgcn_readfirstlane(p - (lane >> 3)) >= len) return;   // no live row
+  const int per = (n_heads + hgroups - 1) / hgroups;
+  qk_rows<HALF>(qkv, ldq, hd, hg * per, min(n_heads, (hg + 1) * per), cu[seq], len, p, lane, qg,
+                qb, kg, kb, rope_cos, rope_sin, kscale);
 }
 
 // dst[r, :] = src[rows[r], :] for rows of 1024 bf16 (one wavefront per row,
@@ -599,32 +549,29 @@ hipError_t launch_gather_rows(const bf16_t* src, const int32_t* rows, int64_t n,
   return hipGetLastError();
 }
 
-hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* vt_base,
-                              const int32_t* tile_seq, const int32_t* tile_p0, int n_tiles,
-                              int n_heads, int head_dim, const float* qg, const float* qb,
-                              const float* kg, const float* kb, const float* rope_cos,
-                              const float* rope_sin, bf16_t* vt, int64_t ld_vt,
-                              hipStream_t stream) {
+hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
+                              const int32_t* tile_p0, int n_tiles, int n_heads, int head_dim,
+                              const float* qg, const float* qb, const float* kg, const float* kb,
+                              const float* rope_cos, const float* rope_sin, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   if (n_heads < 1) return hipErrorInvalidValue;
   const int hd = n_heads * DH;
   // log2(e) / sqrt(head width)
   const float kscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
-  // the heads are split into QK_HEAD_GROUPS groups, one q/k block per group
-  // and quarter tile (the gains and the rotation table row are loaded once
-  // per group)
+  // the heads are split into QK_HEAD_GROUPS groups, one block per group and
+  // quarter tile (the gains and the rotation table row are loaded once per
+  // group)
   const int hgroups = std::min(n_heads, QK_HEAD_GROUPS);
-  const int64_t blocks =
-      (int64_t)n_tiles * (QK_ROWS / 32) * hgroups + (int64_t)n_tiles * n_heads;
+  const int64_t blocks = (int64_t)n_tiles * (QK_ROWS / 32) * hgroups;
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (head_dim == DH)
     qknorm_rope_kernel<DH / 2><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt,
-        hd, n_tiles, n_heads, hgroups, kscale);
+        qkv, cu_seq, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, hd, n_heads, hgroups,
+        kscale);
   else if (head_dim == 80)
     qknorm_rope_kernel<40><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        qkv, cu_seq, vt_base, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, vt, ld_vt,
-        hd, n_tiles, n_heads, hgroups, kscale);
+        qkv, cu_seq, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, hd, n_heads, hgroups,
+        kscale);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

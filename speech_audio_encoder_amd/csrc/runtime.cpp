@@ -117,22 +117,19 @@ struct Plan {
   std::vector<int32_t> frame_base;  // [batch]  8 * cu_clip[b]
   std::vector<int32_t> cu_clip;     // [batch + 1] first clip row of each clip
   std::vector<int32_t> cu_seq;      // [n_seq + 1] first row of each attention sequence
-  std::vector<int32_t> vt_base;     // [n_seq]  first V^T column of each sequence
-  int64_t vt_cols = 0;              // sum of roundup(sequence length, 64)
   std::vector<int32_t> tile_seq, tile_q0;
   // Overlapping windows only: clip row of each layer row, and layer row of
   // each clip row's own window.
   std::vector<int32_t> gather_src;  // [vrows]
   std::vector<int32_t> out_src;     // [rows]
   // Timestamp adapter (40 ms grid): clip b's 2 P_b frames are one sequence.
-  std::vector<int32_t> a_cu, a_vt_base, a_tile_seq, a_tile_q0;
-  int64_t a_vt_cols = 0;
+  std::vector<int32_t> a_cu, a_tile_seq, a_tile_q0;
   std::vector<int32_t> all_rows;    // {0, rows}: the whole batch as one packed block
 };
 
-// V^T columns and attention tiles of sequences starting at cu[0..n].
-void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* vt_base, int64_t* vt_cols,
-               std::vector<int32_t>* tile_seq, std::vector<int32_t>* tile_q0);
+// Attention tiles of sequences starting at cu[0..n].
+void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* tile_seq,
+               std::vector<int32_t>* tile_q0);
 
 constexpr int ATT_QB = 128;
 
@@ -197,13 +194,6 @@ int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles,
   p->vrows = vrows;
   p->cu_seq.push_back((int32_t)vrows);
   const int n_seq = (int)p->cu_seq.size() - 1;
-  p->vt_base.resize(n_seq);
-  int64_t vcols = 0;
-  for (int s = 0; s < n_seq; ++s) {
-    p->vt_base[s] = (int32_t)vcols;
-    vcols += (p->cu_seq[s + 1] - p->cu_seq[s] + 63) / 64 * 64;
-  }
-  p->vt_cols = vcols;
   p->tile_seq.clear();
   p->tile_q0.clear();
   if (with_tiles) {
@@ -219,36 +209,30 @@ int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles,
   p->all_rows = {0, (int32_t)rows};
   p->a_cu.resize(batch + 1);
   for (int b = 0; b <= batch; ++b) p->a_cu[b] = 2 * p->cu_clip[b];
-  seq_tiles(p->a_cu, &p->a_vt_base, &p->a_vt_cols, &p->a_tile_seq, &p->a_tile_q0);
+  seq_tiles(p->a_cu, &p->a_tile_seq, &p->a_tile_q0);
   return ENC_OK;
 }
 
-void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* vt_base, int64_t* vt_cols,
-               std::vector<int32_t>* tile_seq, std::vector<int32_t>* tile_q0) {
+void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* tile_seq,
+               std::vector<int32_t>* tile_q0) {
   const int n = (int)cu.size() - 1;
-  vt_base->resize(n);
   tile_seq->clear();
   tile_q0->clear();
-  int64_t cols = 0;
   for (int s = 0; s < n; ++s) {
     const int len = cu[s + 1] - cu[s];
-    (*vt_base)[s] = (int32_t)cols;
-    cols += (len + 63) / 64 * 64;
     for (int q0 = 0; q0 < len; q0 += ATT_QB) {
       tile_seq->push_back(s);
       tile_q0->push_back(q0);
     }
   }
-  *vt_cols = cols;
 }
 
 // Workspace layout for `rows` packed positions (offsets in bytes).
 struct Layout {
-  size_t x, a, qkv, o, u, vt, total;
-  int64_t ld_vt;
+  size_t x, a, qkv, o, u, total;
 };
 
-Layout layout_for(int64_t rows, int64_t vt_cols) {
+Layout layout_for(int64_t rows) {
   Layout l{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -264,8 +248,6 @@ Layout layout_for(int64_t rows, int64_t vt_cols) {
   l.qkv = take((r + 64) * 3 * D * 2);
   l.o = take(r * D * 2);
   l.u = take(r * std::max(FF, DIN) * 2);   // also holds the stacked log-mel
-  l.ld_vt = std::max<int64_t>(vt_cols, 64);
-  l.vt = take((size_t)H * DH * l.ld_vt * 2);
   l.total = off;
   return l;
 }
@@ -497,7 +479,7 @@ int enc_workspace_bytes(int32_t n_layers, const int64_t* lengths, int32_t batch,
   Plan p;
   int rc = make_plan(lengths, batch, &p, false);
   if (rc != ENC_OK) return rc;
-  *bytes = layout_for(p.rows, p.vt_cols).total;
+  *bytes = layout_for(p.rows).total;
   return ENC_OK;
 }
 
@@ -715,11 +697,10 @@ enum class Tail { kEmbeddings, kFused, kCalibrate, kCtc };
 
 // Adapter workspace for `rows` adapter frames (offsets in bytes).
 struct CtcLayout {
-  size_t x, a, qkv, vt, o, u, z, total;
-  int64_t ld_vt;
+  size_t x, a, qkv, o, u, z, total;
 };
 
-CtcLayout ctc_layout_for(int64_t rows, int64_t vt_cols, int n_pad) {
+CtcLayout ctc_layout_for(int64_t rows, int n_pad) {
   CtcLayout l{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -731,8 +712,6 @@ CtcLayout ctc_layout_for(int64_t rows, int64_t vt_cols, int n_pad) {
   l.x = take(r * D * 4);
   l.a = take(r * D * 2);
   l.qkv = take((r + 64) * 3 * CTC_HD * 2);   // 64 rows of slack for whole key tiles
-  l.ld_vt = std::max<int64_t>(vt_cols, 64);
-  l.vt = take((size_t)CTC_HD * l.ld_vt * 2);
   l.o = take(r * D * 2);
   l.u = take(r * D * 2);
   l.z = take(r * (size_t)n_pad * 4);
@@ -744,12 +723,12 @@ CtcLayout ctc_layout_for(int64_t rows, int64_t vt_cols, int n_pad) {
 // upsampling to 2 rows per position, its layers, final LayerNorm, projection
 // and log-softmax into out [2 rows, n_classes].
 int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_cu,
-                const int32_t* d_vb, const int32_t* d_ts, const int32_t* d_tq, float* out,
+                const int32_t* d_ts, const int32_t* d_tq, float* out,
                 hipStream_t stream) {
   const CtcW& W = *ctx->ctc;
   const int64_t R = 2 * p.rows;
   if (R == 0) return ENC_OK;
-  const CtcLayout lay = ctc_layout_for(R, p.a_vt_cols, W.n_pad);
+  const CtcLayout lay = ctc_layout_for(R, W.n_pad);
   if (lay.total > ctx->ctc_ws_bytes) {
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "stream synchronize");
@@ -768,7 +747,6 @@ int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_c
   float* x = (float*)(ws + lay.x);
   bf16_t* a = (bf16_t*)(ws + lay.a);
   bf16_t* qkv = (bf16_t*)(ws + lay.qkv);
-  bf16_t* vt = (bf16_t*)(ws + lay.vt);
   bf16_t* o = (bf16_t*)(ws + lay.o);
   bf16_t* u = (bf16_t*)(ws + lay.u);
   float* z = (float*)(ws + lay.z);
@@ -782,11 +760,10 @@ int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_c
                                       3 * CTC_HD, R, 3 * CTC_HD, D, ctx->gemm_part,
                                       GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_CTC,
-               launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, CTC_HEADS, CTC_DH, L.q_g,
-                                  L.q_b, L.k_g, L.k_b, W.rope_cos, W.rope_sin, vt, lay.ld_vt,
-                                  stream));
+               launch_qknorm_rope(qkv, d_cu, d_ts, d_tq, n_tiles, CTC_HEADS, CTC_DH, L.q_g,
+                                  L.q_b, L.k_g, L.k_b, W.rope_cos, W.rope_sin, stream));
     ENC_LAUNCH(ENC_K_CTC,
-               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, CTC_HEADS,
+               launch_attention(qkv, d_cu, d_ts, d_tq, n_tiles, CTC_HEADS,
                                 CTC_DH, L.attn_fixed_ref, o, 0.0f, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasResidualF32, o, D, L.w_o, D, L.b_o, x, D, R,
                                       D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
@@ -831,7 +808,7 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   if (p.p_max == 0) return ENC_OK;
 
   // Memory admission before any launch.
-  const Layout lay = layout_for(p.vrows, p.vt_cols);
+  const Layout lay = layout_for(p.vrows);
   if (const char* cap = std::getenv("ENC_WORKSPACE_CAP_BYTES")) {
     const unsigned long long lim = std::strtoull(cap, nullptr, 10);
     if ((unsigned long long)lay.total > lim)
@@ -861,25 +838,23 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   bf16_t* qkv = (bf16_t*)(ws + lay.qkv);
   bf16_t* o = (bf16_t*)(ws + lay.o);
   bf16_t* u = (bf16_t*)(ws + lay.u);
-  bf16_t* vt = (bf16_t*)(ws + lay.vt);
   bf16_t* stk = u;
 
   std::vector<int32_t*> dev;
-  if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.cu_seq, &p.vt_base, &p.tile_seq,
+  if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.cu_seq, &p.tile_seq,
                               &p.tile_q0, &p.cu_clip, &p.gather_src, &p.out_src, &p.a_cu,
-                              &p.a_vt_base, &p.a_tile_seq, &p.a_tile_q0, &p.all_rows},
+                              &p.a_tile_seq, &p.a_tile_q0, &p.all_rows},
                         &dev, stream)) != ENC_OK)
     return rc;
   const int32_t* d_nf = dev[0];
   const int32_t* d_fb = dev[1];
   const int32_t* d_cu = dev[2];
-  const int32_t* d_vb = dev[3];
-  const int32_t* d_ts = dev[4];
-  const int32_t* d_tq = dev[5];
-  const int32_t* d_clip = dev[6];
+  const int32_t* d_ts = dev[3];
+  const int32_t* d_tq = dev[4];
+  const int32_t* d_clip = dev[5];
   const bool overlap = !p.gather_src.empty();
-  const int32_t* d_gather = overlap ? dev[7] : nullptr;
-  const int32_t* d_outsrc = overlap ? dev[8] : nullptr;
+  const int32_t* d_gather = overlap ? dev[6] : nullptr;
+  const int32_t* d_outsrc = overlap ? dev[7] : nullptr;
   const int64_t R = p.vrows;
   const int n_tiles = (int)p.tile_seq.size();
 
@@ -916,11 +891,10 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                              GEMM_PARTIAL_BYTES, stream));
     }
     ENC_LAUNCH(ENC_K_QKNORM_ROPE,
-               launch_qknorm_rope(qkv, d_cu, d_vb, d_ts, d_tq, n_tiles, H, DH, Lw.q_g, Lw.q_b,
-                                  Lw.k_g, Lw.k_b, ctx->rope_cos, ctx->rope_sin, vt, lay.ld_vt,
-                                  stream));
+               launch_qknorm_rope(qkv, d_cu, d_ts, d_tq, n_tiles, H, DH, Lw.q_g, Lw.q_b,
+                                  Lw.k_g, Lw.k_b, ctx->rope_cos, ctx->rope_sin, stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
-               launch_attention(qkv, vt, lay.ld_vt, d_cu, d_vb, d_ts, d_tq, n_tiles, H, DH,
+               launch_attention(qkv, d_cu, d_ts, d_tq, n_tiles, H, DH,
                                 Lw.attn_fixed_ref, o, fp8 ? Lw.r_x[1] : 0.0f, stream));
     if (fp8) {
       ENC_LAUNCH(ENC_K_GEMM_O,
@@ -953,9 +927,9 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   if (calib) return ENC_OK;
   if (ctc) {
     // Encoder states, clip-packed bf16, into the LayerNorm buffer.
-    ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, dev[13], d_outsrc,
+    ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, dev[11], d_outsrc,
                                                    1, p.rows, a, stream));
-    return run_adapter(ctx, p, a, dev[9], dev[10], dev[11], dev[12], (float*)out, stream);
+    return run_adapter(ctx, p, a, dev[8], dev[9], dev[10], (float*)out, stream);
   }
   if (!fused) {
     ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_clip, d_outsrc,
