@@ -66,16 +66,35 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, (int)lo, true);
 }
 
+// Wavefront reductions (every lane of the wavefront active; every lane gets
+// the result).  Inside each row of 16 lanes, DPP moves (quad permutations
+// [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors) leave the row's
+// total in all of its lanes without touching LDS; the four row totals are then
+// read from lanes 0, 16, 32 and 48.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
+                                                               0xF, 0xF, false));
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_move<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_move<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_move<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_move<0x140>(v));   // row_mirror
+  auto lane = [&](int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  };
+  return op(op(lane(0), lane(16)), op(lane(32), lane(48)));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 }  // namespace enc
