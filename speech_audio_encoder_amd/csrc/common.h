@@ -89,6 +89,14 @@ __device__ __forceinline__ float wave_reduce(float v, Op op) {
   return op(op(lane(0), lane(16)), op(lane(32), lane(48)));
 }
 
+// Sum over each aligned group of 8 lanes, in all 8 (the quad permutations
+// and the half-row mirror of the reduction above).
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp_move<0xB1>(v);
+  v += dpp_move<0x4E>(v);
+  return v + dpp_move<0x141>(v);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
   return wave_reduce(v, [](float a, float b) { return a + b; });
 }

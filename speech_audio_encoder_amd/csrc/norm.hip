@@ -267,8 +267,7 @@ __device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, i
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum += a[e] + b[e];
       if (!act) sum = 0.f;
-#pragma unroll
-      for (int o = 4; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      sum = group8_sum(sum);
       const float mean = sum * INV_DH;
       float sq = 0.f;
 #pragma unroll
@@ -278,8 +277,7 @@ __device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, i
         sq += a[e] * a[e] + b[e] * b[e];
       }
       if (!act) sq = 0.f;
-#pragma unroll
-      for (int o = 4; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      sq = group8_sum(sq);
       const float rstd = rsqrtf(sq * INV_DH + LN_EPS);
       // k leaves scaled by log2(e) / sqrt(head width): the attention
       // kernel's scores are then directly the exponents of exp2.
