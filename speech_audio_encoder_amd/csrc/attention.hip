@@ -88,8 +88,7 @@ __device__ __forceinline__ void lds_loads_wait() {
 
 template <bool kFixedRef>
 __global__ __launch_bounds__(64 * NW) void attention_kernel(
-    const bf16_t* __restrict__ qkv, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_q0, int n_tiles,
+    const bf16_t* __restrict__ qkv, const int4* __restrict__ tile_info, int n_tiles,
     int n_items, void* __restrict__ out, float out_scale, int hd, int dh_out) {
   // K in a ring of four 32-key units, V in two 64-key tiles.
   __shared__ uint4 sK[4][KU * DH / 8];   // [key][16 chunks of 8 dims], swizzled
@@ -102,10 +101,10 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   if (item >= n_items) return;
   const int h = item / n_tiles;
   const int tile = item - h * n_tiles;
-  const int seq = tile_seq[tile];
-  const int64_t s0 = cu[seq];
-  const int len = cu[seq + 1] - cu[seq];
-  const int q0 = tile_q0[tile];
+  const int4 ti = tile_info[tile];   // first row, length, first query
+  const int64_t s0 = ti.x;
+  const int len = ti.y;
+  const int q0 = ti.z;
   const int nkt = (len + KT - 1) / KT;   // 64-key tiles
   const int nku = 2 * nkt;               // 32-key units
 
@@ -409,9 +408,9 @@ bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g
   return std::isfinite(log2_range) && log2_range <= 100.0;
 }
 
-hipError_t launch_attention(const bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
-                            const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
-                            bool fixed_ref, void* out, float out_scale, hipStream_t stream) {
+hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_tiles,
+                            int n_heads, int head_dim, bool fixed_ref, void* out, float out_scale,
+                            hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   if (n_heads < 1 || head_dim < 4 || head_dim > DH || head_dim % 4 != 0 ||
       (out_scale > 0.0f && head_dim != DH))
@@ -420,8 +419,9 @@ hipError_t launch_attention(const bf16_t* qkv, const int32_t* cu_seq, const int3
   const int hd = n_heads * DH;
   const int grid = (n_items + 7) / 8 * 8;
   auto kernel = fixed_ref ? attention_kernel<true> : attention_kernel<false>;
-  kernel<<<dim3(grid), dim3(64 * NW), 0, stream>>>(qkv, cu_seq, tile_seq, tile_q0, n_tiles,
-                                                   n_items, out, out_scale, hd, head_dim);
+  kernel<<<dim3(grid), dim3(64 * NW), 0, stream>>>(
+      qkv, reinterpret_cast<const int4*>(tile_info), n_tiles, n_items, out, out_scale, hd,
+      head_dim);
   return hipGetLastError();
 }
 

@@ -82,20 +82,20 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
 hipError_t launch_log_softmax(const float* z, int64_t ldz, int64_t rows, int n, float* out,
                               hipStream_t stream);
 
-// In place on qkv [rows, 3840] bf16, per attention tile (clip tile_seq[i],
-// positions tile_p0[i] .. +127) and head: q <- RoPE(LN_q(q)),
-// k <- RoPE(LN_k(k)) * K_SCORE_SCALE, in place.  cu_seq[b] is clip b's first
-// row.
+// In place on qkv [rows, 3840] bf16, per attention tile and head:
+// q <- RoPE(LN_q(q)), k <- RoPE(LN_k(k)) * K_SCORE_SCALE.  tile_info holds
+// four int32 per tile: the sequence's first row, its length, the tile's first
+// position (the tile covers positions p0 .. p0 + 127 of the sequence), 0.
 // Head slots are 128 wide for every head width: qkv rows hold q, k, v blocks
 // of n_heads x 128 (row stride 3 x n_heads x 128); with head_dim 80 (the
 // timestamp adapter) dims 80..127 of a slot are zero and stay zero, the
 // statistics cover the 80 dims, the rotation pairs (i, i + 40) and k is
 // scaled by log2(e) / sqrt(80).  rope tables hold head_dim / 2 entries per
 // position.  head_dim: 128 or 80.
-hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
-                              const int32_t* tile_p0, int n_tiles, int n_heads, int head_dim,
-                              const float* qg, const float* qb, const float* kg, const float* kb,
-                              const float* rope_cos, const float* rope_sin, hipStream_t stream);
+hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* tile_info, int n_tiles, int n_heads,
+                              int head_dim, const float* qg, const float* qb, const float* kg,
+                              const float* kb, const float* rope_cos, const float* rope_sin,
+                              hipStream_t stream);
 
 // out[b, p, :] = LN_f(x[s, :]) for p < P_b, else 0, with s = cu_seq[b] + p,
 // or src_rows[cu_seq[b] + p] when src_rows is not NULL; bf16 output of shape
@@ -138,17 +138,17 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
 // Bidirectional softmax attention per clip and head.  q, k, v are the three
 // (n_heads x 128)-column groups of qkv [rows, 3 x n_heads x 128] (1280 for
 // the encoder's ten heads), q and k as launch_qknorm_rope leaves them.  Work tile
-// i covers queries [tile_q0[i], min(tile_q0[i] + 128, P_b)) of clip
-// tile_seq[i].  out is bf16 [rows, n_heads x head_dim] with head h in columns
+// i (tile_info as for launch_qknorm_rope) covers queries [q0, min(q0 + 128,
+// length)) of its sequence.  out is bf16 [rows, n_heads x head_dim] with head h in columns
 // h*head_dim... (head_dim <= 128: a narrower head's slot has zero dims past
 // head_dim, which are not stored), or,
 // when out_scale > 0, E4M3 codes of the output times out_scale (saturated at
 // +-448), one byte per element in the same layout.
 // k is read in whole 64-key tiles past a clip's end (those keys are masked),
 // so qkv must have 63 readable rows after its last one.
-hipError_t launch_attention(const bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
-                            const int32_t* tile_q0, int n_tiles, int n_heads, int head_dim,
-                            bool fixed_ref, void* out, float out_scale, hipStream_t stream);
+hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_tiles,
+                            int n_heads, int head_dim, bool fixed_ref, void* out, float out_scale,
+                            hipStream_t stream);
 // fixed_ref may be true only when |q . k| * log2(e) / sqrt(128) <= 100 for
 // every query and key (softmax against a fixed reference instead of a
 // running maximum); attention_fixed_ref_ok decides it from the QK-norm

@@ -313,8 +313,7 @@ __device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, i
 
 template <int HALF>
 __global__ __launch_bounds__(256) void qknorm_rope_kernel(
-    bf16_t* __restrict__ qkv, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ tile_seq, const int32_t* __restrict__ tile_p0,
+    bf16_t* __restrict__ qkv, const int4* __restrict__ tile_info,
     const float* __restrict__ qg, const float* __restrict__ qb, const float* __restrict__ kg,
     const float* __restrict__ kb, const float* __restrict__ rope_cos,
     const float* __restrict__ rope_sin, int hd, int n_heads, int hgroups, float kscale) {
@@ -327,12 +326,12 @@ __global__ __launch_bounds__(256) void qknorm_rope_kernel(
   const int hg = blockIdx.x % hgroups;
   const int tq = blockIdx.x / hgroups;
   const int t = tq / QUARTERS;
-  const int seq = tile_seq[t];
-  const int len = cu[seq + 1] - cu[seq];
-  const int p = tile_p0[t] + (tq % QUARTERS) * 32 + wave * 8 + (lane >> 3);
+  const int4 ti = tile_info[t];   // first row, length, first position
+  const int len = ti.y;
+  const int p = ti.z + (tq % QUARTERS) * 32 + wave * 8 + (lane >> 3);
   if (__builtin_amdgcn_readfirstlane(p - (lane >> 3)) >= len) return;   // no live row
   const int per = (n_heads + hgroups - 1) / hgroups;
-  qk_rows<HALF>(qkv, ldq, hd, hg * per, min(n_heads, (hg + 1) * per), cu[seq], len, p, lane, qg,
+  qk_rows<HALF>(qkv, ldq, hd, hg * per, min(n_heads, (hg + 1) * per), ti.x, len, p, lane, qg,
                 qb, kg, kb, rope_cos, rope_sin, kscale);
 }
 
@@ -547,10 +546,10 @@ hipError_t launch_gather_rows(const bf16_t* src, const int32_t* rows, int64_t n,
   return hipGetLastError();
 }
 
-hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t* tile_seq,
-                              const int32_t* tile_p0, int n_tiles, int n_heads, int head_dim,
-                              const float* qg, const float* qb, const float* kg, const float* kb,
-                              const float* rope_cos, const float* rope_sin, hipStream_t stream) {
+hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* tile_info, int n_tiles, int n_heads,
+                              int head_dim, const float* qg, const float* qb, const float* kg,
+                              const float* kb, const float* rope_cos, const float* rope_sin,
+                              hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   if (n_heads < 1) return hipErrorInvalidValue;
   const int hd = n_heads * DH;
@@ -564,12 +563,12 @@ hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* cu_seq, const int32_t*
   if (blocks > INT32_MAX) return hipErrorInvalidValue;
   if (head_dim == DH)
     qknorm_rope_kernel<DH / 2><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        qkv, cu_seq, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, hd, n_heads, hgroups,
-        kscale);
+        qkv, reinterpret_cast<const int4*>(tile_info), qg, qb, kg, kb, rope_cos, rope_sin, hd,
+        n_heads, hgroups, kscale);
   else if (head_dim == 80)
     qknorm_rope_kernel<40><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
-        qkv, cu_seq, tile_seq, tile_p0, qg, qb, kg, kb, rope_cos, rope_sin, hd, n_heads, hgroups,
-        kscale);
+        qkv, reinterpret_cast<const int4*>(tile_info), qg, qb, kg, kb, rope_cos, rope_sin, hd,
+        n_heads, hgroups, kscale);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

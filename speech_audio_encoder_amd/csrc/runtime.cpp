@@ -117,19 +117,19 @@ struct Plan {
   std::vector<int32_t> frame_base;  // [batch]  8 * cu_clip[b]
   std::vector<int32_t> cu_clip;     // [batch + 1] first clip row of each clip
   std::vector<int32_t> cu_seq;      // [n_seq + 1] first row of each attention sequence
-  std::vector<int32_t> tile_seq, tile_q0;
+  // Attention tiles: {first row, sequence length, first query, 0} each.
+  std::vector<int32_t> tile_info;
   // Overlapping windows only: clip row of each layer row, and layer row of
   // each clip row's own window.
   std::vector<int32_t> gather_src;  // [vrows]
   std::vector<int32_t> out_src;     // [rows]
   // Timestamp adapter (40 ms grid): clip b's 2 P_b frames are one sequence.
-  std::vector<int32_t> a_cu, a_tile_seq, a_tile_q0;
+  std::vector<int32_t> a_cu, a_tile_info;
   std::vector<int32_t> all_rows;    // {0, rows}: the whole batch as one packed block
 };
 
 // Attention tiles of sequences starting at cu[0..n].
-void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* tile_seq,
-               std::vector<int32_t>* tile_q0);
+void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* tile_info);
 
 constexpr int ATT_QB = 128;
 
@@ -193,36 +193,26 @@ int make_plan(const int64_t* lengths, int32_t batch, Plan* p, bool with_tiles,
   if (vrows * 8 > INT32_MAX) return fail(ENC_ERR_TOO_LONG, "batch has too many positions");
   p->vrows = vrows;
   p->cu_seq.push_back((int32_t)vrows);
-  const int n_seq = (int)p->cu_seq.size() - 1;
-  p->tile_seq.clear();
-  p->tile_q0.clear();
-  if (with_tiles) {
-    for (int s = 0; s < n_seq; ++s) {
-      const int len = p->cu_seq[s + 1] - p->cu_seq[s];
-      for (int q0 = 0; q0 < len; q0 += ATT_QB) {
-        p->tile_seq.push_back(s);
-        p->tile_q0.push_back(q0);
-      }
-    }
-  }
+  p->tile_info.clear();
+  if (with_tiles) seq_tiles(p->cu_seq, &p->tile_info);
   // Adapter sequences: every clip whole, at twice the positions.
   p->all_rows = {0, (int32_t)rows};
   p->a_cu.resize(batch + 1);
   for (int b = 0; b <= batch; ++b) p->a_cu[b] = 2 * p->cu_clip[b];
-  seq_tiles(p->a_cu, &p->a_tile_seq, &p->a_tile_q0);
+  seq_tiles(p->a_cu, &p->a_tile_info);
   return ENC_OK;
 }
 
-void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* tile_seq,
-               std::vector<int32_t>* tile_q0) {
+void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* tile_info) {
   const int n = (int)cu.size() - 1;
-  tile_seq->clear();
-  tile_q0->clear();
+  tile_info->clear();
   for (int s = 0; s < n; ++s) {
     const int len = cu[s + 1] - cu[s];
     for (int q0 = 0; q0 < len; q0 += ATT_QB) {
-      tile_seq->push_back(s);
-      tile_q0->push_back(q0);
+      tile_info->push_back(cu[s]);
+      tile_info->push_back(len);
+      tile_info->push_back(q0);
+      tile_info->push_back(0);
     }
   }
 }
@@ -722,8 +712,7 @@ CtcLayout ctc_layout_for(int64_t rows, int n_pad) {
 // The timestamp adapter on clip-packed encoder states h [rows, 1280] (bf16):
 // upsampling to 2 rows per position, its layers, final LayerNorm, projection
 // and log-softmax into out [2 rows, n_classes].
-int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_cu,
-                const int32_t* d_ts, const int32_t* d_tq, float* out,
+int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_ti, float* out,
                 hipStream_t stream) {
   const CtcW& W = *ctx->ctc;
   const int64_t R = 2 * p.rows;
@@ -750,7 +739,7 @@ int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_c
   bf16_t* o = (bf16_t*)(ws + lay.o);
   bf16_t* u = (bf16_t*)(ws + lay.u);
   float* z = (float*)(ws + lay.z);
-  const int n_tiles = (int)p.a_tile_seq.size();
+  const int n_tiles = (int)p.a_tile_info.size() / 4;
   // Upsampling: [rows, 2 x 1280] row-major is [2 rows, 1280] (frame 2t + j).
   ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasF32, h, D, W.w_conv, D, W.b_conv2, x, 2 * D,
                                     p.rows, 2 * D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
@@ -760,11 +749,10 @@ int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_c
                                       3 * CTC_HD, R, 3 * CTC_HD, D, ctx->gemm_part,
                                       GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_CTC,
-               launch_qknorm_rope(qkv, d_cu, d_ts, d_tq, n_tiles, CTC_HEADS, CTC_DH, L.q_g,
-                                  L.q_b, L.k_g, L.k_b, W.rope_cos, W.rope_sin, stream));
-    ENC_LAUNCH(ENC_K_CTC,
-               launch_attention(qkv, d_cu, d_ts, d_tq, n_tiles, CTC_HEADS,
-                                CTC_DH, L.attn_fixed_ref, o, 0.0f, stream));
+               launch_qknorm_rope(qkv, d_ti, n_tiles, CTC_HEADS, CTC_DH, L.q_g, L.q_b, L.k_g,
+                                  L.k_b, W.rope_cos, W.rope_sin, stream));
+    ENC_LAUNCH(ENC_K_CTC, launch_attention(qkv, d_ti, n_tiles, CTC_HEADS, CTC_DH,
+                                           L.attn_fixed_ref, o, 0.0f, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasResidualF32, o, D, L.w_o, D, L.b_o, x, D, R,
                                       D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_layernorm(x, L.ln2_g, L.ln2_b, a, R, stream));
@@ -841,22 +829,19 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   bf16_t* stk = u;
 
   std::vector<int32_t*> dev;
-  if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.cu_seq, &p.tile_seq,
-                              &p.tile_q0, &p.cu_clip, &p.gather_src, &p.out_src, &p.a_cu,
-                              &p.a_tile_seq, &p.a_tile_q0, &p.all_rows},
+  if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.tile_info, &p.cu_clip,
+                              &p.gather_src, &p.out_src, &p.a_tile_info, &p.all_rows},
                         &dev, stream)) != ENC_OK)
     return rc;
   const int32_t* d_nf = dev[0];
   const int32_t* d_fb = dev[1];
-  const int32_t* d_cu = dev[2];
-  const int32_t* d_ts = dev[3];
-  const int32_t* d_tq = dev[4];
-  const int32_t* d_clip = dev[5];
+  const int32_t* d_ti = dev[2];
+  const int32_t* d_clip = dev[3];
   const bool overlap = !p.gather_src.empty();
-  const int32_t* d_gather = overlap ? dev[6] : nullptr;
-  const int32_t* d_outsrc = overlap ? dev[7] : nullptr;
+  const int32_t* d_gather = overlap ? dev[4] : nullptr;
+  const int32_t* d_outsrc = overlap ? dev[5] : nullptr;
   const int64_t R = p.vrows;
-  const int n_tiles = (int)p.tile_seq.size();
+  const int n_tiles = (int)p.tile_info.size() / 4;
 
   // Stacked features of the clips (packed by clip); with overlapping windows
   // they are gathered into window order (context rows repeated) first.
@@ -891,10 +876,10 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                              GEMM_PARTIAL_BYTES, stream));
     }
     ENC_LAUNCH(ENC_K_QKNORM_ROPE,
-               launch_qknorm_rope(qkv, d_cu, d_ts, d_tq, n_tiles, H, DH, Lw.q_g, Lw.q_b,
-                                  Lw.k_g, Lw.k_b, ctx->rope_cos, ctx->rope_sin, stream));
+               launch_qknorm_rope(qkv, d_ti, n_tiles, H, DH, Lw.q_g, Lw.q_b, Lw.k_g, Lw.k_b,
+                                  ctx->rope_cos, ctx->rope_sin, stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
-               launch_attention(qkv, d_cu, d_ts, d_tq, n_tiles, H, DH,
+               launch_attention(qkv, d_ti, n_tiles, H, DH,
                                 Lw.attn_fixed_ref, o, fp8 ? Lw.r_x[1] : 0.0f, stream));
     if (fp8) {
       ENC_LAUNCH(ENC_K_GEMM_O,
@@ -927,9 +912,9 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   if (calib) return ENC_OK;
   if (ctc) {
     // Encoder states, clip-packed bf16, into the LayerNorm buffer.
-    ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, dev[11], d_outsrc,
+    ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, dev[7], d_outsrc,
                                                    1, p.rows, a, stream));
-    return run_adapter(ctx, p, a, dev[8], dev[9], dev[10], (float*)out, stream);
+    return run_adapter(ctx, p, a, dev[6], (float*)out, stream);
   }
   if (!fused) {
     ENC_LAUNCH(ENC_K_FINAL_NORM, launch_final_norm(x, ctx->lnf_g, ctx->lnf_b, d_clip, d_outsrc,
