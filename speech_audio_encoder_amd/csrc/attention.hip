@@ -54,7 +54,7 @@ namespace enc {
 namespace {
 
 constexpr int QTILE = 128;             // queries per workgroup (the plan's tiles)
-constexpr int KT = 64;                 // keys per V^T tile
+constexpr int KT = 64;                 // keys per V tile
 constexpr int KU = 32;                 // keys per K unit (one score block)
 constexpr int KU_BYTES = KU * DH * 2;  // 8 KB
 constexpr int VT_BYTES = KT * DH * 2;  // 16 KB
@@ -62,7 +62,7 @@ constexpr int QB = 1;                  // 32-query blocks per wavefront
 constexpr int QPW = 32 * QB;           // queries per wavefront
 constexpr int NW = QTILE / QPW;        // wavefronts per workgroup
 constexpr int KP = 8 / NW;             // 1-KB pieces of a K unit per wavefront
-constexpr int VP = 16 / NW;            // 1-KB pieces of a V^T tile per wavefront
+constexpr int VP = 16 / NW;            // 1-KB pieces of a V tile per wavefront
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   };
 
   // Probabilities of one unit and O^T += V^T P^T over its two 16-key steps
-  // (kk0, kk0 + 1 of V^T tile j).  Row sums take the bf16 probabilities the
+  // (kk0, kk0 + 1 of V tile j).  Row sums take the bf16 probabilities the
   // products use (one dot2 per pair).
   auto expv = [&](f32x16 (&S)[QB], int j, int kk0) __attribute__((always_inline)) {
     const uint32_t sv = v_lds0 + (j & 1) * VT_BYTES;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     }
   };
 
-  // Prologue: K units 0..2 and V^T tile 0; scores of unit 0.
+  // Prologue: K units 0..2 and V tile 0; scores of unit 0.
   issue_k(0);
   issue_k(1);
   issue_k(2);
@@ -315,8 +315,8 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 
   // Tile j (not the last one): units 2j, 2j+1 go through softmax and V while
   // the scores of units 2j+1 and 2j+2 are computed.  K units 2j+1, 2j+2 and
-  // V^T tile j were loaded during the previous step; this step loads K units
-  // 2j+3, 2j+4 into the slots of 2j-1, 2j and V^T tile j+1 into the buffer
+  // V tile j were loaded during the previous step; this step loads K units
+  // 2j+3, 2j+4 into the slots of 2j-1, 2j and V tile j+1 into the buffer
   // of tile j-1, all read before the barrier.
 #pragma unroll 1
   for (int j = 0; j + 1 < nkt; ++j) {

@@ -1,6 +1,6 @@
 // Row-wise kernels for gfx950: LayerNorm (pre-norm and final), fused QK
-// normalisation + rotary embedding with the V transpose the attention kernel
-// reads, and the element conversions used when weights are copied in.
+// normalisation + rotary embedding, and the element conversions used when
+// weights are copied in.
 //
 // Method: "Nemotron 3.5 Transcribe: From Recorded Speech to Dataset Audits",
 // section "How audio and speakers reach the language model" names QK
@@ -176,17 +176,11 @@ __global__ __launch_bounds__(256) void final_norm_kernel(const float* __restrict
         make_uint2(pack_bf16x2(o[i].x, o[i].y), pack_bf16x2(o[i].z, o[i].w));
 }
 
-// Workgroup: one attention tile (up to 128 positions of one clip) x one head.
-// Grid z = 0 handles q and k, z = 1 v (separate workgroups keep each path's
-// registers low).  q and k: 8 lanes per (row, head); lane j holds dims 8j..8j+7 and
+// QK-norm layout: 8 lanes per (row, head); lane j holds dims 8j..8j+7 and
 // 64+8j..64+8j+7, i.e. eight whole rotation pairs, so the rotation is local,
 // every access is a 16-byte vector and a wavefront's access covers whole
-// 128-byte lines; the statistics reduce over the 8 lanes.  v: each thread
-// transposes an 8 x 8 block in registers; the thread map puts the 8 threads
-// that share a dim block on consecutive position blocks, so every store
-// instruction writes whole 128-byte rows of vt.
-// The clip's keys occupy columns [vt_base[b], vt_base[b] + roundup(P_b, 64))
-// of vt; columns past P_b are written as zeros.
+// 128-byte lines; the statistics reduce over the 8 lanes.  The plan's tiles
+// are QK_ROWS positions; a workgroup takes a quarter of one.
 constexpr int QK_ROWS = 128;
 constexpr int QK_HEAD_GROUPS = 5;   // measured: 2 heads per group for 10 heads
 
