@@ -78,7 +78,7 @@ hipError_t launch_quantize_fp8(const bf16_t* w, int64_t n, const float* amax, fl
 hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
 
 // out[r, c] = z[r, c] - log(sum_c' exp(z[r, c'])) over c, c' < n; z rows of
-// stride ldz, out rows of stride n (fp32).
+// stride ldz (a multiple of 4), out rows of stride n (fp32); n <= 24,576.
 hipError_t launch_log_softmax(const float* z, int64_t ldz, int64_t rows, int n, float* out,
                               hipStream_t stream);
 

@@ -404,48 +404,54 @@ __global__ __launch_bounds__(256) void speaker_fuse_kernel(
   }
 }
 
-// Log-softmax of each row over its first n entries: one workgroup per row
-// keeps a running maximum and sum of exponentials (rescaled when the maximum
-// grows), merges the 256 partial pairs, then writes z - max - log(sum).
+// Log-softmax of one row per workgroup: the row (up to LSM_MAX values) is
+// read once into registers (24 float4 per thread), then its maximum, the sum
+// of exp(z - max) and the output z - max - log(sum) come from the registers.
+constexpr int LSM_CHUNKS = 24;
+constexpr int LSM_MAX = LSM_CHUNKS * 4 * 256;
+
+__device__ __forceinline__ float block_reduce4(float v, float* red, bool is_max) {
+  v = is_max ? wave_max(v) : wave_sum(v);
+  __syncthreads();   // red is reused
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))
+                : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 __global__ __launch_bounds__(256) void log_softmax_kernel(const float* __restrict__ z,
                                                           int64_t ldz, int n,
                                                           float* __restrict__ out) {
-  __shared__ float pm[4], ps[4];
+  __shared__ float red[4];
   const float* zr = z + (int64_t)blockIdx.x * ldz;
-  float m = -INFINITY, sum = 0.0f;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const float v = zr[i];
-    if (v > m) {
-      sum = sum * __expf(m - v) + 1.0f;
-      m = v;
-    } else {
-      sum += __expf(v - m);
-    }
-  }
-  auto merge = [](float& m1, float& s1, float m2, float s2) {
-    const float mm = fmaxf(m1, m2);
-    if (mm == -INFINITY) return;
-    s1 = s1 * __expf(m1 - mm) + s2 * __expf(m2 - mm);
-    m1 = mm;
-  };
+  float4 v[LSM_CHUNKS];
+  float m = -INFINITY;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64);
-    const float s2 = __shfl_xor(sum, o, 64);
-    merge(m, sum, m2, s2);
+  for (int c = 0; c < LSM_CHUNKS; ++c) {
+    const int e = (threadIdx.x + 256 * c) * 4;
+    // ldz is a multiple of 4, so a chunk that starts before n lies in the row
+    v[c] = e < n ? *reinterpret_cast<const float4*>(zr + e)
+                 : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    if (e + 1 >= n) v[c].y = -INFINITY;
+    if (e + 2 >= n) v[c].z = -INFINITY;
+    if (e + 3 >= n) v[c].w = -INFINITY;
+    m = fmaxf(m, fmaxf(fmaxf(v[c].x, v[c].y), fmaxf(v[c].z, v[c].w)));
   }
-  if ((threadIdx.x & 63) == 0) {
-    pm[threadIdx.x >> 6] = m;
-    ps[threadIdx.x >> 6] = sum;
-  }
-  __syncthreads();
-  m = pm[0];
-  sum = ps[0];
+  m = block_reduce4(m, red, true);
+  float sum = 0.0f;
 #pragma unroll
-  for (int w = 1; w < 4; ++w) merge(m, sum, pm[w], ps[w]);
-  const float lse = m + __logf(sum);
+  for (int c = 0; c < LSM_CHUNKS; ++c)
+    sum += (__expf(v[c].x - m) + __expf(v[c].y - m)) + (__expf(v[c].z - m) + __expf(v[c].w - m));
+  const float lse = m + __logf(block_reduce4(sum, red, false));
   float* orow = out + (int64_t)blockIdx.x * n;
-  for (int i = threadIdx.x; i < n; i += 256) orow[i] = zr[i] - lse;
+#pragma unroll
+  for (int c = 0; c < LSM_CHUNKS; ++c) {
+    const int e = (threadIdx.x + 256 * c) * 4;
+    if (e < n) orow[e] = v[c].x - lse;
+    if (e + 1 < n) orow[e + 1] = v[c].y - lse;
+    if (e + 2 < n) orow[e + 2] = v[c].z - lse;
+    if (e + 3 < n) orow[e + 3] = v[c].w - lse;
+  }
 }
 
 __global__ void to_bf16_kernel(const void* __restrict__ src, int src_is_bf16,
@@ -502,7 +508,8 @@ hipError_t launch_quantize_fp8(const bf16_t* w, int64_t n, const float* amax, fl
 hipError_t launch_log_softmax(const float* z, int64_t ldz, int64_t rows, int n, float* out,
                               hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  if (n < 1 || ldz < n || rows > 0x7fffffff) return hipErrorInvalidValue;
+  if (n < 1 || n > LSM_MAX || ldz < n || ldz % 4 != 0 || rows > 0x7fffffff)
+    return hipErrorInvalidValue;
   log_softmax_kernel<<<dim3((unsigned)rows), dim3(256), 0, stream>>>(z, ldz, n, out);
   return hipGetLastError();
 }
