@@ -6,6 +6,7 @@
 // "How audio and speakers reach the language model"; the same page's section
 // "Local encoder windows, recording-wide language context" notes that
 // FlashAttention-style kernels avoid materialising the quadratic score matrix).
+// The timestamp adapter's sixteen heads of width 80 run in the same kernel.
 //
 // Work split: a workgroup of four wavefronts takes 128 queries of one clip
 // and one head, 32 queries per wavefront.  (Two wavefronts of 64 queries, in
@@ -29,9 +30,9 @@
 // softmax overlaps the MFMAs.
 //
 // Softmax reference.  QK-norm bounds every score: after LayerNorm a head
-// vector has norm at most max|gain| * sqrt(128) + |bias|, so |q.k| is bounded
+// vector of width w has norm at most max|gain| * sqrt(w) + |bias|, so |q.k| is bounded
 // by the product of the two norms.  When the launcher is told that this bound
-// keeps scores * log2(e) / sqrt(128) within +-100 (kFixedRef), probabilities
+// keeps scores * log2(e) / sqrt(w) within +-100 (kFixedRef), probabilities
 // are exp2 of the scaled scores against a fixed reference of 0: no running
 // maximum, no rescaling, and fp32 sums cannot overflow.  Otherwise the
 // running maximum is kept lazily: the accumulators are rescaled only when a
@@ -86,10 +87,17 @@ __device__ __forceinline__ void lds_loads_wait() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <bool kFixedRef>
+// HW: head width, 128 (the encoder) or 80 (the timestamp adapter).  Heads
+// are packed at their own width in the qkv rows; in LDS every key row keeps
+// 16 chunks of 8 dims, of which a narrower head fills the first HW / 8.
+template <bool kFixedRef, int HW>
 __global__ __launch_bounds__(64 * NW) void attention_kernel(
     const bf16_t* __restrict__ qkv, const int4* __restrict__ tile_info, int n_tiles,
-    int n_items, void* __restrict__ out, float out_scale, int hd, int dh_out) {
+    int n_items, void* __restrict__ out, float out_scale, int hd) {
+  static_assert(HW % 16 == 0 && HW <= DH, "head width");
+  constexpr int KS = HW / 16;          // 16-dim steps of the scores
+  constexpr int NDB = (HW + 31) / 32;  // 32-dim blocks of the output
+  constexpr int NCH = HW / 8;          // 16-byte chunks of a head row
   // K in a ring of four 32-key units, V in two 64-key tiles.
   __shared__ uint4 sK[4][KU * DH / 8];   // [key][16 chunks of 8 dims], swizzled
   __shared__ uint4 sV[2][KT * DH / 8];   // [key][16 chunks of 8 dims], swizzled
@@ -115,14 +123,14 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   const int lhi = lane >> 5;
 
   // Q^T fragments: query block qb, 16-dim step s.
-  bf16x8 qf[QB][DH / 16];
+  bf16x8 qf[QB][KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = q0 + wave * QPW + qb * 32 + l32;
     const bool ok = q < len;
-    const bf16_t* qrow = qkv + (s0 + (ok ? q : 0)) * (3 * hd) + h * DH + lhi * 8;
+    const bf16_t* qrow = qkv + (s0 + (ok ? q : 0)) * (3 * hd) + h * HW + lhi * 8;
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s) {
+    for (int s = 0; s < KS; ++s) {
       const uint4 u = ok ? *reinterpret_cast<const uint4*>(qrow + s * 16) : make_uint4(0, 0, 0, 0);
       qf[qb][s] = __builtin_bit_cast(bf16x8, u);
     }
@@ -133,20 +141,24 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   // key k holding global chunk c ^ (k%16); this wave loads pieces
   // KP*wave..KP*wave+KP-1.  A V tile is sixteen pieces, LDS chunk c of key k
   // holding global chunk c ^ 4(k%4); this wave loads VP*wave..VP*wave+VP-1.
-  // Offsets are bytes from the unit's / tile's first key row.
+  // Offsets are bytes from the unit's / tile's first key row.  A narrower
+  // head has fewer chunks than the LDS row: lanes whose global chunk lies
+  // past it load chunk - 8 of the same row instead (finite data in LDS chunks
+  // that the scores never read and that only reach output dims >= HW).
+  auto in_head = [](int c) { return NCH == 16 || c < NCH ? c : c - 8; };
   uint32_t koff[KP], vchunk[VP];
 #pragma unroll
   for (int t = 0; t < KP; ++t) {
     const int key = (wave * KP + t) * 4 + (lane >> 4);
-    koff[t] = (uint32_t)(key * (3 * hd * 2) + (((lane & 15) ^ (key & 15)) * 16));
+    koff[t] = (uint32_t)(key * (3 * hd * 2) + in_head((lane & 15) ^ (key & 15)) * 16);
   }
 #pragma unroll
   for (int t = 0; t < VP; ++t) {
     const int key = (wave * VP + t) * 4 + (lane >> 4);
-    vchunk[t] = (uint32_t)(((lane & 15) ^ (4 * (key & 3))) * 16);
+    vchunk[t] = (uint32_t)(in_head((lane & 15) ^ (4 * (key & 3))) * 16);
   }
-  const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + hd + h * DH);
-  const char* vbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + 2 * hd + h * DH);
+  const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + hd + h * HW);
+  const char* vbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + 2 * hd + h * HW);
   const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_void*)&sK[0][0] + wave * KP * 1024;
   const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0] + wave * VP * 1024;
   // K unit u into ring slot u % 4.  Units past the clip's last one re-load
@@ -169,7 +181,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     }
   };
 
-  // Scores arrive in log2 units (k was scaled by log2(e) / sqrt(128)).
+  // Scores arrive in log2 units (k was scaled by log2(e) / sqrt(HW)).
   float m_run[QB], l_run[QB];     // running maxima; this lane's partial row sums
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -177,9 +189,9 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     l_run[qb] = 0.f;
   }
 
-  f32x16 O[DH / 32][QB];
+  f32x16 O[NDB][QB];
 #pragma unroll
-  for (int db = 0; db < DH / 32; ++db)
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -210,7 +222,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) S[qb][v] = 0.f;
 #pragma unroll
-    for (int s = 0; s < DH / 16; ++s) {
+    for (int s = 0; s < KS; ++s) {
       const bf16x8 kf = __builtin_bit_cast(bf16x8, sk[l32 * 16 + ((2 * s) ^ kx)]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
@@ -250,7 +262,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
           const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mn);
           l_run[qb] *= alpha;
 #pragma unroll
-          for (int db = 0; db < DH / 32; ++db)
+          for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int v = 0; v < 16; ++v) O[db][qb][v] *= alpha;
           m_run[qb] = mn;
@@ -288,7 +300,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
       }
       const int kk = kk0 + half;
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db) {
+      for (int db = 0; db < NDB; ++db) {
         // chunk 4 db + q of key row k sits at 4 (db ^ (k%4)) + q, and k%4 = tr_j
         const uint32_t at = sv + kk * 16 * (DH * 2) + tr_off + ((db ^ tr_j) << 6);
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)at);
@@ -358,9 +370,9 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     const float inv = 1.0f / lt;
     if (out_scale > 0.0f) {
       // E4M3 codes of the output times out_scale (the FP8 output projection's input)
-      uint8_t* orow = reinterpret_cast<uint8_t*>(out) + (s0 + q) * hd + h * DH;
+      uint8_t* orow = reinterpret_cast<uint8_t*>(out) + (s0 + q) * hd + h * HW;
 #pragma unroll
-      for (int db = 0; db < DH / 32; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d = db * 32 + 8 * g + 4 * lhi;
@@ -371,16 +383,15 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
         }
       continue;
     }
-    // rows of n_heads x dh_out: a head narrower than its 128-wide slot
-    // (dims >= dh_out are zero) stores only its own dims
-    bf16_t* orow = reinterpret_cast<bf16_t*>(out) + (s0 + q) * (int64_t)(n_items / n_tiles) * dh_out +
-                   h * dh_out;
+    // rows of n_heads x HW; the last 32-dim block of a head narrower than a
+    // multiple of 32 holds dims past HW, which are not stored
+    bf16_t* orow = reinterpret_cast<bf16_t*>(out) + (s0 + q) * (int64_t)hd + h * HW;
 #pragma unroll
-    for (int db = 0; db < DH / 32; ++db)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = db * 32 + 8 * g + 4 * lhi;
-        if (d >= dh_out) continue;
+        if (d >= HW) continue;
         *reinterpret_cast<uint2*>(orow + d) =
             make_uint2(pack_bf16x2(O[db][qb][4 * g] * inv, O[db][qb][4 * g + 1] * inv),
                        pack_bf16x2(O[db][qb][4 * g + 2] * inv, O[db][qb][4 * g + 3] * inv));
@@ -412,16 +423,16 @@ hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_t
                             int n_heads, int head_dim, bool fixed_ref, void* out, float out_scale,
                             hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
-  if (n_heads < 1 || head_dim < 4 || head_dim > DH || head_dim % 4 != 0 ||
-      (out_scale > 0.0f && head_dim != DH))
+  if (n_heads < 1 || (head_dim != DH && head_dim != 80) || (out_scale > 0.0f && head_dim != DH))
     return hipErrorInvalidValue;
   const int n_items = n_tiles * n_heads;
-  const int hd = n_heads * DH;
+  const int hd = n_heads * head_dim;
   const int grid = (n_items + 7) / 8 * 8;
-  auto kernel = fixed_ref ? attention_kernel<true> : attention_kernel<false>;
+  auto kernel = head_dim == DH
+                    ? (fixed_ref ? attention_kernel<true, DH> : attention_kernel<false, DH>)
+                    : (fixed_ref ? attention_kernel<true, 80> : attention_kernel<false, 80>);
   kernel<<<dim3(grid), dim3(64 * NW), 0, stream>>>(
-      qkv, reinterpret_cast<const int4*>(tile_info), n_tiles, n_items, out, out_scale, hd,
-      head_dim);
+      qkv, reinterpret_cast<const int4*>(tile_info), n_tiles, n_items, out, out_scale, hd);
   return hipGetLastError();
 }
 

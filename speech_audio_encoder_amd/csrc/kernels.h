@@ -82,16 +82,14 @@ hipError_t launch_fill_f32(float* p, float v, int64_t n, hipStream_t stream);
 hipError_t launch_log_softmax(const float* z, int64_t ldz, int64_t rows, int n, float* out,
                               hipStream_t stream);
 
-// In place on qkv [rows, 3840] bf16, per attention tile and head:
-// q <- RoPE(LN_q(q)), k <- RoPE(LN_k(k)) * K_SCORE_SCALE.  tile_info holds
-// four int32 per tile: the sequence's first row, its length, the tile's first
-// position (the tile covers positions p0 .. p0 + 127 of the sequence), 0.
-// Head slots are 128 wide for every head width: qkv rows hold q, k, v blocks
-// of n_heads x 128 (row stride 3 x n_heads x 128); with head_dim 80 (the
-// timestamp adapter) dims 80..127 of a slot are zero and stay zero, the
-// statistics cover the 80 dims, the rotation pairs (i, i + 40) and k is
-// scaled by log2(e) / sqrt(80).  rope tables hold head_dim / 2 entries per
-// position.  head_dim: 128 or 80.
+// In place on qkv bf16, per attention tile and head:
+// q <- RoPE(LN_q(q)), k <- RoPE(LN_k(k)) * log2(e) / sqrt(head_dim).
+// tile_info holds four int32 per tile: the sequence's first row, its length,
+// the tile's first position (the tile covers positions p0 .. p0 + 127 of the
+// sequence), 0.  qkv rows hold q, k, v blocks of n_heads x head_dim (row
+// stride 3 x n_heads x head_dim), heads packed at their width; rotation pairs
+// are (i, i + head_dim / 2) and the rope tables hold head_dim / 2 entries per
+// position.  head_dim: 128 (the encoder) or 80 (the timestamp adapter).
 hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* tile_info, int n_tiles, int n_heads,
                               int head_dim, const float* qg, const float* qb, const float* kg,
                               const float* kb, const float* rope_cos, const float* rope_sin,
@@ -136,20 +134,20 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
 
 // --------------------------------------------------------------- attention
 // Bidirectional softmax attention per clip and head.  q, k, v are the three
-// (n_heads x 128)-column groups of qkv [rows, 3 x n_heads x 128] (1280 for
-// the encoder's ten heads), q and k as launch_qknorm_rope leaves them.  Work tile
-// i (tile_info as for launch_qknorm_rope) covers queries [q0, min(q0 + 128,
-// length)) of its sequence.  out is bf16 [rows, n_heads x head_dim] with head h in columns
-// h*head_dim... (head_dim <= 128: a narrower head's slot has zero dims past
-// head_dim, which are not stored), or,
-// when out_scale > 0, E4M3 codes of the output times out_scale (saturated at
-// +-448), one byte per element in the same layout.
+// (n_heads x head_dim)-column groups of qkv [rows, 3 x n_heads x head_dim]
+// (head_dim 128 for the encoder's ten heads, 80 for the timestamp adapter's
+// sixteen), q and k as launch_qknorm_rope leaves them.  Work tile i
+// (tile_info as for launch_qknorm_rope) covers queries [q0, min(q0 + 128,
+// length)) of its sequence.  out is bf16 [rows, n_heads x head_dim] with head
+// h in columns h*head_dim..., or, when out_scale > 0 (head_dim 128 only), E4M3
+// codes of the output times out_scale (saturated at +-448), one byte per
+// element in the same layout.
 // k is read in whole 64-key tiles past a clip's end (those keys are masked),
 // so qkv must have 63 readable rows after its last one.
 hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_tiles,
                             int n_heads, int head_dim, bool fixed_ref, void* out, float out_scale,
                             hipStream_t stream);
-// fixed_ref may be true only when |q . k| * log2(e) / sqrt(128) <= 100 for
+// fixed_ref may be true only when |q . k| * log2(e) / sqrt(head_dim) <= 100 for
 // every query and key (softmax against a fixed reference instead of a
 // running maximum); attention_fixed_ref_ok decides it from the QK-norm
 // parameters of a layer.

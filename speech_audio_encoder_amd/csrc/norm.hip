@@ -199,9 +199,9 @@ __device__ __forceinline__ void unpack8(const uint4 u, float (&f)[8]) {
 // and serve every head; the next head's q and k are loaded while the current
 // one is computed.
 // HALF = half the head width (rotation pairs (i, i + HALF)): 64 for the
-// encoder's heads, 40 for the timestamp adapter's (head slots stay 128 wide,
-// dims 2 HALF .. 127 are zero and untouched).  ldq: row stride of qkv, hd:
-// offset of the k block within a row (heads x 128), kscale: factor on k.
+// encoder's heads, 40 for the timestamp adapter's; heads are packed at their
+// width.  ldq: row stride of qkv, hd: offset of the k block within a row
+// (heads x 2 HALF), kscale: factor on k.
 template <int HALF>
 __device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, int hd, int h0,
                                         int h1, int64_t s0, int len, int p, int lane,
@@ -241,7 +241,7 @@ __device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, i
   bf16_t* row = qkv + (s0 + pl) * ldq + d0;
   // u[0..1]: q dims d0.. and HALF + d0..; u[2..3]: the same of k
   auto load = [&](int h, uint4 (&u)[4]) __attribute__((always_inline)) {
-    const bf16_t* base = row + h * DH;
+    const bf16_t* base = row + h * (2 * HALF);
     u[0] = *reinterpret_cast<const uint4*>(base);
     u[1] = *reinterpret_cast<const uint4*>(base + HALF);
     u[2] = *reinterpret_cast<const uint4*>(base + hd);
@@ -295,7 +295,7 @@ __device__ __forceinline__ void qk_rows(bf16_t* __restrict__ qkv, int64_t ldq, i
         hi[e / 2] = pack_bf16x2(y1[0], y1[1]);
       }
       if (live && act) {
-        bf16_t* base = row + which * hd + h * DH;
+        bf16_t* base = row + which * hd + h * (2 * HALF);
         *reinterpret_cast<uint4*>(base) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         *reinterpret_cast<uint4*>(base + HALF) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
       }
@@ -553,7 +553,7 @@ hipError_t launch_qknorm_rope(bf16_t* qkv, const int32_t* tile_info, int n_tiles
                               hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   if (n_heads < 1) return hipErrorInvalidValue;
-  const int hd = n_heads * DH;
+  const int hd = n_heads * head_dim;
   // log2(e) / sqrt(head width)
   const float kscale = (float)(1.4426950408889634 / std::sqrt((double)head_dim));
   // the heads are split into QK_HEAD_GROUPS groups, one block per group and

@@ -255,11 +255,11 @@ struct LayerW {
   float r_x[4] = {1, 1, 1, 1};     // fp32(1 / s_x): scale of the producer's codes
 };
 
-// Timestamp adapter: 16 heads of 80 in 128-wide slots (QKV rows and bias
-// padded with zeros), projection rows padded to a multiple of 128.
+// Timestamp adapter: 16 heads of 80, packed at their width (q, k, v blocks of
+// 1280 as in the source matrix); projection rows padded to a multiple of 128.
 constexpr int CTC_HEADS = 16;
 constexpr int CTC_DH = 80;
-constexpr int CTC_HD = CTC_HEADS * DH;   // width of a q / k / v block in slots
+constexpr int CTC_HD = CTC_HEADS * CTC_DH;   // width of a q / k / v block
 
 struct CtcW {
   void* mat = nullptr;    // bf16 matrices
@@ -998,13 +998,11 @@ int enc_set_ctc(enc_ctx* ctx, const enc_ctc_weights* w) {
     (void)hipGetLastError();
     return drop(ENC_ERR_NOMEM, "adapter weight allocation failed");
   }
-  // Zeros first: the slots' padding dims and the projection's padding rows.
+  // Zeros first: the projection's padding rows.
   if ((e = hipMemset(W->mat, 0, n_mat * 2)) != hipSuccess ||
       (e = hipMemset(W->vec, 0, n_vec * 4)) != hipSuccess)
     return drop(ENC_ERR_HIP, std::string("adapter weight clear: ") + hipGetErrorString(e));
   const bool bf = w->dtype == ENC_BF16;
-  const size_t esz = bf ? 2 : 4;
-  auto at = [&](const void* base, size_t elems) { return (const void*)((const char*)base + elems * esz); };
   bf16_t* pm = (bf16_t*)W->mat;
   float* pv = (float*)W->vec;
   e = hipSuccess;
@@ -1033,15 +1031,8 @@ int enc_set_ctc(enc_ctx* ctx, const enc_ctc_weights* w) {
     LayerW& T = W->layers[i];
     T.w_qkv = pm;
     T.b_qkv = pv;
-    // head h of block q / k / v: source rows blk 1280 + 80 h .. + 79 go to
-    // slot rows blk (16 x 128) + 128 h .. + 79
-    for (int blk = 0; blk < 3; ++blk)
-      for (int h = 0; h < CTC_HEADS; ++h) {
-        const size_t srow = (size_t)blk * D + (size_t)h * CTC_DH;
-        const size_t drow = (size_t)blk * CTC_HD + (size_t)h * DH;
-        mat(at(S.w_qkv, srow * D), (size_t)CTC_DH * D, pm + drow * D);
-        vec(at(S.b_qkv, srow), CTC_DH, pv + drow);
-      }
+    mat(S.w_qkv, (size_t)3 * CTC_HD * D, pm);
+    vec(S.b_qkv, 3 * CTC_HD, pv);
     pm += (size_t)3 * CTC_HD * D;
     pv += 3 * CTC_HD;
     T.w_o = pm;
