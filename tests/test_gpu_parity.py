@@ -69,13 +69,14 @@ def get_weights(kind):
 
 
 def score_log2_bound(lw):
-    """Bound on |q.k| * log2(e) / sqrt(128) implied by the QK-norm parameters
-    (a LayerNorm'd 128-vector has norm <= sqrt(128)), with the 2^-6 margin the
-    library uses to choose a fixed softmax reference (bound <= 100)."""
+    """Bound on |q.k| * log2(e) / sqrt(w) implied by the QK-norm parameters of
+    head width w (a LayerNorm'd w-vector has norm <= sqrt(w)), with the 2^-6
+    margin the library uses to choose a fixed softmax reference (bound <= 100)."""
+    w = len(lw["q_g"])
     def norm_bound(g, b):
-        return float(np.abs(g).max()) * np.sqrt(128) + float(np.linalg.norm(b))
+        return float(np.abs(g).max()) * np.sqrt(w) + float(np.linalg.norm(b))
     return (norm_bound(lw["q_g"], lw["q_b"]) * norm_bound(lw["k_g"], lw["k_b"])
-            * (1 + 1 / 64) * np.log2(np.e) / np.sqrt(128))
+            * (1 + 1 / 64) * np.log2(np.e) / np.sqrt(w))
 
 
 def prefix(w, n):
@@ -706,8 +707,14 @@ def get_ctc(kind):
     if kind not in _CTC:
         if kind == "full":
             _CTC[kind] = workloads.make_ctc_weights(bf16=True)
-        else:   # perturbed, a small vocabulary (the oracle's projection stays quick)
+        elif kind == "small":   # perturbed, a small vocabulary (the oracle's projection stays quick)
             _CTC[kind] = workloads.make_ctc_weights(bf16=False, perturb=True, n_classes=1000)
+        elif kind == "sharp":   # the same with QK-norm gains x3 (running softmax maximum)
+            cw = workloads.make_ctc_weights(bf16=False, perturb=True, n_classes=1000)
+            for lw in cw["layers"]:
+                lw["q_g"] = lw["q_g"] * 3.0
+                lw["k_g"] = lw["k_g"] * 3.0
+            _CTC[kind] = cw
     return _CTC[kind]
 
 
@@ -756,6 +763,35 @@ def test_forward_ctc_ragged(torch_mod, binding_mod):
         if f:
             ref = ctc.ctc_logprobs(audio[b, :n], w, cw)
             check_logprobs(got[r0:r0 + f], ref, f"ctc clip {b} ({f} frames)")
+        r0 += f
+    assert r0 == got.shape[0]
+
+
+def test_forward_ctc_large_qk_gains_running_max(torch_mod, binding_mod):
+    # adapter heads (width 80) whose QK-norm gains rule out the fixed softmax
+    # reference; the clip spans several 128-frame query tiles and 64-frame key
+    # tiles with a ragged tail
+    from oracle import ctc
+    torch = torch_mod
+    w = get_weights("perturbed")
+    cw = get_ctc("sharp")
+    for lw in cw["layers"]:
+        assert len(lw["q_g"]) == 80 and score_log2_bound(lw) > 100.0
+    for lw in get_ctc("small")["layers"]:
+        assert score_log2_bound(lw) <= 100.0
+    lengths = [700_000, 16_400]
+    audio, lengths = workloads.custom_audio(lengths, seed=103)
+    enc = binding_mod.Encoder(w, dtype="f32")
+    try:
+        enc.set_ctc(cw, dtype="f32")
+        got = run_ctc(torch, enc, audio, lengths)
+    finally:
+        enc.close()
+    r0 = 0
+    for b, n in enumerate(lengths):
+        f = 2 * oracle.position_count(oracle.frame_count(n))
+        ref = ctc.ctc_logprobs(audio[b, :n], w, cw)
+        check_logprobs(got[r0:r0 + f], ref, f"large-gain ctc clip {b} ({f} frames)")
         r0 += f
     assert r0 == got.shape[0]
 
