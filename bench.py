@@ -201,8 +201,8 @@ def main():
             ap.error("--attention needs CORE >= 1 and CONTEXT >= 0")
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the encoder batch would be split by clips across ranks, which this "
-              "build does not implement).", file=sys.stderr)
+              "(splitting the encoder batch by clips across ranks is not implemented).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -7,7 +7,8 @@
 // projection, the attention output projection and the two FFN matrices of
 // "Nemotron 3.5 Transcribe: From Recorded Speech to Dataset Audits", section
 // "How audio and speakers reach the language model" (width 1,280, feed-forward
-// expansion four; exact-erf GELU is this build's reading of the activation).
+// expansion four; the activation is not named there, and exact-erf GELU is the
+// reading taken).
 //
 // Two kernels share the output tiling (256 x 256 tiles, numbered in groups of
 // four tile rows so that neighbouring tiles share A rows and W columns):
