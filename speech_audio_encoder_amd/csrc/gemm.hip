@@ -149,6 +149,11 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_void* lds) {
 // when the load path is busy) or storing results is never the one feeding
 // the matrix cores of its SIMD, and the stores of one tile spread over two
 // phases instead of leaving every CU idle at once.
+// Group 1 reads its first operand fragments of a step from LDS in phase 1,
+// before its compute phase; group 0 can read them only after the barrier
+// that opens its compute phase, so in bf16 it holds back the MFMAs of each
+// step's last 16-wide k and issues them while those first reads are in
+// flight (see compute0).
 // Direct load of 16 bytes per lane from sbase + voff to LDS byte address
 // lds + 16 * lane (sbase and lds uniform).  Written in asm so that the
 // compiler does not track it: the kernel waits for these loads explicitly
@@ -335,6 +340,30 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     interleave();
     mma(f1, false);
   };
+  // Group 0 (bf16) can read its first fragments only after the barrier that
+  // opens its compute phase.  It holds back the MFMAs of a step's last
+  // 16-wide k (their fragments stay in f1) and issues them at the start of
+  // its next compute phase, where they cover the latency of those reads.
+  // The order of summation is unchanged; a tile's last step completes in
+  // full, so nothing is held across an epilogue.
+  auto compute0 = [&](const uint4* a, const uint4* w, bool first, bool pending, bool defer)
+      __attribute__((always_inline)) {
+    load(a, w, 0, f0);
+    if (pending) {
+      mma(f1, false);
+      interleave();
+    }
+    load(a, w, 1, f1);
+    mma(f0, first);
+    interleave();
+    load(a, w, 2, f0);
+    mma(f1, false);
+    interleave();
+    load(a, w, 3, f1);
+    mma(f0, false);
+    interleave();
+    if (!defer) mma(f1, false);
+  };
   // FP8: code step ks covers bf16 steps 2 ks and 2 ks + 1; a fragment is the
   // two 16-byte chunks of those steps.  Step 1's fragments are read while
   // step 0's MFMAs run, each A fragment only after the two MFMAs that use
@@ -476,6 +505,58 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     }
   }
   wg_barrier();
+  if constexpr (!F8) {
+    // bf16: each group runs a loop of its own, so that group 0's held-back
+    // fragments (compute0) are live only where it needs them.  Both loops
+    // pass two barriers per step.  Group 0 peels a tile's first step (no
+    // held-back MFMAs to issue) and last step (none to hold back, and the
+    // tile's epilogue) out of its inner loop: its held-back fragments are
+    // then never live across an epilogue.
+    if (grp == 0) {
+      auto phase2 = [&](int g) __attribute__((always_inline)) {
+        wg_barrier();
+        wait_vm0();   // A(g+1), issued a step ago
+        if (g + 2 < total) issue(g + 2, true);   // into the slot of A(g-1)
+      };
+#pragma unroll 1
+      for (int r = 0; r < my_tiles; ++r) {
+        const int g0 = r * KT;
+        compute0(sA[g0 % 3], sW[g0 & 1], true, false, true);
+        phase2(g0);
+        wg_barrier();
+#pragma unroll 1
+        for (int kt = 1; kt < KT - 1; ++kt) {
+          const int g = g0 + kt;
+          compute0(sA[g % 3], sW[g & 1], false, true, true);
+          phase2(g);
+          wg_barrier();
+        }
+        const int gl = g0 + KT - 1;
+        compute0(sA[gl % 3], sW[gl & 1], false, true, false);
+        phase2(gl);
+        epilogue(r);
+        wg_barrier();
+      }
+    } else {
+#pragma unroll 1
+      for (int g = 0; g < total; ++g) {
+        const int r = g / KT, kt = g - r * KT;
+        const uint4* a = sA[g % 3];
+        const uint4* w = sW[g & 1];
+        if (g + 1 < total) issue(g + 1, false);   // W(g+1)
+        if (kt == 0 && r > 0) epilogue(r - 1);
+        preload(a, w);
+        wg_barrier();
+        if (kt == 0) step(a, w, true);
+        else step(a, w, false);
+        wait_vm0();   // W(g+1) landed
+        wg_barrier();
+      }
+      if (total > 0) epilogue(my_tiles - 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
   for (int g = 0; g < total; ++g) {
     const int r = g / KT, kt = g - r * KT;
     const uint4* a = sA[g % 3];
