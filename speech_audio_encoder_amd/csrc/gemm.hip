@@ -149,11 +149,9 @@ __device__ __forceinline__ void dma16(const void* gptr, lds_void* lds) {
 // when the load path is busy) or storing results is never the one feeding
 // the matrix cores of its SIMD, and the stores of one tile spread over two
 // phases instead of leaving every CU idle at once.
-// Group 1 reads its first operand fragments of a step from LDS in phase 1,
-// before its compute phase; group 0 can read them only after the barrier
-// that opens its compute phase, so in bf16 it holds back the MFMAs of each
-// step's last 16-wide k and issues them while those first reads are in
-// flight (see compute0).
+// In bf16 each group reads a step's first operand fragments from LDS at the
+// start of its own compute phase and covers their latency with the MFMAs of
+// the previous step's last 16-wide k, which it held back (see compute0).
 // Direct load of 16 bytes per lane from sbase + voff to LDS byte address
 // lds + 16 * lane (sbase and lds uniform).  Written in asm so that the
 // compiler does not track it: the kernel waits for these loads explicitly
@@ -340,10 +338,11 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     interleave();
     mma(f1, false);
   };
-  // Group 0 (bf16) can read its first fragments only after the barrier that
-  // opens its compute phase.  It holds back the MFMAs of a step's last
-  // 16-wide k (their fragments stay in f1) and issues them at the start of
-  // its next compute phase, where they cover the latency of those reads.
+  // bf16: a group reads its first fragments of a step at the start of its
+  // compute phase (group 0 could not read them earlier: the barrier that
+  // opens its phase publishes them).  It holds back the MFMAs of a step's
+  // last 16-wide k (their fragments stay in f1) and issues them at the start
+  // of its next compute phase, where they cover the latency of those reads.
   // The order of summation is unchanged; a tile's last step completes in
   // full, so nothing is held across an epilogue.
   auto compute0 = [&](const uint4* a, const uint4* w, bool first, bool pending, bool defer)
@@ -506,12 +505,12 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   }
   wg_barrier();
   if constexpr (!F8) {
-    // bf16: each group runs a loop of its own, so that group 0's held-back
+    // bf16: each group runs a loop of its own, so that its held-back
     // fragments (compute0) are live only where it needs them.  Both loops
-    // pass two barriers per step.  Group 0 peels a tile's first step (no
-    // held-back MFMAs to issue) and last step (none to hold back, and the
-    // tile's epilogue) out of its inner loop: its held-back fragments are
-    // then never live across an epilogue.
+    // pass two barriers per step.  Each peels a tile's first step (no
+    // held-back MFMAs to issue; group 1 stores the previous tile there) and
+    // last step (none to hold back; group 0 stores the tile there) out of its
+    // inner loop, so held-back fragments are never live across an epilogue.
     if (grp == 0) {
       auto phase2 = [&](int g) __attribute__((always_inline)) {
         wg_barrier();
@@ -538,19 +537,29 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         wg_barrier();
       }
     } else {
-#pragma unroll 1
-      for (int g = 0; g < total; ++g) {
-        const int r = g / KT, kt = g - r * KT;
-        const uint4* a = sA[g % 3];
-        const uint4* w = sW[g & 1];
-        if (g + 1 < total) issue(g + 1, false);   // W(g+1)
-        if (kt == 0 && r > 0) epilogue(r - 1);
-        preload(a, w);
+      auto phase1 = [&](int g) __attribute__((always_inline)) {
+        if (g + 1 < total) issue(g + 1, false);   // W(g+1) into the slot of W(g-1)
+      };
+      auto phase2 = [&](int g, bool first, bool pending, bool defer)
+          __attribute__((always_inline)) {
         wg_barrier();
-        if (kt == 0) step(a, w, true);
-        else step(a, w, false);
+        compute0(sA[g % 3], sW[g & 1], first, pending, defer);
         wait_vm0();   // W(g+1) landed
         wg_barrier();
+      };
+#pragma unroll 1
+      for (int r = 0; r < my_tiles; ++r) {
+        const int g0 = r * KT;
+        phase1(g0);
+        if (r > 0) epilogue(r - 1);
+        phase2(g0, true, false, true);
+#pragma unroll 1
+        for (int kt = 1; kt < KT - 1; ++kt) {
+          phase1(g0 + kt);
+          phase2(g0 + kt, false, true, true);
+        }
+        phase1(g0 + KT - 1);
+        phase2(g0 + KT - 1, false, true, false);
       }
       if (total > 0) epilogue(my_tiles - 1);
     }
