@@ -676,7 +676,10 @@ __global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
 
   // DMA: wave w loads 2 x 16 rows of A and of W per step (rows (w*2+i)*16 + lane/4).
   const int drow = wave * 32 + (lane >> 2);
-  const int dcol = ((lane & 3) ^ ((lane >> 3) & 3)) * 8;
+  // LDS chunk c of row r holds global chunk c ^ ((r / 4) % 4): the operand
+  // reads (16 lanes = 16 consecutive rows of 64 bytes at a time) then touch
+  // every group of four banks once.
+  const int dcol = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
   const bf16_t* ia[2];
   const bf16_t* iw[2];
 #pragma unroll
@@ -695,7 +698,7 @@ __global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
     ++ikt;
   };
 
-  const int rsw = (l32 >> 1) & 3;
+  const int rsw = (l32 >> 2) & 3;
   const int wofs = PIECE * 4 + (wn * 64 + l32) * 4;
   const int aofs = (wm * 64 + l32) * 4;
 
