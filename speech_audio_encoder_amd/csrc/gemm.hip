@@ -303,11 +303,13 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   bf16x8 f0[6], f1[6];
   auto load = [&](const uint4* a, const uint4* w, int sl, bf16x8 (&f)[6])
       __attribute__((always_inline)) {
+    // in the order the MFMAs consume them (W 0 and A 0 feed the first)
     const int pc = (2 * sl + lhi) ^ rsw;
+    f[0] = __builtin_bit_cast(bf16x8, w[wofs + pc]);
+    f[2] = __builtin_bit_cast(bf16x8, a[aofs + pc]);
+    f[1] = __builtin_bit_cast(bf16x8, w[wofs + 256 + pc]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) f[i] = __builtin_bit_cast(bf16x8, w[wofs + i * 256 + pc]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f[2 + j] = __builtin_bit_cast(bf16x8, a[aofs + j * 256 + pc]);
+    for (int j = 1; j < 4; ++j) f[2 + j] = __builtin_bit_cast(bf16x8, a[aofs + j * 256 + pc]);
   };
   auto mma = [&](const bf16x8 (&f)[6], bool fresh) __attribute__((always_inline)) {
     const f32x16 z = {};
