@@ -21,13 +21,13 @@ given; this oracle takes the plainest reading, the per-tensor FP8 scheme
   * y = (q_x . q_w) * fp32(s_x * s_w) + b, accumulated exactly here (float64)
     and in fp32 on the GPU;
   * the input projection, attention itself, the norms and the rotation stay
-    as in the bf16 encoder, whose matrix-product and attention operands are
-    bf16: the stacked log-mel features and W_in of the input projection, and
-    q, k, v (the QKV product's output as stored, q and k again after
-    normalisation and rotation) are rounded to bf16 here.  The unquantized
-    oracle can leave that rounding to its tolerance; this one cannot,
-    because every E4M3 code is a decision taken on values computed from
-    those operands, and both sides must take it in the same precision.
+    as in the unquantized encoder oracle (float32 operands).
+The pages fix no operand precision outside the four quantized maps, so none
+is emulated.  ``operand`` (default: none) lets a caller apply a map to the
+attention operands (q, k, v) and to the input projection's operands; it is
+used only to measure how far a change of their precision moves the FP8
+result, since every E4M3 code is a rounding decision that any upstream
+difference can flip.
 """
 
 import numpy as np
@@ -89,10 +89,12 @@ def prepare_fp8(weights):
     return out
 
 
-def encoder_layer_fp8(x, lw, qw, scales, record=None):
+def encoder_layer_fp8(x, lw, qw, scales, record=None, operand=None):
     """One pre-norm block with FP8 linear maps; scales = input scales of
     (QKV, O, up, down).  record: a list that receives the amax of the four
-    linear inputs (calibration), in which case the layer runs unquantized."""
+    linear inputs (calibration), in which case the layer runs unquantized.
+    operand: optional map applied to q, k, v (measurement of precision
+    spread only; None leaves them as computed)."""
     d = x.shape[1]
     dh = lw["q_g"].shape[0]
     nh = d // dh
@@ -104,8 +106,7 @@ def encoder_layer_fp8(x, lw, qw, scales, record=None):
         wq, s_w = qw[name]
         return linear_fp8(inp, wq, s_w, lw[bname], scales[i])
 
-    # bf16 attention operands, except in calibration (the unquantized model)
-    op = (lambda t: t) if record is not None else round_bf16
+    op = (lambda t: t) if operand is None else operand
     h = layer_norm(x, lw["ln1_g"], lw["ln1_b"])
     qkv = op(lin(h, 0, "w_qkv", "b_qkv"))
     cos, sin = rope_tables(x.shape[0], dh)
@@ -124,22 +125,24 @@ def encoder_layer_fp8(x, lw, qw, scales, record=None):
     return x + lin(u, 3, "w_down", "b_down")
 
 
-def _stacked_input(x, weights):
-    """Input projection on bf16 operands (stacked features and W_in)."""
-    feats = round_bf16(stack_frames(logmel(x)))
-    return linear(feats, round_bf16(weights["w_in"]), weights["b_in"])
+def _stacked_input(x, weights, operand=None):
+    """Input projection (unquantized), optionally on mapped operands."""
+    op = (lambda t: t) if operand is None else operand
+    feats = op(stack_frames(logmel(x)))
+    return linear(feats, op(weights["w_in"]), weights["b_in"])
 
 
-def encode_fp8(x, weights, input_scales, n_layers=None, qw=None):
+def encode_fp8(x, weights, input_scales, n_layers=None, qw=None, operand=None):
     """Waveform of one clip -> embeddings [P, d] with FP8 linear maps.
-    input_scales: [n_layers][4] scales of the (QKV, O, up, down) inputs."""
+    input_scales: [n_layers][4] scales of the (QKV, O, up, down) inputs.
+    operand: see encoder_layer_fp8 (measurement only)."""
     layers = weights["layers"][:n_layers] if n_layers else weights["layers"]
     qw = qw if qw is not None else prepare_fp8({"layers": layers})
-    h = _stacked_input(x, weights)
+    h = _stacked_input(x, weights, operand)
     if h.shape[0] == 0:
         return np.zeros((0, h.shape[1]), dtype=np.float32)
     for i, lw in enumerate(layers):
-        h = encoder_layer_fp8(h, lw, qw[i], input_scales[i])
+        h = encoder_layer_fp8(h, lw, qw[i], input_scales[i], operand=operand)
     return layer_norm(h, weights["lnf_g"], weights["lnf_b"])
 
 

@@ -85,3 +85,41 @@ def test_upsampled_frames_are_independent_per_tap():
     h2[2] += 1.0
     diff = np.abs(ctc.upsample(h2, w, b) - base).max(axis=1)
     assert np.nonzero(diff)[0].tolist() == [4, 5]
+
+
+def test_adapter_chain_with_constant_layers_matches_torch():
+    # With every matrix of a layer zero, the attention branch returns its
+    # output bias and the FFN branch its output bias, so layer l adds the
+    # constant c_l = b_o + b_down.  The adapter is then the composition
+    #   log_softmax(linear(layer_norm(conv_transpose1d(H) + c_1 + c_2)))
+    # of torch routines: a dropped or misplaced final LayerNorm, a layer
+    # before the upsampling, or a missing projection bias all change it.
+    rng = np.random.default_rng(11)
+    cw = small_ctc(n_classes=37)
+    for lw in cw["layers"]:
+        for name in ("w_qkv", "w_o", "w_up", "w_down"):
+            lw[name] = np.zeros_like(lw[name])
+        lw["b_o"] = rng.normal(0, 2.0, lw["b_o"].shape).astype(np.float32)
+        lw["b_down"] = rng.normal(0, 2.0, lw["b_down"].shape).astype(np.float32)
+    cw["b_out"] = rng.normal(0, 1.0, cw["b_out"].shape).astype(np.float32)
+    cw["w_out"] = rng.normal(0, 0.5, cw["w_out"].shape).astype(np.float32)
+    h = rng.normal(size=(6, 160)).astype(np.float32)
+    F = torch.nn.functional
+    t = torch.from_numpy
+    wt = t(np.ascontiguousarray(cw["w_conv"].transpose(2, 1, 0))).double()   # [in, out, k]
+    x = F.conv_transpose1d(t(h.T[None]).double(), wt, t(cw["b_conv"]).double(), stride=2)[0].T
+    for lw in cw["layers"]:
+        x = x + t(lw["b_o"]).double() + t(lw["b_down"]).double()
+    x = F.layer_norm(x, (160,), t(cw["lnf_g"]).double(), t(cw["lnf_b"]).double(), eps=1e-5)
+    ref = torch.log_softmax(F.linear(x, t(cw["w_out"]).double(), t(cw["b_out"]).double()), -1)
+    got = ctc.adapter_from_states(h, cw)
+    assert got.shape == (12, 37)
+    np.testing.assert_allclose(got, ref.numpy(), atol=2e-4)
+    # the pin is sensitive to where the final LayerNorm sits: applied before
+    # the second layer instead, the result moves far outside the tolerance
+    y = F.conv_transpose1d(t(h.T[None]).double(), wt, t(cw["b_conv"]).double(), stride=2)[0].T
+    y = y + t(cw["layers"][0]["b_o"]).double() + t(cw["layers"][0]["b_down"]).double()
+    y = F.layer_norm(y, (160,), t(cw["lnf_g"]).double(), t(cw["lnf_b"]).double(), eps=1e-5)
+    y = y + t(cw["layers"][1]["b_o"]).double() + t(cw["layers"][1]["b_down"]).double()
+    wrong = torch.log_softmax(F.linear(y, t(cw["w_out"]).double(), t(cw["b_out"]).double()), -1)
+    assert np.abs(wrong.numpy() - got).max() > 0.1

@@ -126,3 +126,121 @@ def test_fp8_encoder_close_to_unquantized_and_calibration():
     bad = fp8.encode_fp8(clips[0], w, scales * 1e-3)
     assert np.abs(bad - ref).max() > 3 * np.abs(got - ref).max()
     assert fp8.encode_fp8(np.zeros(300, np.float32), w, scales).shape == (0, 256)
+
+
+# ------------------------------------------------------------------
+# The FP8 layer against a torch layer that casts through float8_e4m3fn at
+# exactly the four stated points (the inputs of the QKV, output, FFN-up and
+# FFN-down maps), with weight codes from the definition (bf16 value, scale
+# amax / 448, codes of w * fp32(1 / s_w)).  Input scales are powers of two,
+# so a value's code is the torch cast of value / s exactly; each map gets a
+# different scale chosen so that value / s reaches [224, 448) at the
+# largest input, and the wrong scale for a map saturates its top values or
+# coarsens its small ones.
+F = torch.nn.functional
+
+
+def _pin_weights():
+    w = workloads.make_weights(1, bf16=False, perturb=True, d=64, dh=16, ffn=256)
+    lw = w["layers"][0]
+    lw["ln1_g"] = lw["ln1_g"] * np.float32(0.4)     # LN1 output narrower than the GELU output
+    lw["ln2_g"] = lw["ln2_g"] * np.float32(6.0)     # LN2 output wider than both
+    lw["w_down"] = lw["w_down"] * np.float32(4.0)
+    return lw
+
+
+def _torch_fp8_layer(x, lw, scales, quantize_at=("qkv", "o", "up", "down")):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))  # noqa: E731
+    d = x.shape[1]
+    dh = len(lw["q_g"])
+
+    def qdq(v, s):
+        return (v / s).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float32)
+
+    def lin8(v, wname, bname, s_x, point):
+        wb = t(lw[wname]).to(torch.bfloat16).to(torch.float32)
+        s_w = wb.abs().max() / torch.tensor(448.0)
+        codes = (wb * (torch.tensor(1.0) / s_w)).clamp(-448.0, 448.0)
+        codes = codes.to(torch.float8_e4m3fn).to(torch.float64)
+        if point in quantize_at:
+            acc = qdq(v, s_x).double() @ codes.T
+            alpha = (torch.tensor(s_x, dtype=torch.float32) * s_w).double()
+            return (acc * alpha).float() + t(lw[bname])
+        return F.linear(v, t(lw[wname]), t(lw[bname]))
+
+    xt = t(x)
+    h = F.layer_norm(xt, (d,), t(lw["ln1_g"]), t(lw["ln1_b"]), eps=1e-5)
+    qkv = lin8(h, "w_qkv", "b_qkv", scales[0], "qkv")
+    n = x.shape[0]
+    ang = torch.arange(n, dtype=torch.float64)[:, None] * \
+        10000.0 ** (-torch.arange(dh // 2, dtype=torch.float64) / (dh // 2))
+    rot = torch.polar(torch.ones_like(ang), ang).to(torch.complex64)
+
+    def norm_rot(v, g, b):
+        v = F.layer_norm(v, (dh,), t(lw[g]), t(lw[b]), eps=1e-5)
+        z = torch.complex(v[:, :dh // 2], v[:, dh // 2:]) * rot
+        return torch.cat([z.real, z.imag], dim=1)
+
+    heads = []
+    for hh in range(d // dh):
+        q = norm_rot(qkv[:, hh * dh:(hh + 1) * dh], "q_g", "q_b")
+        k = norm_rot(qkv[:, d + hh * dh:d + (hh + 1) * dh], "k_g", "k_b")
+        v = qkv[:, 2 * d + hh * dh:2 * d + (hh + 1) * dh]
+        heads.append(F.scaled_dot_product_attention(q[None], k[None], v[None])[0])
+    o = torch.cat(heads, dim=1)
+    if "o_out" in quantize_at:     # a mistake the pin must catch: quantize the output
+        x1 = xt + qdq(lin8(o, "w_o", "b_o", scales[1], "none"), scales[1])
+    else:
+        x1 = xt + lin8(o, "w_o", "b_o", scales[1], "o")
+    h2 = F.layer_norm(x1, (d,), t(lw["ln2_g"]), t(lw["ln2_b"]), eps=1e-5)
+    u = F.gelu(lin8(h2, "w_up", "b_up", scales[2], "up"))
+    return (x1 + lin8(u, "w_down", "b_down", scales[3], "down")).numpy()
+
+
+def _pin_case():
+    lw = _pin_weights()
+    x = (3.0 * np.random.default_rng(12).normal(size=(11, 64))).astype(np.float32)
+    rec = []
+    fp8.encoder_layer_fp8(x, lw, None, None, record=rec)
+    scales = [np.float32(2.0 ** np.floor(np.log2(a / 224.0))) for a in rec]
+    return lw, x, scales, rec
+
+
+def test_fp8_layer_casts_exactly_at_the_four_map_inputs():
+    lw, x, scales, rec = _pin_case()
+    ratios = [a / s for a, s in zip(rec, scales)]
+    assert all(224.0 <= r < 448.0 for r in ratios), ratios
+    assert len(set(float(s) for s in scales)) == 4, scales      # one scale per map
+    qw = fp8.prepare_fp8({"layers": [lw]})[0]
+    got = fp8.encoder_layer_fp8(x, lw, qw, scales)
+    ref = _torch_fp8_layer(x, lw, scales)
+    scale = np.abs(ref).max()
+    assert np.abs(got - ref).max() <= 1e-5 * scale
+    # against the unquantized layer the difference is quantization-sized
+    plain = oracle.encoder_layer(x, lw)
+    assert np.abs(got - plain).max() > 1e-3 * scale
+
+
+@pytest.mark.parametrize("mistake", ["swap_qkv_up", "swap_o_down", "no_quant_o",
+                                     "quantize_o_output", "no_quant_down"])
+def test_fp8_layer_pin_rejects_plausible_mistakes(mistake):
+    # The torch reference with one plausible mistake (a scale index swapped,
+    # a map left unquantized, the output of w_o quantized instead of its
+    # input) lands far outside the tolerance the oracle meets above.
+    lw, x, scales, _ = _pin_case()
+    qw = fp8.prepare_fp8({"layers": [lw]})[0]
+    got = fp8.encoder_layer_fp8(x, lw, qw, scales)
+    s = list(scales)
+    points = ("qkv", "o", "up", "down")
+    if mistake == "swap_qkv_up":
+        s[0], s[2] = s[2], s[0]
+    elif mistake == "swap_o_down":
+        s[1], s[3] = s[3], s[1]
+    elif mistake == "no_quant_o":
+        points = ("qkv", "up", "down")
+    elif mistake == "quantize_o_output":
+        points = ("qkv", "o_out", "up", "down")
+    elif mistake == "no_quant_down":
+        points = ("qkv", "o", "up")
+    wrong = _torch_fp8_layer(x, lw, s, points)
+    assert np.abs(got - wrong).max() > 100 * 1e-5 * np.abs(got).max()
