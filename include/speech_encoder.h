@@ -161,6 +161,33 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                 void* out_embeddings, hipStream_t stream);
 
 /*
+ * enc_forward_noalloc: enc_forward for callers that cannot allocate device
+ * memory during the call -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, output and
+ * results as enc_forward (same kernels, bit-identical embeddings), but every
+ * per-call device buffer (workspace, plan arrays, split-K partial sums) comes
+ * from one static device array of ENC_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends; the call allocates
+ * nothing and frees nothing (the context's pinned plan staging is made by
+ * enc_create).
+ *   Limit: the workspace must fit ENC_NOALLOC_SCRATCH_BYTES minus 66 MiB
+ *   (about 7,000 positions in one call, i.e. roughly nine minutes of audio;
+ *   enc_workspace_bytes reports a batch's need); larger batches return
+ *   ENC_ERR_NOMEM before anything is enqueued.
+ *   Sharing: every enc_forward_noalloc call on a GPU, from any context or
+ *   thread, uses that GPU's one array, which keeps the last call's contents.
+ *   Calls that overlap on one GPU (different streams, or no ordering between
+ *   them) race and give undefined results; serialize them.  No part of the
+ *   array needs to start at zero: each call writes every element it reads.
+ *   Kernel timing brackets (enc_profile_kernel) do not apply to this call.
+ * Errors: as enc_forward (ENC_ERR_NOMEM when the batch exceeds the limit;
+ * ENC_ERR_HIP if the array's device address could not be obtained).
+ */
+#define ENC_NOALLOC_SCRATCH_BYTES (256u << 20)
+int enc_forward_noalloc(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                        void* out_embeddings, hipStream_t stream);
+
+/*
  * enc_set_attention: the attention scope of later enc_forward calls on ctx.
  * The pages describe the encoder as trained on 30-second chunks and served
  * with local windows (500 positions of core plus 50 of context on each side,

@@ -27,7 +27,8 @@ KERNELS = ["frontend", "gemm_in", "layernorm", "gemm_qkv", "qknorm_rope", "atten
            "gemm_o", "gemm_up", "gemm_down", "final_norm", "speaker_fuse", "connector", "ctc",
            "ctc_out"]
 
-EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_set_attention", "enc_set_connector",
+EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_forward_noalloc", "enc_set_attention",
+           "enc_set_connector",
            "enc_forward_fused", "enc_set_precision", "enc_calibrate", "enc_set_ctc",
            "enc_forward_ctc", "enc_destroy", "enc_shapes",
            "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
@@ -95,6 +96,8 @@ def load_library(path=LIB_PATH):
                                ctypes.c_void_p, ctypes.c_void_p]
     lib.enc_forward.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
                                 ctypes.c_void_p, ctypes.c_void_p]
+    lib.enc_forward_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, i64p, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.enc_set_attention.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32]
     lib.enc_set_connector.argtypes = [ctypes.c_void_p, ctypes.POINTER(EncConnectorWeights)]
@@ -225,6 +228,25 @@ def enc_forward(ctx, audio, lengths, out=None, stream=None):
                                       ptr, len(arr), ctypes.c_void_p(out.data_ptr()),
                                       _stream_handle(stream)))
     return out
+
+
+def enc_forward_noalloc(ctx, audio, lengths, out, stream=None):
+    """enc_forward through the entry point that allocates nothing; the caller
+    passes the output ``out`` (bf16 [B, P_max, 1280])."""
+    arr, ptr = _lengths_array(lengths)
+    _check(load_library().enc_forward_noalloc(ctypes.c_void_p(ctx),
+                                              ctypes.c_void_p(audio.data_ptr()), ptr, len(arr),
+                                              ctypes.c_void_p(out.data_ptr()),
+                                              _stream_handle(stream)))
+    return out
+
+
+def enc_forward_noalloc_raw(ctx, audio_ptr, lengths, out_ptr, stream_ptr=0):
+    """enc_forward_noalloc with raw pointers; returns the status code (tests)."""
+    arr, ptr = _lengths_array(lengths)
+    return load_library().enc_forward_noalloc(ctypes.c_void_p(ctx), ctypes.c_void_p(audio_ptr),
+                                              ptr, len(arr), ctypes.c_void_p(out_ptr),
+                                              ctypes.c_void_p(stream_ptr))
 
 
 def packed_rows(lengths):

@@ -16,6 +16,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -99,6 +100,55 @@ bool build_frontend_tables(FrontendTables* t) {
     off += count;
   }
   return true;
+}
+
+}  // namespace
+
+// ------------------------------------------------ no-allocation scratch
+// Per-call device memory of enc_forward_noalloc: split-K partial sums, the
+// plan arrays and the workspace, carved from one static array that every GPU
+// the library runs on holds until the process ends.  In host code `scratch`
+// names a host-side stand-in; device code only ever sees the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[ENC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t SCRATCH_PART_OFF = 0;
+constexpr size_t SCRATCH_PLAN_OFF = enc::GEMM_PARTIAL_BYTES;
+constexpr size_t SCRATCH_PLAN_BYTES = (size_t)2 << 20;
+constexpr size_t SCRATCH_WS_OFF = SCRATCH_PLAN_OFF + SCRATCH_PLAN_BYTES;
+constexpr size_t SCRATCH_WS_BYTES = (size_t)ENC_NOALLOC_SCRATCH_BYTES - SCRATCH_WS_OFF;
+static_assert(SCRATCH_WS_OFF % 256 == 0, "scratch regions stay 256-byte aligned");
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+bool g_scratch_tried[MAX_DEVICES];
+hipError_t g_scratch_err[MAX_DEVICES];
+unsigned char* g_scratch_ptr[MAX_DEVICES];
+
+// Once per device, with that device current: the device address of its copy
+// of `scratch`.  The result (or the error) is kept for enc_forward_noalloc.
+void scratch_setup(int dev) {
+  if (dev < 0 || dev >= MAX_DEVICES) return;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_tried[dev]) return;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  g_scratch_err[dev] = e;
+  g_scratch_ptr[dev] = e == hipSuccess ? (unsigned char*)ptr : nullptr;
+  g_scratch_tried[dev] = true;
+  if (e != hipSuccess) (void)hipGetLastError();
+}
+
+unsigned char* scratch_for(int dev, hipError_t* err) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (dev < 0 || dev >= MAX_DEVICES || !g_scratch_tried[dev]) {
+    *err = hipErrorNotInitialized;
+    return nullptr;
+  }
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
 }
 
 // -------------------------------------------------------------- launch plan
@@ -313,6 +363,7 @@ struct enc_ctx {
   int prof_kernel = -1;
   std::vector<hipEvent_t> prof_events;   // pairs
   size_t prof_used = 0;
+  bool in_noalloc = false;   // inside enc_forward_noalloc: no timing brackets
 };
 
 namespace {
@@ -343,19 +394,30 @@ void release(enc_ctx* c) {
   delete c;
 }
 
-// Upload the plan's int32 arrays (concatenated) to ctx->plan_dev on `stream`.
-int upload_plan(enc_ctx* c, const std::vector<const std::vector<int32_t>*>& parts,
-                std::vector<int32_t*>* dev_ptrs, hipStream_t stream) {
+// Int32 entries the plan's arrays take once concatenated (64-entry aligned).
+size_t plan_entries(const std::vector<const std::vector<int32_t>*>& parts) {
   size_t total = 0;
   for (auto* v : parts) total += align_up(v->size(), 64);
-  total = std::max<size_t>(total, 64);
+  return std::max<size_t>(total, 64);
+}
+
+// Upload the plan's int32 arrays (concatenated) on `stream`: to ctx->plan_dev
+// (grown on demand), or, when fixed_dev is given, to fixed_dev, in which case
+// nothing is allocated and the caller has checked that the plan fits both
+// fixed_dev and the pinned staging buffer made at enc_create.
+int upload_plan(enc_ctx* c, const std::vector<const std::vector<int32_t>*>& parts,
+                std::vector<int32_t*>* dev_ptrs, hipStream_t stream,
+                int32_t* fixed_dev = nullptr) {
+  const size_t total = plan_entries(parts);
   hipError_t e;
   if (c->plan_pending) {
     e = hipEventSynchronize(c->plan_copied);
     if (e != hipSuccess) return hip_fail(e, "waiting for the previous plan upload");
     c->plan_pending = false;
   }
-  if (total > c->plan_host_cap) {
+  if (fixed_dev) {
+    if (total > c->plan_host_cap) return fail(ENC_ERR_NOMEM, "plan exceeds the staging buffer");
+  } else if (total > c->plan_host_cap) {
     if (c->plan_host) (void)hipHostFree(c->plan_host);
     c->plan_host = nullptr;
     c->plan_host_cap = 0;
@@ -363,7 +425,7 @@ int upload_plan(enc_ctx* c, const std::vector<const std::vector<int32_t>*>& part
     if (e != hipSuccess) return fail(ENC_ERR_NOMEM, "pinned plan buffer allocation failed");
     c->plan_host_cap = total;
   }
-  if (total > c->plan_cap) {
+  if (!fixed_dev && total > c->plan_cap) {
     if (c->plan_dev) {
       e = hipStreamSynchronize(stream);
       if (e != hipSuccess) return hip_fail(e, "stream synchronize");
@@ -375,14 +437,15 @@ int upload_plan(enc_ctx* c, const std::vector<const std::vector<int32_t>*>& part
     if (e != hipSuccess) return fail(ENC_ERR_NOMEM, "plan buffer allocation failed");
     c->plan_cap = total;
   }
+  int32_t* dst = fixed_dev ? fixed_dev : c->plan_dev;
   size_t off = 0;
   dev_ptrs->clear();
   for (auto* v : parts) {
     if (!v->empty()) std::memcpy(c->plan_host + off, v->data(), v->size() * 4);
-    dev_ptrs->push_back(c->plan_dev + off);
+    dev_ptrs->push_back(dst + off);
     off += align_up(v->size(), 64);
   }
-  e = hipMemcpyAsync(c->plan_dev, c->plan_host, off * 4, hipMemcpyHostToDevice, stream);
+  e = hipMemcpyAsync(dst, c->plan_host, off * 4, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "plan upload");
   e = hipEventRecord(c->plan_copied, stream);
   if (e != hipSuccess) return hip_fail(e, "plan event");
@@ -416,7 +479,8 @@ struct ProfScope {
   hipStream_t s;
   bool on;
   size_t idx;
-  ProfScope(enc_ctx* ctx, int id, hipStream_t stream) : c(ctx), s(stream), on(ctx->prof_kernel == id) {
+  ProfScope(enc_ctx* ctx, int id, hipStream_t stream)
+      : c(ctx), s(stream), on(ctx->prof_kernel == id && !ctx->in_noalloc) {
     if (!on) return;
     idx = c->prof_used;
     while (c->prof_events.size() < idx + 2) {
@@ -585,6 +649,13 @@ int enc_create(const enc_weights* w, enc_ctx** out) {
   if (e == hipSuccess) e = hipMemcpy(c->rope_cos, rc_cos.data(), rope_bytes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipMemcpy(c->rope_sin, rc_sin.data(), rope_bytes, hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hipEventCreateWithFlags(&c->plan_copied, hipEventDisableTiming);
+  // Pinned plan staging large enough for any plan enc_forward_noalloc accepts.
+  if (e == hipSuccess) {
+    e = hipHostMalloc((void**)&c->plan_host, SCRATCH_PLAN_BYTES, hipHostMallocDefault);
+    if (e == hipSuccess) c->plan_host_cap = SCRATCH_PLAN_BYTES / 4;
+    else c->plan_host = nullptr;
+  }
+  if (e == hipSuccess) scratch_setup(c->device);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   // Per layer: may attention use a fixed softmax reference (bounded scores)?
   for (int i = 0; i < L && e == hipSuccess; ++i) {
@@ -769,8 +840,11 @@ int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_t
   return ENC_OK;
 }
 
+// no_alloc: every per-call buffer comes from the static scratch array
+// (enc_forward_noalloc); otherwise from the context, grown on demand.
 int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
-                void* out, const float* activity, Tail tail, hipStream_t stream) {
+                void* out, const float* activity, Tail tail, hipStream_t stream,
+                bool no_alloc = false) {
   if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
   const bool fused = tail == Tail::kFused;
   const bool calib = tail == Tail::kCalibrate;
@@ -797,14 +871,36 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
 
   // Memory admission before any launch.
   const Layout lay = layout_for(p.vrows);
-  if (const char* cap = std::getenv("ENC_WORKSPACE_CAP_BYTES")) {
+  const std::vector<const std::vector<int32_t>*> plan_parts = {
+      &p.n_frames, &p.frame_base, &p.tile_info, &p.cu_clip,
+      &p.gather_src, &p.out_src, &p.a_tile_info, &p.all_rows};
+  float* part = ctx->gemm_part;
+  const size_t part_bytes = GEMM_PARTIAL_BYTES;
+  char* ws = (char*)ctx->ws;
+  int32_t* plan_dst = nullptr;
+  if (no_alloc) {
+    hipError_t se;
+    unsigned char* sp = scratch_for(ctx->device, &se);
+    if (!sp) return hip_fail(se, "scratch address (hipGetSymbolAddress)");
+    if (lay.total > SCRATCH_WS_BYTES)
+      return fail(ENC_ERR_NOMEM, "workspace of " + std::to_string(lay.total) +
+                                     " bytes exceeds the no-allocation scratch (" +
+                                     std::to_string(SCRATCH_WS_BYTES) + " bytes)");
+    if (plan_entries(plan_parts) * 4 > SCRATCH_PLAN_BYTES ||
+        plan_entries(plan_parts) > ctx->plan_host_cap)
+      return fail(ENC_ERR_NOMEM, "plan arrays exceed the no-allocation scratch");
+    part = (float*)(sp + SCRATCH_PART_OFF);
+    plan_dst = (int32_t*)(sp + SCRATCH_PLAN_OFF);
+    ws = (char*)(sp + SCRATCH_WS_OFF);
+  }
+  if (const char* cap = no_alloc ? nullptr : std::getenv("ENC_WORKSPACE_CAP_BYTES")) {
     const unsigned long long lim = std::strtoull(cap, nullptr, 10);
     if ((unsigned long long)lay.total > lim)
       return fail(ENC_ERR_NOMEM, "workspace of " + std::to_string(lay.total) +
                                      " bytes exceeds ENC_WORKSPACE_CAP_BYTES=" + cap);
   }
   if ((rc = switch_stream(ctx, stream)) != ENC_OK) return rc;
-  if (lay.total > ctx->ws_bytes) {
+  if (!no_alloc && lay.total > ctx->ws_bytes) {
     hipError_t e = hipStreamSynchronize(stream);
     if (e != hipSuccess) return hip_fail(e, "stream synchronize");
     (void)hipFree(ctx->ws);
@@ -818,9 +914,9 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                      " bytes failed");
     }
     ctx->ws_bytes = lay.total;
+    ws = (char*)ctx->ws;
   }
   // The workspace row layout depends on `rows`; the pointers below follow it.
-  char* ws = (char*)ctx->ws;
   float* x = (float*)(ws + lay.x);
   bf16_t* a = (bf16_t*)(ws + lay.a);
   bf16_t* qkv = (bf16_t*)(ws + lay.qkv);
@@ -829,10 +925,7 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   bf16_t* stk = u;
 
   std::vector<int32_t*> dev;
-  if ((rc = upload_plan(ctx, {&p.n_frames, &p.frame_base, &p.tile_info, &p.cu_clip,
-                              &p.gather_src, &p.out_src, &p.a_tile_info, &p.all_rows},
-                        &dev, stream)) != ENC_OK)
-    return rc;
+  if ((rc = upload_plan(ctx, plan_parts, &dev, stream, plan_dst)) != ENC_OK) return rc;
   const int32_t* d_nf = dev[0];
   const int32_t* d_fb = dev[1];
   const int32_t* d_ti = dev[2];
@@ -854,7 +947,7 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                                      ctx->tables, stk, stream));
   }
   ENC_LAUNCH(ENC_K_GEMM_IN, launch_gemm(Epilogue::kBiasF32, stk, DIN, ctx->w_in, DIN, ctx->b_in, x,
-                                        D, R, D, DIN, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+                                        D, R, D, DIN, part, part_bytes, stream));
   uint8_t* a8 = (uint8_t*)a;   // E4M3 operands of the FP8 path reuse the bf16 buffers
   uint8_t* o8 = (uint8_t*)o;
   uint8_t* u8 = (uint8_t*)u;
@@ -866,14 +959,14 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                                        stream));
       ENC_LAUNCH(ENC_K_GEMM_QKV,
                  launch_gemm_fp8(Epilogue::kBiasBf16, a8, D, Lw.q8[0], D, Lw.alpha[0], 0.0f,
-                                 Lw.b_qkv, qkv, 3 * D, R, 3 * D, D, ctx->gemm_part,
-                                 GEMM_PARTIAL_BYTES, stream));
+                                 Lw.b_qkv, qkv, 3 * D, R, 3 * D, D, part,
+                                 part_bytes, stream));
     } else {
       ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln1_g, Lw.ln1_b, a, R, stream));
       if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(a, R * D, amax + 4 * li + 0, stream));
       ENC_LAUNCH(ENC_K_GEMM_QKV, launch_gemm(Epilogue::kBiasBf16, a, D, Lw.w_qkv, D, Lw.b_qkv,
-                                             qkv, 3 * D, R, 3 * D, D, ctx->gemm_part,
-                                             GEMM_PARTIAL_BYTES, stream));
+                                             qkv, 3 * D, R, 3 * D, D, part,
+                                             part_bytes, stream));
     }
     ENC_LAUNCH(ENC_K_QKNORM_ROPE,
                launch_qknorm_rope(qkv, d_ti, n_tiles, H, DH, Lw.q_g, Lw.q_b, Lw.k_g, Lw.k_b,
@@ -884,30 +977,30 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
     if (fp8) {
       ENC_LAUNCH(ENC_K_GEMM_O,
                  launch_gemm_fp8(Epilogue::kBiasResidualF32, o8, D, Lw.q8[1], D, Lw.alpha[1],
-                                 0.0f, Lw.b_o, x, D, R, D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES,
+                                 0.0f, Lw.b_o, x, D, R, D, D, part, part_bytes,
                                  stream));
       ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm_fp8(x, Lw.ln2_g, Lw.ln2_b, Lw.r_x[2], a8, R,
                                                        stream));
       ENC_LAUNCH(ENC_K_GEMM_UP,
                  launch_gemm_fp8(Epilogue::kBiasGeluFp8, a8, D, Lw.q8[2], D, Lw.alpha[2],
-                                 Lw.r_x[3], Lw.b_up, u8, FF, R, FF, D, ctx->gemm_part,
-                                 GEMM_PARTIAL_BYTES, stream));
+                                 Lw.r_x[3], Lw.b_up, u8, FF, R, FF, D, part,
+                                 part_bytes, stream));
       ENC_LAUNCH(ENC_K_GEMM_DOWN,
                  launch_gemm_fp8(Epilogue::kBiasResidualF32, u8, FF, Lw.q8[3], FF, Lw.alpha[3],
-                                 0.0f, Lw.b_down, x, D, R, D, FF, ctx->gemm_part,
-                                 GEMM_PARTIAL_BYTES, stream));
+                                 0.0f, Lw.b_down, x, D, R, D, FF, part,
+                                 part_bytes, stream));
       continue;
     }
     if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(o, R * D, amax + 4 * li + 1, stream));
     ENC_LAUNCH(ENC_K_GEMM_O, launch_gemm(Epilogue::kBiasResidualF32, o, D, Lw.w_o, D, Lw.b_o, x,
-                                         D, R, D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+                                         D, R, D, D, part, part_bytes, stream));
     ENC_LAUNCH(ENC_K_LAYERNORM, launch_layernorm(x, Lw.ln2_g, Lw.ln2_b, a, R, stream));
     if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(a, R * D, amax + 4 * li + 2, stream));
     ENC_LAUNCH(ENC_K_GEMM_UP, launch_gemm(Epilogue::kBiasGeluBf16, a, D, Lw.w_up, D, Lw.b_up, u,
-                                          FF, R, FF, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+                                          FF, R, FF, D, part, part_bytes, stream));
     if (calib) ENC_LAUNCH(K_UNTIMED, launch_amax_bf16(u, R * FF, amax + 4 * li + 3, stream));
     ENC_LAUNCH(ENC_K_GEMM_DOWN, launch_gemm(Epilogue::kBiasResidualF32, u, FF, Lw.w_down, FF,
-                                            Lw.b_down, x, D, R, D, FF, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
+                                            Lw.b_down, x, D, R, D, FF, part, part_bytes, stream));
   }
   if (calib) return ENC_OK;
   if (ctc) {
@@ -927,8 +1020,8 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                                  ctx->spk_b, ctx->spk_tab, a, stream));
   ENC_LAUNCH(ENC_K_CONNECTOR,
              launch_gemm(Epilogue::kBiasBf16, a, D, ctx->w_conn, D, ctx->b_conn, out,
-                         ctx->conn_dim, p.rows, ctx->conn_dim, D, ctx->gemm_part,
-                         GEMM_PARTIAL_BYTES, stream));
+                         ctx->conn_dim, p.rows, ctx->conn_dim, D, part,
+                         part_bytes, stream));
   return ENC_OK;
 }
 
@@ -938,6 +1031,16 @@ int enc_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                 void* out_embeddings, hipStream_t stream) {
   return run_forward(ctx, audio, lengths, batch, out_embeddings, nullptr, Tail::kEmbeddings,
                      stream);
+}
+
+int enc_forward_noalloc(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
+                        void* out_embeddings, hipStream_t stream) {
+  if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  ctx->in_noalloc = true;
+  const int rc = run_forward(ctx, audio, lengths, batch, out_embeddings, nullptr,
+                             Tail::kEmbeddings, stream, true);
+  ctx->in_noalloc = false;
+  return rc;
 }
 
 int enc_forward_fused(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
