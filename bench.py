@@ -113,7 +113,7 @@ def kernel_bytes(name, rows, lengths):
     return {
         "frontend": 4 * int(sum(lengths)) + 2 * 128 * 8 * rows,   # audio in, bf16 stack out
         "layernorm": rows * D * (4 + 2),
-        "qknorm_rope": rows * (2 * D * 2 * 2 + D * 2 * 2),         # q,k read+write, v read+write
+        "qknorm_rope": rows * 2 * D * 2 * 2,                       # q and k read and written (bf16)
         "final_norm": rows * D * (4 + 2),
     }.get(name)
 
@@ -145,16 +145,30 @@ def measured_traffic(workload, kernel):
     return int(round(c["bytes_per_launch"]))
 
 
+def stratified_order(lengths):
+    """Clip indices in an order whose every prefix spreads evenly over the
+    length range: the clips sorted by length, visited in bit-reversed rank
+    order (van der Corput), so that a time-bounded sample is not biased to
+    short or long clips."""
+    ranked = np.argsort(lengths, kind="stable")
+    n = len(ranked)
+    bits = max(1, int(np.ceil(np.log2(max(n, 2)))))
+    rev = sorted(range(1 << bits), key=lambda r: int(format(r, f"0{bits}b")[::-1], 2))
+    return [int(ranked[r]) for r in rev if r < n]
+
+
 def cpu_baseline(audio, lengths, weights, core=0, context=0, budget_s=12.0):
-    """Time the oracle (as it stands) on whole clips until ~budget_s of CPU."""
+    """Time the oracle (as it stands) on whole clips until ~budget_s of CPU,
+    the clips taken in an order spread evenly over the workload's lengths."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
         cores = os.cpu_count() or 1
-    order = np.argsort(lengths)          # shortest first keeps the sample bounded
+    order = stratified_order(lengths)
     done_samples, spent, clips = 0, 0.0, 0
+    picked = []
     for b in order:
         n = int(lengths[b])
         t0 = time.perf_counter()
@@ -165,12 +179,17 @@ def cpu_baseline(audio, lengths, weights, core=0, context=0, budget_s=12.0):
         spent += time.perf_counter() - t0
         done_samples += n
         clips += 1
+        picked.append(n / SAMPLE_RATE)
         if spent >= budget_s:
             break
     secs = done_samples / SAMPLE_RATE
+    all_s = np.asarray(lengths, dtype=np.float64) / SAMPLE_RATE
     return {"value": secs / spent, "unit": "audio-s/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{clips} whole clip(s) of the workload, shortest first, "
-                      f"{secs:.1f} audio-s, 32 layers, {spent:.1f} s wall"}
+            "sample": f"{clips} of {len(lengths)} whole clip(s), spread evenly over the "
+                      f"workload's lengths ({min(picked):.1f}-{max(picked):.1f} s, mean "
+                      f"{np.mean(picked):.1f} s; workload mean {all_s.mean():.1f} s), "
+                      f"{secs:.1f} audio-s, {len(weights['layers'])} layers, "
+                      f"{spent:.1f} s wall"}
 
 
 def main():
@@ -188,8 +207,9 @@ def main():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"],
                     help="linear maps of the layers in bf16 or FP8 (E4M3, per-tensor scales)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true",
-                    help="also time every kernel class (extra untimed steps)")
+    ap.add_argument("--no-breakdown", action="store_true",
+                    help="skip timing every kernel class (one extra untimed step per "
+                         "class); the roofline then takes the FFN-up GEMM")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times), "
                          "to scale HBM byte counters")
@@ -264,7 +284,7 @@ def main():
     torch.cuda.synchronize()
 
     breakdown = {}
-    if args.breakdown:
+    if not args.no_breakdown:
         for kname in binding.KERNELS:
             binding.enc_profile_kernel(enc.ctx, kname)
             step()
@@ -273,11 +293,11 @@ def main():
         binding.enc_profile_kernel(enc.ctx, -1)
         torch.cuda.synchronize()
 
-    # Dominant kernel: the FFN expansion GEMM (a third of all MFMA flops here);
-    # it is bracketed with HIP events on the library's stream during the timed steps.
+    # Dominant kernel: the slowest class per step that has a roofline model
+    # (flops or bytes), from the breakdown; it is then bracketed with HIP
+    # events on the library's stream during the timed steps.
     dom = "gemm_up"
     if breakdown:
-        # the slowest class that has a roofline model (flops or bytes)
         known = [k for k in breakdown if kernel_flops(k, 1, [1]) is not None
                  or kernel_bytes(k, 1, [1]) is not None]
         dom = max(known, key=lambda k: breakdown[k]["ms"])

@@ -317,6 +317,15 @@ int enc_calibrate(enc_ctx* ctx, const float* audio, const int64_t* lengths, int3
                   float* amax, hipStream_t stream);
 
 /*
+ * enc_fp8_input_scales: host-only.  The input scales enc_set_precision takes,
+ * from the amax values enc_calibrate returns (merged over batches by the
+ * caller): scales[i] = amax[i] / 448 in fp32, or 1 where amax[i] is 0 (a map
+ * whose input was all zero).  n = n_layers * 4.  Errors: ENC_ERR_ARG (NULL
+ * with n > 0, n < 0, an amax that is negative or not finite).
+ */
+int enc_fp8_input_scales(const float* amax, int32_t n, float* scales);
+
+/*
  * CTC timestamp adapter.  The Dataset Audits page, section "4. Use alignment
  * and audio questions as supporting evidence", describes a ~50M-parameter
  * adapter on the unfused ASR states (width 1,280, 80 ms grid): a stride-two

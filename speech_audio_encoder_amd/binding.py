@@ -30,7 +30,7 @@ KERNELS = ["frontend", "gemm_in", "layernorm", "gemm_qkv", "qknorm_rope", "atten
 EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_forward_noalloc", "enc_set_attention",
            "enc_set_connector",
            "enc_forward_fused", "enc_set_precision", "enc_calibrate", "enc_set_ctc",
-           "enc_forward_ctc", "enc_destroy", "enc_shapes",
+           "enc_forward_ctc", "enc_fp8_input_scales", "enc_destroy", "enc_shapes",
            "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
 
 ENC_PREC_BF16 = 0
@@ -117,6 +117,8 @@ def load_library(path=LIB_PATH):
                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.enc_last_error.restype = ctypes.c_char_p
     lib.enc_last_error.argtypes = []
+    lib.enc_fp8_input_scales.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_float)]
     lib.enc_profile_kernel.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     lib.enc_profile_read.argtypes = [ctypes.c_void_p, i64p, ctypes.POINTER(ctypes.c_double)]
     for name in EXPORTS:
@@ -325,9 +327,14 @@ def enc_calibrate(ctx, audio, lengths, n_layers, stream=None):
 
 
 def scales_from_amax(amax):
-    """Input scales amax / 448 (1 where amax is 0), float32."""
-    a = np.asarray(amax, dtype=np.float32)
-    return np.where(a > 0, a / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    """Input scales from calibration amax values (the library's
+    enc_fp8_input_scales), same shape, float32."""
+    a = np.ascontiguousarray(amax, dtype=np.float32)
+    out = np.empty_like(a)
+    fp = ctypes.POINTER(ctypes.c_float)
+    _check(load_library().enc_fp8_input_scales(a.ctypes.data_as(fp), a.size,
+                                               out.ctypes.data_as(fp)))
+    return out
 
 
 def enc_set_ctc(ctx, cw, dtype="bf16", device="cuda"):

@@ -32,9 +32,13 @@
 // Softmax reference.  QK-norm bounds every score: after LayerNorm a head
 // vector of width w has norm at most max|gain| * sqrt(w) + |bias|, so |q.k| is bounded
 // by the product of the two norms.  When the launcher is told that this bound
-// keeps scores * log2(e) / sqrt(w) within +-100 (kFixedRef), probabilities
+// keeps scores * log2(e) / sqrt(w) within +-64 (kFixedRef), probabilities
 // are exp2 of the scaled scores against a fixed reference of 0: no running
-// maximum, no rescaling, and fp32 sums cannot overflow.  Otherwise the
+// maximum, no rescaling.  Each probability lies in [2^-64, 2^64], so a row
+// sum over at most 90,000 keys stays below 2^81, and an output accumulator
+// below 2^81 * max|v|: fp32 (to 2^128) holds both unless |v| exceeds 2^47,
+// which a bf16 product of LayerNorm outputs and 0.02-scale weights cannot
+// approach.  Otherwise the
 // running maximum is kept lazily: the accumulators are rescaled only when a
 // query's unit maximum exceeds it by more than 8 (log2 units); in between,
 // probabilities are taken against the stale maximum (they stay below 2^8),
@@ -416,7 +420,7 @@ bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g
   // 2^-6 covers bf16 rounding of q and k and fp32 rounding of the products.
   const double bound = norm_bound(q_g, q_b) * norm_bound(k_g, k_b) * (1.0 + 1.0 / 64);
   const double log2_range = bound * 1.4426950408889634 / std::sqrt((double)dh);
-  return std::isfinite(log2_range) && log2_range <= 100.0;
+  return std::isfinite(log2_range) && log2_range <= 64.0;
 }
 
 hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_tiles,

@@ -168,6 +168,9 @@ __device__ __forceinline__ void dma16_s(const char* sbase, uint32_t voff, uint32
 }
 #pragma clang diagnostic pop
 __device__ __forceinline__ void wait_vm0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// LDS reads issued by this wavefront have completed (before a barrier after
+// which another wavefront, or this one, may refill the slot they read).
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -518,6 +521,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         wg_barrier();
         wait_vm0();   // A(g+1), issued a step ago
         if (g + 2 < total) issue(g + 2, true);   // into the slot of A(g-1)
+        // the held-back fragments' reads of A(g) and W(g), issued a phase
+        // ago, have completed before the barrier after which group 1 writes
+        // W(g+2) over W(g)
+        wait_lgkm0();
       };
 #pragma unroll 1
       for (int r = 0; r < my_tiles; ++r) {
@@ -540,6 +547,10 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
       }
     } else {
       auto phase1 = [&](int g) __attribute__((always_inline)) {
+        // the held-back fragments' reads of A(g-1) and W(g-1), issued a phase
+        // ago, have completed before W(g+1) is written over W(g-1) and before
+        // the barrier after which group 0 writes A(g+2) over A(g-1)
+        wait_lgkm0();
         if (g + 1 < total) issue(g + 1, false);   // W(g+1) into the slot of W(g-1)
       };
       auto phase2 = [&](int g, bool first, bool pending, bool defer)

@@ -147,7 +147,7 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
 hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_tiles,
                             int n_heads, int head_dim, bool fixed_ref, void* out, float out_scale,
                             hipStream_t stream);
-// fixed_ref may be true only when |q . k| * log2(e) / sqrt(head_dim) <= 100 for
+// fixed_ref may be true only when |q . k| * log2(e) / sqrt(head_dim) <= 64 for
 // every query and key (softmax against a fixed reference instead of a
 // running maximum); attention_fixed_ref_ok decides it from the QK-norm
 // parameters of a layer.

@@ -1215,6 +1215,16 @@ int enc_calibrate(enc_ctx* ctx, const float* audio, const int64_t* lengths, int3
   return ENC_OK;
 }
 
+int enc_fp8_input_scales(const float* amax, int32_t n, float* scales) {
+  if (n < 0) return fail(ENC_ERR_ARG, "n must be >= 0");
+  if (n > 0 && (!amax || !scales)) return fail(ENC_ERR_ARG, "NULL argument");
+  for (int32_t i = 0; i < n; ++i)
+    if (!(amax[i] >= 0.0f) || !std::isfinite(amax[i]))
+      return fail(ENC_ERR_ARG, "amax[" + std::to_string(i) + "] is negative or not finite");
+  for (int32_t i = 0; i < n; ++i) scales[i] = amax[i] > 0.0f ? amax[i] / 448.0f : 1.0f;
+  return ENC_OK;
+}
+
 int enc_set_precision(enc_ctx* ctx, int32_t precision, const float* input_scales) {
   if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
   if (precision == ENC_PREC_BF16) {

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from speech_audio_encoder_amd import binding
@@ -101,3 +102,15 @@ def test_null_context_is_rejected(lib):
 def test_packed_rows_closed_form():
     assert binding.packed_rows([0, 399, 400, 559, 560, 1680, 57_600_000]) == \
         0 + 0 + 1 + 1 + 1 + 2 + 45_000
+
+
+def test_fp8_input_scales_host_call(lib):
+    # amax / 448 in fp32, 1 for an all-zero input, errors for bad amax
+    amax = np.array([[5.0, 0.0, 448.0, 1e-30]], np.float32)
+    got = binding.scales_from_amax(amax)
+    assert got.shape == amax.shape and got.dtype == np.float32
+    assert got.tolist() == [[np.float32(5.0) / np.float32(448.0), 1.0, 1.0,
+                             np.float32(1e-30) / np.float32(448.0)]]
+    for bad in (-1.0, np.inf, np.nan):
+        with pytest.raises(binding.EncoderError):
+            binding.scales_from_amax(np.array([1.0, bad], np.float32))
