@@ -184,7 +184,7 @@ constexpr int PBK = 64;   // K step of the persistent kernel
 // byte; one 64-code MFMA step takes the two consecutive 16-byte fragments a
 // lane would feed to two bf16 steps (A and W use the same assignment of
 // bytes to k, so every product pairs the right codes).
-template <Epilogue EPI, bool F8>
+template <Epilogue EPI, bool F8, bool XA>
 __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, int64_t M, int K,
@@ -199,6 +199,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   const int my_tiles = slot < n_big ? (n_big - 1 - slot) / G + 1 : 0;
   const int KT = K / PBK;
   const int total = my_tiles * KT;
+  // XA: residual tile preloaded into the accumulators (see below the epilogue)
+  static_assert(!XA || (EPI == Epilogue::kBiasResidualF32 && !F8), "XA: bf16 residual products");
+  constexpr bool x_in_acc = XA;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
     int tm, tn;
     tile_coords(r * G + slot, tiles_m, tiles_n, tm, tn);
     const int64_t am = (int64_t)tm * BIG;
-    if constexpr (!F8 && EPI != Epilogue::kBiasBf16) {
+    if constexpr (!F8 && EPI != Epilogue::kBiasBf16 && !XA) {
       if (is_a) {
         if (off_tile != r) {
 #pragma unroll
@@ -488,15 +491,51 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         const int64_t m = mb + j * 32;
         if (m < M) {
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq)
-            store4<EPI, F8>(Cv, ldc, m, nw + i * 32 + 8 * qq + 4 * lhi, bv[qq], alpha, oscale,
-                            acc[i][j][4 * qq], acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2],
-                            acc[i][j][4 * qq + 3]);
+          for (int qq = 0; qq < 4; ++qq) {
+            if constexpr (x_in_acc)   // the residual is already in the accumulators
+              store4<Epilogue::kBiasF32, F8>(Cv, ldc, m, nw + i * 32 + 8 * qq + 4 * lhi, bv[qq],
+                                             alpha, oscale, acc[i][j][4 * qq],
+                                             acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2],
+                                             acc[i][j][4 * qq + 3]);
+            else
+              store4<EPI, F8>(Cv, ldc, m, nw + i * 32 + 8 * qq + 4 * lhi, bv[qq], alpha, oscale,
+                              acc[i][j][4 * qq], acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2],
+                              acc[i][j][4 * qq + 3]);
+          }
         }
       }
     }
   };
 
+  // XA (residual products whose tiles make exactly one round, e.g. the
+  // attention output and FFN-down projections of a batch of ~13k rows): the
+  // tile's fp32 residual is loaded into the accumulators before the first
+  // MFMA, under the pipeline fill, instead of being read back in the
+  // epilogue, where every CU would read it at the same moment; the epilogue
+  // then adds the bias and stores.  (The sum x + (products) + bias is formed
+  // in that order instead of x + (products + bias).)
+  auto load_x = [&]() __attribute__((always_inline)) {
+    int tm, tn;
+    tile_coords(slot, tiles_m, tiles_n, tm, tn);
+    const int64_t mb = (int64_t)tm * BIG + grp * 128 + l32;
+    const int nw = tn * BIG + q * 64;
+    const float* X = reinterpret_cast<const float*>(Cv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t m = min<int64_t>(mb + 32 * j, M - 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const float4 v =
+              *reinterpret_cast<const float4*>(X + m * ldc + nw + 32 * i + 8 * qq + 4 * lhi);
+          acc[i][j][4 * qq] = v.x;
+          acc[i][j][4 * qq + 1] = v.y;
+          acc[i][j][4 * qq + 2] = v.z;
+          acc[i][j][4 * qq + 3] = v.w;
+        }
+    }
+  };
   // Prologue: A of steps 0 and 1 (group 0), W of step 0 (group 1).
   if (total > 0) {
     if (grp == 0) {
@@ -529,7 +568,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
 #pragma unroll 1
       for (int r = 0; r < my_tiles; ++r) {
         const int g0 = r * KT;
-        compute0(sA[g0 % 3], sW[g0 & 1], true, false, true);
+        if constexpr (x_in_acc) load_x();   // the only tile
+        compute0(sA[g0 % 3], sW[g0 & 1], !x_in_acc, false, true);
         phase2(g0);
         wg_barrier();
 #pragma unroll 1
@@ -565,7 +605,8 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
         const int g0 = r * KT;
         phase1(g0);
         if (r > 0) epilogue(r - 1);
-        phase2(g0, true, false, true);
+        if constexpr (x_in_acc) load_x();   // the only tile, under group 0's first phase
+        phase2(g0, !x_in_acc, false, true);
 #pragma unroll 1
         for (int kt = 1; kt < KT - 1; ++kt) {
           phase1(g0 + kt);
@@ -902,8 +943,17 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   }
   // Full rounds go to the persistent kernel, the remainder to 128 x 128 pieces.
   const int n_big = (tiles / cus) * cus;
-  gemm_big_kernel<EPI, F8><<<dim3(cus), dim3(512), 0, stream>>>(
-      A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big, alpha, oscale);
+  if constexpr (EPI == Epilogue::kBiasResidualF32 && !F8) {
+    if (n_big == cus)   // one round: every CU holds exactly one tile
+      gemm_big_kernel<EPI, F8, true><<<dim3(cus), dim3(512), 0, stream>>>(
+          A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big, alpha, oscale);
+    else
+      gemm_big_kernel<EPI, F8, false><<<dim3(cus), dim3(512), 0, stream>>>(
+          A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big, alpha, oscale);
+  } else {
+    gemm_big_kernel<EPI, F8, false><<<dim3(cus), dim3(512), 0, stream>>>(
+        A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big, alpha, oscale);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tiles == n_big) return e;
   PieceMap pm{0, n_big, tiles_m, tiles_n, N / PIECE};
