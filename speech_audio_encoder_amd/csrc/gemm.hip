@@ -865,10 +865,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
   const int n = (int)n0 + c;
   if (m >= M) return;
   const float* src = part + (int64_t)pid * splits * (PIECE * PIECE) + e;
-  float4 s = *reinterpret_cast<const float4*>(src);
-  for (int k = 1; k < splits; ++k) {
-    const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)k * (PIECE * PIECE));
-    s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+  // eight partials in flight at a time, summed in split order
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < splits; k0 += 8) {
+    float4 t[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < splits)
+        t[k] = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * (PIECE * PIECE));
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k0 + k < splits) {
+        if (k0 + k == 0) {
+          s = t[k];
+        } else {
+          s.x += t[k].x; s.y += t[k].y; s.z += t[k].z; s.w += t[k].w;
+        }
+      }
   }
   store4<EPI, F8>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), alpha, oscale, s.x,
                   s.y, s.z, s.w);
