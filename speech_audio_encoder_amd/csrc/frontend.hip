@@ -8,26 +8,29 @@
 // Hann window, power |X_k|^2 for k = 0..256, Slaney mel bank (peak 1), natural
 // log of (energy + 2^-24).
 //
-// One wavefront transforms one frame at a time; the workgroups are persistent
-// and read the window, twiddle and mel tables from LDS, copied once per
-// workgroup (from global memory each frame's loads would form a chain of
-// dependent cache round trips).  The 400 real samples, zero-padded to
-// 512, are packed as 256 complex values z[n] = s[2n] + i s[2n+1]; a radix-4
-// Stockham FFT of length 256 (four stages, one radix-4 butterfly per lane per
-// stage, ping-pong through LDS) gives Z, and the split
+// Four frames per wavefront, 16 lanes per frame.  The 400 real samples,
+// zero-padded to 512, are packed as 256 complex values z[n] = s[2n] + i s[2n+1]
+// and transformed as a 16 x 16 decomposition, n = 16 n1 + n2, k = k1 + 16 k2:
+// lane n2 holds z[16 n1 + n2] for all n1 and takes a 16-point DFT over n1 in
+// registers (itself two radix-4 passes); the outputs are multiplied by
+// W256^(n2 k1) and transposed through LDS, so that lane k1 holds the column
+// k1 and a second 16-point DFT over n2 gives Z[k1 + 16 k2] in register k2.
+// The split
 //   X[k] = (Z[k] + conj Z[-k]) / 2 - i W512^k (Z[k] - conj Z[-k]) / 2
-// recovers the 257 non-negative bins.
+// recovers the 257 non-negative bins; X[k] and X[256 - k] come from the same
+// pair (Z[k], Z[256 - k]), so lane j takes the pairs of its registers 0..7,
+// whose partners (lane 16 - j, registers 15..8) arrive through LDS.
 //
-// Precision: the window, transform, power and mel sums run in float64 (tables
-// built on the host in float64); the mel energies are rounded to float32 for
-// the log, whose result is float32.  Below
-// 1 kHz the mel bands are narrower than one bin, so a band's energy can be a
-// single bin's power; when that power is small, a float32 transform's absolute
-// error (about 1e-6 of the frame's spectral norm) turns into a log error of
-// order 1e-3.  In float64 that error is ~1e-11.  The cost is ~14 kflop of
-// fp64 per frame, small next to the frame's 2.3 KB of memory traffic.
-// Memory traffic is the audio read (frames overlap by 240 samples; the overlap
-// is served from cache) plus the feature write.
+// Precision: the window, transform, split and power run in float64; the
+// powers are then rounded to float32 and the mel sums, the 2^-24 guard and the
+// log run in float32.  Below 1 kHz the mel bands are narrower than one bin, so
+// a band's energy can be a single bin's power; when that power is small, a
+// float32 transform's absolute error (about 1e-6 of the frame's spectral norm)
+// would turn into a log error of order 1e-3.  In float64 that error is ~1e-11.
+// Once a power is formed, rounding it (and the mel weights) to float32 is a
+// relative change of 2^-24 in a sum of non-negative terms, so the log moves by
+// ~1e-7.  Memory traffic is the audio read (frames overlap by 240 samples;
+// the overlap is served from cache) plus the feature write.
 
 #include <algorithm>
 
@@ -38,13 +41,76 @@ namespace enc {
 
 namespace {
 
-constexpr int WAVES = 8;
-constexpr int FB_LDS = 2048;   // clips whose frame offsets are searched in LDS
+constexpr int WAVES = 8;          // wavefronts per workgroup (one workgroup per CU)
+constexpr int ROWS = 4;           // frames per wavefront, 16 lanes each
+constexpr int FB_LDS = 1024;      // clips whose frame offsets are searched in LDS
+constexpr int SLOT_ROW = 272;     // 16-byte LDS slots per frame: 16 x 17 (padded)
+constexpr int TAPS = 13;          // 16 n1 + n2 < 200 needs n1 <= 12
 
-typedef Cpx c32;
+typedef Cpx c64;
 
-__device__ __forceinline__ c32 cmul(c32 a, c32 b) {
+__device__ __forceinline__ c64 cadd(c64 a, c64 b) { return {a.re + b.re, a.im + b.im}; }
+__device__ __forceinline__ c64 csub(c64 a, c64 b) { return {a.re - b.re, a.im - b.im}; }
+__device__ __forceinline__ c64 cmul(c64 a, c64 b) {
   return {a.re * b.re - a.im * b.im, a.re * b.im + a.im * b.re};
+}
+
+// 4-point DFT in place (W4 = -i).  U3ZERO: the last input is zero.
+template <bool U3ZERO>
+__device__ __forceinline__ void dft4(c64& u0, c64& u1, c64& u2, c64& u3) {
+  const c64 s02 = cadd(u0, u2), d02 = csub(u0, u2);
+  const c64 s13 = U3ZERO ? u1 : cadd(u1, u3);
+  const c64 d13 = U3ZERO ? u1 : csub(u1, u3);
+  u0 = cadd(s02, s13);
+  u2 = csub(s02, s13);
+  u1 = {d02.re + d13.im, d02.im - d13.re};   // d02 - i d13
+  u3 = {d02.re - d13.im, d02.im + d13.re};   // d02 + i d13
+}
+
+// x * W16^m for the exponents m = b c (b, c = 1..3) of the 16-point DFT.
+template <int M>
+__device__ __forceinline__ c64 mul_w16(c64 x) {
+  constexpr double C1 = 0.92387953251128675613;   // cos(pi / 8)
+  constexpr double S1 = 0.38268343236508977173;   // sin(pi / 8)
+  constexpr double R2 = 0.70710678118654752440;   // sqrt(1 / 2)
+  if constexpr (M == 4) return {x.im, -x.re};
+  else if constexpr (M == 2) return {R2 * (x.re + x.im), R2 * (x.im - x.re)};
+  else if constexpr (M == 6) return {R2 * (x.im - x.re), -R2 * (x.re + x.im)};
+  else {
+    constexpr double wr = M == 1 ? C1 : M == 3 ? S1 : -C1;   // M == 9
+    constexpr double wi = M == 1 ? -S1 : M == 3 ? -C1 : S1;
+    return cmul(x, c64{wr, wi});
+  }
+}
+
+// 16-point DFT in place, natural order in and out: v[k] <- sum_n v[n] W16^(nk).
+// n = 4a + b, k = c + 4d: 4-point DFTs over a, twiddles W16^(bc), 4-point
+// DFTs over b.  TAIL_ZERO: v[13], v[14], v[15] are zero on entry.
+template <bool TAIL_ZERO>
+__device__ __forceinline__ void dft16(c64 (&v)[16]) {
+  dft4<false>(v[0], v[4], v[8], v[12]);
+#pragma unroll
+  for (int b = 1; b < 4; ++b) dft4<TAIL_ZERO>(v[b], v[4 + b], v[8 + b], v[12 + b]);
+  // v[4c + b] now holds the c-th output of column b
+  v[5] = mul_w16<1>(v[5]);
+  v[6] = mul_w16<2>(v[6]);
+  v[7] = mul_w16<3>(v[7]);
+  v[9] = mul_w16<2>(v[9]);
+  v[10] = mul_w16<4>(v[10]);
+  v[11] = mul_w16<6>(v[11]);
+  v[13] = mul_w16<3>(v[13]);
+  v[14] = mul_w16<6>(v[14]);
+  v[15] = mul_w16<9>(v[15]);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) dft4<false>(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]);
+  // v[4c + d] holds output c + 4d: transpose the 4 x 4 index
+  c64 t[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) t[i] = v[i];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[c + 4 * d] = t[4 * c + d];
 }
 
 // Clip index of packed frame g: largest b with base[b] <= g (base ascending).
@@ -62,12 +128,12 @@ __device__ __forceinline__ int find_clip(P base, int batch, int64_t g) {
 // wavefront's operations in issue order, so a compiler barrier suffices.
 __device__ __forceinline__ void wave_lds_sync() { asm volatile("" ::: "memory"); }
 
-// Persistent: a workgroup copies the tables (and, for up to FB_LDS clips, the
-// frame offsets) into LDS once, then each wavefront takes frames
-// g = wave_id, wave_id + waves, ... .
+// Persistent: a workgroup copies the window, the mel weights (and, for up to
+// FB_LDS clips, the frame offsets) into LDS once; each wavefront then takes
+// frame quads q = wave_id, wave_id + waves, ... (frames 4q .. 4q + 3).
 template <bool STACKED>
 __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
-    const float* __restrict__ audio, int64_t audio_stride,
+    const float* __restrict__ audio, int64_t audio_stride, int pair_loads,
     const int32_t* __restrict__ n_frames,     // [batch] F_b
     const int32_t* __restrict__ frame_base,   // [batch] first packed frame (STACKED)
     int batch, int64_t f_max, int64_t total_frames,
@@ -75,26 +141,22 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
     float* __restrict__ out_f32,              // [batch, f_max, 128]   (!STACKED)
     bf16_t* __restrict__ out_bf16)            // [sum 8 P_b, 128]       (STACKED)
 {
-  __shared__ double s_hann[WIN];
-  __shared__ c32 s_tw256[256];
-  __shared__ c32 s_tw512[NBIN];
-  __shared__ int32_t s_mel_start[NMEL], s_mel_count[NMEL], s_mel_off[NMEL];
-  __shared__ double s_mel_w[MEL_NNZ_MAX];
+  __shared__ __align__(16) double s_hann[WIN + 16];
+  __shared__ float s_melw[MEL_TRIP_TOTAL * 16];
   __shared__ int32_t s_fb[FB_LDS];
-  // per wavefront: the transform in place; the power spectrum (257 doubles)
-  // then overwrites its first half
-  __shared__ c32 buf[WAVES][256];
+  __shared__ c64 s_tw[16 * 16];    // [k1][j] = W256^(j k1)
+  __shared__ c64 s_tws[128];       // [k] = W512^k, k < 128
+  // per wavefront and frame row: the transpose (16 x 17 slots), then the
+  // partner exchange (16 x 9 slots), then the float32 power spectrum
+  __shared__ c64 s_buf[WAVES][ROWS * SLOT_ROW];
 
   const int tid = threadIdx.x;
-  for (int i = tid; i < WIN; i += 64 * WAVES) s_hann[i] = tab->hann[i];
-  for (int i = tid; i < 256; i += 64 * WAVES) s_tw256[i] = tab->tw256[i];
-  for (int i = tid; i < NBIN; i += 64 * WAVES) s_tw512[i] = tab->tw512[i];
-  for (int i = tid; i < NMEL; i += 64 * WAVES) {
-    s_mel_start[i] = tab->mel_start[i];
-    s_mel_count[i] = tab->mel_count[i];
-    s_mel_off[i] = tab->mel_offset[i];
+  for (int i = tid; i < WIN + 16; i += 64 * WAVES) s_hann[i] = tab->hann[i];
+  for (int i = tid; i < MEL_TRIP_TOTAL * 16; i += 64 * WAVES) s_melw[i] = (&tab->mel_w4[0][0])[i];
+  for (int i = tid; i < 256; i += 64 * WAVES) {
+    s_tw[i] = tab->tw256[((i >> 4) * (i & 15)) & 255];
+    if (i < 128) s_tws[i] = tab->tw512[i];
   }
-  for (int i = tid; i < MEL_NNZ_MAX; i += 64 * WAVES) s_mel_w[i] = tab->mel_w[i];
   const bool fb_in_lds = STACKED && batch <= FB_LDS;
   if (fb_in_lds)
     for (int i = tid; i < batch; i += 64 * WAVES) s_fb[i] = frame_base[i];
@@ -102,146 +164,167 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
 
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int64_t stride = (int64_t)gridDim.x * WAVES;
-  c32* fb = buf[wave];
-  double* pw = reinterpret_cast<double*>(fb);
+  const int row = lane >> 4;
+  const int j = lane & 15;
+  c64* rb = s_buf[wave] + row * SLOT_ROW;         // this frame's LDS slots
+  float* pb = reinterpret_cast<float*>(rb);       // power spectrum, 257 (+pad) floats
 
-  // Frame g: clip, frame in clip, validity; its 400 samples (lane j holds
-  // samples 2n, 2n + 1 of n = j + 64 r) are fetched one frame ahead.
-  auto locate = [&](int64_t g, int& b, int64_t& t) __attribute__((always_inline)) {
-    if (STACKED) {
-      b = fb_in_lds ? find_clip(s_fb, batch, g) : find_clip(frame_base, batch, g);
-      t = g - (fb_in_lds ? s_fb[b] : frame_base[b]);
+  // per lane: the first bin read for each of its bands
+  int mel_lo[MEL_GROUPS];
+#pragma unroll
+  for (int i = 0; i < MEL_GROUPS; ++i) mel_lo[i] = tab->mel_rstart[j + 16 * i];
+  // bin 128 (lane 0's register 8) is its own partner; the other lanes write
+  // that value to a slot past the spectrum that no band reads
+  const int p128 = j == 0 ? 128 : NBIN + j;
+
+  // Frame of this lane's row in quad q: its validity and samples (lane j holds
+  // samples 2n, 2n + 1 of n = 16 n1 + j), fetched one quad ahead.  Invalid
+  // frames and the taps past the window read in-bounds samples that the zero
+  // window (or the zero output) discards.
+  auto fetch = [&](int64_t q, float (&xs)[2 * TAPS], bool& ok) __attribute__((always_inline)) {
+    const int64_t g = q * ROWS + row;
+    int b = 0;
+    int64_t t = 0;
+    if (g < total_frames) {
+      if (STACKED) {
+        b = fb_in_lds ? find_clip(s_fb, batch, g) : find_clip(frame_base, batch, g);
+        t = g - (fb_in_lds ? s_fb[b] : frame_base[b]);
+      } else {
+        b = (int)(g / f_max);
+        t = g - (int64_t)b * f_max;
+      }
+    }
+    ok = g < total_frames && t < n_frames[b];
+    const float* x = ok ? audio + (int64_t)b * audio_stride + t * HOP : audio;
+    if (pair_loads) {
+#pragma unroll
+      for (int n1 = 0; n1 < TAPS; ++n1) {
+        const int n = min(16 * n1 + j, WIN / 2 - 1);
+        const float2 p = *reinterpret_cast<const float2*>(x + 2 * n);
+        xs[2 * n1] = p.x;
+        xs[2 * n1 + 1] = p.y;
+      }
     } else {
-      b = (int)(g / f_max);
-      t = g - (int64_t)b * f_max;
-    }
-  };
-  auto fetch = [&](int64_t g, float (&xs)[8], bool& valid) __attribute__((always_inline)) {
-    int b;
-    int64_t t;
-    locate(g, b, t);
-    valid = t < n_frames[b];
-    const float* x = audio + (int64_t)b * audio_stride + t * HOP;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = lane + 64 * r;
-      // the row stride (longest clip) may be odd: two 4-byte loads
-      const bool in = valid && n < WIN / 2;
-      xs[2 * r] = in ? x[2 * n] : 0.f;
-      xs[2 * r + 1] = in ? x[2 * n + 1] : 0.f;
+      for (int n1 = 0; n1 < TAPS; ++n1) {
+        const int n = min(16 * n1 + j, WIN / 2 - 1);
+        xs[2 * n1] = x[2 * n];
+        xs[2 * n1 + 1] = x[2 * n + 1];
+      }
     }
   };
 
-  int64_t g = (int64_t)blockIdx.x * WAVES + wave;
-  float xs[8];
-  bool valid = false;
-  if (g < total_frames) fetch(g, xs, valid);
-  for (; g < total_frames; g += stride) {
-    c32 v[4];
+  const int64_t n_quads = (total_frames + ROWS - 1) / ROWS;
+  const int64_t qstride = (int64_t)gridDim.x * WAVES;
+  int64_t q = (int64_t)blockIdx.x * WAVES + wave;
+  float xs[2 * TAPS];
+  bool ok = false;
+  if (q < n_quads) fetch(q, xs, ok);
+  for (; q < n_quads; q += qstride) {
+    c64 v[16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = lane + 64 * r;
-      v[r] = n < WIN / 2 ? c32{(double)xs[2 * r] * s_hann[2 * n],
-                                (double)xs[2 * r + 1] * s_hann[2 * n + 1]}
-                         : c32{0.0, 0.0};
+    for (int n1 = 0; n1 < TAPS; ++n1) {
+      const int n = 16 * n1 + j;
+      const double2 h = *reinterpret_cast<const double2*>(s_hann + 2 * n);   // zero past WIN
+      v[n1] = {(double)xs[2 * n1] * h.x, (double)xs[2 * n1 + 1] * h.y};
     }
-    const bool cur_valid = valid;
-    if (g + stride < total_frames) fetch(g + stride, xs, valid);   // next frame's samples
+#pragma unroll
+    for (int n1 = TAPS; n1 < 16; ++n1) v[n1] = {0.0, 0.0};
+    const bool cur_ok = ok;
+    const int64_t g = q * ROWS + row;
+    if (q + qstride < n_quads) fetch(q + qstride, xs, ok);   // next quad's samples
 
+    // pass 1 over n1, twiddles, transpose (write slot k1 * 17 + j, read j * 17 + n2)
+    dft16<true>(v);
 #pragma unroll
-    for (int stage = 0; stage < 4; ++stage) {
-      const int ns = 1 << (2 * stage);           // 1, 4, 16, 64
-      if (stage > 0) {
+    for (int k1 = 1; k1 < 16; ++k1) v[k1] = cmul(v[k1], s_tw[k1 * 16 + j]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = fb[lane + 64 * r];
-        wave_lds_sync();   // every lane's reads before any lane's writes
-      }
-      const int k = lane & (ns - 1);
-      const int step = k * (64 >> (2 * stage));  // twiddle index unit: 2 pi / 256
-#pragma unroll
-      for (int r = 1; r < 4; ++r) v[r] = cmul(v[r], s_tw256[(r * step) & 255]);
-      const c32 a0 = {v[0].re + v[2].re, v[0].im + v[2].im};
-      const c32 a1 = {v[0].re - v[2].re, v[0].im - v[2].im};
-      const c32 a2 = {v[1].re + v[3].re, v[1].im + v[3].im};
-      const c32 a3 = {v[1].im - v[3].im, v[3].re - v[1].re};   // -i (v1 - v3)
-      const int base = (lane >> (2 * stage)) * (ns * 4) + k;
-      fb[base] = {a0.re + a2.re, a0.im + a2.im};
-      fb[base + ns] = {a1.re + a3.re, a1.im + a3.im};
-      fb[base + 2 * ns] = {a0.re - a2.re, a0.im - a2.im};
-      fb[base + 3 * ns] = {a1.re - a3.re, a1.im - a3.im};
-      wave_lds_sync();
-    }
-
-    // Split the packed transform into the 257 real-input bins and take power
-    // (all of Z is read before the power spectrum overwrites it).
-    c32 za[5], zb[5];
-#pragma unroll
-    for (int r = 0; r < 5; ++r) {
-      const int k = lane + 64 * r;
-      za[r] = fb[k & 255];
-      zb[r] = fb[(256 - k) & 255];
-    }
+    for (int k1 = 0; k1 < 16; ++k1) rb[k1 * 17 + j] = v[k1];
     wave_lds_sync();
 #pragma unroll
-    for (int r = 0; r < 5; ++r) {
-      const int k = lane + 64 * r;
-      if (k <= 256) {
-        const c32 a = za[r];
-        const c32 bconj = {zb[r].re, -zb[r].im};
-        const c32 e = {0.5 * (a.re + bconj.re), 0.5 * (a.im + bconj.im)};
-        const c32 d = {0.5 * (a.re - bconj.re), 0.5 * (a.im - bconj.im)};
-        // o = -i d, then X = e + W512^k o
-        const c32 o = {d.im, -d.re};
-        const c32 wo = cmul(s_tw512[k], o);
-        const double xr = e.re + wo.re, xi = e.im + wo.im;
-        pw[k] = xr * xr + xi * xi;
-      }
-    }
+    for (int n2 = 0; n2 < 16; ++n2) v[n2] = rb[j * 17 + n2];
+    wave_lds_sync();
+    // pass 2 over n2: v[k2] = Z[j + 16 k2]
+    dft16<false>(v);
+
+    // partners: lane j writes registers 8..15 to slots 9j + 0..7 and register
+    // 0 to slot 9j + 8; the partner of Z[j + 16 r] (r < 8) is Z[256 - j - 16 r],
+    // register 15 - r of lane 16 - j, or for lane 0 its own register 16 - r
+#pragma unroll
+    for (int s = 0; s < 8; ++s) rb[9 * j + s] = v[8 + s];
+    rb[9 * j + 8] = v[0];
+    wave_lds_sync();
+    const c64* pr = rb + 9 * ((16 - j) & 15) + (j == 0 ? 1 : 0);
+    c64 w[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) w[r] = pr[7 - r];
     wave_lds_sync();
 
+    // split and power, times 4 (the mel weights carry the 1/4)
+    double pk[8], pm[8];
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int m = lane + 64 * r;
-      float val = 0.f;
-      if (cur_valid) {
-        const int k0 = s_mel_start[m];
-        const int cnt = s_mel_count[m];
-        const double* wm = s_mel_w + s_mel_off[m];
-        // bands span at most 12 bins here: the first 16 terms are unrolled
-        // (independent LDS reads), in the same order as the plain sum
-        double acc = 0.0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (i < cnt) acc += wm[i] * pw[k0 + i];
-        for (int i = 16; i < cnt; ++i) acc += wm[i] * pw[k0 + i];
-        // natural log of (energy + 2^-24), taken in fp32 on the sum rounded to
-        // fp32: log2 in hardware (v_log_f32, ~1 ulp) times ln 2; the result's
-        // absolute error is ~1e-6, against a 1e-3 tolerance
-        val = __builtin_amdgcn_logf((float)(acc + 5.9604644775390625e-08)) *
-              0.69314718055994531f;
-      }
-      if (STACKED) out_bf16[g * NMEL + m] = f32_to_bf16(val);
-      else out_f32[g * NMEL + m] = val;
+    for (int r = 0; r < 8; ++r) {
+      const c64 a = v[r], b = w[r];
+      const c64 e = {a.re + b.re, a.im - b.im};   // Z[k] + conj Z[-k]
+      const c64 d = {a.re - b.re, a.im + b.im};   // Z[k] - conj Z[-k]
+      const c64 wo = cmul(s_tws[j + 16 * r], c64{d.im, -d.re});
+      const double xr = e.re + wo.re, xi = e.im + wo.im;   // 2 X[k]
+      const double yr = e.re - wo.re, yi = e.im - wo.im;   // 2 conj X[256 - k]
+      pk[r] = xr * xr + xi * xi;
+      pm[r] = yr * yr + yi * yi;
     }
-    wave_lds_sync();   // this frame's reads of pw before the next frame's writes
+    const double p_mid = 4.0 * (v[8].re * v[8].re + v[8].im * v[8].im);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      pb[j + 16 * r] = (float)pk[r];
+      pb[256 - j - 16 * r] = (float)pm[r];
+    }
+    pb[p128] = (float)p_mid;
+    wave_lds_sync();
+
+    // mel bands j + 16 i, log, store
+    int row0 = 0;
+#pragma unroll
+    for (int i = 0; i < MEL_GROUPS; ++i) {
+      const float* pp = pb + mel_lo[i];
+      float acc = 0.f;
+#pragma unroll
+      for (int t = 0; t < MEL_GROUP_TRIP[i]; ++t)
+        acc = fmaf(s_melw[(row0 + t) * 16 + j], pp[t], acc);
+      row0 += MEL_GROUP_TRIP[i];
+      // natural log of (energy + 2^-24): log2 in hardware (v_log_f32, ~1 ulp)
+      // times ln 2
+      const float val =
+          cur_ok ? __builtin_amdgcn_logf(acc + 5.9604644775390625e-08f) * 0.69314718055994531f
+                 : 0.f;
+      if (g < total_frames) {
+        if (STACKED) out_bf16[g * NMEL + j + 16 * i] = f32_to_bf16(val);
+        else out_f32[g * NMEL + j + 16 * i] = val;
+      }
+    }
+    wave_lds_sync();   // this quad's reads of the spectrum before the next quad's writes
   }
 }
 
 int g_fe_grid = 0;
 
-// Workgroups of the persistent grid: as many as the LDS lets reside (two per
+// Workgroups of the persistent grid: as many as the LDS lets reside (one per
 // CU) on every CU.
 int frontend_grid() {
   if (g_fe_grid == 0) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_fe_grid = 2 * n;
+      g_fe_grid = n;
     else
-      g_fe_grid = 512;
+      g_fe_grid = 256;
   }
   return g_fe_grid;
+}
+
+// Two-float loads need every frame's first sample 8-byte aligned.
+int pair_aligned(const float* audio, int64_t audio_stride) {
+  return (audio_stride % 2 == 0) && (reinterpret_cast<uintptr_t>(audio) % 8 == 0);
 }
 
 }  // namespace
@@ -251,9 +334,11 @@ hipError_t launch_logmel_padded(const float* audio, int64_t audio_stride, const 
                                 hipStream_t stream) {
   const int64_t total = (int64_t)batch * f_max;
   if (total == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((total + WAVES - 1) / WAVES, frontend_grid());
+  const int64_t quads = (total + ROWS - 1) / ROWS;
+  const int64_t blocks = std::min<int64_t>((quads + WAVES - 1) / WAVES, frontend_grid());
   logmel_kernel<false><<<dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream>>>(
-      audio, audio_stride, n_frames, nullptr, batch, f_max, total, tab, out, nullptr);
+      audio, audio_stride, pair_aligned(audio, audio_stride), n_frames, nullptr, batch, f_max,
+      total, tab, out, nullptr);
   return hipGetLastError();
 }
 
@@ -261,10 +346,11 @@ hipError_t launch_logmel_stacked(const float* audio, int64_t audio_stride, const
                                  const int32_t* frame_base, int batch, int64_t total_frames,
                                  const FrontendTables* tab, bf16_t* out, hipStream_t stream) {
   if (total_frames == 0) return hipSuccess;
-  const int64_t blocks =
-      std::min<int64_t>((total_frames + WAVES - 1) / WAVES, frontend_grid());
+  const int64_t quads = (total_frames + ROWS - 1) / ROWS;
+  const int64_t blocks = std::min<int64_t>((quads + WAVES - 1) / WAVES, frontend_grid());
   logmel_kernel<true><<<dim3((unsigned)blocks), dim3(64 * WAVES), 0, stream>>>(
-      audio, audio_stride, n_frames, frame_base, batch, 0, total_frames, tab, nullptr, out);
+      audio, audio_stride, pair_aligned(audio, audio_stride), n_frames, frame_base, batch, 0,
+      total_frames, tab, nullptr, out);
   return hipGetLastError();
 }
 

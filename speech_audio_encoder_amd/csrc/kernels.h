@@ -14,17 +14,22 @@ struct Cpx {
   double re, im;
 };
 
-constexpr int MEL_NNZ_MAX = 1024;
+// Mel bands are summed by 16 lanes per frame: lane j takes bands j + 16 i
+// (i = 0..7), and band group i reads MEL_GROUP_TRIP[i] consecutive bins (the
+// widest band of the group; narrower bands carry zero weights).
+constexpr int MEL_GROUPS = 8;
+constexpr int MEL_GROUP_TRIP[MEL_GROUPS] = {2, 2, 2, 3, 4, 6, 9, 12};
+constexpr int MEL_TRIP_TOTAL = 40;
 
 // Constant tables of the frontend, built on the host in float64.
 struct FrontendTables {
-  double hann[WIN];             // periodic Hann window
+  double hann[WIN + 16];        // periodic Hann window, zero past WIN
   Cpx tw256[256];               // exp(-2 pi i m / 256)
   Cpx tw512[NBIN + 1];          // exp(-2 pi i k / 512), k = 0..256 (+1 pad)
-  int32_t mel_start[NMEL];      // first bin with nonzero weight
-  int32_t mel_count[NMEL];      // number of bins from mel_start
-  int32_t mel_offset[NMEL];     // offset of the band's weights in mel_w
-  double mel_w[MEL_NNZ_MAX];
+  int32_t mel_rstart[NMEL];     // first bin read for band m (<= NBIN - trip)
+  // weight / 4 of bin mel_rstart[m] + t for band m = j + 16 i, at row
+  // (sum of the trips of groups before i) + t, column j; float32
+  float mel_w4[MEL_TRIP_TOTAL][16];
 };
 
 // ---------------------------------------------------------------- frontend

@@ -62,7 +62,8 @@ double mel_to_hz(double m) {
 
 bool build_frontend_tables(FrontendTables* t) {
   const double pi = 3.14159265358979323846;
-  for (int n = 0; n < WIN; ++n) t->hann[n] = 0.5 - 0.5 * std::cos(2.0 * pi * n / WIN);
+  for (int n = 0; n < WIN + 16; ++n)
+    t->hann[n] = n < WIN ? 0.5 - 0.5 * std::cos(2.0 * pi * n / WIN) : 0.0;
   for (int m = 0; m < 256; ++m) {
     const double a = -2.0 * pi * m / 256.0;
     t->tw256[m] = {std::cos(a), std::sin(a)};
@@ -76,30 +77,37 @@ bool build_frontend_tables(FrontendTables* t) {
   double edge[NMEL + 2];
   const double top = hz_to_mel(8000.0);
   for (int i = 0; i < NMEL + 2; ++i) edge[i] = mel_to_hz(top * i / (NMEL + 1));
-  int off = 0;
-  for (int m = 0; m < NMEL; ++m) {
-    int first = -1, count = 0;
-    for (int k = 0; k < NBIN; ++k) {
-      const double f = k * 16000.0 / NFFT;
-      const double up = (f - edge[m]) / (edge[m + 1] - edge[m]);
-      const double down = (edge[m + 2] - f) / (edge[m + 2] - edge[m + 1]);
-      const double w = std::max(0.0, std::min(up, down));
-      if (w > 0.0) {
-        if (first < 0) first = k;
-        // bands are contiguous runs of bins
-        if (k != first + count) return false;
-        if (off + count >= MEL_NNZ_MAX) return false;
-        t->mel_w[off + count] = w;
-        ++count;
+  for (int r = 0; r < MEL_TRIP_TOTAL; ++r)
+    for (int j = 0; j < 16; ++j) t->mel_w4[r][j] = 0.0f;
+  int row0 = 0;
+  for (int i = 0; i < MEL_GROUPS; ++i) {
+    const int trip = MEL_GROUP_TRIP[i];
+    for (int j = 0; j < 16; ++j) {
+      const int m = j + 16 * i;
+      int first = -1, count = 0;
+      double w[NBIN];
+      for (int k = 0; k < NBIN; ++k) {
+        const double f = k * 16000.0 / NFFT;
+        const double up = (f - edge[m]) / (edge[m + 1] - edge[m]);
+        const double down = (edge[m + 2] - f) / (edge[m + 2] - edge[m + 1]);
+        const double wk = std::max(0.0, std::min(up, down));
+        if (wk > 0.0) {
+          if (first < 0) first = k;
+          // bands are contiguous runs of bins, no wider than their group's trip
+          if (k != first + count || count >= trip) return false;
+          w[count++] = wk;
+        }
       }
+      if (first < 0) return false;
+      // the read window [rstart, rstart + trip) stays inside the 257 bins
+      const int rstart = std::min(first, NBIN - trip);
+      t->mel_rstart[m] = rstart;
+      for (int c = 0; c < count; ++c)
+        t->mel_w4[row0 + first - rstart + c][j] = (float)(0.25 * w[c]);
     }
-    if (first < 0) return false;
-    t->mel_start[m] = first;
-    t->mel_count[m] = count;
-    t->mel_offset[m] = off;
-    off += count;
+    row0 += trip;
   }
-  return true;
+  return row0 == MEL_TRIP_TOTAL;
 }
 
 }  // namespace
