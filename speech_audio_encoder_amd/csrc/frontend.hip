@@ -45,6 +45,7 @@ constexpr int WAVES = 8;          // wavefronts per workgroup (one workgroup per
 constexpr int ROWS = 4;           // frames per wavefront, 16 lanes each
 constexpr int FB_LDS = 1024;      // clips whose frame offsets are searched in LDS
 constexpr int SLOT_ROW = 272;     // 16-byte LDS slots per frame: 16 x 17 (padded)
+constexpr int P_ROW = 336;        // floats per frame of the power spectrum (336 = 16 mod 64)
 constexpr int TAPS = 13;          // 16 n1 + n2 < 200 needs n1 <= 12
 
 typedef Cpx c64;
@@ -80,6 +81,27 @@ __device__ __forceinline__ c64 mul_w16(c64 x) {
     constexpr double wr = M == 1 ? C1 : M == 3 ? S1 : -C1;   // M == 9
     constexpr double wi = M == 1 ? -S1 : M == 3 ? -C1 : S1;
     return cmul(x, c64{wr, wi});
+  }
+}
+
+// x * W32^r for r = 0..7 (r is a compile-time constant after unrolling).
+__device__ __forceinline__ c64 mul_w32(int r, c64 x) {
+  constexpr double R2 = 0.70710678118654752440;   // sqrt(1 / 2) = cos(pi / 4)
+  constexpr double C1 = 0.98078528040323044913;   // cos(pi / 16)
+  constexpr double S1 = 0.19509032201612826785;   // sin(pi / 16)
+  constexpr double C2 = 0.92387953251128675613;   // cos(pi / 8)
+  constexpr double S2 = 0.38268343236508977173;   // sin(pi / 8)
+  constexpr double C3 = 0.83146961230254523708;   // cos(3 pi / 16)
+  constexpr double S3 = 0.55557023301960222474;   // sin(3 pi / 16)
+  switch (r) {   // W32^r = cos(pi r / 16) - i sin(pi r / 16)
+    case 0: return x;
+    case 1: return cmul(x, c64{C1, -S1});
+    case 2: return cmul(x, c64{C2, -S2});
+    case 3: return cmul(x, c64{C3, -S3});
+    case 4: return {R2 * (x.re + x.im), R2 * (x.im - x.re)};
+    case 5: return cmul(x, c64{S3, -C3});
+    case 6: return cmul(x, c64{S2, -C2});
+    default: return cmul(x, c64{S1, -C1});
   }
 }
 
@@ -144,8 +166,6 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
   __shared__ __align__(16) double s_hann[WIN + 16];
   __shared__ float s_melw[MEL_TRIP_TOTAL * 16];
   __shared__ int32_t s_fb[FB_LDS];
-  __shared__ c64 s_tw[16 * 16];    // [k1][j] = W256^(j k1)
-  __shared__ c64 s_tws[128];       // [k] = W512^k, k < 128
   // per wavefront and frame row: the transpose (16 x 17 slots), then the
   // partner exchange (16 x 9 slots), then the float32 power spectrum
   __shared__ c64 s_buf[WAVES][ROWS * SLOT_ROW];
@@ -153,10 +173,6 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
   const int tid = threadIdx.x;
   for (int i = tid; i < WIN + 16; i += 64 * WAVES) s_hann[i] = tab->hann[i];
   for (int i = tid; i < MEL_TRIP_TOTAL * 16; i += 64 * WAVES) s_melw[i] = (&tab->mel_w4[0][0])[i];
-  for (int i = tid; i < 256; i += 64 * WAVES) {
-    s_tw[i] = tab->tw256[((i >> 4) * (i & 15)) & 255];
-    if (i < 128) s_tws[i] = tab->tw512[i];
-  }
   const bool fb_in_lds = STACKED && batch <= FB_LDS;
   if (fb_in_lds)
     for (int i = tid; i < batch; i += 64 * WAVES) s_fb[i] = frame_base[i];
@@ -167,8 +183,20 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
   const int row = lane >> 4;
   const int j = lane & 15;
   c64* rb = s_buf[wave] + row * SLOT_ROW;         // this frame's LDS slots
-  float* pb = reinterpret_cast<float*>(rb);       // power spectrum, 257 (+pad) floats
+  // power spectrum, 257 floats (+ a slot per lane past them); the rows start
+  // 16 banks apart, so that the four rows' float accesses do not collide
+  float* pb = reinterpret_cast<float*>(s_buf[wave]) + row * P_ROW;
 
+  // per lane: the inter-pass twiddle W256^(j k1) = W256^(j c) W64^(j d) for
+  // k1 = c + 4d is formed from wa[c] = W256^(j c) and wb[d] = W256^(4 j d);
+  // the split twiddle W512^(j + 16 r) = W512^j W32^r from w512 = W512^j
+  c64 wa[4], wb[4];
+#pragma unroll
+  for (int c = 1; c < 4; ++c) {
+    wa[c] = tab->tw256[j * c];
+    wb[c] = tab->tw256[(4 * j * c) & 255];
+  }
+  const c64 w512 = tab->tw512[j];
   // per lane: the first bin read for each of its bands
   int mel_lo[MEL_GROUPS];
 #pragma unroll
@@ -221,11 +249,11 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
   bool ok = false;
   if (q < n_quads) fetch(q, xs, ok);
   for (; q < n_quads; q += qstride) {
+    // windowed samples; the lane's taps are zero past WIN
     c64 v[16];
 #pragma unroll
     for (int n1 = 0; n1 < TAPS; ++n1) {
-      const int n = 16 * n1 + j;
-      const double2 h = *reinterpret_cast<const double2*>(s_hann + 2 * n);   // zero past WIN
+      const double2 h = *reinterpret_cast<const double2*>(s_hann + 2 * (16 * n1 + j));
       v[n1] = {(double)xs[2 * n1] * h.x, (double)xs[2 * n1 + 1] * h.y};
     }
 #pragma unroll
@@ -237,7 +265,11 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
     // pass 1 over n1, twiddles, transpose (write slot k1 * 17 + j, read j * 17 + n2)
     dft16<true>(v);
 #pragma unroll
-    for (int k1 = 1; k1 < 16; ++k1) v[k1] = cmul(v[k1], s_tw[k1 * 16 + j]);
+    for (int k1 = 1; k1 < 16; ++k1) {
+      const int c = k1 & 3, d = k1 >> 2;
+      const c64 t = c == 0 ? wb[d] : d == 0 ? wa[c] : cmul(wa[c], wb[d]);
+      v[k1] = cmul(v[k1], t);
+    }
 #pragma unroll
     for (int k1 = 0; k1 < 16; ++k1) rb[k1 * 17 + j] = v[k1];
     wave_lds_sync();
@@ -267,7 +299,7 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
       const c64 a = v[r], b = w[r];
       const c64 e = {a.re + b.re, a.im - b.im};   // Z[k] + conj Z[-k]
       const c64 d = {a.re - b.re, a.im + b.im};   // Z[k] - conj Z[-k]
-      const c64 wo = cmul(s_tws[j + 16 * r], c64{d.im, -d.re});
+      const c64 wo = cmul(w512, mul_w32(r, c64{d.im, -d.re}));
       const double xr = e.re + wo.re, xi = e.im + wo.im;   // 2 X[k]
       const double yr = e.re - wo.re, yi = e.im - wo.im;   // 2 conj X[256 - k]
       pk[r] = xr * xr + xi * xi;
@@ -282,15 +314,26 @@ __global__ __launch_bounds__(64 * WAVES) void logmel_kernel(
     pb[p128] = (float)p_mid;
     wave_lds_sync();
 
-    // mel bands j + 16 i, log, store
+    // mel bands j + 16 i (all reads issued first), log, store
+    float wv[MEL_TRIP_TOTAL], pv[MEL_TRIP_TOTAL];
+#pragma unroll
+    for (int t = 0; t < MEL_TRIP_TOTAL; ++t) wv[t] = s_melw[t * 16 + j];
+    {
+      int row0 = 0;
+#pragma unroll
+      for (int i = 0; i < MEL_GROUPS; ++i) {
+#pragma unroll
+        for (int t = 0; t < MEL_GROUP_TRIP[i]; ++t) pv[row0 + t] = pb[mel_lo[i] + t];
+        row0 += MEL_GROUP_TRIP[i];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     int row0 = 0;
 #pragma unroll
     for (int i = 0; i < MEL_GROUPS; ++i) {
-      const float* pp = pb + mel_lo[i];
       float acc = 0.f;
 #pragma unroll
-      for (int t = 0; t < MEL_GROUP_TRIP[i]; ++t)
-        acc = fmaf(s_melw[(row0 + t) * 16 + j], pp[t], acc);
+      for (int t = 0; t < MEL_GROUP_TRIP[i]; ++t) acc = fmaf(wv[row0 + t], pv[row0 + t], acc);
       row0 += MEL_GROUP_TRIP[i];
       // natural log of (energy + 2^-24): log2 in hardware (v_log_f32, ~1 ulp)
       // times ln 2
