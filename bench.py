@@ -10,6 +10,7 @@ bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                       [--attention CORE,CONTEXT] [--fused | --ctc] [--precision bf16|fp8]
+                      [--running-max-steps N]
 
 --fused runs the encoder through speaker fusion and the 1280 -> 2688 connector
 (synthetic speaker activity) instead of stopping at the embeddings.
@@ -21,6 +22,11 @@ stopping at the embeddings; flops count the adapter at its real head width.
 --precision fp8 runs the four linear maps of every layer on E4M3 codes with
 per-tensor scales (input scales from the library's calibration on the same
 batch, untimed); GEMM flops are then priced at the fp8 MFMA peak.
+
+--running-max-steps N (default 5) then times N steps of the same workload with
+every layer's QK-norm gains tripled: the score bound then exceeds the fixed
+softmax reference's range and the attention keeps a running maximum; the
+line's "running_max" object gives that step time and its attention time.
 
 --attention encodes each clip in windows of CORE positions with CONTEXT
 positions of context on each side (500,50 are the serving windows, 375,0 the
@@ -192,6 +198,52 @@ def cpu_baseline(audio, lengths, weights, core=0, context=0, budget_s=12.0):
                       f"{spent:.1f} s wall"}
 
 
+def score_log2_bound(lw):
+    """Bound on |q.k| log2(e) / sqrt(w) from a layer's QK-norm parameters (a
+    LayerNorm'd w-vector has norm <= sqrt(w)), with the library's 2^-6 margin;
+    above 64 the attention keeps a running softmax maximum."""
+    w = len(lw["q_g"])
+
+    def norm_bound(g, b):
+        g = np.asarray(g, dtype=np.float64)
+        b = np.asarray(b, dtype=np.float64)
+        return float(np.abs(g).max()) * np.sqrt(w) + float(np.linalg.norm(b))
+    bound = norm_bound(lw["q_g"], lw["q_b"]) * norm_bound(lw["k_g"], lw["k_b"]) * (1 + 1 / 64)
+    return bound * 1.4426950408889634 / np.sqrt(w)
+
+
+def running_max_timing(weights, dtype, core, context, x, lengths, out, steps, stream):
+    """Step time of the same workload with every layer's QK-norm gains tripled
+    (same shapes and work; the attention takes its running-maximum softmax)."""
+    import torch
+    from speech_audio_encoder_amd import binding
+    sharp = dict(weights)
+    sharp["layers"] = [dict(lw, q_g=np.asarray(lw["q_g"]) * 3.0, k_g=np.asarray(lw["k_g"]) * 3.0)
+                       for lw in weights["layers"]]
+    bounds = [score_log2_bound(lw) for lw in sharp["layers"]]
+    enc = binding.Encoder(sharp, dtype=dtype)
+    if core:
+        enc.set_attention(core, context)
+    for _ in range(2):
+        enc.forward(x, lengths, out=out)
+    binding.enc_profile_kernel(enc.ctx, "attention")
+    enc.forward(x, lengths, out=out)
+    n_att, att_ms = binding.enc_profile_read(enc.ctx)
+    binding.enc_profile_kernel(enc.ctx, -1)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        enc.forward(x, lengths, out=out)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    enc.close()
+    return {"qk_gain_scale": 3.0, "min_score_log2_bound": round(min(bounds), 2),
+            "path": "running maximum" if min(bounds) > 64.0 else "fixed reference",
+            "steps": steps, "ms_per_step": round(ev0.elapsed_time(ev1) / steps, 4),
+            "attention_ms_per_step": round(att_ms, 4), "attention_launches": n_att}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -210,6 +262,10 @@ def main():
     ap.add_argument("--no-breakdown", action="store_true",
                     help="skip timing every kernel class (one extra untimed step per "
                          "class); the roofline then takes the FFN-up GEMM")
+    ap.add_argument("--running-max-steps", type=int, default=5,
+                    help="after the timed steps, time this many steps of an encoder whose "
+                         "QK-norm gains are tripled, so that attention keeps a running softmax "
+                         "maximum (0: skip; plain bf16 forward only)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times), "
                          "to scale HBM byte counters")
@@ -388,9 +444,12 @@ def main():
     }
     if breakdown:
         result["kernel_ms_per_step"] = breakdown
+    enc.close()
+    if args.running_max_steps > 0 and not (args.fused or args.ctc or fp8):
+        result["running_max"] = running_max_timing(weights, dtype, core, context, x, lengths, out,
+                                                   args.running_max_steps, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(audio, lengths, weights, core, context)
-    enc.close()
     print(json.dumps(result), flush=True)
 
 
