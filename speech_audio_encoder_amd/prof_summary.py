@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 output for the encoder's kernels.
 
-Two reports, written as Markdown under ``profiles/``:
+Reports, written as Markdown under ``profiles/``:
 
 * ``kernels``: per-kernel calls / total / average duration from a
   ``--kernel-trace`` CSV (``<name>_kernel_trace.csv``);
@@ -9,6 +9,8 @@ Two reports, written as Markdown under ``profiles/``:
   (SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F8, add+mul ops / 512): busy share of
   all SIMDs' cycles while the GPU was active, and executed MFMA flops over
   the dispatch durations against the dtype's dense peak;
+* ``l2``: L2 (TCC) hits and misses per launch of each class from one
+  ``--pmc`` run of TCC_HIT_sum and TCC_MISS_sum;
 * ``traffic``: HBM bytes per dispatch from two ``--pmc`` runs (FETCH_SIZE,
   WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
   for a plain device copy of known size (``bench.py --copy-calibration-mib``),
@@ -20,6 +22,7 @@ Two reports, written as Markdown under ``profiles/``:
 Usage:
   python -m speech_audio_encoder_amd.prof_summary kernels TRACE_CSV OUT_MD "COMMAND"
   python -m speech_audio_encoder_amd.prof_summary mfma COUNTER_CSV AGENT_CSV OUT_MD "COMMAND" [SKIP]
+  python -m speech_audio_encoder_amd.prof_summary l2 COUNTER_CSV OUT_MD "COMMAND"
   python -m speech_audio_encoder_amd.prof_summary traffic WORKLOAD FETCH_CSV WRITE_CSV \\
       COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB OUT_MD "COMMANDS"
 """
@@ -295,6 +298,32 @@ def traffic_report(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_cs
         f.write("\n".join(lines) + "\n")
 
 
+def l2_report(counter_csv, out_md, command):
+    """Per kernel class: L2 (TCC) hits and misses per launch from one --pmc
+    run of TCC_HIT_sum and TCC_MISS_sum, and the hit rate.  A miss goes to
+    the data fabric (the memory-side Infinity Cache, then HBM), so misses
+    bound the fetch traffic of a class from above of what HBM itself serves."""
+    disp = collections.OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        d = disp.setdefault(int(r["Dispatch_Id"]), dict(r))
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    rows = sorted(disp.values(), key=lambda r: int(r["Start_Timestamp"]))
+    lines = ["# L2 hits and misses per kernel class: " + os.path.basename(out_md)[:-3], "",
+             "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+             "TCC_HIT_sum and TCC_MISS_sum summed over the class's dispatches (all eight XCDs' "
+             "L2s), per launch of the class.", "",
+             "| class | launches | L2 hits / launch (M) | L2 misses / launch (M) | hit rate |",
+             "|---|---:|---:|---:|---:|"]
+    for cls, (rs, n) in class_launches(rows).items():
+        hit = sum(r.get("TCC_HIT_sum", 0.0) for r in rs)
+        miss = sum(r.get("TCC_MISS_sum", 0.0) for r in rs)
+        rate = 100.0 * hit / (hit + miss) if hit + miss else 0.0
+        lines.append(f"| {cls} | {n} | {hit / max(n, 1) / 1e6:.2f} | {miss / max(n, 1) / 1e6:.2f} | "
+                     f"{rate:.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def read_traffic(md_path):
     """The JSON record at the end of a traffic report, or None."""
     try:
@@ -311,6 +340,8 @@ if __name__ == "__main__":
     elif sys.argv[1] == "mfma":
         mfma_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5],
                     int(sys.argv[6]) if len(sys.argv) > 6 else 0)
+    elif sys.argv[1] == "l2":
+        l2_report(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "traffic":
         traffic_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                        int(sys.argv[7]), sys.argv[8], sys.argv[9])
