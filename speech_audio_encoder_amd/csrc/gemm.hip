@@ -23,9 +23,10 @@
 //    64-wide K slices of whole 128-byte lines.  The stream of steps runs on
 //    across the workgroup's tiles.
 //  * gemm_piece_kernel (+ splitk_reduce_kernel) -- the tiles left after the
-//    last full round, or the whole product when it has fewer 256 x 256 tiles
-//    than CUs, as 128 x 128 pieces split along K when needed so that every CU
-//    is busy (a 256 x 256 tile per CU would leave most CUs idle).
+//    last full round (and FP8 products with fewer 256 x 256 tiles than CUs),
+//    as 128 x 128 pieces split along K when needed so that every CU is busy.
+//  * gemm_small_kernel (+ gemm_small_reduce) -- bf16 products with fewer
+//    256 x 256 tiles than CUs (few rows), as 64 x 64 pieces.
 //
 // Each lane ends up owning one output row and runs of four consecutive
 // columns: the epilogue adds bias / residual / GELU in registers and stores
@@ -887,6 +888,139 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
                   s.y, s.z, s.w);
 }
 
+// ------------------------------------------------- 64 x 64 pieces (few rows)
+// Whole products with fewer 256 x 256 tiles than CUs (a 30-second clip: 375
+// rows) are cut into 64 x 64 pieces.  That gives every CU work without
+// splitting K for most shapes, so no partial sums are written and no
+// reduction runs.  A workgroup of four wavefronts (32 x 32 outputs each, one
+// accumulator) moves 64-wide K slices of A and W (whole 128-byte lines) into
+// a ring of four 16 KB LDS stages by direct loads, three in flight; the
+// kernel is bound by that data movement, not by its MFMAs.  Products that
+// still leave CUs idle split K, with partial sums and gemm_small_reduce.
+constexpr int SP = 64;    // piece edge
+constexpr int SBK = 64;   // K step
+constexpr int SNS = 4;    // ring stages
+
+template <Epilogue EPI, bool PARTIAL>
+__global__ __launch_bounds__(256, 2) void gemm_small_kernel(
+    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
+    const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, float* __restrict__ part,
+    int64_t M, int K, int pieces_n, int splits) {
+  constexpr int STG = 2 * SP * SBK / 8;   // uint4 per stage: A rows, then W rows (16 KB)
+  __shared__ uint4 st[SNS][STG];
+
+  const int split = blockIdx.x % splits;
+  const int pid = blockIdx.x / splits;
+  const int64_t m0 = (int64_t)(pid / pieces_n) * SP;
+  const int64_t n0 = (int64_t)(pid % pieces_n) * SP;
+  if (m0 >= M) return;
+  const int kc = K / splits;
+  const int kb = split * kc;
+  const int KT = kc / SBK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+
+  // DMA: a stage is 16 blocks of 8 rows x 128 bytes (A rows 0..63, then W
+  // rows 0..63); wave w fills blocks 4w .. 4w+3, lane l the LDS chunk l % 8 of
+  // row l / 8 of a block, which holds global chunk (l % 8) ^ ((row / 2) % 8)
+  // (the XOR keeps the operand reads below conflict-free).
+  const bf16_t* src[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int blk = wave * 4 + t;
+    const int row = (blk & 7) * 8 + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+    src[t] = blk < 8 ? A + min<int64_t>(m0 + row, M - 1) * lda + kb + chunk * 8
+                     : W + (n0 + row) * ldw + kb + chunk * 8;
+  }
+  int ikt = 0;
+  auto issue = [&](int slot) __attribute__((always_inline)) {
+    const int k0 = min(ikt, KT - 1) * SBK;   // past the end: re-read the last step
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      dma16(src[t] + k0, (lds_void*)(&st[slot][0] + (wave * 4 + t) * 64));
+    ++ikt;
+  };
+
+  // operand rows: A row wm*32 + l32, W row wn*32 + l32 (LDS rows of 8 chunks)
+  const int rsw = (l32 >> 1) & 7;
+  const int aofs = (wm * 32 + l32) * 8;
+  const int wofs = SP * 8 + (wn * 32 + l32) * 8;
+  f32x16 acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+
+  constexpr int VM = 4 * (SNS - 2);
+  constexpr int WAIT_STEP = (VM & 15) | ((VM >> 4) << 14) | 0x0070;   // vmcnt(8) lgkmcnt(0)
+#pragma unroll
+  for (int i = 0; i < SNS - 1; ++i) issue(i);
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(WAIT_STEP);   // this step's stage has landed
+    __builtin_amdgcn_s_barrier();            // ... for every wavefront; the oldest stage is free
+    issue((kt + SNS - 1) % SNS);
+    const uint4* sp = st[kt % SNS];
+    bf16x8 fa[4], fw[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int pc = (2 * sl + lhi) ^ rsw;
+      fw[sl] = __builtin_bit_cast(bf16x8, sp[wofs + pc]);
+      fa[sl] = __builtin_bit_cast(bf16x8, sp[aofs + pc]);
+    }
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl], fa[sl], acc, 0, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // loads past the last step land before LDS is released
+
+  const int64_t m = m0 + wm * 32 + l32;
+  const int nw = (int)n0 + wn * 32;
+  if constexpr (PARTIAL) {
+    // partial layout: [pid][split][64 rows][64 cols] fp32
+    float* dst = part + ((int64_t)pid * splits + split) * (SP * SP) + (wm * 32 + l32) * SP + wn * 32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(dst + 8 * q + 4 * lhi) =
+          make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+  } else {
+    float4 bv[4];
+    load_bias32(bias, nw, lhi, bv);
+    if (m < M) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        store4<EPI, false>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], 1.0f, 1.0f, acc[4 * q],
+                           acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    }
+  }
+}
+
+// Sum the split partials of each 64 x 64 piece in split order and apply the
+// epilogue; one thread per 4 consecutive columns.
+template <Epilogue EPI>
+__global__ __launch_bounds__(256) void gemm_small_reduce(const float* __restrict__ part,
+                                                         const float* __restrict__ bias,
+                                                         void* __restrict__ Cv, int64_t ldc,
+                                                         int64_t M, int pieces_n, int splits) {
+  const int pid = blockIdx.y;
+  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // element in the piece
+  const int64_t m = (int64_t)(pid / pieces_n) * SP + e / SP;
+  const int n = (pid % pieces_n) * SP + e % SP;
+  if (m >= M) return;
+  const float* src = part + (int64_t)pid * splits * (SP * SP) + e;
+  float4 s = *reinterpret_cast<const float4*>(src);
+  for (int k = 1; k < splits; ++k) {
+    const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)k * (SP * SP));
+    s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
+  }
+  store4<EPI, false>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), 1.0f, 1.0f, s.x,
+                     s.y, s.z, s.w);
+}
+
 int g_num_cus = 0;
 
 int num_cus() {
@@ -937,6 +1071,36 @@ hipError_t launch_pieces(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t 
   return hipGetLastError();
 }
 
+// Split K (a divisor of K / 64) only while the pieces that hold rows still
+// fit one workgroup per CU and their partial sums fit `part`.
+template <Epilogue EPI>
+hipError_t launch_small(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
+                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
+                        float* part, size_t part_bytes, int cus, hipStream_t stream) {
+  const int pieces_n = N / SP;
+  const int pieces = (int)((M + SP - 1) / SP) * pieces_n;
+  const int units = K / SBK;
+  int splits = 1;
+  for (int sp = 2; sp <= units; ++sp) {
+    if (units % sp) continue;
+    if ((int64_t)pieces * sp > cus) break;
+    if ((size_t)pieces * sp * SP * SP * sizeof(float) > part_bytes) break;
+    splits = sp;
+  }
+  if (splits == 1) {
+    gemm_small_kernel<EPI, false><<<dim3(pieces), dim3(256), 0, stream>>>(
+        A, lda, W, ldw, bias, C, ldc, part, M, K, pieces_n, 1);
+    return hipGetLastError();
+  }
+  gemm_small_kernel<EPI, true><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
+      A, lda, W, ldw, bias, C, ldc, part, M, K, pieces_n, splits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  gemm_small_reduce<EPI><<<dim3(SP * SP / 1024, pieces), dim3(256), 0, stream>>>(
+      part, bias, C, ldc, M, pieces_n, splits);
+  return hipGetLastError();
+}
+
 template <Epilogue EPI, bool F8>
 hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, const float* bias,
                     void* C, int64_t ldc, int64_t M, int N, int K, float* part,
@@ -946,7 +1110,11 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   const int tiles = tiles_m * tiles_n;
   const int cus = num_cus();
   if (tiles < cus) {
-    // Fewer big tiles than CUs: the whole product as 128 x 128 pieces.
+    // Fewer big tiles than CUs: the whole product as 64 x 64 pieces (bf16),
+    // or 128 x 128 pieces (FP8).
+    if constexpr (!F8)
+      return launch_small<EPI>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes, cus,
+                               stream);
     PieceMap pm{1, 0, tiles_m, tiles_n, N / PIECE};
     const int live = (int)((M + PIECE - 1) / PIECE) * (N / PIECE);
     // piece ids cover whole big-tile rows; ids past M return at once
