@@ -22,16 +22,18 @@
 //    the global side by choosing which 16-byte chunk each lane fetches), in
 //    64-wide K slices of whole 128-byte lines.  The stream of steps runs on
 //    across the workgroup's tiles.
-//  * gemm_piece_kernel (+ splitk_reduce_kernel) -- the tiles left after the
-//    last full round (and FP8 products with fewer 256 x 256 tiles than CUs),
-//    as 128 x 128 pieces split along K when needed so that every CU is busy.
-//  * gemm_small_kernel (+ gemm_small_reduce) -- bf16 products with fewer
-//    256 x 256 tiles than CUs (few rows), as 64 x 64 pieces.
+//  * gemm_small_kernel (+ gemm_small_reduce) -- in bf16, the tiles left after
+//    the last full round and the whole product when it has fewer 256 x 256
+//    tiles than CUs (few rows), as 64 x 64 pieces, split along K only when
+//    even these leave CUs idle.
+//  * gemm_piece_kernel (+ splitk_reduce_kernel) -- the same for FP8, as
+//    128 x 128 pieces split along K when needed so that every CU is busy.
 //
 // Each lane ends up owning one output row and runs of four consecutive
 // columns: the epilogue adds bias / residual / GELU in registers and stores
 // 8- or 16-byte vectors.
 
+#include <algorithm>
 #include <cstdlib>
 
 #include "common.h"
@@ -901,19 +903,41 @@ constexpr int SP = 64;    // piece edge
 constexpr int SBK = 64;   // K step
 constexpr int SNS = 4;    // ring stages
 
+// Piece pid's first row and column: mode 0, the sixteen 64 x 64 pieces of
+// each big tile t_begin, t_begin + 1, ...; mode 1, a plain grid of pieces_n
+// pieces per row.
+struct SmallMap {
+  int mode;
+  int t_begin, tiles_m, tiles_n;   // mode 0
+  int pieces_n;                    // mode 1
+};
+
+__device__ __forceinline__ void small_coords(int pid, const SmallMap& sm, int64_t& m0,
+                                             int64_t& n0) {
+  if (sm.mode == 0) {
+    int tm, tn;
+    tile_coords(sm.t_begin + (pid >> 4), sm.tiles_m, sm.tiles_n, tm, tn);
+    m0 = (int64_t)tm * BIG + (pid & 3) * SP;
+    n0 = (int64_t)tn * BIG + ((pid >> 2) & 3) * SP;
+  } else {
+    m0 = (int64_t)(pid / sm.pieces_n) * SP;
+    n0 = (int64_t)(pid % sm.pieces_n) * SP;
+  }
+}
+
 template <Epilogue EPI, bool PARTIAL>
 __global__ __launch_bounds__(256, 2) void gemm_small_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, float* __restrict__ part,
-    int64_t M, int K, int pieces_n, int splits) {
+    int64_t M, int K, SmallMap sm, int splits) {
   constexpr int STG = 2 * SP * SBK / 8;   // uint4 per stage: A rows, then W rows (16 KB)
   __shared__ uint4 st[SNS][STG];
 
   const int split = blockIdx.x % splits;
   const int pid = blockIdx.x / splits;
-  const int64_t m0 = (int64_t)(pid / pieces_n) * SP;
-  const int64_t n0 = (int64_t)(pid % pieces_n) * SP;
-  if (m0 >= M) return;
+  int64_t m0, n0;
+  small_coords(pid, sm, m0, n0);
+  if (m0 >= M) return;   // a piece of the last tile row wholly past M
   const int kc = K / splits;
   const int kb = split * kc;
   const int KT = kc / SBK;
@@ -1005,11 +1029,13 @@ template <Epilogue EPI>
 __global__ __launch_bounds__(256) void gemm_small_reduce(const float* __restrict__ part,
                                                          const float* __restrict__ bias,
                                                          void* __restrict__ Cv, int64_t ldc,
-                                                         int64_t M, int pieces_n, int splits) {
+                                                         int64_t M, SmallMap sm, int splits) {
   const int pid = blockIdx.y;
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // element in the piece
-  const int64_t m = (int64_t)(pid / pieces_n) * SP + e / SP;
-  const int n = (pid % pieces_n) * SP + e % SP;
+  int64_t m0, n0;
+  small_coords(pid, sm, m0, n0);
+  const int64_t m = m0 + e / SP;
+  const int n = (int)n0 + e % SP;
   if (m >= M) return;
   const float* src = part + (int64_t)pid * splits * (SP * SP) + e;
   float4 s = *reinterpret_cast<const float4*>(src);
@@ -1073,31 +1099,31 @@ hipError_t launch_pieces(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t 
 
 // Split K (a divisor of K / 64) only while the pieces that hold rows still
 // fit one workgroup per CU and their partial sums fit `part`.
+// `live` pieces hold rows (of `pieces` launched).
 template <Epilogue EPI>
 hipError_t launch_small(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
-                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
-                        float* part, size_t part_bytes, int cus, hipStream_t stream) {
-  const int pieces_n = N / SP;
-  const int pieces = (int)((M + SP - 1) / SP) * pieces_n;
+                        const float* bias, void* C, int64_t ldc, int64_t M, int K, float* part,
+                        size_t part_bytes, const SmallMap& sm, int live, int pieces, int cus,
+                        hipStream_t stream) {
   const int units = K / SBK;
   int splits = 1;
   for (int sp = 2; sp <= units; ++sp) {
     if (units % sp) continue;
-    if ((int64_t)pieces * sp > cus) break;
+    if ((int64_t)live * sp > cus) break;
     if ((size_t)pieces * sp * SP * SP * sizeof(float) > part_bytes) break;
     splits = sp;
   }
   if (splits == 1) {
     gemm_small_kernel<EPI, false><<<dim3(pieces), dim3(256), 0, stream>>>(
-        A, lda, W, ldw, bias, C, ldc, part, M, K, pieces_n, 1);
+        A, lda, W, ldw, bias, C, ldc, part, M, K, sm, 1);
     return hipGetLastError();
   }
   gemm_small_kernel<EPI, true><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
-      A, lda, W, ldw, bias, C, ldc, part, M, K, pieces_n, splits);
+      A, lda, W, ldw, bias, C, ldc, part, M, K, sm, splits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   gemm_small_reduce<EPI><<<dim3(SP * SP / 1024, pieces), dim3(256), 0, stream>>>(
-      part, bias, C, ldc, M, pieces_n, splits);
+      part, bias, C, ldc, M, sm, splits);
   return hipGetLastError();
 }
 
@@ -1112,9 +1138,11 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   if (tiles < cus) {
     // Fewer big tiles than CUs: the whole product as 64 x 64 pieces (bf16),
     // or 128 x 128 pieces (FP8).
-    if constexpr (!F8)
-      return launch_small<EPI>(A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes, cus,
-                               stream);
+    if constexpr (!F8) {
+      const int pieces = (int)((M + SP - 1) / SP) * (N / SP);
+      return launch_small<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
+                               SmallMap{1, 0, 0, 0, N / SP}, pieces, pieces, cus, stream);
+    }
     PieceMap pm{1, 0, tiles_m, tiles_n, N / PIECE};
     const int live = (int)((M + PIECE - 1) / PIECE) * (N / PIECE);
     // piece ids cover whole big-tile rows; ids past M return at once
@@ -1137,6 +1165,21 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tiles == n_big) return e;
+  if constexpr (!F8) {
+    // the tail tiles as 64 x 64 pieces, sixteen per tile (measured 2.7% per
+    // step faster than 128 x 128 pieces with split K on the 64-clip batch)
+    const int pieces = 16 * (tiles - n_big);
+    int live = 0;
+    for (int t = n_big; t < tiles; ++t) {
+      const int per_group = GROUP_M * tiles_n;
+      const int first_m = (t / per_group) * GROUP_M;
+      const int gsize = std::min(tiles_m - first_m, GROUP_M);
+      const int64_t tm = first_m + (t - (t / per_group) * per_group) % gsize;
+      live += 4 * (int)std::min<int64_t>(4, (M - tm * BIG + SP - 1) / SP);
+    }
+    return launch_small<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
+                             SmallMap{0, n_big, tiles_m, tiles_n, 0}, live, pieces, cus, stream);
+  }
   PieceMap pm{0, n_big, tiles_m, tiles_n, N / PIECE};
   return launch_pieces<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm,
                                 4 * (tiles - n_big), 4 * (tiles - n_big), cus, alpha, oscale,
