@@ -22,12 +22,10 @@
 //    the global side by choosing which 16-byte chunk each lane fetches), in
 //    64-wide K slices of whole 128-byte lines.  The stream of steps runs on
 //    across the workgroup's tiles.
-//  * gemm_small_kernel (+ gemm_small_reduce) -- in bf16, the tiles left after
-//    the last full round and the whole product when it has fewer 256 x 256
+//  * gemm_small_kernel (+ gemm_small_reduce) -- the tiles left after the
+//    last full round, and the whole product when it has fewer 256 x 256
 //    tiles than CUs (few rows), as 64 x 64 pieces, split along K only when
 //    even these leave CUs idle.
-//  * gemm_piece_kernel (+ splitk_reduce_kernel) -- the same for FP8, as
-//    128 x 128 pieces split along K when needed so that every CU is busy.
 //
 // Each lane ends up owning one output row and runs of four consecutive
 // columns: the epilogue adds bias / residual / GELU in registers and stores
@@ -44,7 +42,6 @@ namespace enc {
 namespace {
 
 constexpr int BIG = 256;    // big tile edge
-constexpr int BKS = 32;     // piece kernel K step
 constexpr int GROUP_M = 4;  // tile rows per ordering group
 
 // Exact-erf GELU, x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), with erf taken from
@@ -656,240 +653,6 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-// ------------------------------------------------------- 128 x 128 pieces
-// Work the persistent kernel does not cover -- the tiles left after its last
-// full round, or the whole product when there are fewer 256 x 256 tiles than
-// CUs -- is cut into 128 x 128 pieces, and K into `splits` ranges when that
-// is needed to occupy every CU.  A workgroup (four wavefronts of 64 x 64)
-// takes one (piece, split): the same direct-to-LDS ring as the big kernel,
-// 4 stages of 32-wide K steps (16 KB each), so two workgroups fit on a CU and
-// cover each other's waits.  With one split the epilogue is applied directly;
-// otherwise fp32 partial sums go to `part` and splitk_reduce_kernel adds them
-// in a fixed order (deterministic) and applies the epilogue.
-constexpr int PIECE = 128;
-constexpr int PNS = 4;
-
-struct PieceMap {
-  int mode;       // 0: pieces of leftover big tiles t_begin.., 1: a plain grid
-  int t_begin;    // mode 0
-  int tiles_m, tiles_n;
-  int pieces_n;   // mode 1: pieces per row of pieces (N / 128)
-};
-
-__device__ __forceinline__ void piece_coords(int pid, const PieceMap& pm, int64_t& m0, int64_t& n0) {
-  if (pm.mode == 0) {
-    int tm, tn;
-    tile_coords(pm.t_begin + (pid >> 2), pm.tiles_m, pm.tiles_n, tm, tn);
-    m0 = (int64_t)tm * BIG + (pid & 1) * PIECE;
-    n0 = (int64_t)tn * BIG + ((pid >> 1) & 1) * PIECE;
-  } else {
-    // groups of 8 piece rows, column-major inside a group
-    const int per_group = 8 * pm.pieces_n;
-    const int group = pid / per_group;
-    const int pieces_m = (pm.tiles_m * BIG) / PIECE;   // rounded up to whole big tiles
-    const int first = group * 8;
-    const int gsize = min(pieces_m - first, 8);
-    const int r = pid - group * per_group;
-    m0 = (int64_t)(first + r % gsize) * PIECE;
-    n0 = (int64_t)(r / gsize) * PIECE;
-  }
-}
-
-template <Epilogue EPI, bool PARTIAL, bool F8>
-__global__ __launch_bounds__(256, 2) void gemm_piece_kernel(
-    const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
-    const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, float* __restrict__ part,
-    int64_t M, int K, PieceMap pm, int splits, float alpha, float oscale) {
-  constexpr int STG = 2 * PIECE * BKS / 8;   // uint4 per stage (16 KB)
-  __shared__ uint4 st0[STG];
-  __shared__ uint4 st1[STG];
-  __shared__ uint4 st2[STG];
-  __shared__ uint4 st3[STG];
-  auto stage = [&](int i) -> uint4* {
-    switch (i & 3) {
-      case 0: return st0;
-      case 1: return st1;
-      case 2: return st2;
-      default: return st3;
-    }
-  };
-
-  const int split = blockIdx.x % splits;
-  const int pid = blockIdx.x / splits;
-  int64_t m0, n0;
-  piece_coords(pid, pm, m0, n0);
-  if (m0 >= M) return;   // whole piece past the last row (plain grid rounding)
-  const int kc = K / splits;
-  const int kb = split * kc;
-  const int KT = kc / BKS;   // multiple of PNS
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-  const int l32 = lane & 31;
-  const int lhi = lane >> 5;
-
-  // DMA: wave w loads 2 x 16 rows of A and of W per step (rows (w*2+i)*16 + lane/4).
-  const int drow = wave * 32 + (lane >> 2);
-  // LDS chunk c of row r holds global chunk c ^ ((r / 4) % 4): the operand
-  // reads (16 lanes = 16 consecutive rows of 64 bytes at a time) then touch
-  // every group of four banks once.
-  const int dcol = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
-  const bf16_t* ia[2];
-  const bf16_t* iw[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    ia[i] = A + min<int64_t>(m0 + drow + 16 * i, M - 1) * lda + kb + dcol;
-    iw[i] = W + (n0 + drow + 16 * i) * ldw + kb + dcol;
-  }
-  int ikt = 0;
-  auto issue = [&](uint4* sp) {
-    const int k0 = min(ikt, KT - 1) * BKS;   // past the end: re-read the last step
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      dma16(ia[i] + k0, (lds_void*)(sp + (wave * 2 + i) * 64));
-      dma16(iw[i] + k0, (lds_void*)(sp + PIECE * 4 + (wave * 2 + i) * 64));
-    }
-    ++ikt;
-  };
-
-  const int rsw = (l32 >> 2) & 3;
-  const int wofs = PIECE * 4 + (wn * 64 + l32) * 4;
-  const int aofs = (wm * 64 + l32) * 4;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  constexpr int VM = 4 * (PNS - 2);
-  constexpr int WAIT_STEP = (VM & 15) | ((VM >> 4) << 14) | 0x0070;   // vmcnt(8) lgkmcnt(0)
-#pragma unroll
-  for (int i = 0; i < PNS - 1; ++i) issue(stage(i));
-  for (int kt = 0; kt < KT; kt += PNS) {
-#pragma unroll
-    for (int u = 0; u < PNS; ++u) {
-      __builtin_amdgcn_s_waitcnt(WAIT_STEP);
-      __builtin_amdgcn_s_barrier();
-      issue(stage(u + PNS - 1));
-      const uint4* sp = stage(u);
-      bf16x8 fw[2][2], fa[2][2];
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        const int pc = (2 * sl + lhi) ^ rsw;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const uint4 uw = sp[wofs + i * 128 + pc];
-          fw[sl][i] = *reinterpret_cast<const bf16x8*>(&uw);
-          const uint4 ua = sp[aofs + i * 128 + pc];
-          fa[sl][i] = *reinterpret_cast<const bf16x8*>(&ua);
-        }
-      }
-      if constexpr (F8) {
-        // one 64-code step: the two 16-byte fragments of the bf16 steps
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                __builtin_shufflevector(__builtin_bit_cast(i32x4, fw[0][i]),
-                                        __builtin_bit_cast(i32x4, fw[1][i]), 0, 1, 2, 3, 4, 5, 6,
-                                        7),
-                __builtin_shufflevector(__builtin_bit_cast(i32x4, fa[0][j]),
-                                        __builtin_bit_cast(i32x4, fa[1][j]), 0, 1, 2, 3, 4, 5, 6,
-                                        7),
-                acc[i][j], 0, 0, 0, 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl][i], fa[sl][j], acc[i][j],
-                                                                  0, 0, 0);
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);   // loads past the last step land before LDS is released
-
-  if constexpr (PARTIAL) {
-    // Partial layout: [pid][split][128 rows][128 cols] fp32.
-    float* dst = part + ((int64_t)pid * splits + split) * (PIECE * PIECE);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = wm * 64 + j * 32 + l32;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = wn * 64 + i * 32 + 8 * q + 4 * lhi;
-          *reinterpret_cast<float4*>(dst + r * PIECE + c) =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                          acc[i][j][4 * q + 3]);
-        }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int nw = (int)(n0 + wn * 64 + i * 32);
-      float4 bv[4];
-      load_bias32(bias, nw, lhi, bv);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t m = m0 + wm * 64 + j * 32 + l32;
-        if (m >= M) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          store4<EPI, F8>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], alpha, oscale, acc[i][j][4 * q],
-                      acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-      }
-    }
-  }
-}
-
-// Sum the split partials of each piece (split order 0, 1, ...) and apply the
-// epilogue.  One thread per 4 consecutive columns.
-template <Epilogue EPI, bool F8>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(
-    const float* __restrict__ part, const float* __restrict__ bias, void* __restrict__ Cv,
-    int64_t ldc, int64_t M, PieceMap pm, int splits, float alpha, float oscale) {
-  const int pid = blockIdx.y;
-  int64_t m0, n0;
-  piece_coords(pid, pm, m0, n0);
-  const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // element in the piece
-  const int r = e / PIECE, c = e % PIECE;
-  const int64_t m = m0 + r;
-  const int n = (int)n0 + c;
-  if (m >= M) return;
-  const float* src = part + (int64_t)pid * splits * (PIECE * PIECE) + e;
-  // eight partials in flight at a time, summed in split order
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = 0; k0 < splits; k0 += 8) {
-    float4 t[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k0 + k < splits)
-        t[k] = *reinterpret_cast<const float4*>(src + (int64_t)(k0 + k) * (PIECE * PIECE));
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (k0 + k < splits) {
-        if (k0 + k == 0) {
-          s = t[k];
-        } else {
-          s.x += t[k].x; s.y += t[k].y; s.z += t[k].z; s.w += t[k].w;
-        }
-      }
-  }
-  store4<EPI, F8>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), alpha, oscale, s.x,
-                  s.y, s.z, s.w);
-}
-
 // ------------------------------------------------- 64 x 64 pieces (few rows)
 // Whole products with fewer 256 x 256 tiles than CUs (a 30-second clip: 375
 // rows) are cut into 64 x 64 pieces.  That gives every CU work without
@@ -925,11 +688,13 @@ __device__ __forceinline__ void small_coords(int pid, const SmallMap& sm, int64_
   }
 }
 
-template <Epilogue EPI, bool PARTIAL>
+// F8: E4M3 codes moved as pairs (K, lda, ldw in units of two codes), as in
+// the other kernels; a 64-code MFMA takes the fragments of two bf16 k-steps.
+template <Epilogue EPI, bool PARTIAL, bool F8>
 __global__ __launch_bounds__(256, 2) void gemm_small_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, float* __restrict__ part,
-    int64_t M, int K, SmallMap sm, int splits) {
+    int64_t M, int K, SmallMap sm, int splits, float alpha, float oscale) {
   constexpr int STG = 2 * SP * SBK / 8;   // uint4 per stage: A rows, then W rows (16 KB)
   __shared__ uint4 st[SNS][STG];
 
@@ -996,9 +761,20 @@ __global__ __launch_bounds__(256, 2) void gemm_small_kernel(
       fw[sl] = __builtin_bit_cast(bf16x8, sp[wofs + pc]);
       fa[sl] = __builtin_bit_cast(bf16x8, sp[aofs + pc]);
     }
+    if constexpr (F8) {
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl], fa[sl], acc, 0, 0, 0);
+      for (int h = 0; h < 2; ++h)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            __builtin_shufflevector(__builtin_bit_cast(i32x4, fw[2 * h]),
+                                    __builtin_bit_cast(i32x4, fw[2 * h + 1]), 0, 1, 2, 3, 4, 5, 6, 7),
+            __builtin_shufflevector(__builtin_bit_cast(i32x4, fa[2 * h]),
+                                    __builtin_bit_cast(i32x4, fa[2 * h + 1]), 0, 1, 2, 3, 4, 5, 6, 7),
+            acc, 0, 0, 0, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl], fa[sl], acc, 0, 0, 0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);   // loads past the last step land before LDS is released
 
@@ -1017,19 +793,20 @@ __global__ __launch_bounds__(256, 2) void gemm_small_kernel(
     if (m < M) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        store4<EPI, false>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], 1.0f, 1.0f, acc[4 * q],
-                           acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        store4<EPI, F8>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], alpha, oscale, acc[4 * q],
+                        acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
     }
   }
 }
 
 // Sum the split partials of each 64 x 64 piece in split order and apply the
 // epilogue; one thread per 4 consecutive columns.
-template <Epilogue EPI>
+template <Epilogue EPI, bool F8>
 __global__ __launch_bounds__(256) void gemm_small_reduce(const float* __restrict__ part,
                                                          const float* __restrict__ bias,
                                                          void* __restrict__ Cv, int64_t ldc,
-                                                         int64_t M, SmallMap sm, int splits) {
+                                                         int64_t M, SmallMap sm, int splits,
+                                                         float alpha, float oscale) {
   const int pid = blockIdx.y;
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // element in the piece
   int64_t m0, n0;
@@ -1043,8 +820,8 @@ __global__ __launch_bounds__(256) void gemm_small_reduce(const float* __restrict
     const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)k * (SP * SP));
     s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
   }
-  store4<EPI, false>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), 1.0f, 1.0f, s.x,
-                     s.y, s.z, s.w);
+  store4<EPI, F8>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), alpha, oscale, s.x,
+                  s.y, s.z, s.w);
 }
 
 int g_num_cus = 0;
@@ -1061,50 +838,14 @@ int num_cus() {
   return g_num_cus;
 }
 
-// Split K (into a divisor of K / 128 ranges) as far as the pieces that hold
-// rows stay within one workgroup per CU (measured: two per CU, with twice the
-// partial sums to write and reduce, was 2% slower per encoder step), and the
-// partial sums of every piece id within the partial buffer.
-int choose_splits(int live_pieces, int grid_pieces, int K, int cus, size_t part_bytes) {
-  const int units = K / (BKS * PNS);
-  int splits = 1;
-  for (int sp = 2; sp <= units; ++sp) {
-    if (units % sp) continue;
-    if ((int64_t)live_pieces * sp > cus) break;
-    if ((size_t)grid_pieces * sp * PIECE * PIECE * sizeof(float) > part_bytes) break;
-    splits = sp;
-  }
-  return splits;
-}
-
-template <Epilogue EPI, bool F8>
-hipError_t launch_pieces(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
-                         const float* bias, void* C, int64_t ldc, int64_t M, int K, float* part,
-                         size_t part_bytes, const PieceMap& pm, int live_pieces, int pieces,
-                         int cus, float alpha, float oscale, hipStream_t stream) {
-  const int splits = choose_splits(live_pieces, pieces, K, cus, part_bytes);
-  if (splits == 1) {
-    gemm_piece_kernel<EPI, false, F8><<<dim3(pieces), dim3(256), 0, stream>>>(
-        A, lda, W, ldw, bias, C, ldc, part, M, K, pm, 1, alpha, oscale);
-    return hipGetLastError();
-  }
-  gemm_piece_kernel<EPI, true, F8><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
-      A, lda, W, ldw, bias, C, ldc, part, M, K, pm, splits, alpha, oscale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  splitk_reduce_kernel<EPI, F8><<<dim3(PIECE * PIECE / 1024, pieces), dim3(256), 0, stream>>>(
-      part, bias, C, ldc, M, pm, splits, alpha, oscale);
-  return hipGetLastError();
-}
-
 // Split K (a divisor of K / 64) only while the pieces that hold rows still
 // fit one workgroup per CU and their partial sums fit `part`.
 // `live` pieces hold rows (of `pieces` launched).
-template <Epilogue EPI>
+template <Epilogue EPI, bool F8>
 hipError_t launch_small(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                         const float* bias, void* C, int64_t ldc, int64_t M, int K, float* part,
                         size_t part_bytes, const SmallMap& sm, int live, int pieces, int cus,
-                        hipStream_t stream) {
+                        float alpha, float oscale, hipStream_t stream) {
   const int units = K / SBK;
   int splits = 1;
   for (int sp = 2; sp <= units; ++sp) {
@@ -1114,16 +855,16 @@ hipError_t launch_small(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t l
     splits = sp;
   }
   if (splits == 1) {
-    gemm_small_kernel<EPI, false><<<dim3(pieces), dim3(256), 0, stream>>>(
-        A, lda, W, ldw, bias, C, ldc, part, M, K, sm, 1);
+    gemm_small_kernel<EPI, false, F8><<<dim3(pieces), dim3(256), 0, stream>>>(
+        A, lda, W, ldw, bias, C, ldc, part, M, K, sm, 1, alpha, oscale);
     return hipGetLastError();
   }
-  gemm_small_kernel<EPI, true><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
-      A, lda, W, ldw, bias, C, ldc, part, M, K, sm, splits);
+  gemm_small_kernel<EPI, true, F8><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
+      A, lda, W, ldw, bias, C, ldc, part, M, K, sm, splits, alpha, oscale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  gemm_small_reduce<EPI><<<dim3(SP * SP / 1024, pieces), dim3(256), 0, stream>>>(
-      part, bias, C, ldc, M, sm, splits);
+  gemm_small_reduce<EPI, F8><<<dim3(SP * SP / 1024, pieces), dim3(256), 0, stream>>>(
+      part, bias, C, ldc, M, sm, splits, alpha, oscale);
   return hipGetLastError();
 }
 
@@ -1136,21 +877,13 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   const int tiles = tiles_m * tiles_n;
   const int cus = num_cus();
   if (tiles < cus) {
-    // Fewer big tiles than CUs: the whole product as 64 x 64 pieces (bf16),
-    // or 128 x 128 pieces (FP8).
-    if constexpr (!F8) {
-      const int pieces = (int)((M + SP - 1) / SP) * (N / SP);
-      return launch_small<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
-                               SmallMap{1, 0, 0, 0, N / SP}, pieces, pieces, cus, stream);
-    }
-    PieceMap pm{1, 0, tiles_m, tiles_n, N / PIECE};
-    const int live = (int)((M + PIECE - 1) / PIECE) * (N / PIECE);
-    // piece ids cover whole big-tile rows; ids past M return at once
-    const int grid_pieces = ((tiles_m * BIG) / PIECE) * (N / PIECE);
-    return launch_pieces<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm, live,
-                                  grid_pieces, cus, alpha, oscale, stream);
+    // Fewer big tiles than CUs: the whole product as 64 x 64 pieces.
+    const int pieces = (int)((M + SP - 1) / SP) * (N / SP);
+    return launch_small<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
+                                 SmallMap{1, 0, 0, 0, N / SP}, pieces, pieces, cus, alpha, oscale,
+                                 stream);
   }
-  // Full rounds go to the persistent kernel, the remainder to 128 x 128 pieces.
+  // Full rounds go to the persistent kernel, the remainder to 64 x 64 pieces.
   const int n_big = (tiles / cus) * cus;
   if constexpr (EPI == Epilogue::kBiasResidualF32 && !F8) {
     if (n_big == cus)   // one round: every CU holds exactly one tile
@@ -1165,25 +898,21 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || tiles == n_big) return e;
-  if constexpr (!F8) {
-    // the tail tiles as 64 x 64 pieces, sixteen per tile (measured 2.7% per
-    // step faster than 128 x 128 pieces with split K on the 64-clip batch)
-    const int pieces = 16 * (tiles - n_big);
-    int live = 0;
-    for (int t = n_big; t < tiles; ++t) {
-      const int per_group = GROUP_M * tiles_n;
-      const int first_m = (t / per_group) * GROUP_M;
-      const int gsize = std::min(tiles_m - first_m, GROUP_M);
-      const int64_t tm = first_m + (t - (t / per_group) * per_group) % gsize;
-      live += 4 * (int)std::min<int64_t>(4, (M - tm * BIG + SP - 1) / SP);
-    }
-    return launch_small<EPI>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
-                             SmallMap{0, n_big, tiles_m, tiles_n, 0}, live, pieces, cus, stream);
+  // The tail tiles as 64 x 64 pieces, sixteen per tile (measured 2.7% per
+  // step faster in bf16, 3.3% in FP8, than 128 x 128 pieces with split K on
+  // the 64-clip batch).
+  const int pieces = 16 * (tiles - n_big);
+  int live = 0;
+  for (int t = n_big; t < tiles; ++t) {
+    const int per_group = GROUP_M * tiles_n;
+    const int first_m = (t / per_group) * GROUP_M;
+    const int gsize = std::min(tiles_m - first_m, GROUP_M);
+    const int64_t tm = first_m + (t - (t / per_group) * per_group) % gsize;
+    live += 4 * (int)std::min<int64_t>(4, (M - tm * BIG + SP - 1) / SP);
   }
-  PieceMap pm{0, n_big, tiles_m, tiles_n, N / PIECE};
-  return launch_pieces<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes, pm,
-                                4 * (tiles - n_big), 4 * (tiles - n_big), cus, alpha, oscale,
-                                stream);
+  return launch_small<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
+                               SmallMap{0, n_big, tiles_m, tiles_n, 0}, live, pieces, cus, alpha,
+                               oscale, stream);
 }
 
 template <bool F8>
@@ -1214,7 +943,7 @@ hipError_t launch_cols(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t*
 }
 
 // Whole 256-column tiles first; a last strip of 128 columns (N % 256 == 128)
-// is a product of its own on the piece kernel.  c_elem: bytes per C element.
+// is a product of its own (on the 64 x 64 pieces).  c_elem: bytes per C element.
 template <bool F8>
 hipError_t launch_split_n(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W,
                           int64_t ldw, const float* bias, void* C, int64_t ldc, int64_t M, int N,
@@ -1237,7 +966,9 @@ hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t*
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                        float* part, size_t part_bytes, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  if (N <= 0 || N % PIECE != 0 || K % (BKS * 8) != 0 || epi == Epilogue::kBiasGeluFp8)
+  // N in 128-column strips, K in whole 64-wide steps of both kernels (the
+  // documented contract asks K % 256 == 0)
+  if (N <= 0 || N % 128 != 0 || K % 256 != 0 || epi == Epilogue::kBiasGeluFp8)
     return hipErrorInvalidValue;
   const size_t c_elem = (epi == Epilogue::kBiasBf16 || epi == Epilogue::kBiasGeluBf16) ? 2 : 4;
   return launch_split_n<false>(epi, A, lda, W, ldw, bias, C, ldc, M, N, K, part, part_bytes, 1.0f,
@@ -1249,9 +980,9 @@ hipError_t launch_gemm_fp8(Epilogue epi, const uint8_t* A, int64_t lda, const ui
                            int64_t ldc, int64_t M, int N, int K, float* part, size_t part_bytes,
                            hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  // Codes are moved as pairs (bf16-sized units): K / 2 must be a multiple of
-  // the piece kernel's split unit (BKS * PNS) and the strides even.
-  if (N <= 0 || N % PIECE != 0 || K % (2 * BKS * PNS) != 0 || (lda & 1) || (ldw & 1) ||
+  // Codes are moved as pairs (bf16-sized units): K / 2 must be a whole number
+  // of 64-wide steps (K % 256 codes, as documented) and the strides even.
+  if (N <= 0 || N % 128 != 0 || K % 256 != 0 || (lda & 1) || (ldw & 1) ||
       epi == Epilogue::kBiasGeluBf16)
     return hipErrorInvalidValue;
   const size_t c_elem = epi == Epilogue::kBiasGeluFp8 ? 1 : epi == Epilogue::kBiasBf16 ? 2 : 4;

@@ -108,7 +108,7 @@ hipError_t launch_final_norm(const float* x, const float* g, const float* b, con
                              hipStream_t stream);
 
 // FP8 variant: A [M, K] and W [N, K] hold E4M3 codes (row strides lda, ldw in
-// bytes, both even; K % 128 == 0, N % 128 == 0); C (op)= acc * alpha + bias
+// bytes, both even; K % 256 == 0, N % 128 == 0); C (op)= acc * alpha + bias
 // with the epilogues above (kBiasGeluFp8 writes E4M3 codes of
 // gelu(.) * out_scale, saturated at +-448); ldc counts elements of C (bytes
 // for E4M3 output).
