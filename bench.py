@@ -124,6 +124,33 @@ def kernel_bytes(name, rows, lengths):
     }.get(name)
 
 
+def class_rooflines(breakdown, rows, pos, lengths, clip_rows, fp8):
+    """Each timed kernel class against its own bounds: algorithmic TFLOP/s
+    over the MFMA peak (matrix-core classes) and algorithmic bytes / s over
+    the HBM peak (row kernels; attention, which is both, gets both: q, k, v
+    read and its output written once)."""
+    out = {}
+    for k, b in breakdown.items():
+        if not b["launches"] or b["ms"] <= 0:
+            continue
+        t = b["ms"] / b["launches"] / 1000.0
+        rec = {"us_per_launch": round(1e6 * t, 2)}
+        fl = kernel_flops(k, rows, pos, clip_rows)
+        if fl is not None:
+            peak = PEAK_FP8_TFLOPS if fp8 and k in ("gemm_qkv", "gemm_o", "gemm_up",
+                                                    "gemm_down") else PEAK_BF16_TFLOPS
+            rec["tflops"] = round(fl / t / 1e12, 1)
+            rec["frac_mfma"] = round(fl / t / 1e12 / peak, 4)
+        by = kernel_bytes(k, rows, lengths)
+        if k == "attention":
+            by = 4 * rows * D * 2
+        if by is not None:
+            rec["tbps"] = round(by / t / 1e12, 3)
+            rec["frac_hbm"] = round(by / t / 1e9 / PEAK_HBM_GBS, 4)
+        out[k] = rec
+    return out
+
+
 def gemm_bytes(name, rows, fp8=False):
     """Algorithmic HBM bytes of one GEMM launch: A and W read once, C written
     once (bf16, E4M3 for the FP8 path's GELU output, or fp32 read+write for
@@ -444,6 +471,8 @@ def main():
     }
     if breakdown:
         result["kernel_ms_per_step"] = breakdown
+        result["class_rooflines"] = class_rooflines(breakdown, rows, pos, lengths,
+                                                    sum(clip_pos), fp8)
     enc.close()
     if args.running_max_steps > 0 and not (args.fused or args.ctc or fp8):
         result["running_max"] = running_max_timing(weights, dtype, core, context, x, lengths, out,
