@@ -271,6 +271,27 @@ def running_max_timing(weights, dtype, core, context, x, lengths, out, steps, st
             "attention_ms_per_step": round(att_ms, 4), "attention_launches": n_att}
 
 
+def peak_probe(roof, nbytes=1 << 30, reps=5):
+    """What the device sustains (the library's probe kernels: back-to-back bf16
+    MFMAs on register operands, and a device copy of 1 GiB), with the dominant
+    kernel's achieved rate as a fraction of it."""
+    import torch
+    from speech_audio_encoder_amd import binding
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    tflops, gbs = binding.enc_probe_peaks(dst, src, reps)
+    del src, dst
+    out = {"mfma_bf16_tflops": round(tflops, 1), "copy_gbs": round(gbs, 1),
+           "copy_bytes": nbytes,
+           "note": "register-only dense bf16 MFMA loop on every SIMD; device copy, "
+                   "bytes read + written"}
+    if roof.get("unit") == "TFLOP/s" and roof.get("peak") == PEAK_BF16_TFLOPS:
+        out["dominant_frac_of_measured"] = round(roof["achieved"] / tflops, 4)
+    elif roof.get("unit") == "GB/s":
+        out["dominant_frac_of_measured"] = round(roof["achieved"] / gbs, 4)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +314,8 @@ def main():
                     help="after the timed steps, time this many steps of an encoder whose "
                          "QK-norm gains are tripled, so that attention keeps a running softmax "
                          "maximum (0: skip; plain bf16 forward only)")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip measuring the device's sustained MFMA rate and copy bandwidth")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (5 times), "
                          "to scale HBM byte counters")
@@ -477,6 +500,8 @@ def main():
     if args.running_max_steps > 0 and not (args.fused or args.ctc or fp8):
         result["running_max"] = running_max_timing(weights, dtype, core, context, x, lengths, out,
                                                    args.running_max_steps, stream)
+    if not args.no_peak_probe:
+        result["measured_peaks"] = peak_probe(roof)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(audio, lengths, weights, core, context)
     print(json.dumps(result), flush=True)

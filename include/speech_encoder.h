@@ -429,6 +429,26 @@ const char* enc_last_error(void);
 int enc_profile_kernel(enc_ctx* ctx, int32_t kernel_id);
 int enc_profile_read(enc_ctx* ctx, int64_t* launches, double* total_ms);
 
+/*
+ * enc_probe_peaks: what this device sustains, measured, as context for the
+ * roofline fractions of the encoder's kernels (the published MI355X peaks,
+ * 2.5 PFLOP/s dense bf16 and 8 TB/s, assume the peak clock and ideal DRAM
+ * efficiency).  Not part of the encoder.
+ *   (a) a register-only kernel of back-to-back dense bf16 MFMAs
+ *       (v_mfma_f32_32x32x16_bf16, eight independent accumulators per
+ *       wavefront, two wavefronts per SIMD on every CU) -> *mfma_tflops,
+ *       dense bf16 TFLOP/s;
+ *   (b) a device copy of `bytes` bytes from src to dst, 16 bytes per lane
+ *       -> *copy_gbs, bytes read plus bytes written per second, in GB/s.
+ * Each runs once untimed, then `reps` times between two HIP events on
+ * `stream` (NULL: the default stream); the call waits for them.
+ * dst, src: caller-owned device buffers of `bytes` bytes, bytes % 16 == 0,
+ * bytes >= 1 MiB; dst's contents are overwritten (it also receives the MFMA
+ * kernel's sums).  reps >= 1.  Errors: ENC_ERR_ARG, ENC_ERR_HIP.
+ */
+int enc_probe_peaks(void* dst, const void* src, size_t bytes, int32_t reps, void* stream,
+                    double* mfma_tflops, double* copy_gbs);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,7 @@ back to anything else.
 
 Function names follow the C calls: ``enc_create``, ``enc_logmel``,
 ``enc_forward``, ``enc_destroy``, ``enc_shapes``, ``enc_workspace_bytes``,
-``enc_last_error``, ``enc_profile_kernel``, ``enc_profile_read``.
+``enc_last_error``, ``enc_profile_kernel``, ``enc_profile_read``, ``enc_probe_peaks``.
 """
 
 import ctypes
@@ -31,7 +31,8 @@ EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_forward_noalloc", "en
            "enc_set_connector",
            "enc_forward_fused", "enc_set_precision", "enc_calibrate", "enc_set_ctc",
            "enc_forward_ctc", "enc_fp8_input_scales", "enc_destroy", "enc_shapes",
-           "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read"]
+           "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read",
+           "enc_probe_peaks"]
 
 ENC_PREC_BF16 = 0
 ENC_PREC_FP8 = 1
@@ -121,6 +122,10 @@ def load_library(path=LIB_PATH):
                                          ctypes.POINTER(ctypes.c_float)]
     lib.enc_profile_kernel.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     lib.enc_profile_read.argtypes = [ctypes.c_void_p, i64p, ctypes.POINTER(ctypes.c_double)]
+    lib.enc_probe_peaks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]
     for name in EXPORTS:
         if name not in ("enc_destroy", "enc_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -408,6 +413,20 @@ def enc_profile_read(ctx):
     _check(load_library().enc_profile_read(ctypes.c_void_p(ctx), ctypes.byref(n),
                                            ctypes.byref(ms)))
     return n.value, ms.value
+
+
+def enc_probe_peaks(dst, src, reps=5, stream=None):
+    """(dense bf16 MFMA TFLOP/s, device-copy GB/s) measured on this device;
+    dst and src are same-sized device tensors (>= 1 MiB, dst overwritten)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not (dst.is_cuda and src.is_cuda):
+        raise ValueError("dst and src must be device tensors of the same size")
+    tf, gbs = ctypes.c_double(), ctypes.c_double()
+    _check(load_library().enc_probe_peaks(ctypes.c_void_p(dst.data_ptr()),
+                                          ctypes.c_void_p(src.data_ptr()), nbytes, int(reps),
+                                          _stream_handle(stream), ctypes.byref(tf),
+                                          ctypes.byref(gbs)))
+    return tf.value, gbs.value
 
 
 class Encoder:

@@ -24,6 +24,7 @@
 #include "../../include/speech_encoder.h"
 #include "common.h"
 #include "kernels.h"
+#include "peak.h"
 
 using namespace enc;
 
@@ -1360,6 +1361,48 @@ int enc_profile_read(enc_ctx* ctx, int64_t* launches, double* total_ms) {
   *launches = (int64_t)(ctx->prof_used / 2);
   *total_ms = sum;
   ctx->prof_used = 0;
+  return ENC_OK;
+}
+
+int enc_probe_peaks(void* dst, const void* src, size_t bytes, int32_t reps, void* stream_v,
+                    double* mfma_tflops, double* copy_gbs) {
+  if (!dst || !src || !mfma_tflops || !copy_gbs)
+    return fail(ENC_ERR_ARG, "NULL argument");
+  if (bytes % 16 != 0 || bytes < ((size_t)1 << 20) || reps < 1)
+    return fail(ENC_ERR_ARG, "bytes must be a multiple of 16 and >= 1 MiB, reps >= 1");
+  hipStream_t stream = (hipStream_t)stream_v;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  const int grid = 2 * cus;   // eight wavefronts per CU: two per SIMD
+  if ((size_t)grid * 256 * sizeof(float) > bytes) return fail(ENC_ERR_ARG, "dst too small");
+  const int iters = 20000;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  e = hipEventCreate(&ev[0]);
+  if (e == hipSuccess) e = hipEventCreate(&ev[1]);
+  auto timed = [&](auto&& launch, double* ms) -> hipError_t {
+    hipError_t r = launch();   // untimed first run
+    if (r != hipSuccess) return r;
+    r = hipEventRecord(ev[0], stream);
+    for (int i = 0; r == hipSuccess && i < reps; ++i) r = launch();
+    if (r == hipSuccess) r = hipEventRecord(ev[1], stream);
+    if (r == hipSuccess) r = hipEventSynchronize(ev[1]);
+    float t = 0.f;
+    if (r == hipSuccess) r = hipEventElapsedTime(&t, ev[0], ev[1]);
+    *ms = t;
+    return r;
+  };
+  double ms_mfma = 0.0, ms_copy = 0.0;
+  if (e == hipSuccess)
+    e = timed([&] { return launch_mfma_loop((float*)dst, grid, iters, stream); }, &ms_mfma);
+  if (e == hipSuccess)
+    e = timed([&] { return launch_copy16(dst, src, bytes, stream); }, &ms_copy);
+  for (hipEvent_t x : ev)
+    if (x) (void)hipEventDestroy(x);
+  if (e != hipSuccess) return hip_fail(e, "peak probes");
+  *mfma_tflops = (double)mfma_loop_flops(grid, iters) * reps / (ms_mfma * 1e-3) / 1e12;
+  *copy_gbs = 2.0 * (double)bytes * reps / (ms_copy * 1e-3) / 1e9;
   return ENC_OK;
 }
 

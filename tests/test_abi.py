@@ -114,3 +114,19 @@ def test_fp8_input_scales_host_call(lib):
     for bad in (-1.0, np.inf, np.nan):
         with pytest.raises(binding.EncoderError):
             binding.scales_from_amax(np.array([1.0, bad], np.float32))
+
+
+def test_probe_peaks_argument_errors(lib):
+    # checked on the host before anything reaches the device
+    tf, gbs = ctypes.c_double(), ctypes.c_double()
+    buf = ctypes.c_void_p(16)   # never dereferenced: every call below fails its checks
+    assert lib.enc_probe_peaks(None, buf, 1 << 20, 1, None, ctypes.byref(tf),
+                               ctypes.byref(gbs)) == binding.ENC_ERR_ARG
+    assert lib.enc_probe_peaks(buf, buf, (1 << 20) + 8, 1, None, ctypes.byref(tf),
+                               ctypes.byref(gbs)) == binding.ENC_ERR_ARG
+    assert lib.enc_probe_peaks(buf, buf, 1 << 19, 1, None, ctypes.byref(tf),
+                               ctypes.byref(gbs)) == binding.ENC_ERR_ARG
+    assert lib.enc_probe_peaks(buf, buf, 1 << 20, 0, None, ctypes.byref(tf),
+                               ctypes.byref(gbs)) == binding.ENC_ERR_ARG
+    assert lib.enc_probe_peaks(buf, buf, 1 << 20, 1, None, None,
+                               ctypes.byref(gbs)) == binding.ENC_ERR_ARG
