@@ -5,8 +5,10 @@ resident in HBM: log-mel frontend, 8-frame stack, input projection, 32
 Transformer layers, final norm (bf16 operands, fp32 accumulation).  Prints one
 JSON line with audio-seconds encoded per second, the achieved fraction of the
 bf16 MFMA peak, the roofline of the dominant kernel (timed with HIP events on
-the library's stream during the timed steps) and the CPU oracle timed on a
-bounded sample of the same workload.
+the library's stream during the timed steps), the device's measured ceilings
+(``measured_peaks``: a register-only bf16 MFMA loop and a 1 GiB device copy,
+the library's probe kernels; ``--no-peak-probe`` skips them) and the CPU
+oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                       [--attention CORE,CONTEXT] [--fused | --ctc] [--precision bf16|fp8]
