@@ -11,6 +11,10 @@ Reports, written as Markdown under ``profiles/``:
   the dispatch durations against the dtype's dense peak;
 * ``l2``: L2 (TCC) hits and misses per launch of each class from one
   ``--pmc`` run of TCC_HIT_sum and TCC_MISS_sum;
+* ``lds``: LDS instructions, LDS active share, bank-conflict cycles and MFMA
+  busy share per class from one ``--pmc`` run of SQ_INSTS_LDS,
+  SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT, SQ_VALU_MFMA_BUSY_CYCLES and
+  GRBM_GUI_ACTIVE;
 * ``traffic``: HBM bytes per dispatch from two ``--pmc`` runs (FETCH_SIZE,
   WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
   for a plain device copy of known size (``bench.py --copy-calibration-mib``),
@@ -23,6 +27,7 @@ Usage:
   python -m speech_audio_encoder_amd.prof_summary kernels TRACE_CSV OUT_MD "COMMAND"
   python -m speech_audio_encoder_amd.prof_summary mfma COUNTER_CSV AGENT_CSV OUT_MD "COMMAND" [SKIP]
   python -m speech_audio_encoder_amd.prof_summary l2 COUNTER_CSV OUT_MD "COMMAND"
+  python -m speech_audio_encoder_amd.prof_summary lds COUNTER_CSV AGENT_CSV OUT_MD "COMMAND"
   python -m speech_audio_encoder_amd.prof_summary traffic WORKLOAD FETCH_CSV WRITE_CSV \\
       COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB OUT_MD "COMMANDS"
 """
@@ -324,6 +329,47 @@ def l2_report(counter_csv, out_md, command):
         f.write("\n".join(lines) + "\n")
 
 
+def lds_report(counter_csv, agent_csv, out_md, command):
+    """Per kernel class: LDS and matrix-core activity from one --pmc run of
+    SQ_INSTS_LDS, SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT,
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE.  The LDS counters are summed
+    over the CUs, the MFMA counter over the SIMDs and GRBM_GUI_ACTIVE over the
+    XCDs, so a share is the counter / (GRBM_GUI_ACTIVE / XCDs x units)."""
+    agent = [r for r in csv.DictReader(open(agent_csv)) if int(r.get("Simd_Count") or 0) > 0][0]
+    n_simd, n_xcd = int(agent["Simd_Count"]), int(agent["Num_Xcc"])
+    n_cu = n_simd // 4
+    disp = collections.OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        d = disp.setdefault(int(r["Dispatch_Id"]), dict(r))
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    rows = sorted(disp.values(), key=lambda r: int(r["Start_Timestamp"]))
+    lines = ["# LDS and MFMA activity per kernel class: " + os.path.basename(out_md)[:-3], "",
+             "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+             f"Agent: {agent.get('Name', '')}, {n_cu} CUs ({n_simd} SIMDs) in {n_xcd} XCDs.  "
+             "LDS active = SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / XCDs x CUs): the share of "
+             "the class's time the LDS of an average CU spends on indexed reads and writes; "
+             "conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; MFMA busy as in the MFMA "
+             "report.", "",
+             "| class | launches | avg us | LDS instr / launch (M) | LDS active | "
+             "bank-conflict cycles | MFMA busy |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    for cls, (rs, n) in class_launches(rows).items():
+        gui = sum(r.get("GRBM_GUI_ACTIVE", 0.0) for r in rs)
+        act = sum(r.get("SQ_LDS_IDX_ACTIVE", 0.0) for r in rs)
+        conf = sum(r.get("SQ_LDS_BANK_CONFLICT", 0.0) for r in rs)
+        ins = sum(r.get("SQ_INSTS_LDS", 0.0) for r in rs)
+        busy = sum(r.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for r in rs)
+        t_us = sum(_dur_us(r) for r in rs)
+        per_unit = gui / n_xcd if gui else 0.0
+        lds = 100.0 * act / (per_unit * n_cu) if per_unit else 0.0
+        mf = 100.0 * busy / (per_unit * n_simd) if per_unit else 0.0
+        cf = 100.0 * conf / act if act else 0.0
+        lines.append(f"| {cls} | {n} | {t_us / max(n, 1):.1f} | {ins / max(n, 1) / 1e6:.2f} | "
+                     f"{lds:.1f}% | {cf:.1f}% | {mf:.1f}% |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def read_traffic(md_path):
     """The JSON record at the end of a traffic report, or None."""
     try:
@@ -342,6 +388,8 @@ if __name__ == "__main__":
                     int(sys.argv[6]) if len(sys.argv) > 6 else 0)
     elif sys.argv[1] == "l2":
         l2_report(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "lds":
+        lds_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     elif sys.argv[1] == "traffic":
         traffic_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6],
                        int(sys.argv[7]), sys.argv[8], sys.argv[9])
