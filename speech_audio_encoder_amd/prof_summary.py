@@ -15,6 +15,8 @@ Reports, written as Markdown under ``profiles/``:
   busy share per class from one ``--pmc`` run of SQ_INSTS_LDS,
   SQ_LDS_IDX_ACTIVE, SQ_LDS_BANK_CONFLICT, SQ_VALU_MFMA_BUSY_CYCLES and
   GRBM_GUI_ACTIVE;
+* ``counters``: any counters of one ``--pmc`` run per launch of each class
+  (derived ``*Latency`` counters averaged over the dispatches);
 * ``traffic``: HBM bytes per dispatch from two ``--pmc`` runs (FETCH_SIZE,
   WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads
   for a plain device copy of known size (``bench.py --copy-calibration-mib``),
@@ -28,6 +30,7 @@ Usage:
   python -m speech_audio_encoder_amd.prof_summary mfma COUNTER_CSV AGENT_CSV OUT_MD "COMMAND" [SKIP]
   python -m speech_audio_encoder_amd.prof_summary l2 COUNTER_CSV OUT_MD "COMMAND"
   python -m speech_audio_encoder_amd.prof_summary lds COUNTER_CSV AGENT_CSV OUT_MD "COMMAND"
+  python -m speech_audio_encoder_amd.prof_summary counters COUNTER_CSV OUT_MD "COMMAND"
   python -m speech_audio_encoder_amd.prof_summary traffic WORKLOAD FETCH_CSV WRITE_CSV \\
       COPY_FETCH_CSV COPY_WRITE_CSV COPY_MIB OUT_MD "COMMANDS"
 """
@@ -370,6 +373,35 @@ def lds_report(counter_csv, agent_csv, out_md, command):
         f.write("\n".join(lines) + "\n")
 
 
+def counters_report(counter_csv, out_md, command):
+    """Per kernel class: every counter of one --pmc run per launch (summed
+    over the class's dispatches), except derived latencies (names ending in
+    "Latency", in cycles), which are averaged over the dispatches."""
+    disp = collections.OrderedDict()
+    names = []
+    for r in csv.DictReader(open(counter_csv)):
+        d = disp.setdefault(int(r["Dispatch_Id"]), dict(r))
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        if r["Counter_Name"] not in names:
+            names.append(r["Counter_Name"])
+    rows = sorted(disp.values(), key=lambda r: int(r["Start_Timestamp"]))
+    lines = ["# Counters per kernel class: " + os.path.basename(out_md)[:-3], "",
+             "Command (from the repository root, on one MI355X):", "", "```", command, "```", "",
+             "Per launch of the class (sum over its dispatches); `*Latency`: mean over the "
+             "dispatches, in cycles.", "",
+             "| class | launches | avg us | " + " | ".join(names) + " |",
+             "|---|---:|---:|" + "---:|" * len(names)]
+    for cls, (rs, n) in class_launches(rows).items():
+        vals = []
+        for k in names:
+            v = [r.get(k, 0.0) for r in rs]
+            vals.append(sum(v) / len(v) if k.endswith("Latency") else sum(v) / max(n, 1))
+        t_us = sum(_dur_us(r) for r in rs) / max(n, 1)
+        lines.append(f"| {cls} | {n} | {t_us:.1f} | " + " | ".join(f"{v:.4g}" for v in vals) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def read_traffic(md_path):
     """The JSON record at the end of a traffic report, or None."""
     try:
@@ -388,6 +420,8 @@ if __name__ == "__main__":
                     int(sys.argv[6]) if len(sys.argv) > 6 else 0)
     elif sys.argv[1] == "l2":
         l2_report(sys.argv[2], sys.argv[3], sys.argv[4])
+    elif sys.argv[1] == "counters":
+        counters_report(sys.argv[2], sys.argv[3], sys.argv[4])
     elif sys.argv[1] == "lds":
         lds_report(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5])
     elif sys.argv[1] == "traffic":
