@@ -75,3 +75,50 @@ def test_mfma_report_busy_share(tmp_path):
     cells = [c.strip() for c in row.strip("|").split("|")]
     assert cells[1] == "1" and cells[3] == "50.0%"
     assert cells[4] == "0.5120" and cells[5] == "512.0" and cells[6] == "20.5% bf16"
+
+
+def _counter_csv(path, rows):
+    """rows: (dispatch id, kernel name, counter, value, start, end)."""
+    lines = ["Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp"]
+    for d, n, c, v, t0, t1 in rows:
+        lines.append(f'{d},"void enc::(anonymous namespace)::{n}(int)",{c},{v},{t0},{t1}')
+    path.write_text("\n".join(lines) + "\n")
+
+
+def test_lds_report_shares(tmp_path):
+    # 256 CUs (1,024 SIMDs) in 8 XCDs; GRBM_GUI_ACTIVE summed over the XCDs is
+    # 8 x 1000 cycles, so an average CU was active for 1000 of them: LDS active
+    # 64,000 CU-cycles -> 25%, a quarter of those conflict cycles, MFMA busy
+    # 102,400 SIMD-cycles -> 10%
+    agent = tmp_path / "agent.csv"
+    agent.write_text("Name,Simd_Count,Num_Xcc\ngfx950,1024,8\n")
+    ctr = tmp_path / "ctr.csv"
+    name = "attention_kernel<true, 128>"
+    _counter_csv(ctr, [(1, name, c, v, 0, 2000) for c, v in (
+        ("SQ_INSTS_LDS", 3e6), ("SQ_LDS_IDX_ACTIVE", 64000), ("SQ_LDS_BANK_CONFLICT", 16000),
+        ("SQ_VALU_MFMA_BUSY_CYCLES", 102400), ("GRBM_GUI_ACTIVE", 8000))])
+    out = tmp_path / "l.md"
+    prof_summary.lds_report(str(ctr), str(agent), str(out), "cmd")
+    row = [ln for ln in out.read_text().splitlines() if ln.startswith("| attention")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1] == "1" and cells[2] == "2.0" and cells[3] == "3.00"
+    assert cells[4] == "25.0%" and cells[5] == "25.0%" and cells[6] == "10.0%"
+
+
+def test_counters_report_sums_per_launch_and_averages_latency(tmp_path):
+    # two layers' LayerNorm launches: counters summed per launch (1 + 3 -> 2),
+    # a derived latency averaged over the dispatches (100, 300 -> 200)
+    ctr = tmp_path / "ctr.csv"
+    rows = []
+    for d, (w, lat) in enumerate([(1, 100), (3, 300)], start=1):
+        rows.append((d, "layernorm_kernel", "SQ_WAIT_ANY", w, 0, 4000))
+        rows.append((d, "layernorm_kernel", "VmemLatency", lat, 0, 4000))
+    _counter_csv(ctr, rows)
+    out = tmp_path / "c.md"
+    prof_summary.counters_report(str(ctr), str(out), "cmd")
+    text = out.read_text().splitlines()
+    head = [ln for ln in text if ln.startswith("| class")][0]
+    assert [c.strip() for c in head.strip("|").split("|")][3:] == ["SQ_WAIT_ANY", "VmemLatency"]
+    row = [ln for ln in text if ln.startswith("| layernorm")][0]
+    cells = [c.strip() for c in row.strip("|").split("|")]
+    assert cells[1] == "2" and cells[2] == "4.0" and cells[3] == "2" and cells[4] == "200"
