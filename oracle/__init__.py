@@ -36,3 +36,4 @@ from .fusion import (  # noqa: F401
 )
 from . import fp8  # noqa: F401
 from . import ctc  # noqa: F401
+from . import align  # noqa: F401
