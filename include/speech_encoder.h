@@ -383,6 +383,42 @@ int enc_set_ctc(enc_ctx* ctx, const enc_ctc_weights* w);
 int enc_forward_ctc(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                     float* out_logprobs, hipStream_t stream);
 
+/*
+ * enc_ctc_align: CTC forced alignment of given token sequences onto CTC
+ * log-probabilities -- the step that turns the adapter's frame
+ * probabilities and a generated transcript into token timestamps
+ * ("Nemotron 3.5 Transcribe: From Recorded Speech to Dataset Audits",
+ * section "4. Use alignment and audio questions as supporting evidence").
+ * Per clip, the most probable CTC path that spells the tokens (Viterbi over
+ * blank, y1, blank, ..., yL, blank; a blank separates equal neighbours),
+ * decided in float32; ties go to staying in a state, then to the nearer
+ * predecessor, and at the end to the final blank.
+ *   log_probs  DEVICE fp32, clip-packed rows [sum_b frames[b], ld]: clip b's
+ *              rows follow the earlier clips' (enc_forward_ctc's output, with
+ *              frames[b] = 2 P_b and ld = n_classes); class n_classes - 1 is
+ *              the blank.  Any finite scores work (they need not be
+ *              normalised).
+ *   frames     HOST int64 [batch], >= 0.
+ *   tokens     HOST int32, every clip's token ids concatenated, each in
+ *              0 .. n_classes - 2 (NULL if there are none).
+ *   n_tokens   HOST int64 [batch], >= 0, at most 1,023 per clip.
+ *   spans      DEVICE int32 [sum_b n_tokens[b], 2]: first and last frame the
+ *              path spends on each token (frame f at f x 40 ms on the
+ *              adapter's grid); -1, -1 for a clip without alignment.
+ *   scores     DEVICE fp32 [batch]: the best path's log-probability; -inf
+ *              when the tokens cannot fit the frames (fewer frames than
+ *              tokens plus equal neighbours) -- a review signal, not an error.
+ * Runs on `stream` on the context's device; the context keeps a workspace of
+ * about sum_b frames[b] x (2 n_tokens[b] + 1) bytes, grown as needed (calls
+ * on one context must not overlap).  Errors: ENC_ERR_ARG (NULL pointers,
+ * ld < n_classes, negative counts, a token outside the vocabulary),
+ * ENC_ERR_TOO_LONG (more than 1,023 tokens in a clip), ENC_ERR_NOMEM,
+ * ENC_ERR_HIP; nothing is launched then.
+ */
+int enc_ctc_align(enc_ctx* ctx, const float* log_probs, int64_t ld, int32_t n_classes,
+                  const int64_t* frames, const int32_t* tokens, const int64_t* n_tokens,
+                  int32_t batch, int32_t* spans, float* scores, hipStream_t stream);
+
 /* enc_destroy: wait for the context's device work and free it.  NULL is a
  * no-op. */
 void enc_destroy(enc_ctx* ctx);

@@ -7,7 +7,8 @@ back to anything else.
 
 Function names follow the C calls: ``enc_create``, ``enc_logmel``,
 ``enc_forward``, ``enc_destroy``, ``enc_shapes``, ``enc_workspace_bytes``,
-``enc_last_error``, ``enc_profile_kernel``, ``enc_profile_read``, ``enc_probe_peaks``.
+``enc_last_error``, ``enc_profile_kernel``, ``enc_profile_read``, ``enc_probe_peaks``,
+``enc_ctc_align``.
 """
 
 import ctypes
@@ -32,7 +33,7 @@ EXPORTS = ["enc_create", "enc_logmel", "enc_forward", "enc_forward_noalloc", "en
            "enc_forward_fused", "enc_set_precision", "enc_calibrate", "enc_set_ctc",
            "enc_forward_ctc", "enc_fp8_input_scales", "enc_destroy", "enc_shapes",
            "enc_workspace_bytes", "enc_last_error", "enc_profile_kernel", "enc_profile_read",
-           "enc_probe_peaks"]
+           "enc_probe_peaks", "enc_ctc_align"]
 
 ENC_PREC_BF16 = 0
 ENC_PREC_FP8 = 1
@@ -126,6 +127,9 @@ def load_library(path=LIB_PATH):
                                     ctypes.c_int32, ctypes.c_void_p,
                                     ctypes.POINTER(ctypes.c_double),
                                     ctypes.POINTER(ctypes.c_double)]
+    lib.enc_ctc_align.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  i64p, ctypes.POINTER(ctypes.c_int32), i64p, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     for name in EXPORTS:
         if name not in ("enc_destroy", "enc_last_error"):
             getattr(lib, name).restype = ctypes.c_int
@@ -415,6 +419,32 @@ def enc_profile_read(ctx):
     return n.value, ms.value
 
 
+def enc_ctc_align(ctx, log_probs, frames, tokens_per_clip, n_classes, stream=None):
+    """CTC forced alignment: log_probs cuda fp32 [sum frames, ld] (clip-packed,
+    blank = n_classes - 1), frames [B], tokens_per_clip: B sequences of token
+    ids -> (spans cuda int32 [sum L, 2], scores cuda fp32 [B])."""
+    import torch
+    fr, fr_ptr = _lengths_array(frames)
+    nt = np.ascontiguousarray([len(t) for t in tokens_per_clip], dtype=np.int64)
+    if len(nt) != len(fr):
+        raise ValueError("one token sequence per clip")
+    toks = np.ascontiguousarray(np.concatenate([np.asarray(t, dtype=np.int64).reshape(-1)
+                                                for t in tokens_per_clip] or [np.zeros(0)]),
+                                dtype=np.int32)
+    n_tok = int(nt.sum())
+    dev = log_probs.device
+    spans = torch.empty((n_tok, 2), dtype=torch.int32, device=dev)
+    scores = torch.empty(len(fr), dtype=torch.float32, device=dev)
+    ld = log_probs.stride(0) if log_probs.dim() == 2 else n_classes
+    _check(load_library().enc_ctc_align(
+        ctypes.c_void_p(ctx), ctypes.c_void_p(log_probs.data_ptr()), int(ld), int(n_classes),
+        fr_ptr, toks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if n_tok else None,
+        nt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(fr),
+        ctypes.c_void_p(spans.data_ptr()) if n_tok else None, ctypes.c_void_p(scores.data_ptr()),
+        _stream_handle(stream)))
+    return spans, scores
+
+
 def enc_probe_peaks(dst, src, reps=5, stream=None):
     """(dense bf16 MFMA TFLOP/s, device-copy GB/s) measured on this device;
     dst and src are same-sized device tensors (>= 1 MiB, dst overwritten)."""
@@ -453,6 +483,10 @@ class Encoder:
 
     def forward_ctc(self, audio, lengths, out=None):
         return enc_forward_ctc(self.ctx, audio, lengths, self.n_classes, out)
+
+    def ctc_align(self, log_probs, frames, tokens_per_clip, n_classes=None):
+        return enc_ctc_align(self.ctx, log_probs, frames, tokens_per_clip,
+                             n_classes if n_classes is not None else self.n_classes)
 
     def set_precision(self, precision, input_scales=None):
         """"bf16", or "fp8" with input scales [n_layers, 4]."""

@@ -16,7 +16,8 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libspeech_encoder.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["frontend.hip", "gemm.hip", "norm.hip", "attention.hip", "peak.hip", "runtime.cpp"]
+SOURCES = ["frontend.hip", "gemm.hip", "norm.hip", "attention.hip", "align.hip", "peak.hip",
+           "runtime.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed-fp32 instructions are switched off for every device compile.

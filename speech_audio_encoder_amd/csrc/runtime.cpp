@@ -25,6 +25,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "peak.h"
+#include "align.h"
 
 using namespace enc;
 
@@ -364,6 +365,11 @@ struct enc_ctx {
   CtcW* ctc = nullptr;
   void* ctc_ws = nullptr;
   size_t ctc_ws_bytes = 0;
+  // Forced alignment (enc_ctc_align): device workspace and host staging.
+  void* align_ws = nullptr;
+  size_t align_ws_bytes = 0;
+  std::vector<char> align_host;
+  hipEvent_t align_copied = nullptr;   // the last upload from align_host has been read
   // Precision of the layers' linear maps (enc_set_precision).
   int precision = ENC_PREC_BF16;
   void* fp8_mem = nullptr;   // E4M3 weight codes (all layers)
@@ -396,6 +402,8 @@ void release(enc_ctx* c) {
     delete c->ctc;
   }
   (void)hipFree(c->ctc_ws);
+  (void)hipFree(c->align_ws);
+  if (c->align_copied) (void)hipEventDestroy(c->align_copied);
   (void)hipFree(c->amax_dev);
   if (c->plan_host) (void)hipHostFree(c->plan_host);
   if (c->plan_copied) (void)hipEventDestroy(c->plan_copied);
@@ -1060,6 +1068,87 @@ int enc_forward_fused(enc_ctx* ctx, const float* audio, const int64_t* lengths, 
 int enc_forward_ctc(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_t batch,
                     float* out_logprobs, hipStream_t stream) {
   return run_forward(ctx, audio, lengths, batch, out_logprobs, nullptr, Tail::kCtc, stream);
+}
+
+int enc_ctc_align(enc_ctx* ctx, const float* log_probs, int64_t ld, int32_t n_classes,
+                  const int64_t* frames, const int32_t* tokens, const int64_t* n_tokens,
+                  int32_t batch, int32_t* spans, float* scores, hipStream_t stream) {
+  if (!ctx) return fail(ENC_ERR_ARG, "ctx is NULL");
+  if (batch < 0) return fail(ENC_ERR_ARG, "batch < 0");
+  if (batch == 0) return ENC_OK;
+  if (!frames || !n_tokens || !scores) return fail(ENC_ERR_ARG, "NULL argument");
+  if (n_classes < 2 || ld < n_classes) return fail(ENC_ERR_ARG, "need n_classes >= 2, ld >= n_classes");
+  int64_t rows = 0, n_tok = 0;
+  int max_states = 1;
+  for (int b = 0; b < batch; ++b) {
+    if (frames[b] < 0 || n_tokens[b] < 0) return fail(ENC_ERR_ARG, "negative count");
+    if (2 * n_tokens[b] + 1 > ALIGN_MAX_STATES)
+      return fail(ENC_ERR_TOO_LONG, "clip " + std::to_string(b) + " has " +
+                                        std::to_string(n_tokens[b]) + " tokens (at most " +
+                                        std::to_string((ALIGN_MAX_STATES - 1) / 2) + ")");
+    if (frames[b] > 0x7fffffff) return fail(ENC_ERR_TOO_LONG, "too many frames");
+    rows += frames[b];
+    n_tok += n_tokens[b];
+    max_states = std::max(max_states, (int)(2 * n_tokens[b] + 1));
+  }
+  if (n_tok > 0 && (!tokens || !spans)) return fail(ENC_ERR_ARG, "NULL tokens or spans");
+  if (rows > 0 && !log_probs) return fail(ENC_ERR_ARG, "NULL log_probs");
+  for (int64_t i = 0; i < n_tok; ++i)
+    if (tokens[i] < 0 || tokens[i] >= n_classes - 1)
+      return fail(ENC_ERR_ARG, "token " + std::to_string(i) + " outside 0 .. n_classes - 2");
+  int rc = check_device(ctx);
+  if (rc != ENC_OK) return rc;
+  // workspace: clip records, tokens, then each clip's choices (frames x states bytes)
+  const size_t clip_bytes = (size_t)batch * sizeof(AlignClip);
+  const size_t tok_at = (clip_bytes + 255) / 256 * 256;
+  const size_t back_at = (tok_at + (size_t)n_tok * 4 + 255) / 256 * 256;
+  std::vector<AlignClip> rec(batch);
+  size_t back = 0;
+  int64_t row = 0, tok_off = 0;
+  for (int b = 0; b < batch; ++b) {
+    rec[b] = AlignClip{row, (int64_t)back, (int32_t)frames[b], (int32_t)tok_off,
+                       (int32_t)n_tokens[b], 0};
+    back += (size_t)frames[b] * (size_t)(2 * n_tokens[b] + 1);
+    row += frames[b];
+    tok_off += n_tokens[b];
+  }
+  if (tok_off > 0x7fffffff) return fail(ENC_ERR_TOO_LONG, "too many tokens");
+  const size_t total = back_at + back;
+  if (total > ctx->align_ws_bytes) {
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    (void)hipFree(ctx->align_ws);
+    ctx->align_ws = nullptr;
+    ctx->align_ws_bytes = 0;
+    if (hipMalloc(&ctx->align_ws, total) != hipSuccess) {
+      ctx->align_ws = nullptr;
+      (void)hipGetLastError();
+      return fail(ENC_ERR_NOMEM, "alignment workspace allocation of " + std::to_string(total) +
+                                     " bytes failed");
+    }
+    ctx->align_ws_bytes = total;
+  }
+  char* ws = (char*)ctx->align_ws;
+  // the previous call's upload may still read the staging buffer
+  if (ctx->align_copied) {
+    hipError_t e = hipEventSynchronize(ctx->align_copied);
+    if (e != hipSuccess) return hip_fail(e, "alignment staging event");
+  } else {
+    hipError_t e = hipEventCreateWithFlags(&ctx->align_copied, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "alignment staging event");
+  }
+  ctx->align_host.resize(back_at);
+  std::memcpy(ctx->align_host.data(), rec.data(), clip_bytes);
+  if (n_tok) std::memcpy(ctx->align_host.data() + tok_at, tokens, (size_t)n_tok * 4);
+  hipError_t e = hipMemcpyAsync(ws, ctx->align_host.data(), back_at, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "alignment upload");
+  e = hipEventRecord(ctx->align_copied, stream);
+  if (e != hipSuccess) return hip_fail(e, "alignment staging event");
+  e = launch_ctc_align(log_probs, ld, n_classes - 1, (const AlignClip*)ws, batch,
+                       (const int32_t*)(ws + tok_at), (uint8_t*)(ws + back_at), spans, scores,
+                       max_states, stream);
+  if (e != hipSuccess) return hip_fail(e, "launch_ctc_align");
+  return ENC_OK;
 }
 
 int enc_set_ctc(enc_ctx* ctx, const enc_ctc_weights* w) {

@@ -290,3 +290,46 @@ def make_ctc_weights(bf16=True, perturb=False, d=D_MODEL, dh=CTC_HEAD_DIM, ffn=C
         cw["layers"].append({name: tensor(layer, tid, kind, _shape(kind, d, dh, ffn, 0))
                              for name, kind, tid in _LAYER_TENSORS})
     return cw
+
+
+def alignment_case(frames, n_tokens, n_classes, seed, planted=True, repeats=0.1):
+    """Synthetic CTC frame scores and a token sequence for forced alignment.
+
+    Scores: float32 [frames, n_classes] drawn from N(-12, 2^2) (blank is the
+    last class).  Tokens: n_tokens ids in 0 .. n_classes - 2, each equal to its
+    predecessor with probability `repeats`.  With `planted`, one valid
+    segmentation of the tokens into frames (blank runs between tokens where
+    room allows, always between equal neighbours) is drawn and its classes
+    get +10 in their frames, so one path stands out; the scores are not
+    normalised (the alignment needs no normalisation).  Returns (scores,
+    tokens)."""
+    rng = np.random.default_rng(seed)
+    lp = rng.normal(-12.0, 2.0, size=(frames, n_classes)).astype(np.float32)
+    tokens = []
+    for i in range(n_tokens):
+        if i and rng.random() < repeats:
+            tokens.append(tokens[-1])
+        else:
+            tokens.append(int(rng.integers(0, n_classes - 1)))
+    if planted and n_tokens:
+        blank = n_classes - 1
+        need = n_tokens + sum(1 for a, b in zip(tokens, tokens[1:]) if a == b)
+        if frames >= need:
+            # one frame per token and one blank between equal neighbours, the
+            # spare frames spread at random over tokens and blank gaps
+            runs = []   # (class, length)
+            for i, tk in enumerate(tokens):
+                if i and tokens[i - 1] == tk:
+                    runs.append([blank, 1])
+                elif i:
+                    runs.append([blank, 0])
+                runs.append([tk, 1])
+            runs = [[blank, 0]] + runs + [[blank, 0]]
+            spare = frames - need
+            for j in rng.integers(0, len(runs), size=spare):
+                runs[int(j)][1] += 1
+            t = 0
+            for cls, n in runs:
+                lp[t:t + n, cls] += 10.0
+                t += n
+    return lp, tokens

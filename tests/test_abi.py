@@ -130,3 +130,12 @@ def test_probe_peaks_argument_errors(lib):
                                ctypes.byref(gbs)) == binding.ENC_ERR_ARG
     assert lib.enc_probe_peaks(buf, buf, 1 << 20, 1, None, None,
                                ctypes.byref(gbs)) == binding.ENC_ERR_ARG
+
+
+def test_ctc_align_argument_errors(lib):
+    # rejected on the host before any device work
+    fr = (ctypes.c_int64 * 1)(10)
+    nt = (ctypes.c_int64 * 1)(1)
+    tk = (ctypes.c_int32 * 1)(3)
+    assert lib.enc_ctc_align(None, None, 50, 50, fr, tk, nt, 1, None, None,
+                             None) == binding.ENC_ERR_ARG
