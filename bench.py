@@ -11,7 +11,8 @@ the library's probe kernels; ``--no-peak-probe`` skips them) and the CPU
 oracle timed on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                      [--attention CORE,CONTEXT] [--fused | --ctc] [--precision bf16|fp8]
+                      [--attention CORE,CONTEXT] [--fused | --ctc [--align]]
+                      [--precision bf16|fp8]
                       [--running-max-steps N]
 
 --fused runs the encoder through speaker fusion and the 1280 -> 2688 connector
@@ -20,6 +21,9 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 --ctc runs the encoder and the CTC timestamp adapter (upsampling to the 40 ms
 grid, two 16-head layers, 23,863-way projection, log-softmax) instead of
 stopping at the embeddings; flops count the adapter at its real head width.
+--align (implies --ctc) also force-aligns a synthetic token sequence per clip
+onto the adapter's output in every step, and reports the alignment alone in
+an "align" object.
 
 --precision fp8 runs the four linear maps of every layer on E4M3 codes with
 per-tensor scales (input scales from the library's calibration on the same
@@ -273,6 +277,27 @@ def running_max_timing(weights, dtype, core, context, x, lengths, out, steps, st
             "attention_ms_per_step": round(att_ms, 4), "attention_launches": n_att}
 
 
+def align_timing(enc, logprobs, frames, tokens, lengths, stream, reps=10):
+    """The forced alignment alone (enc_ctc_align on the step's own adapter
+    output), timed with HIP events on the library's stream."""
+    import torch
+    for _ in range(2):
+        enc.ctc_align(logprobs, frames, tokens)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        enc.ctc_align(logprobs, frames, tokens)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    audio_s = sum(lengths) / SAMPLE_RATE
+    return {"ms_per_call": round(ms, 4), "clips": len(frames), "frames": int(sum(frames)),
+            "tokens": int(sum(len(t) for t in tokens)), "longest_clip_frames": int(max(frames)),
+            "us_per_frame_of_longest_clip": round(1000.0 * ms / max(1, max(frames)), 3),
+            "audio_s_per_s": round(audio_s / (ms / 1000.0), 1),
+            "note": "one workgroup per clip; the frames of a clip are a sequential chain"}
+
+
 def peak_probe(roof, nbytes=1 << 30, reps=5):
     """What the device sustains (the library's probe kernels: back-to-back bf16
     MFMAs on register operands, and a device copy of 1 GiB), with the dominant
@@ -304,6 +329,10 @@ def main():
                     help="'full' or CORE,CONTEXT for windowed attention")
     ap.add_argument("--fused", action="store_true",
                     help="encoder + speaker fusion + connector (language-model input rows)")
+    ap.add_argument("--align", action="store_true",
+                    help="with --ctc: also force-align a synthetic token sequence per clip "
+                         "(about six tokens per audio second) onto the adapter's output in "
+                         "every step, and time the alignment alone")
     ap.add_argument("--ctc", action="store_true",
                     help="encoder + CTC timestamp adapter (log-probabilities on the 40 ms grid)")
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"],
@@ -365,12 +394,19 @@ def main():
     if fp8:
         amax = enc.calibrate(x, lengths)
         enc.set_precision("fp8", binding.scales_from_amax(amax))
+    if args.align:
+        args.ctc = True
     if args.ctc:
         enc.set_ctc(workloads.make_ctc_weights(bf16=True))
         out = torch.empty((2 * sum(clip_pos), enc.n_classes), dtype=torch.float32, device="cuda")
+        align_frames = [2 * p for p in clip_pos]
+        align_tokens = [workloads.alignment_case(0, min(f // 4, 1023), enc.n_classes, 500 + b)[1]
+                        for b, f in enumerate(align_frames)]
 
         def step():
             enc.forward_ctc(x, lengths, out=out)
+            if args.align:
+                enc.ctc_align(out, align_frames, align_tokens)
     elif args.fused:
         cw = workloads.make_connector_weights(bf16=True)
         enc.set_connector(cw)
@@ -489,6 +525,8 @@ def main():
                    "attention": "full" if not core else f"windows core={core} context={context}",
                    "precision": args.precision,
                    "output": "fused + connector rows [R, 2688]" if args.fused
+                   else "CTC log-probabilities [2R, 23863] fp32 + forced alignment of "
+                        "synthetic tokens" if args.align
                    else "CTC log-probabilities [2R, 23863] fp32" if args.ctc
                    else "embeddings [B, P_max, 1280]",
                    "algorithmic_tflop_per_step": round(total_flops / 1e12, 4)},
@@ -498,6 +536,8 @@ def main():
         result["kernel_ms_per_step"] = breakdown
         result["class_rooflines"] = class_rooflines(breakdown, rows, pos, lengths,
                                                     sum(clip_pos), fp8)
+    if args.align:
+        result["align"] = align_timing(enc, out, align_frames, align_tokens, lengths, stream)
     enc.close()
     if args.running_max_steps > 0 and not (args.fused or args.ctc or fp8):
         result["running_max"] = running_max_timing(weights, dtype, core, context, x, lengths, out,

@@ -13,10 +13,11 @@
 // the state that stays, then s - 1, then s - 2, and between the final
 // states to the blank.
 //
-// Work split: one workgroup of 256 threads per clip.  The recursion over
+// Work split: one workgroup of four wavefronts per clip.  The recursion over
 // frames is sequential; within a frame every state is independent, so thread
 // i owns states i, i + 256, ... (SPT of them) and the scores of the previous
-// frame live in LDS (two buffers, one barrier per frame).  The
+// frame live in LDS (two buffers, one barrier per frame).  The choices of 32
+// frames gather in LDS before they are copied out together.  The
 // log-probabilities a thread needs are gathered DEPTH frames ahead into
 // registers, so the per-frame chain does not wait on global memory.  Each
 // frame's choices (0, 1, 2: how far back the best predecessor lies) are
@@ -34,10 +35,12 @@ namespace enc {
 
 namespace {
 
-constexpr int AT = 256;          // threads per workgroup
+constexpr int AT = 256;          // threads per workgroup (four wavefronts)
 constexpr int WALK = 64;         // frames per backtracking window
 constexpr int WIN_W = 2 * WALK + 1;   // states a window can span
+constexpr int CHUNK = 32;        // frames whose choices are gathered in LDS before a copy out
 
+// SPT states per thread, log-probabilities prefetched DEPTH frames ahead.
 template <int SPT, int DEPTH>
 __global__ __launch_bounds__(AT) void ctc_align_kernel(const float* __restrict__ lp, int64_t ld,
                                                        int blank, const AlignClip* __restrict__ clips,
@@ -47,6 +50,7 @@ __global__ __launch_bounds__(AT) void ctc_align_kernel(const float* __restrict__
                                                        float* __restrict__ scores) {
   __shared__ float dp[2][AT * SPT];
   __shared__ uint8_t win[WALK][WIN_W + 3];
+  __shared__ uint8_t chunk[CHUNK * AT * SPT];   // choices of up to CHUNK frames, [frame][state]
   __shared__ int s_rep;
 
   const int tid = threadIdx.x;
@@ -99,42 +103,69 @@ __global__ __launch_bounds__(AT) void ctc_align_kernel(const float* __restrict__
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
 #pragma unroll
-    for (int k = 0; k < SPT; ++k)
-      pre[d][k] = (1 + d < T && live[k]) ? base[(int64_t)(1 + d) * ld + lab[k]] : 0.f;
+    for (int k = 0; k < SPT; ++k) pre[d][k] = base[(int64_t)min(1 + d, T - 1) * ld + lab[k]];
   __syncthreads();
 
-  // frames t = t0 + d (d = 0 .. DEPTH-1), t0 = 1, 1 + DEPTH, ...
-  for (int t0 = 1; t0 < T; t0 += DEPTH) {
+  // Frames t = t0 + d (d = 0 .. DEPTH-1), t0 = 1, 1 + DEPTH, ...  The
+  // choices of CHUNK frames gather in LDS and are then copied out together:
+  // a global store inside the per-frame chain would make every frame wait
+  // for all outstanding loads (loads and stores share one counter and may
+  // complete out of order), the prefetched log-probabilities included.
+  static_assert(CHUNK % DEPTH == 0, "chunk of whole prefetch rounds");
+  for (int c0 = 1; c0 < T; c0 += CHUNK) {
+    for (int t0 = c0; t0 < c0 + CHUNK && t0 < T; t0 += DEPTH) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int t = t0 + d;
-      if (t >= T) break;
-      const float* prv = dp[(t - 1) & 1];
-      float* cur = dp[t & 1];
+      for (int d = 0; d < DEPTH; ++d) {
+        const int t = t0 + d;
+        const bool act = t < T;   // the last round's frames past T only keep the pattern
+        const float* prv = dp[(t - 1) & 1];
+        float* cur = dp[t & 1];
+        uint8_t* ch = chunk + (t - c0) * S;
+        // (every lane computes and loads in every frame of the round --
+        // states past S read in-bounds LDS and the blank's column, frames
+        // past T reload the last row -- so that no load sits in a branch and
+        // each frame waits only for the load made DEPTH frames earlier; only
+        // live states of frames before T are stored)
+        const int tn = min(t + DEPTH, T - 1);   // past the end: a spare in-bounds load
 #pragma unroll
-      for (int k = 0; k < SPT; ++k) {
-        if (!live[k]) continue;
-        const int s = tid + AT * k;
-        float best = prv[s];
-        uint8_t bp = 0;
-        const float m1 = s >= 1 ? prv[s - 1] : -INFINITY;
-        if (m1 > best) {
-          best = m1;
-          bp = 1;
+        for (int k = 0; k < SPT; ++k) {
+          const int s = tid + AT * k;
+          float best = prv[s];
+          uint8_t bp = 0;
+          const float m1 = s >= 1 ? prv[max(s - 1, 0)] : -INFINITY;
+          if (m1 > best) {
+            best = m1;
+            bp = 1;
+          }
+          const float m2 = skip[k] ? prv[max(s - 2, 0)] : -INFINITY;
+          if (m2 > best) {
+            best = m2;
+            bp = 2;
+          }
+          const float v = pre[d][k] + best;
+          if (act && live[k]) {
+            cur[s] = v;
+            ch[s] = bp;
+          }
+          // the same register, DEPTH frames later
+          pre[d][k] = base[(int64_t)tn * ld + lab[k]];
         }
-        const float m2 = skip[k] ? prv[s - 2] : -INFINITY;
-        if (m2 > best) {
-          best = m2;
-          bp = 2;
-        }
-        cur[s] = pre[d][k] + best;
-        bk[(int64_t)t * S + s] = bp;
-        // the same register, DEPTH frames later
-        const int tn = t + DEPTH;
-        pre[d][k] = tn < T ? base[(int64_t)tn * ld + lab[k]] : 0.f;
+        // LDS only: the scores and choices of this frame are written
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
-      __syncthreads();
     }
+    // copy the chunk's choices (frames c0 .. c0 + rows - 1, contiguous in
+    // both places) out; the barrier lets the next chunk reuse the buffer
+    const int bytes = min(CHUNK, T - c0) * S;
+    uint8_t* dst = bk + (int64_t)c0 * S;
+    for (int e = tid; e < bytes; e += AT) dst[e] = chunk[e];
+    // wait here, once per chunk, for the stores (and every prefetch in
+    // flight), so that within a chunk only loads are outstanding and each
+    // frame waits just for its own log-probabilities
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // final state (ties to the blank), score
