@@ -143,3 +143,20 @@ def test_align_errors(enc):
     assert e.value.code == binding.ENC_ERR_TOO_LONG
     spans, scores = binding.enc_ctc_align(enc.ctx, lp, [], [], 50)   # no clips
     assert spans.numel() == 0 and scores.numel() == 0
+
+
+def test_align_with_impossible_classes(enc):
+    # log-probabilities of -inf (classes that cannot occur in a frame): paths
+    # through them are excluded on both sides; a clip whose every path is
+    # excluded has no alignment
+    n_classes = 64
+    rng = np.random.default_rng(41)
+    rows, frames, tokens = build([(120, 30, 42, True), (80, 20, 43, False), (50, 10, 44, True)],
+                                 n_classes)
+    mask = rng.random(rows.shape) < 0.2
+    mask[:, n_classes - 1] = False   # the blank stays possible
+    rows[mask] = -np.inf
+    rows[150:160, :] = -np.inf   # ten frames of the second clip: nothing can be emitted
+    spans, scores = run_gpu(enc, rows, frames, tokens, n_classes)
+    compare(rows, frames, tokens, n_classes, spans, scores, "impossible classes")
+    assert np.isfinite(scores[0]) and np.isneginf(scores[1]) and np.isfinite(scores[2])
