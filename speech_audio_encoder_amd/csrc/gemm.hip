@@ -668,40 +668,48 @@ constexpr int SNS = 4;    // ring stages
 
 // Piece pid's first row and column: mode 0, the sixteen 64 x 64 pieces of
 // each big tile t_begin, t_begin + 1, ...; mode 1, a plain grid of pieces_n
-// pieces per row.
+// pieces of PM rows x 64 columns per piece row.
 struct SmallMap {
   int mode;
   int t_begin, tiles_m, tiles_n;   // mode 0
   int pieces_n;                    // mode 1
 };
 
+template <int PM>
 __device__ __forceinline__ void small_coords(int pid, const SmallMap& sm, int64_t& m0,
                                              int64_t& n0) {
-  if (sm.mode == 0) {
+  if (PM == SP && sm.mode == 0) {
     int tm, tn;
     tile_coords(sm.t_begin + (pid >> 4), sm.tiles_m, sm.tiles_n, tm, tn);
     m0 = (int64_t)tm * BIG + (pid & 3) * SP;
     n0 = (int64_t)tn * BIG + ((pid >> 2) & 3) * SP;
   } else {
-    m0 = (int64_t)(pid / sm.pieces_n) * SP;
+    m0 = (int64_t)(pid / sm.pieces_n) * PM;
     n0 = (int64_t)(pid % sm.pieces_n) * SP;
   }
 }
 
+// PM: rows of a piece, 64 (two workgroups per CU) or 128 (each wavefront
+// 64 x 32 outputs in two accumulators; a 24 KB stage moves 128 + 64 rows for
+// twice the products of a 64 x 64 piece, 43 instead of 32 flops per byte).
 // F8: E4M3 codes moved as pairs (K, lda, ldw in units of two codes), as in
 // the other kernels; a 64-code MFMA takes the fragments of two bf16 k-steps.
-template <Epilogue EPI, bool PARTIAL, bool F8>
-__global__ __launch_bounds__(256, 2) void gemm_small_kernel(
+template <Epilogue EPI, bool PARTIAL, bool F8, int PM>
+__global__ __launch_bounds__(256, PM == SP ? 2 : 1) void gemm_small_kernel(
     const bf16_t* __restrict__ A, int64_t lda, const bf16_t* __restrict__ W, int64_t ldw,
     const float* __restrict__ bias, void* __restrict__ Cv, int64_t ldc, float* __restrict__ part,
     int64_t M, int K, SmallMap sm, int splits, float alpha, float oscale) {
-  constexpr int STG = 2 * SP * SBK / 8;   // uint4 per stage: A rows, then W rows (16 KB)
+  static_assert(PM == SP || PM == 2 * SP, "piece rows");
+  constexpr int NB = (PM + SP) / 8;        // 8-row blocks of a stage: A rows, then W rows
+  constexpr int NBW = NB / 4;              // blocks per wavefront
+  constexpr int NA = PM / SP;              // accumulators per wavefront
+  constexpr int STG = NB * 64;             // uint4 per stage (16 or 24 KB)
   __shared__ uint4 st[SNS][STG];
 
   const int split = blockIdx.x % splits;
   const int pid = blockIdx.x / splits;
   int64_t m0, n0;
-  small_coords(pid, sm, m0, n0);
+  small_coords<PM>(pid, sm, m0, n0);
   if (m0 >= M) return;   // a piece of the last tile row wholly past M
   const int kc = K / splits;
   const int kb = split * kc;
@@ -715,38 +723,43 @@ __global__ __launch_bounds__(256, 2) void gemm_small_kernel(
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  // DMA: a stage is 16 blocks of 8 rows x 128 bytes (A rows 0..63, then W
-  // rows 0..63); wave w fills blocks 4w .. 4w+3, lane l the LDS chunk l % 8 of
-  // row l / 8 of a block, which holds global chunk (l % 8) ^ ((row / 2) % 8)
-  // (the XOR keeps the operand reads below conflict-free).
-  const bf16_t* src[4];
+  // DMA: a stage is NB blocks of 8 rows x 128 bytes (A rows 0..PM-1, then W
+  // rows 0..63); wave w fills blocks NBW w .. NBW w + NBW - 1, lane l the LDS
+  // chunk l % 8 of row l / 8 of a block, which holds global chunk
+  // (l % 8) ^ ((row / 2) % 8) (the XOR keeps the operand reads below
+  // conflict-free).
+  const bf16_t* src[NBW];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int blk = wave * 4 + t;
-    const int row = (blk & 7) * 8 + (lane >> 3);
+  for (int t = 0; t < NBW; ++t) {
+    const int blk = wave * NBW + t;
+    const bool is_a = blk < PM / 8;
+    const int row = (is_a ? blk : blk - PM / 8) * 8 + (lane >> 3);
     const int chunk = (lane & 7) ^ ((row >> 1) & 7);
-    src[t] = blk < 8 ? A + min<int64_t>(m0 + row, M - 1) * lda + kb + chunk * 8
-                     : W + (n0 + row) * ldw + kb + chunk * 8;
+    src[t] = is_a ? A + min<int64_t>(m0 + row, M - 1) * lda + kb + chunk * 8
+                  : W + (n0 + row) * ldw + kb + chunk * 8;
   }
   int ikt = 0;
   auto issue = [&](int slot) __attribute__((always_inline)) {
     const int k0 = min(ikt, KT - 1) * SBK;   // past the end: re-read the last step
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
-      dma16(src[t] + k0, (lds_void*)(&st[slot][0] + (wave * 4 + t) * 64));
+    for (int t = 0; t < NBW; ++t)
+      dma16(src[t] + k0, (lds_void*)(&st[slot][0] + (wave * NBW + t) * 64));
     ++ikt;
   };
 
-  // operand rows: A row wm*32 + l32, W row wn*32 + l32 (LDS rows of 8 chunks)
+  // operand rows: A rows wm*PM/2 + 32 b + l32, W row wn*32 + l32 (LDS rows of
+  // 8 chunks)
   const int rsw = (l32 >> 1) & 7;
-  const int aofs = (wm * 32 + l32) * 8;
-  const int wofs = SP * 8 + (wn * 32 + l32) * 8;
-  f32x16 acc;
+  const int aofs = (wm * (PM / 2) + l32) * 8;
+  const int wofs = PM * 8 + (wn * 32 + l32) * 8;
+  f32x16 acc[NA];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int b = 0; b < NA; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[b][v] = 0.f;
 
-  constexpr int VM = 4 * (SNS - 2);
-  constexpr int WAIT_STEP = (VM & 15) | ((VM >> 4) << 14) | 0x0070;   // vmcnt(8) lgkmcnt(0)
+  constexpr int VM = NBW * (SNS - 2);
+  constexpr int WAIT_STEP = (VM & 15) | ((VM >> 4) << 14) | 0x0070;   // vmcnt(VM) lgkmcnt(0)
 #pragma unroll
   for (int i = 0; i < SNS - 1; ++i) issue(i);
   for (int kt = 0; kt < KT; ++kt) {
@@ -754,54 +767,69 @@ __global__ __launch_bounds__(256, 2) void gemm_small_kernel(
     __builtin_amdgcn_s_barrier();            // ... for every wavefront; the oldest stage is free
     issue((kt + SNS - 1) % SNS);
     const uint4* sp = st[kt % SNS];
-    bf16x8 fa[4], fw[4];
+    bf16x8 fa[NA][4], fw[4];
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
       const int pc = (2 * sl + lhi) ^ rsw;
       fw[sl] = __builtin_bit_cast(bf16x8, sp[wofs + pc]);
-      fa[sl] = __builtin_bit_cast(bf16x8, sp[aofs + pc]);
+#pragma unroll
+      for (int b = 0; b < NA; ++b)
+        fa[b][sl] = __builtin_bit_cast(bf16x8, sp[aofs + b * 256 + pc]);
     }
     if constexpr (F8) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            __builtin_shufflevector(__builtin_bit_cast(i32x4, fw[2 * h]),
-                                    __builtin_bit_cast(i32x4, fw[2 * h + 1]), 0, 1, 2, 3, 4, 5, 6, 7),
-            __builtin_shufflevector(__builtin_bit_cast(i32x4, fa[2 * h]),
-                                    __builtin_bit_cast(i32x4, fa[2 * h + 1]), 0, 1, 2, 3, 4, 5, 6, 7),
-            acc, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < NA; ++b)
+          acc[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              __builtin_shufflevector(__builtin_bit_cast(i32x4, fw[2 * h]),
+                                      __builtin_bit_cast(i32x4, fw[2 * h + 1]), 0, 1, 2, 3, 4, 5,
+                                      6, 7),
+              __builtin_shufflevector(__builtin_bit_cast(i32x4, fa[b][2 * h]),
+                                      __builtin_bit_cast(i32x4, fa[b][2 * h + 1]), 0, 1, 2, 3, 4,
+                                      5, 6, 7),
+              acc[b], 0, 0, 0, 0, 0, 0);
     } else {
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl], fa[sl], acc, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < NA; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[sl], fa[b][sl], acc[b], 0, 0, 0);
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // loads past the last step land before LDS is released
 
-  const int64_t m = m0 + wm * 32 + l32;
   const int nw = (int)n0 + wn * 32;
   if constexpr (PARTIAL) {
-    // partial layout: [pid][split][64 rows][64 cols] fp32
-    float* dst = part + ((int64_t)pid * splits + split) * (SP * SP) + (wm * 32 + l32) * SP + wn * 32;
+    // partial layout: [pid][split][PM rows][64 cols] fp32
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(dst + 8 * q + 4 * lhi) =
-          make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    for (int b = 0; b < NA; ++b) {
+      float* dst = part + ((int64_t)pid * splits + split) * (PM * SP) +
+                   (wm * (PM / 2) + 32 * b + l32) * SP + wn * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(dst + 8 * q + 4 * lhi) =
+            make_float4(acc[b][4 * q], acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]);
+    }
   } else {
     float4 bv[4];
     load_bias32(bias, nw, lhi, bv);
-    if (m < M) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        store4<EPI, F8>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], alpha, oscale, acc[4 * q],
-                        acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    for (int b = 0; b < NA; ++b) {
+      const int64_t m = m0 + wm * (PM / 2) + 32 * b + l32;
+      if (m < M) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          store4<EPI, F8>(Cv, ldc, m, nw + 8 * q + 4 * lhi, bv[q], alpha, oscale, acc[b][4 * q],
+                          acc[b][4 * q + 1], acc[b][4 * q + 2], acc[b][4 * q + 3]);
+      }
     }
   }
 }
 
-// Sum the split partials of each 64 x 64 piece in split order and apply the
+// Sum the split partials of each PM x 64 piece in split order and apply the
 // epilogue; one thread per 4 consecutive columns.
-template <Epilogue EPI, bool F8>
+template <Epilogue EPI, bool F8, int PM>
 __global__ __launch_bounds__(256) void gemm_small_reduce(const float* __restrict__ part,
                                                          const float* __restrict__ bias,
                                                          void* __restrict__ Cv, int64_t ldc,
@@ -810,14 +838,14 @@ __global__ __launch_bounds__(256) void gemm_small_reduce(const float* __restrict
   const int pid = blockIdx.y;
   const int e = (blockIdx.x * 256 + threadIdx.x) * 4;   // element in the piece
   int64_t m0, n0;
-  small_coords(pid, sm, m0, n0);
+  small_coords<PM>(pid, sm, m0, n0);
   const int64_t m = m0 + e / SP;
   const int n = (int)n0 + e % SP;
   if (m >= M) return;
-  const float* src = part + (int64_t)pid * splits * (SP * SP) + e;
+  const float* src = part + (int64_t)pid * splits * (PM * SP) + e;
   float4 s = *reinterpret_cast<const float4*>(src);
   for (int k = 1; k < splits; ++k) {
-    const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)k * (SP * SP));
+    const float4 t = *reinterpret_cast<const float4*>(src + (int64_t)k * (PM * SP));
     s.x += t.x; s.y += t.y; s.z += t.z; s.w += t.w;
   }
   store4<EPI, F8>(Cv, ldc, m, n, *reinterpret_cast<const float4*>(bias + n), alpha, oscale, s.x,
@@ -841,29 +869,34 @@ int num_cus() {
 // Split K (a divisor of K / 64) only while the pieces that hold rows still
 // fit one workgroup per CU and their partial sums fit `part`.
 // `live` pieces hold rows (of `pieces` launched).
-template <Epilogue EPI, bool F8>
-hipError_t launch_small(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
-                        const float* bias, void* C, int64_t ldc, int64_t M, int K, float* part,
-                        size_t part_bytes, const SmallMap& sm, int live, int pieces, int cus,
-                        float alpha, float oscale, hipStream_t stream) {
+int small_splits(int K, int live, int pieces, int pm, int cus, size_t part_bytes) {
   const int units = K / SBK;
   int splits = 1;
   for (int sp = 2; sp <= units; ++sp) {
     if (units % sp) continue;
     if ((int64_t)live * sp > cus) break;
-    if ((size_t)pieces * sp * SP * SP * sizeof(float) > part_bytes) break;
+    if ((size_t)pieces * sp * pm * SP * sizeof(float) > part_bytes) break;
     splits = sp;
   }
+  return splits;
+}
+
+template <Epilogue EPI, bool F8, int PM>
+hipError_t launch_small(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
+                        const float* bias, void* C, int64_t ldc, int64_t M, int K, float* part,
+                        size_t part_bytes, const SmallMap& sm, int live, int pieces, int cus,
+                        float alpha, float oscale, hipStream_t stream) {
+  const int splits = small_splits(K, live, pieces, PM, cus, part_bytes);
   if (splits == 1) {
-    gemm_small_kernel<EPI, false, F8><<<dim3(pieces), dim3(256), 0, stream>>>(
+    gemm_small_kernel<EPI, false, F8, PM><<<dim3(pieces), dim3(256), 0, stream>>>(
         A, lda, W, ldw, bias, C, ldc, part, M, K, sm, 1, alpha, oscale);
     return hipGetLastError();
   }
-  gemm_small_kernel<EPI, true, F8><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
+  gemm_small_kernel<EPI, true, F8, PM><<<dim3(pieces * splits), dim3(256), 0, stream>>>(
       A, lda, W, ldw, bias, C, ldc, part, M, K, sm, splits, alpha, oscale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  gemm_small_reduce<EPI, F8><<<dim3(SP * SP / 1024, pieces), dim3(256), 0, stream>>>(
+  gemm_small_reduce<EPI, F8, PM><<<dim3(PM * SP / 1024, pieces), dim3(256), 0, stream>>>(
       part, bias, C, ldc, M, sm, splits, alpha, oscale);
   return hipGetLastError();
 }
@@ -877,11 +910,26 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   const int tiles = tiles_m * tiles_n;
   const int cus = num_cus();
   if (tiles < cus) {
-    // Fewer big tiles than CUs: the whole product as 64 x 64 pieces.
+    // Fewer big tiles than CUs: the whole product as pieces.  Pieces of 128
+    // rows move 43 instead of 32 flops per byte through the CU's load path
+    // but hold one workgroup per CU (96 KB of LDS) instead of two, whose
+    // start-up and epilogue then overlap nothing: they are taken when they
+    // still occupy 7/8 of the CUs and each workgroup runs at least 16 K steps
+    // (30-s clip, same box: FFN up 17.1 -> 15.4 us and FFN down 19.4 ->
+    // 18.5 us per launch; QKV with 180 such pieces and the attention output
+    // projection with 5-step splits were slower and keep 64-row pieces).
+    {
+      const int pieces = (int)((M + 2 * SP - 1) / (2 * SP)) * (N / SP);
+      const int splits = small_splits(K, pieces, pieces, 2 * SP, cus, part_bytes);
+      if (pieces * splits >= cus - cus / 8 && K / SBK / splits >= 16)
+        return launch_small<EPI, F8, 2 * SP>(A, lda, W, ldw, bias, C, ldc, M, K, part,
+                                             part_bytes, SmallMap{1, 0, 0, 0, N / SP}, pieces,
+                                             pieces, cus, alpha, oscale, stream);
+    }
     const int pieces = (int)((M + SP - 1) / SP) * (N / SP);
-    return launch_small<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
-                                 SmallMap{1, 0, 0, 0, N / SP}, pieces, pieces, cus, alpha, oscale,
-                                 stream);
+    return launch_small<EPI, F8, SP>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
+                                     SmallMap{1, 0, 0, 0, N / SP}, pieces, pieces, cus, alpha,
+                                     oscale, stream);
   }
   // Full rounds go to the persistent kernel, the remainder to 64 x 64 pieces.
   const int n_big = (tiles / cus) * cus;
@@ -910,9 +958,9 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
     const int64_t tm = first_m + (t - (t / per_group) * per_group) % gsize;
     live += 4 * (int)std::min<int64_t>(4, (M - tm * BIG + SP - 1) / SP);
   }
-  return launch_small<EPI, F8>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
-                               SmallMap{0, n_big, tiles_m, tiles_n, 0}, live, pieces, cus, alpha,
-                               oscale, stream);
+  return launch_small<EPI, F8, SP>(A, lda, W, ldw, bias, C, ldc, M, K, part, part_bytes,
+                                   SmallMap{0, n_big, tiles_m, tiles_n, 0}, live, pieces, cus,
+                                   alpha, oscale, stream);
 }
 
 template <bool F8>
