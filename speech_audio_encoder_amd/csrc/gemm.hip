@@ -23,9 +23,9 @@
 //    64-wide K slices of whole 128-byte lines.  The stream of steps runs on
 //    across the workgroup's tiles.
 //  * gemm_small_kernel (+ gemm_small_reduce) -- the tiles left after the
-//    last full round, and the whole product when it has fewer 256 x 256
-//    tiles than CUs (few rows), as 64 x 64 pieces, split along K only when
-//    even these leave CUs idle.
+//    last full round, as 64 x 64 pieces, and the whole product when it has
+//    fewer 256 x 256 tiles than CUs (few rows), as 64 x 64 or 128 x 64
+//    pieces, split along K only when even these leave CUs idle.
 //
 // Each lane ends up owning one output row and runs of four consecutive
 // columns: the epilogue adds bias / residual / GELU in registers and stores
@@ -653,9 +653,9 @@ __global__ __launch_bounds__(512, 1) void gemm_big_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-// ------------------------------------------------- 64 x 64 pieces (few rows)
+// ------------------------------------------------- pieces (few rows, tails)
 // Whole products with fewer 256 x 256 tiles than CUs (a 30-second clip: 375
-// rows) are cut into 64 x 64 pieces.  That gives every CU work without
+// rows) are cut into 64 x 64 (or 128 x 64, see launch_t) pieces.  That gives every CU work without
 // splitting K for most shapes, so no partial sums are written and no
 // reduction runs.  A workgroup of four wavefronts (32 x 32 outputs each, one
 // accumulator) moves 64-wide K slices of A and W (whole 128-byte lines) into
