@@ -909,7 +909,14 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   const int tiles_n = N / BIG;
   const int tiles = tiles_m * tiles_n;
   const int cus = num_cus();
-  if (tiles < cus) {
+  // A remainder of more than half a round of tiles runs as one more, partial
+  // round of the persistent kernel: as 64 x 64 pieces (about a quarter of a
+  // tile's time each at two per CU) it would take longer than one tile
+  // (10-minute recording, M = 7,500: QKV's 194 remaining tiles and the 150
+  // tiles of the attention output and FFN-down products).  bf16 only, as
+  // measured.
+  const bool partial_round = !F8 && (tiles % cus) * 2 > cus;
+  if (tiles < cus && !partial_round) {
     // Fewer big tiles than CUs: the whole product as pieces.  Pieces of 128
     // rows move 43 instead of 32 flops per byte through the CU's load path
     // but hold one workgroup per CU (96 KB of LDS) instead of two, whose
@@ -932,10 +939,11 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
                                      SmallMap{1, 0, 0, 0, N / SP}, pieces, pieces, cus, alpha,
                                      oscale, stream);
   }
-  // Full rounds go to the persistent kernel, the remainder to 64 x 64 pieces.
-  const int n_big = (tiles / cus) * cus;
+  // Full rounds (and a partial last one) go to the persistent kernel, the
+  // remainder to 64 x 64 pieces.
+  const int n_big = partial_round ? tiles : (tiles / cus) * cus;
   if constexpr (EPI == Epilogue::kBiasResidualF32 && !F8) {
-    if (n_big == cus)   // one round: every CU holds exactly one tile
+    if (n_big <= cus)   // one round: every CU holds at most one tile
       gemm_big_kernel<EPI, F8, true><<<dim3(cus), dim3(512), 0, stream>>>(
           A, lda, W, ldw, bias, C, ldc, M, K, tiles_m, tiles_n, n_big, alpha, oscale);
     else
