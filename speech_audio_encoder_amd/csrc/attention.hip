@@ -94,10 +94,18 @@ __device__ __forceinline__ void lds_loads_wait() {
 // HW: head width, 128 (the encoder) or 80 (the timestamp adapter).  Heads
 // are packed at their own width in the qkv rows; in LDS every key row keeps
 // 16 chunks of 8 dims, of which a narrower head fills the first HW / 8.
+// Key splits (fixed reference only): with splits > 1 the keys of a clip are
+// cut into runs of t_split 64-key tiles, item i of the launch takes run
+// i % splits of work item i / splits, and instead of the normalised output
+// it writes its unnormalised sums O (fp32, [split][row][head][HW]) and row
+// sums l ([split][row][head]) to opart / lpart; against a fixed reference
+// the partial sums of the runs add up to those of the whole clip
+// (attention_combine_kernel).
 template <bool kFixedRef, int HW>
 __global__ __launch_bounds__(64 * NW) void attention_kernel(
     const bf16_t* __restrict__ qkv, const int4* __restrict__ tile_info, int n_tiles,
-    int n_items, void* __restrict__ out, float out_scale, int hd) {
+    int n_items, void* __restrict__ out, float out_scale, int hd, int splits, int t_split,
+    float* __restrict__ opart, float* __restrict__ lpart, int64_t part_rows) {
   static_assert(HW % 16 == 0 && HW <= DH, "head width");
   constexpr int KS = HW / 16;          // 16-dim steps of the scores
   constexpr int NDB = (HW + 31) / 32;  // 32-dim blocks of the output
@@ -111,14 +119,31 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   const int per = gridDim.x >> 3;
   const int item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   if (item >= n_items) return;
-  const int h = item / n_tiles;
-  const int tile = item - h * n_tiles;
+  const int split = item % splits;
+  const int h = item / splits / n_tiles;
+  const int tile = item / splits - h * n_tiles;
   const int4 ti = tile_info[tile];   // first row, length, first query
   const int64_t s0 = ti.x;
-  const int len = ti.y;
+  const int len = ti.y;              // queries (and keys of the whole clip)
   const int q0 = ti.z;
-  const int nkt = (len + KT - 1) / KT;   // 64-key tiles
-  const int nku = 2 * nkt;               // 32-key units
+  const int n_heads = hd / HW;
+  // keys of this run: [kfirst, kfirst + klen) of the clip
+  const int kfirst = split * t_split * KT;
+  const int klen = splits > 1 ? min(len - kfirst, t_split * KT) : len;
+  if (klen <= 0) {
+    // an empty run (a clip shorter than the longest): zero partial sums
+    for (int e = threadIdx.x; e < QTILE * (HW + 1); e += 64 * NW) {
+      const int r = e / (HW + 1), d = e - r * (HW + 1);
+      const int q = q0 + r;
+      if (q >= len) continue;
+      const int64_t pr = ((int64_t)split * part_rows + s0 + q) * n_heads + h;
+      if (d < HW) opart[pr * HW + d] = 0.f;
+      else lpart[pr] = 0.f;
+    }
+    return;
+  }
+  const int nkt = (klen + KT - 1) / KT;   // 64-key tiles
+  const int nku = 2 * nkt;                // 32-key units
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -161,8 +186,10 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     const int key = (wave * VP + t) * 4 + (lane >> 4);
     vchunk[t] = (uint32_t)(in_head((lane & 15) ^ (4 * (key & 3))) * 16);
   }
-  const char* kbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + hd + h * HW);
-  const char* vbase = reinterpret_cast<const char*>(qkv + s0 * (3 * hd) + 2 * hd + h * HW);
+  const char* kbase =
+      reinterpret_cast<const char*>(qkv + (s0 + kfirst) * (3 * hd) + hd + h * HW);
+  const char* vbase =
+      reinterpret_cast<const char*>(qkv + (s0 + kfirst) * (3 * hd) + 2 * hd + h * HW);
   const uint32_t k_lds = (uint32_t)(uintptr_t)(lds_void*)&sK[0][0] + wave * KP * 1024;
   const uint32_t v_lds = (uint32_t)(uintptr_t)(lds_void*)&sV[0][0] + wave * VP * 1024;
   // K unit u into ring slot u % 4.  Units past the clip's last one re-load
@@ -173,14 +200,14 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 #pragma unroll
     for (int t = 0; t < KP; ++t) dma16(g + koff[t], l + t * 1024);
   };
-  // V tile j (keys 64 j ..) into buffer j % 2.  Keys past the clip take the
-  // clip's last row: their probability is exactly 0, and a row of the clip is
+  // V tile j (keys 64 j ..) into buffer j % 2.  Keys past the run take the
+  // run's last row: their probability is exactly 0, and a row of the clip is
   // finite whatever lies beyond it.
   auto issue_v = [&](int j) __attribute__((always_inline)) {
     const uint32_t l = v_lds + (j & 1) * VT_BYTES;
 #pragma unroll
     for (int t = 0; t < VP; ++t) {
-      const int key = min(j * KT + (wave * VP + t) * 4 + (lane >> 4), len - 1);
+      const int key = min(j * KT + (wave * VP + t) * 4 + (lane >> 4), klen - 1);
       dma16(vbase + (int64_t)key * (3 * hd * 2) + vchunk[t], l + t * 1024);
     }
   };
@@ -239,13 +266,13 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   // by more than 8.
   auto decide = [&](f32x16 (&S)[QB], int u) __attribute__((always_inline)) {
     const int kv0 = u * KU;
-    if (kv0 + KU > len) {
+    if (kv0 + KU > klen) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kv0 + 8 * (v >> 2) + 4 * lhi + (v & 3);
-          S[qb][v] = key < len ? S[qb][v] : -INFINITY;
+          S[qb][v] = key < klen ? S[qb][v] : -INFINITY;
         }
     }
     if constexpr (!kFixedRef) {
@@ -357,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     lds_loads_wait();
     __syncthreads();
     if constexpr (kFixedRef) decide(SA, 2 * j);
-    const bool second = j * KT + KU < len;
+    const bool second = j * KT + KU < klen;
     if (second) qk(SB, 2 * j + 1);
     expv(SA, j, 0);
     if (second) {
@@ -371,6 +398,21 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
     const int q = q0 + wave * QPW + qb * 32 + l32;
     if (q >= len) continue;
+    if (splits > 1) {
+      const int64_t pr = ((int64_t)split * part_rows + s0 + q) * n_heads + h;
+      float* orow = opart + pr * HW;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * lhi;
+          if (d >= HW) continue;
+          *reinterpret_cast<float4*>(orow + d) = make_float4(
+              O[db][qb][4 * g], O[db][qb][4 * g + 1], O[db][qb][4 * g + 2], O[db][qb][4 * g + 3]);
+        }
+      if (lhi == 0) lpart[pr] = lt;
+      continue;
+    }
     const float inv = 1.0f / lt;
     if (out_scale > 0.0f) {
       // E4M3 codes of the output times out_scale (the FP8 output projection's input)
@@ -403,6 +445,57 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
   }
 }
 
+// Output of a key-split launch: for every query row and head, the partial
+// sums of the runs added in run order, O / l, stored as the unsplit kernel
+// stores it.  One thread per 4 dims of a query row and head (every run's
+// loads issued before the first add); blockIdx.y = head * n_tiles + tile.
+constexpr int MAX_SPLITS = 8;
+template <int HW>
+__global__ __launch_bounds__(256) void attention_combine_kernel(
+    const int4* __restrict__ tile_info, int n_tiles, int splits,
+    const float* __restrict__ opart, const float* __restrict__ lpart, int64_t part_rows,
+    void* __restrict__ out, float out_scale, int hd) {
+  constexpr int V4 = HW / 4;   // 4-dim groups of a head row
+  const int h = blockIdx.y / n_tiles;
+  const int tile = blockIdx.y - h * n_tiles;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= QTILE * V4) return;
+  const int4 ti = tile_info[tile];
+  const int r = e / V4, c = e - r * V4;
+  const int q = ti.z + r;
+  if (q >= ti.y) return;
+  const int64_t row = ti.x + q;
+  const int n_heads = hd / HW;
+  float4 t[MAX_SPLITS];
+  float lv[MAX_SPLITS];
+#pragma unroll
+  for (int sp = 0; sp < MAX_SPLITS; ++sp) {
+    if (sp < splits) {
+      const int64_t pr = ((int64_t)sp * part_rows + row) * n_heads + h;
+      t[sp] = *reinterpret_cast<const float4*>(opart + pr * HW + 4 * c);
+      lv[sp] = lpart[pr];
+    }
+  }
+  float4 o = t[0];
+  float l = lv[0];
+#pragma unroll
+  for (int sp = 1; sp < MAX_SPLITS; ++sp) {
+    if (sp < splits) {
+      o.x += t[sp].x; o.y += t[sp].y; o.z += t[sp].z; o.w += t[sp].w;
+      l += lv[sp];
+    }
+  }
+  const float inv = 1.0f / l;
+  if (out_scale > 0.0f) {
+    const float sc = inv * out_scale;
+    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(out) + row * hd + h * HW + 4 * c) =
+        pack_fp8x4(o.x * sc, o.y * sc, o.z * sc, o.w * sc);
+  } else {
+    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(out) + row * hd + h * HW + 4 * c) =
+        make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
+  }
+}
+
 }  // namespace
 
 bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g,
@@ -425,18 +518,58 @@ bool attention_fixed_ref_ok(const float* q_g, const float* q_b, const float* k_g
 
 hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_tiles,
                             int n_heads, int head_dim, bool fixed_ref, void* out, float out_scale,
-                            hipStream_t stream) {
+                            int max_len, int64_t rows, float* opart, size_t opart_bytes,
+                            float* lpart, size_t lpart_bytes, hipStream_t stream) {
   if (n_tiles == 0) return hipSuccess;
   if (n_heads < 1 || (head_dim != DH && head_dim != 80) || (out_scale > 0.0f && head_dim != DH))
     return hipErrorInvalidValue;
   const int n_items = n_tiles * n_heads;
   const int hd = n_heads * head_dim;
-  const int grid = (n_items + 7) / 8 * 8;
+  // Key runs.  Two workgroups of this kernel fit a CU, so the work items run
+  // in waves of 2 x CUs; for long sequences a launch whose items fill one
+  // wave and a small part of the next (a 10-minute recording: 590 items for
+  // 512 slots) pays a second full item time for that part.  Cutting each
+  // item's keys into `splits` runs and adding the runs' partial sums in a
+  // second pass shortens the items; the cut is taken when the modelled time
+  // (waves x key tiles per run, plus the partial sums written and read back
+  // at the cost of about one key tile per 8 MB) drops by a tenth.  Only long
+  // sequences (the fixed costs of a workgroup are measured to dominate short
+  // ones) and only with a fixed softmax reference, where runs add directly.
+  int splits = 1, t_split = 0;
+  const int max_kt = (max_len + KT - 1) / KT;
+  if (fixed_ref && opart && lpart && max_kt >= 32) {
+    const int64_t slots = 2 * (int64_t)num_cus();
+    auto waves = [&](int64_t units) { return (units + slots - 1) / slots; };
+    const double base = (double)waves(n_items) * max_kt;
+    double best = base;
+    for (int sp = 2; sp <= MAX_SPLITS; ++sp) {
+      const size_t obytes = (size_t)sp * rows * n_heads * head_dim * sizeof(float);
+      const size_t lbytes = (size_t)sp * rows * n_heads * sizeof(float);
+      if (obytes > opart_bytes || lbytes > lpart_bytes) break;
+      const int per = (max_kt + sp - 1) / sp;
+      const double cost = (double)waves((int64_t)n_items * sp) * per + 2.0 * obytes / 8e6;
+      if (cost < best) {
+        best = cost;
+        splits = sp;
+        t_split = per;
+      }
+    }
+    if (best > 0.9 * base) splits = 1;
+  }
+  const int launch_items = n_items * splits;
+  const int grid = (launch_items + 7) / 8 * 8;
   auto kernel = head_dim == DH
                     ? (fixed_ref ? attention_kernel<true, DH> : attention_kernel<false, DH>)
                     : (fixed_ref ? attention_kernel<true, 80> : attention_kernel<false, 80>);
   kernel<<<dim3(grid), dim3(64 * NW), 0, stream>>>(
-      qkv, reinterpret_cast<const int4*>(tile_info), n_tiles, n_items, out, out_scale, hd);
+      qkv, reinterpret_cast<const int4*>(tile_info), n_tiles, launch_items, out, out_scale, hd,
+      splits, t_split, opart, lpart, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  auto combine = head_dim == DH ? attention_combine_kernel<DH> : attention_combine_kernel<80>;
+  combine<<<dim3((QTILE * (head_dim / 4) + 255) / 256, n_items), dim3(256), 0, stream>>>(
+      reinterpret_cast<const int4*>(tile_info), n_tiles, splits, opart, lpart, rows, out,
+      out_scale, hd);
   return hipGetLastError();
 }
 

@@ -852,19 +852,6 @@ __global__ __launch_bounds__(256) void gemm_small_reduce(const float* __restrict
                   s.y, s.z, s.w);
 }
 
-int g_num_cus = 0;
-
-int num_cus() {
-  if (g_num_cus == 0) {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-      g_num_cus = n;
-    else
-      g_num_cus = 256;
-  }
-  return g_num_cus;
-}
 
 // Split K (a divisor of K / 64) only while the pieces that hold rows still
 // fit one workgroup per CU and their partial sums fit `part`.
@@ -1018,6 +1005,19 @@ hipError_t launch_split_n(Epilogue epi, const bf16_t* A, int64_t lda, const bf16
 }
 
 }  // namespace
+
+int num_cus() {
+  static int n_cus = 0;
+  if (n_cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      n_cus = n;
+    else
+      n_cus = 256;
+  }
+  return n_cus;
+}
 
 hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,

@@ -61,6 +61,9 @@ enum class Epilogue {
 
 constexpr size_t GEMM_PARTIAL_BYTES = (size_t)2 * 512 * 128 * 128 * sizeof(float);
 
+// Compute units of the current device (queried once).
+int num_cus();
+
 hipError_t launch_gemm(Epilogue epi, const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw,
                        const float* bias, void* C, int64_t ldc, int64_t M, int N, int K,
                        float* part, size_t part_bytes, hipStream_t stream);
@@ -149,9 +152,15 @@ hipError_t launch_to_f32(const void* src, bool src_is_bf16, float* dst, int64_t 
 // element in the same layout.
 // k is read in whole 64-key tiles past a clip's end (those keys are masked),
 // so qkv must have 63 readable rows after its last one.
+// max_len: the longest sequence among the tiles; rows: the rows of qkv.
+// With a fixed reference and long sequences whose work items would leave most
+// of a last wave of workgroups idle, the keys are cut into runs whose partial
+// sums go to opart / lpart (scratch of opart_bytes / lpart_bytes, free during
+// the call; NULL never cuts) and are added by a second kernel.
 hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_tiles,
                             int n_heads, int head_dim, bool fixed_ref, void* out, float out_scale,
-                            hipStream_t stream);
+                            int max_len, int64_t rows, float* opart, size_t opart_bytes,
+                            float* lpart, size_t lpart_bytes, hipStream_t stream);
 // fixed_ref may be true only when |q . k| * log2(e) / sqrt(head_dim) <= 64 for
 // every query and key (softmax against a fixed reference instead of a
 // running maximum); attention_fixed_ref_ok decides it from the QK-norm

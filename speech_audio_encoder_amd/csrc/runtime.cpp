@@ -277,6 +277,13 @@ void seq_tiles(const std::vector<int32_t>& cu, std::vector<int32_t>* tile_info) 
   }
 }
 
+// Longest sequence among the tiles (records of first row, length, first query).
+int max_tile_len(const std::vector<int32_t>& tile_info) {
+  int m = 0;
+  for (size_t i = 1; i < tile_info.size(); i += 4) m = std::max(m, (int)tile_info[i]);
+  return m;
+}
+
 // Workspace layout for `rows` packed positions (offsets in bytes).
 struct Layout {
   size_t x, a, qkv, o, u, total;
@@ -840,7 +847,8 @@ int run_adapter(enc_ctx* ctx, const Plan& p, const bf16_t* h, const int32_t* d_t
                launch_qknorm_rope(qkv, d_ti, n_tiles, CTC_HEADS, CTC_DH, L.q_g, L.q_b, L.k_g,
                                   L.k_b, W.rope_cos, W.rope_sin, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_attention(qkv, d_ti, n_tiles, CTC_HEADS, CTC_DH,
-                                           L.attn_fixed_ref, o, 0.0f, stream));
+                                           L.attn_fixed_ref, o, 0.0f, 0, R, nullptr, 0, nullptr,
+                                           0, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_gemm(Epilogue::kBiasResidualF32, o, D, L.w_o, D, L.b_o, x, D, R,
                                       D, D, ctx->gemm_part, GEMM_PARTIAL_BYTES, stream));
     ENC_LAUNCH(ENC_K_CTC, launch_layernorm(x, L.ln2_g, L.ln2_b, a, R, stream));
@@ -952,6 +960,7 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
   const int32_t* d_outsrc = overlap ? dev[5] : nullptr;
   const int64_t R = p.vrows;
   const int n_tiles = (int)p.tile_info.size() / 4;
+  const int max_len = max_tile_len(p.tile_info);
 
   // Stacked features of the clips (packed by clip); with overlapping windows
   // they are gathered into window order (context rows repeated) first.
@@ -989,8 +998,10 @@ int run_forward(enc_ctx* ctx, const float* audio, const int64_t* lengths, int32_
                launch_qknorm_rope(qkv, d_ti, n_tiles, H, DH, Lw.q_g, Lw.q_b, Lw.k_g, Lw.k_b,
                                   ctx->rope_cos, ctx->rope_sin, stream));
     ENC_LAUNCH(ENC_K_ATTENTION,
-               launch_attention(qkv, d_ti, n_tiles, H, DH,
-                                Lw.attn_fixed_ref, o, fp8 ? Lw.r_x[1] : 0.0f, stream));
+               launch_attention(qkv, d_ti, n_tiles, H, DH, Lw.attn_fixed_ref, o,
+                                fp8 ? Lw.r_x[1] : 0.0f, max_len, R, (float*)u,
+                                (size_t)R * std::max(FF, DIN) * 2, (float*)a, (size_t)R * D * 2,
+                                stream));
     if (fp8) {
       ENC_LAUNCH(ENC_K_GEMM_O,
                  launch_gemm_fp8(Epilogue::kBiasResidualF32, o8, D, Lw.q8[1], D, Lw.alpha[1],
