@@ -22,6 +22,10 @@
 // tile through the transposing LDS read (ds_read_b64_tr_b16), whose addresses
 // also pick the keys in the order of the probabilities' accumulator layout.
 //
+// Long sequences whose work items would leave most of a last wave of
+// workgroups idle cut each item's keys into runs and add the runs' partial
+// sums in attention_combine_kernel (see launch_attention).
+//
 // Pipeline: K goes global -> LDS in 32-key units (a ring of four) and V in
 // 64-key tiles (two buffers) by direct loads (global_load_lds, 16 bytes per
 // lane, swizzle applied on the global side), one barrier per 64 keys.  The
