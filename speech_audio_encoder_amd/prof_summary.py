@@ -149,7 +149,10 @@ def class_launches(rows):
             continue
         e = per.setdefault(cls, [[], 0])
         e[0].append(r)
-        if cls != prev or cls in SINGLE_KERNEL:
+        # the kernel that adds key runs' partial sums belongs to the
+        # attention launch before it
+        cont = cls == prev and short_name(r["Kernel_Name"]).startswith("attention_combine")
+        if cls != prev or (cls in SINGLE_KERNEL and not cont):
             e[1] += 1
         prev = cls
     return per

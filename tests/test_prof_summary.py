@@ -122,3 +122,15 @@ def test_counters_report_sums_per_launch_and_averages_latency(tmp_path):
     row = [ln for ln in text if ln.startswith("| layernorm")][0]
     cells = [c.strip() for c in row.strip("|").split("|")]
     assert cells[1] == "2" and cells[2] == "4.0" and cells[3] == "2" and cells[4] == "200"
+
+
+def test_attention_key_runs_count_as_one_launch():
+    # a key-split attention launch is the attention kernel followed by the
+    # kernel that adds the runs' partial sums
+    layer_split = [k("layernorm_kernel"), gemm(0), k("qknorm_rope_kernel"),
+                   k("attention_kernel<true, 128>"), k("attention_combine_kernel<128>"), gemm(2),
+                   k("layernorm_kernel"), gemm(1), gemm(2)]
+    rows = [k("logmel_kernel<true>"), gemm(3)] + layer_split * 3
+    per = prof_summary.class_launches(rows)
+    assert per["attention"][1] == 3 and len(per["attention"][0]) == 6
+    assert per["layernorm"][1] == 6
