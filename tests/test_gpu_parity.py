@@ -313,6 +313,28 @@ def test_forward_ragged_perturbed_weights(torch_mod, ctx_for):
             check_embeddings(got[b, :p], ref, f"ragged clip {b} (P={p})")
 
 
+def test_forward_key_runs_ragged(torch_mod, ctx_for):
+    # A clip of 2,100 positions (33 key tiles) with short clips: 210 work
+    # items fill less than one wave of attention workgroups, so the launcher
+    # cuts the keys into two runs and adds their partial sums; the short
+    # clips' second runs are empty (zero partial sums).  Same inputs through
+    # the oracle, clip by clip.
+    torch = torch_mod
+    lengths = [400 + 16_799 * 160, 480_000, 16_000, 0]
+    audio, lengths = workloads.custom_audio(lengths, seed=43)
+    assert oracle.position_count(oracle.frame_count(lengths[0])) == 2_100
+    w = get_weights("perturbed")
+    got = run_forward(torch, ctx_for("perturbed", 2, "f32"), audio, lengths)
+    again = run_forward(torch, ctx_for("perturbed", 2, "f32"), audio, lengths)
+    np.testing.assert_array_equal(got, again)
+    for b, n in enumerate(lengths):
+        p = oracle.position_count(oracle.frame_count(n))
+        assert np.all(got[b, p:] == 0.0), f"clip {b}: padded rows not zero"
+        if p:
+            ref = oracle.encode(audio[b, :n], w)
+            check_embeddings(got[b, :p], ref, f"key-run clip {b} (P={p})")
+
+
 def test_forward_large_qk_gains_running_max(torch_mod, ctx_for):
     # QK-norm gains large enough that the scores need a running softmax
     # maximum (the bounded fast path is not allowed); clips spanning several
