@@ -451,14 +451,14 @@ __global__ __launch_bounds__(64 * NW) void attention_kernel(
 
 // Output of a key-split launch: for every query row and head, the partial
 // sums of the runs added in run order, O / l, stored as the unsplit kernel
-// stores it.  One thread per 4 dims of a query row and head (every run's
+// stores it (bf16).  One thread per 4 dims of a query row and head (every run's
 // loads issued before the first add); blockIdx.y = head * n_tiles + tile.
 constexpr int MAX_SPLITS = 8;
 template <int HW>
 __global__ __launch_bounds__(256) void attention_combine_kernel(
     const int4* __restrict__ tile_info, int n_tiles, int splits,
     const float* __restrict__ opart, const float* __restrict__ lpart, int64_t part_rows,
-    void* __restrict__ out, float out_scale, int hd) {
+    bf16_t* __restrict__ out, int hd) {
   constexpr int V4 = HW / 4;   // 4-dim groups of a head row
   const int h = blockIdx.y / n_tiles;
   const int tile = blockIdx.y - h * n_tiles;
@@ -490,14 +490,8 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(
     }
   }
   const float inv = 1.0f / l;
-  if (out_scale > 0.0f) {
-    const float sc = inv * out_scale;
-    *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(out) + row * hd + h * HW + 4 * c) =
-        pack_fp8x4(o.x * sc, o.y * sc, o.z * sc, o.w * sc);
-  } else {
-    *reinterpret_cast<uint2*>(reinterpret_cast<bf16_t*>(out) + row * hd + h * HW + 4 * c) =
-        make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
-  }
+  *reinterpret_cast<uint2*>(out + row * hd + h * HW + 4 * c) =
+      make_uint2(pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv));
 }
 
 }  // namespace
@@ -538,10 +532,11 @@ hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_t
   // (waves x key tiles per run, plus the partial sums written and read back
   // at the cost of about one key tile per 8 MB) drops by a tenth.  Only long
   // sequences (the fixed costs of a workgroup are measured to dominate short
-  // ones) and only with a fixed softmax reference, where runs add directly.
+  // ones) and only with a fixed softmax reference, where runs add directly,
+  // and a bf16 output (the E4M3 output of the FP8 variant keeps whole items).
   int splits = 1, t_split = 0;
   const int max_kt = (max_len + KT - 1) / KT;
-  if (fixed_ref && opart && lpart && max_kt >= 32) {
+  if (fixed_ref && out_scale <= 0.0f && opart && lpart && max_kt >= 32) {
     const int64_t slots = 2 * (int64_t)num_cus();
     auto waves = [&](int64_t units) { return (units + slots - 1) / slots; };
     const double base = (double)waves(n_items) * max_kt;
@@ -572,8 +567,8 @@ hipError_t launch_attention(const bf16_t* qkv, const int32_t* tile_info, int n_t
   if (e != hipSuccess || splits == 1) return e;
   auto combine = head_dim == DH ? attention_combine_kernel<DH> : attention_combine_kernel<80>;
   combine<<<dim3((QTILE * (head_dim / 4) + 255) / 256, n_items), dim3(256), 0, stream>>>(
-      reinterpret_cast<const int4*>(tile_info), n_tiles, splits, opart, lpart, rows, out,
-      out_scale, hd);
+      reinterpret_cast<const int4*>(tile_info), n_tiles, splits, opart, lpart, rows,
+      reinterpret_cast<bf16_t*>(out), hd);
   return hipGetLastError();
 }
 
