@@ -896,13 +896,16 @@ hipError_t launch_t(const bf16_t* A, int64_t lda, const bf16_t* W, int64_t ldw, 
   const int tiles_n = N / BIG;
   const int tiles = tiles_m * tiles_n;
   const int cus = num_cus();
-  // A remainder of more than half a round of tiles runs as one more, partial
-  // round of the persistent kernel: as 64 x 64 pieces (about a quarter of a
-  // tile's time each at two per CU) it would take longer than one tile
-  // (10-minute recording, M = 7,500: QKV's 194 remaining tiles and the 150
-  // tiles of the attention output and FFN-down products).  bf16 only, as
-  // measured.
-  const bool partial_round = !F8 && (tiles % cus) * 2 > cus;
+  // A remainder of more than a quarter of a round of tiles runs as one more,
+  // partial round of the persistent kernel: as 64 x 64 pieces it takes
+  // longer than one tile.  Measured (same box, alternating runs): the
+  // 10-minute recording's QKV (194 remaining tiles) and attention output and
+  // FFN-down products (150 tiles, one partial round), 27.90 -> 25.05 ms per
+  // step; in the one-hour recording's 30-s chunks the remainders of 80
+  // (QKV), 112 (O, FFN down) and 192 (FFN up) tiles, 72.09 -> 70.90 ms with
+  // a half-round threshold and 69.77 -> 69.10 ms going from a third to a
+  // quarter.  bf16 only, as measured.
+  const bool partial_round = !F8 && (tiles % cus) * 4 > cus;
   if (tiles < cus && !partial_round) {
     // Fewer big tiles than CUs: the whole product as pieces.  Pieces of 128
     // rows move 43 instead of 32 flops per byte through the CU's load path
